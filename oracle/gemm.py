@@ -1,0 +1,151 @@
+"""The plain GEMM the hot path must reproduce, in float64 -- test infrastructure.
+
+What is computed (all in float64 on exactly decoded inputs):
+
+* Contraction.  ``y[i, j] = sum_k a[i, k] * b[k, j]`` for row-major
+  ``a[M, K]`` and ``b[K, N]``: the naive triple loop that the DeepGEMM page
+  (section 3.2, 朴素版的性能基线) keeps as the golden reference, with the
+  element ``A[m*K + k] * B[k*N + n]`` indexing of that section.  numpy's
+  float64 matmul serves as the summation step; its rounding error (about
+  ``K * 2**-53`` relative to ``sum_k |a||b|``) is eight orders of magnitude
+  below the tolerances it is used against.
+* Bias.  A linear layer is a GEMM followed by a bias add (GEMM compute-cost
+  page, section 2.1, the note on nn.Linear; the formula ``Y = X W + b`` of its
+  section 3.1): ``y[i, j] += bias[j]``, broadcast over rows.
+* Activation.  Fused epilogue order is "add bias, apply activation, write
+  back" (GEMM compute-cost page, section 5.1).  The activation is the tanh
+  form of GeLU: ``0.5 * y * (1 + tanh(sqrt(2/pi) * (y + 0.044715 * y**3)))``.
+* FP8 block scales.  FP8 inputs carry one fp32 scale per group (DeepGEMM page,
+  section 2.4): one per (row, 128-wide K group) of A and one per 128 x 128
+  block of B.  Each element is dequantised as ``decode(q) * scale`` before the
+  same contraction; both factors are exact in float64, so the dequantised
+  operands are exact.
+* FLOP count.  A multiply-add counts as two operations, so an ``[M,K]x[K,N]``
+  product costs ``2*M*N*K`` (GEMM compute-cost page, section 3.1); the bias is
+  not counted.
+* Error metric.  ``err[i, j] = |c - y| / D[i, j]`` with
+  ``D = sum_k |a[i,k]| |b[k,j]| + |bias[j]|``; the check passes when
+  ``max err <= tol``.  ``D == 0`` gives 0 when ``c == y`` and infinity
+  otherwise; a NaN in ``c`` gives infinity.
+"""
+
+import math
+
+import numpy as np
+
+from .formats import bf16_decode, e4m3_decode
+
+EPI_NONE = 0
+EPI_BIAS = 1
+EPI_BIAS_GELU_TANH = 2
+
+FP8_GROUP = 128  # K-group width of the A scales; B scales cover 128 x 128 blocks
+
+GELU_C = math.sqrt(2.0 / math.pi)
+GELU_A = 0.044715
+
+
+def gelu_tanh(y):
+    """tanh-approximation GeLU in float64."""
+    y = np.asarray(y, dtype=np.float64)
+    return 0.5 * y * (1.0 + np.tanh(GELU_C * (y + GELU_A * y * y * y)))
+
+
+def gemm_f64(a, b, bias=None, epilogue=EPI_NONE):
+    """Reference result and tolerance denominators for ``epi(a @ b + bias)``.
+
+    a: float64 [M, K]; b: float64 [K, N]; bias: float64 [N] or None.
+    Returns (y, D): y float64 [M, N] is the exact-input result (no output
+    rounding); D float64 [M, N] is ``sum_k |a||b| (+ |bias|)``.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shape mismatch: a{a.shape} b{b.shape}")
+    M, N = a.shape[0], b.shape[1]
+    if a.shape[1] == 0:
+        y = np.zeros((M, N))
+        d = np.zeros((M, N))
+    else:
+        y = a @ b
+        d = np.abs(a) @ np.abs(b)
+    if epilogue in (EPI_BIAS, EPI_BIAS_GELU_TANH):
+        if bias is None:
+            raise ValueError("bias epilogue without bias")
+        bias = np.asarray(bias, dtype=np.float64).reshape(1, N)
+        y = y + bias
+        d = d + np.abs(bias)
+    elif epilogue != EPI_NONE:
+        raise ValueError(f"unknown epilogue {epilogue}")
+    if epilogue == EPI_BIAS_GELU_TANH:
+        y = gelu_tanh(y)
+    return y, d
+
+
+def gemm_bf16_bits(a_bits, b_bits, bias_bits=None, epilogue=EPI_NONE):
+    """Oracle for the bf16 path on raw uint16 codes (row-major, any 2-D view)."""
+    a = bf16_decode(a_bits)
+    b = bf16_decode(b_bits)
+    bias = None if bias_bits is None else bf16_decode(bias_bits)
+    return gemm_f64(a, b, bias, epilogue)
+
+
+def dequant_fp8_a(qa_bits, sa):
+    """A[i, k] = decode(qa[i, k]) * sA[i, k // 128]  (exact in float64)."""
+    qa = e4m3_decode(qa_bits)
+    sa = np.asarray(sa, dtype=np.float32).astype(np.float64)
+    M, K = qa.shape
+    g = np.arange(K) // FP8_GROUP
+    if sa.shape != (M, (K + FP8_GROUP - 1) // FP8_GROUP):
+        raise ValueError(f"sA shape {sa.shape} for A {qa.shape}")
+    return qa * sa[:, g]
+
+
+def dequant_fp8_b(qb_bits, sb):
+    """B[k, j] = decode(qb[k, j]) * sB[k // 128, j // 128]  (exact in float64)."""
+    qb = e4m3_decode(qb_bits)
+    sb = np.asarray(sb, dtype=np.float32).astype(np.float64)
+    K, N = qb.shape
+    gk = np.arange(K) // FP8_GROUP
+    gn = np.arange(N) // FP8_GROUP
+    if sb.shape != ((K + FP8_GROUP - 1) // FP8_GROUP, (N + FP8_GROUP - 1) // FP8_GROUP):
+        raise ValueError(f"sB shape {sb.shape} for B {qb.shape}")
+    return qb * sb[gk][:, gn]
+
+
+def gemm_fp8_blockscaled_bits(qa_bits, sa, qb_bits, sb):
+    """Oracle for the FP8 block-scaled path: dequantise, then contract."""
+    return gemm_f64(dequant_fp8_a(qa_bits, sa), dequant_fp8_b(qb_bits, sb))
+
+
+def flop_count(M, N, K):
+    """2*M*N*K: one multiply-add is two floating-point operations."""
+    return 2 * int(M) * int(N) * int(K)
+
+
+def error_ratio(c, y, d):
+    """Elementwise ``|c - y| / D`` with the zero-denominator and NaN rules."""
+    c = np.asarray(c, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    d = np.asarray(d, dtype=np.float64)
+    diff = np.abs(c - y)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(d > 0, diff / np.where(d > 0, d, 1.0), np.where(diff == 0, 0.0, np.inf))
+    err = np.where(np.isnan(c) | np.isnan(diff), np.inf, err)
+    return err
+
+
+def compare(c, y, d, tol):
+    """Summary of the check: max / mean error ratio, its position, pass flag."""
+    err = error_ratio(c, y, d)
+    if err.size == 0:
+        return {"max_err": 0.0, "mean_err": 0.0, "argmax": None, "ok": True, "tol": tol}
+    idx = int(np.argmax(err))
+    mx = float(err.flat[idx])
+    return {
+        "max_err": mx,
+        "mean_err": float(np.mean(np.where(np.isfinite(err), err, 0.0))),
+        "argmax": tuple(int(v) for v in np.unravel_index(idx, err.shape)),
+        "ok": bool(mx <= tol),
+        "tol": tol,
+    }

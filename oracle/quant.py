@@ -1,0 +1,61 @@
+"""Per-group FP8 quantiser -- test infrastructure.
+
+The DeepGEMM page (section 2.4, low-precision numerics) describes scaling a
+row or a small block of data by one factor so that it fits the narrow FP8
+range, with groups of about 128 elements or a small matrix block.  The
+groups here are the ones the GEMM consumes: one scale per (row, 128-wide K
+group) of the activation matrix A and one per 128 x 128 block of the weight
+matrix B.  The readings used for the points the page leaves open:
+
+* scale ``s = amax / 448`` in fp32 (round to nearest), where ``amax`` is the
+  largest magnitude over the in-range elements of the group; a group that is
+  all zero gets ``s = 1``;
+* code ``q = e4m3(clamp(x / s, -448, 448))`` with ``x / s`` in fp32 and the
+  cast rounding to nearest, ties to even (saturating before the cast);
+* dequantised value ``decode(q) * s``;
+* groups at ragged edges cover only the elements inside the matrix.
+"""
+
+import numpy as np
+
+from .formats import E4M3_MAX, e4m3_encode_rne
+
+GROUP = 128
+
+
+def _quantise_group(x):
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    s = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(E4M3_MAX))
+    scaled = (x / s).astype(np.float32)
+    scaled = np.clip(scaled, -E4M3_MAX, E4M3_MAX)
+    return e4m3_encode_rne(scaled), s
+
+
+def quantise_rows_1x128(x):
+    """A [M, K] fp32 -> (codes uint8 [M, K], scales fp32 [M, ceil(K/128)])."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    G = (K + GROUP - 1) // GROUP
+    q = np.zeros((M, K), dtype=np.uint8)
+    s = np.zeros((M, G), dtype=np.float32)
+    for i in range(M):
+        for g in range(G):
+            sl = slice(g * GROUP, min(K, (g + 1) * GROUP))
+            q[i, sl], s[i, g] = _quantise_group(x[i, sl])
+    return q, s
+
+
+def quantise_blocks_128x128(x):
+    """B [K, N] fp32 -> (codes uint8 [K, N], scales fp32 [ceil(K/128), ceil(N/128)])."""
+    x = np.asarray(x, dtype=np.float32)
+    K, N = x.shape
+    G, H = (K + GROUP - 1) // GROUP, (N + GROUP - 1) // GROUP
+    q = np.zeros((K, N), dtype=np.uint8)
+    s = np.zeros((G, H), dtype=np.float32)
+    for g in range(G):
+        for h in range(H):
+            rs = slice(g * GROUP, min(K, (g + 1) * GROUP))
+            cs = slice(h * GROUP, min(N, (h + 1) * GROUP))
+            q[rs, cs], s[g, h] = _quantise_group(x[rs, cs])
+    return q, s

@@ -1,0 +1,351 @@
+"""Pins of the CPU oracle against things other than itself (no GPU needed).
+
+Each test fixes one part of the oracle to a library routine run exhaustively,
+exact rational arithmetic, a closed form, an invariant, or a figure the pages
+print (tests/golden/page_figures.json), chosen so that a dropped term, a
+wrong sign or index, or a transposed operand in the oracle fails one of them.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import workloads as wl
+from oracle import formats, gemm, quant
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+# ---------------------------------------------------------------- formats ---
+
+def test_bf16_decode_all_codes_match_torch():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = formats.bf16_decode(codes)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_encode_rne_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e30).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-30).astype(np.float32),
+        # exact ties: low half == 0x8000 with even and odd upper halves
+        (np.arange(0x3F800000, 0x3F800000 + 64 * 0x10000, 0x10000, dtype=np.uint32)
+         | np.uint32(0x8000)).view(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.4e38, -3.4e38], dtype=np.float32),
+    ])
+    ours = formats.bf16_encode_rne(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    # 1 + 2**-8 is exactly half way between 1 and 1 + 2**-7: ties to even -> 1.0
+    assert formats.bf16_encode_rne(np.float32(1 + 2.0 ** -8)) == 0x3F80
+    assert formats.bf16_encode_rne(np.float32(1 + 3 * 2.0 ** -8)) == 0x3F82
+
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = formats.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_round_trips_every_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = formats.e4m3_decode(codes)
+    assert np.array_equal(formats.e4m3_encode_rne(vals), codes)
+
+
+def test_e4m3_encode_ties_and_clamped_cast_match_torch():
+    assert formats.e4m3_encode_rne(np.array([1.0625]))[0] == formats.e4m3_encode_rne(np.array([1.0]))[0]
+    assert formats.e4m3_decode(formats.e4m3_encode_rne(np.array([1.1875])))[0] == 1.25
+    assert formats.e4m3_decode(formats.e4m3_encode_rne(np.array([2.0 ** -10])))[0] == 0.0
+    assert formats.e4m3_decode(formats.e4m3_encode_rne(np.array([3 * 2.0 ** -10])))[0] == 2 * 2.0 ** -9
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.uniform(-448, 448, 100000), rng.standard_normal(100000) * 0.01,
+        rng.standard_normal(100000) * 30, np.array([448.0, -448.0, 0.0, -0.0, 2.0 ** -6]),
+    ]).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ours = formats.e4m3_encode_rne(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    with pytest.raises(ValueError):
+        formats.e4m3_encode_rne(np.array([449.0]))
+
+
+# --------------------------------------------------------------- quantiser ---
+
+def _ulp_e4m3(v):
+    """Spacing of e4m3 codes at magnitude v (subnormal spacing below 2**-6)."""
+    v = np.abs(v)
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -6)))
+    return np.ldexp(1.0, (e - 3).astype(int))
+
+
+def test_quantiser_invariants():
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal((5, 300)).astype(np.float32)
+    a[1, 128:256] = 0.0                      # an all-zero group
+    a[2, 7] = 40.0                           # an outlier
+    q, s = quant.quantise_rows_1x128(a)
+    assert s.shape == (5, 3)
+    assert s[1, 1] == 1.0 and np.all(q[1, 128:256] == 0)
+    dec = formats.e4m3_decode(q)
+    for i in range(5):
+        for g in range(3):
+            sl = slice(128 * g, min(300, 128 * (g + 1)))
+            x = a[i, sl].astype(np.float64)
+            if np.all(x == 0):
+                continue
+            assert np.max(np.abs(dec[i, sl])) == 448.0
+            assert s[i, g] == np.float32(np.float32(np.max(np.abs(a[i, sl]))) / np.float32(448))
+            scaled = x / float(s[i, g])
+            err = np.abs(scaled - dec[i, sl])
+            assert np.all(err <= 0.5 * _ulp_e4m3(scaled) * (1 + 1e-6) + 1e-12)
+            nz = dec[i, sl] != 0
+            assert np.all(np.sign(dec[i, sl][nz]) == np.sign(x[nz]))
+
+
+def test_quantiser_matches_generator_bits():
+    rng = np.random.default_rng(3)
+    a = (rng.standard_normal((33, 300)) * np.where(rng.random((33, 300)) < 0.01, 20, 1)).astype(np.float32)
+    b = (rng.standard_normal((260, 390)) * 0.02).astype(np.float32)
+    qa, sa = quant.quantise_rows_1x128(a)
+    qb, sb = quant.quantise_blocks_128x128(b)
+    tqa, tsa = wl.quantise_a_1x128(torch.from_numpy(a))
+    tqb, tsb = wl.quantise_b_128x128(torch.from_numpy(b))
+    assert np.array_equal(qa, wl.bits_u8(tqa)) and np.array_equal(sa, tsa.numpy())
+    assert np.array_equal(qb, wl.bits_u8(tqb)) and np.array_equal(sb, tsb.numpy())
+    assert sb.shape == (3, 4)
+
+
+# ----------------------------------------------------------- contraction ---
+
+def _exact_gemm(a, b, bias=None):
+    M, K = a.shape
+    N = b.shape[1]
+    fa = [[Fraction(float(a[i, k])) for k in range(K)] for i in range(M)]
+    fb = [[Fraction(float(b[k, j])) for j in range(N)] for k in range(K)]
+    y = np.zeros((M, N), dtype=object)
+    d = np.zeros((M, N), dtype=object)
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            t = Fraction(0)
+            for k in range(K):
+                p = fa[i][k] * fb[k][j]
+                s += p
+                t += abs(p)
+            if bias is not None:
+                s += Fraction(float(bias[j]))
+                t += abs(Fraction(float(bias[j])))
+            y[i, j] = s
+            d[i, j] = t
+    return y, d
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (8, 8, 8), (6, 4, 9), (67, 50, 9)])
+def test_contraction_matches_exact_rationals(shape):
+    M, N, K = shape
+    g = torch.Generator().manual_seed(M * 1000 + N * 10 + K)
+    a = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    b = torch.randn(K, N, generator=g).to(torch.bfloat16)
+    bias = torch.randn(N, generator=g).to(torch.bfloat16)
+    ab, bb, biasb = wl.bits_u16(a), wl.bits_u16(b), wl.bits_u16(bias)
+    for epi in (gemm.EPI_NONE, gemm.EPI_BIAS):
+        y, d = gemm.gemm_bf16_bits(ab, bb, biasb if epi else None, epi)
+        ey, ed = _exact_gemm(formats.bf16_decode(ab), formats.bf16_decode(bb),
+                             formats.bf16_decode(biasb) if epi else None)
+        bound = (K + 1) * 2.0 ** -52
+        for i in range(M):
+            for j in range(N):
+                assert abs(Fraction(float(y[i, j])) - ey[i, j]) <= Fraction(bound) * ed[i, j]
+                assert abs(Fraction(float(d[i, j])) - ed[i, j]) <= Fraction(bound) * ed[i, j]
+
+
+def test_identity_gives_b_exactly():
+    K, N = 37, 23
+    eye = torch.eye(K).to(torch.bfloat16)
+    b = torch.randn(K, N, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    y, _ = gemm.gemm_bf16_bits(wl.bits_u16(eye), wl.bits_u16(b))
+    assert np.array_equal(y, formats.bf16_decode(wl.bits_u16(b)))
+    # right identity on a non-square A: A @ I == A (catches a transposed operand)
+    a = torch.randn(11, K, generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    y2, _ = gemm.gemm_bf16_bits(wl.bits_u16(a), wl.bits_u16(eye))
+    assert np.array_equal(y2, formats.bf16_decode(wl.bits_u16(a)))
+
+
+def test_rank_one_and_all_ones_closed_forms():
+    M, N, K = 9, 13, 300
+    rng = np.random.default_rng(7)
+    u = rng.integers(-8, 9, M).astype(np.float32)
+    v = rng.integers(-8, 9, N).astype(np.float32)
+    a = np.repeat(u[:, None], K, axis=1)
+    b = np.repeat(v[None, :], K, axis=0)
+    y, d = gemm.gemm_bf16_bits(formats.bf16_encode_rne(a), formats.bf16_encode_rne(b))
+    assert np.array_equal(y, K * np.outer(u, v).astype(np.float64))
+    assert np.array_equal(d, K * np.abs(np.outer(u, v)).astype(np.float64))
+    ones_a = formats.bf16_encode_rne(np.ones((M, K), np.float32))
+    ones_b = formats.bf16_encode_rne(np.ones((K, N), np.float32))
+    y1, _ = gemm.gemm_bf16_bits(ones_a, ones_b)
+    assert np.all(y1 == K)
+
+
+def test_empty_k_gives_bias_only():
+    a = np.zeros((3, 0), np.uint16)
+    b = np.zeros((0, 4), np.uint16)
+    bias = formats.bf16_encode_rne(np.array([1.0, -2.0, 0.5, 3.0], np.float32))
+    y, d = gemm.gemm_bf16_bits(a, b, bias, gemm.EPI_BIAS)
+    assert np.array_equal(y, np.tile([1.0, -2.0, 0.5, 3.0], (3, 1)))
+    assert np.array_equal(d, np.abs(y))
+
+
+# --------------------------------------------------------------- epilogue ---
+
+def test_gelu_tanh_pins():
+    assert gemm.gelu_tanh(0.0) == 0.0
+    y = np.linspace(-9, 9, 2001)
+    # tanh is odd, so gelu(y) - gelu(-y) == y
+    assert np.allclose(gemm.gelu_tanh(y) - gemm.gelu_tanh(-y), y, rtol=1e-15, atol=1e-15)
+    ref = F.gelu(torch.from_numpy(y), approximate="tanh").numpy()
+    assert np.allclose(gemm.gelu_tanh(y), ref, rtol=1e-14, atol=1e-15)
+    assert abs(float(gemm.gelu_tanh(1.0)) - 0.8411919906082768) < 1e-15
+    # and it differs from the erf form (catches a wrong activation)
+    assert abs(float(gemm.gelu_tanh(1.0)) - 0.5 * (1 + math.erf(1 / math.sqrt(2)))) > 1e-5
+
+
+def test_bias_gelu_order_is_bias_then_activation():
+    a = formats.bf16_encode_rne(np.array([[1.0, 2.0]], np.float32))
+    b = formats.bf16_encode_rne(np.array([[0.5, -1.0], [0.25, 1.0]], np.float32))
+    bias = formats.bf16_encode_rne(np.array([-1.0, 0.5], np.float32))
+    y, d = gemm.gemm_bf16_bits(a, b, bias, gemm.EPI_BIAS_GELU_TANH)
+    pre = np.array([1 * 0.5 + 2 * 0.25 - 1.0, -1.0 + 2.0 + 0.5])
+    assert np.allclose(y[0], F.gelu(torch.from_numpy(pre), approximate="tanh").numpy(), rtol=0, atol=1e-15)
+    assert np.array_equal(d[0], np.array([0.5 + 0.5 + 1.0, 1.0 + 2.0 + 0.5]))
+
+
+# ------------------------------------------------------------------ FP8 -----
+
+def _fp8_small(M, N, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randn(M, K, generator=g)
+    b = torch.randn(K, N, generator=g) * 0.02
+    qa, sa = quant.quantise_rows_1x128(a.numpy())
+    qb, sb = quant.quantise_blocks_128x128(b.numpy())
+    return qa, sa, qb, sb
+
+
+def test_fp8_dequantisation_indexing_brute_force():
+    M, N, K = 5, 300, 260
+    qa, sa, qb, sb = _fp8_small(M, N, K, 8)
+    ah = gemm.dequant_fp8_a(qa, sa)
+    bh = gemm.dequant_fp8_b(qb, sb)
+    for i in range(M):
+        for k in range(0, K, 7):
+            assert ah[i, k] == formats.e4m3_decode(qa[i, k]) * float(sa[i, k // 128])
+    for k in range(0, K, 13):
+        for j in range(0, N, 11):
+            assert bh[k, j] == formats.e4m3_decode(qb[k, j]) * float(sb[k // 128, j // 128])
+
+
+def test_fp8_integer_codes_unit_scales_exact():
+    M, N, K = 4, 6, 256
+    rng = np.random.default_rng(9)
+    ia = rng.integers(-4, 5, (M, K)).astype(np.float64)
+    ib = rng.integers(-4, 5, (K, N)).astype(np.float64)
+    qa, qb = formats.e4m3_encode_rne(ia), formats.e4m3_encode_rne(ib)
+    y, _ = gemm.gemm_fp8_blockscaled_bits(qa, np.ones((M, 2), np.float32), qb, np.ones((2, 1), np.float32))
+    assert np.array_equal(y, ia @ ib)  # small integers: float64 matmul is exact
+
+
+def test_fp8_scale_power_of_two_scales_row_and_block():
+    M, N, K = 6, 260, 384
+    qa, sa, qb, sb = _fp8_small(M, N, K, 10)
+    y, _ = gemm.gemm_fp8_blockscaled_bits(qa, sa, qb, sb)
+    sa2 = sa.copy()
+    sa2[3, :] *= 8.0
+    y2, _ = gemm.gemm_fp8_blockscaled_bits(qa, sa2, qb, sb)
+    assert np.array_equal(y2[3], 8.0 * y[3])
+    assert np.array_equal(np.delete(y2, 3, 0), np.delete(y, 3, 0))
+    # one 128x128 block of B scaled by 2**-3: only columns of that block change,
+    # and only by the contribution of that K group
+    sb2 = sb.copy()
+    sb2[1, 2] *= 0.125
+    y3, _ = gemm.gemm_fp8_blockscaled_bits(qa, sa, qb, sb2)
+    assert np.array_equal(y3[:, :256], y[:, :256])
+    ah = gemm.dequant_fp8_a(qa, sa)
+    bh = gemm.dequant_fp8_b(qb, sb)
+    part = ah[:, 128:256] @ bh[128:256, 256:]
+    assert np.allclose(y3[:, 256:], y[:, 256:] - part + 0.125 * part, rtol=0, atol=1e-12)
+
+
+def test_fp8_equals_bf16_path_on_dequantised_inputs():
+    qa, sa, qb, sb = _fp8_small(7, 130, 200, 11)
+    y, d = gemm.gemm_fp8_blockscaled_bits(qa, sa, qb, sb)
+    y2, d2 = gemm.gemm_f64(gemm.dequant_fp8_a(qa, sa), gemm.dequant_fp8_b(qb, sb))
+    assert np.array_equal(y, y2) and np.array_equal(d, d2)
+
+
+# --------------------------------------------------- metric and FLOP count ---
+
+def test_error_metric_reports_injected_delta():
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal((5, 7))
+    d = np.abs(y) + 1.0
+    c = y.copy()
+    c[2, 3] += 0.25
+    r = gemm.compare(c, y, d, tol=1e-3)
+    assert r["argmax"] == (2, 3) and not r["ok"]
+    assert abs(r["max_err"] - 0.25 / d[2, 3]) < 1e-15
+    z = gemm.error_ratio(np.array([0.0, 1.0, np.nan]), np.zeros(3), np.zeros(3))
+    assert z[0] == 0 and np.isinf(z[1]) and np.isinf(z[2])
+
+
+def test_flop_count_against_page_figures():
+    fig = json.load(open(GOLDEN))
+    sq = fig["square_4096_flops"]
+    flops = gemm.flop_count(sq["M"], sq["N"], sq["K"])
+    assert flops == 137_438_953_472
+    assert abs(flops - sq["page_value"]) <= sq["rounding"]
+    rate = fig["square_4096_rate_at_half_ms"]
+    tflops = flops / rate["seconds"] / 1e12
+    assert abs(tflops - rate["page_value_tflops"]) <= rate["rounding"]
+    util = fig["square_4096_utilisation_vs_500"]
+    assert abs(tflops / util["peak_tflops"] - util["page_value_fraction"]) <= util["rounding"]
+    assert gemm.flop_count(1, 1, 1) == 2 and gemm.flop_count(3, 5, 0) == 0
+
+
+# ----------------------------------------------------------------- inputs ---
+
+def test_generator_is_deterministic_and_shaped():
+    w = wl.WORKLOADS["tiny"]
+    a1, b1, _ = wl.bf16_inputs(w)
+    a2, b2, _ = wl.bf16_inputs(w)
+    assert torch.equal(a1, a2) and torch.equal(b1, b2)
+    assert a1.dtype == torch.bfloat16 and a1.shape == (64, 64)
+    assert float(a1.abs().max()) <= 1.0
+
+
+def test_fp8_generator_outlier_rate_and_scale_shapes():
+    w = wl.WORKLOADS["fp8"]
+    qa, sa, qb, sb = wl.fp8_inputs(w, M=256, N=384, K=512)
+    assert qa.shape == (256, 512) and sa.shape == (256, 4)
+    assert qb.shape == (512, 384) and sb.shape == (4, 3)
+    dec = formats.e4m3_decode(wl.bits_u8(qa))
+    assert np.all(np.max(np.abs(dec.reshape(256, 4, 128)), axis=2) == 448.0)
