@@ -1,0 +1,262 @@
+"""Benchmark of the GEMM hot path on one MI355X; prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload square]
+                    [--no-secondary] [--no-cpu-baseline]
+
+A step is one library call on the headline workload (the square bf16 GEMM
+M = N = K = 4096, bf16 output) with all inputs resident in HBM.  W untimed
+warm-up steps, then exactly K timed steps between two synchronisations;
+value = 2*M*N*K / (time per step), in TFLOP/s (the FLOP count of the GEMM
+compute-cost page, section 3.1; rates and utilisation are the "three numbers"
+of the DeepGEMM page, section 3.4).
+
+Also reported in the same line:
+  roofline      the dominant kernel's average launch time from HIP events on
+                the launch stream, as achieved TFLOP/s (or GB/s) against the
+                MI355X dense peak, plus HBM traffic from the committed
+                rocprofv3 counter summary when it matches the current source;
+  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded row sample
+                of the same workload (rank 0, one GPU only);
+  secondary     the other workloads (FFN pair, thin-M LM head at M = 1, 8,
+                32, 64, FP8 block-scaled and its ragged variant), each timed
+                the same way with its own roofline figure.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "GEMM TFLOPS & % MFMA peak (bf16/fp8); HBM GB/s % peak on thin-M LM head"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square",
+                    help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary-steps", type=int, default=50)
+    return ap.parse_args()
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "tiled_gemm_04_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "tiled": ["common.h", "launch.h", "gemm_bf16_tiled.hip"],
+    "thin": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
+    "fp8": ["common.h", "launch.h", "gemm_fp8_blockscaled.hip"],
+}
+
+
+def committed_traffic(workload, family):
+    """HBM bytes per launch from profiles/<workload>_pmc.md, or None.
+
+    The summary holds lines 'source_digest: <hex>' and
+    'hbm_bytes_per_launch: <int>'; the figure is used only while the digest
+    matches the kernel's current source.
+    """
+    path = os.path.join(PROFILES, f"{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    dig = re.search(r"source_digest:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not dig or not val or dig.group(1) != source_digest(KERNEL_SOURCES[family]):
+        return None
+    return int(val.group(1))
+
+
+class Case:
+    """One workload: inputs resident on the GPU and a launch closure."""
+
+    def __init__(self, name, dev):
+        import torch
+
+        import tiled_gemm_04_amd as tg
+        import workloads as wl
+
+        self.name = name
+        w = wl.WORKLOADS[name]
+        self.w = w
+        self.M, self.N, self.K = w.M, w.N, w.K
+        self.flops = 2 * w.M * w.N * w.K
+        if w.fp8:
+            qa, sa, qb, sb = wl.fp8_inputs(w, device=dev)
+            c = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev)
+            self.launch = lambda: tg.gemm_fp8_blockscaled(qa, sa, qb, sb, c)
+            self.family = "fp8"
+            self.kernel = tg.gemm_fp8_kernel_name(w.M, w.N, w.K)
+            self.bytes = w.M * w.K + w.K * w.N + 2 * w.M * w.N + 4 * (sa.numel() + sb.numel())
+            self.bound, self.peak = "mfma", PEAK_FP8_TFLOPS
+            self.dtype = "fp8_e4m3"
+        else:
+            if name == "ffn_down":
+                a = wl.ffn_hidden(w.M, w.K, w.seed, dev)
+                _, b, bias = wl.bf16_inputs(w, device=dev)
+            else:
+                a, b, bias = wl.bf16_inputs(w, device=dev)
+            out = torch.float32 if w.out_f32 else torch.bfloat16
+            c = torch.empty(w.M, w.N, dtype=out, device=dev)
+            self.launch = lambda: tg.gemm_bf16(a, b, bias, c, epilogue=w.epilogue)
+            self.kernel = tg.gemm_bf16_kernel_name(w.M, w.N, w.K, w.epilogue,
+                                                   tg.OUT_F32 if w.out_f32 else tg.OUT_BF16)
+            self.family = "thin" if "thin" in self.kernel else "tiled"
+            out_bytes = 4 if w.out_f32 else 2
+            self.bytes = 2 * (w.M * w.K + w.K * w.N) + out_bytes * w.M * w.N + (
+                2 * w.N if bias is not None else 0)
+            thin = self.family == "thin"
+            self.bound = "hbm" if thin else "mfma"
+            self.peak = PEAK_HBM_GBS if thin else PEAK_BF16_TFLOPS
+            self.dtype = "bf16"
+        self.inputs_for_oracle = None if w.fp8 else (a, b)
+
+    def time(self, steps, warmup):
+        """(ms per step from the bracketing synchronisations, mean kernel ms from events)."""
+        import torch
+
+        for _ in range(warmup):
+            self.launch()
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record()
+            self.launch()
+            ends[i].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+        return (t1 - t0) * 1e3 / steps, sum(ev) / len(ev), sorted(ev)[len(ev) // 2]
+
+    def roofline(self, kernel_ms):
+        if self.bound == "hbm":
+            achieved = self.bytes / (kernel_ms * 1e-3) / 1e9
+            unit = "GB/s"
+        else:
+            achieved = self.flops / (kernel_ms * 1e-3) / 1e12
+            unit = "TFLOP/s"
+        traffic = committed_traffic(self.name, self.family)
+        return {"bound": self.bound, "achieved": round(achieved, 2), "peak": self.peak, "unit": unit,
+                "frac": round(achieved / self.peak, 4), "traffic": traffic,
+                "kernel": self.kernel, "kernel_ms_mean": round(kernel_ms, 5),
+                "algorithmic_bytes": self.bytes, "flop": self.flops}
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The fp64 oracle on a bounded row sample of the headline workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import workloads as wl
+    from oracle import gemm as og
+
+    a, b = case.inputs_for_oracle
+    a_bits = wl.bits_u16(a)
+    b_bits = wl.bits_u16(b)
+    rows = 16
+    t0 = time.perf_counter()
+    og.gemm_bf16_bits(a_bits[:rows], b_bits)
+    probe = time.perf_counter() - t0
+    rows = int(min(case.M, max(rows, rows * budget_s / max(probe, 1e-3))))
+    t0 = time.perf_counter()
+    og.gemm_bf16_bits(a_bits[:rows], b_bits)
+    dt = time.perf_counter() - t0
+    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                   if i.get("user_api") == "blas"), default=1)
+    flops = 2 * rows * case.N * case.K
+    del np
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"rows 0..{rows - 1} of the {case.M}x{case.N}x{case.K} {case.name} GEMM "
+                      f"(fp64 decode + contraction + |a||b| denominators)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the GEMM is measured "
+                                   "on one device's share (multi-GPU sharding is not built)"}))
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    head = Case(args.workload, dev)
+    ms_step, kern_ms, kern_med = head.time(args.steps, args.warmup)
+    value = head.flops / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.dtype,
+        "data": "synthetic (seeded, shapes and distributions of the source pages' workloads)",
+        "config": {"workload": f"{head.name}: C[{head.M},{head.N}] = A[{head.M},{head.K}] . "
+                               f"B[{head.K},{head.N}]", "M": head.M, "N": head.N, "K": head.K,
+                   "kernel": head.kernel},
+        "roofline": head.roofline(kern_ms),
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+    }
+    line["roofline"]["kernel_ms_median"] = round(kern_med, 5)
+    del head.launch
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = {}
+        for name in ("ffn_up", "ffn_down", "thin_m1", "thin_m8", "thin_m32", "thin_m64", "fp8",
+                     "fp8_ragged", "tiny"):
+            if name == args.workload:
+                continue
+            c = Case(name, dev)
+            ms, km, kmed = c.time(args.secondary_steps, 5)
+            r = c.roofline(km)
+            sec[name] = {"ms_per_call": round(ms, 5), "kernel_ms_mean": r["kernel_ms_mean"],
+                         "kernel_ms_median": round(kmed, 5),
+                         "tflops": round(c.flops / (km * 1e-3) / 1e12, 2),
+                         "gbs": round(c.bytes / (km * 1e-3) / 1e9, 1),
+                         "bound": r["bound"], "frac": r["frac"], "kernel": c.kernel,
+                         "traffic": r["traffic"]}
+            del c
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
+
+    if not args.no_cpu_baseline and head.inputs_for_oracle is not None:
+        line["cpu_baseline"] = cpu_baseline(head)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

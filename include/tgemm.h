@@ -1,0 +1,160 @@
+/*
+ * tgemm -- dense GEMM for LLM linear layers on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the shared library libtgemm.so.  Every entry point takes plain
+ * device pointers and sizes; no framework types cross this boundary.
+ *
+ * Sources cited by short name:
+ *   "GEMM compute-cost page"  kwkr.cn/news/191298 (why GEMM dominates LLM
+ *                             compute; the linear layer Y = X W + b of its
+ *                             section 3.1, the fused bias+activation
+ *                             epilogue of section 5.1, the LM head of 7.2).
+ *   "DeepGEMM page"           zwxr.cn/news/240083 (a DeepGEMM-style kernel
+ *                             library: simple callable interface in section
+ *                             1.3, row-major naive reference in 3.2, FP8
+ *                             group scales in 2.4, fusion hooks in 5.1).
+ *
+ * Conventions shared by all calls
+ * -------------------------------
+ * Layout.   Matrices are row-major: element (i, j) of a matrix with row
+ *           stride ld sits at ptr[i * ld + j] (the A[m*K + k], B[k*N + n]
+ *           indexing of the DeepGEMM page, section 3.2).  The inner stride is
+ *           always 1.
+ * Memory.   All pointers are device pointers owned by the caller.  The
+ *           library never allocates, frees or keeps them, and holds no
+ *           mutable global state; calls from several host threads are safe.
+ *           C must not overlap A, B, bias or the scale arrays (not checked).
+ * Streams.  `stream` is a hipStream_t passed as void*; NULL is the default
+ *           stream.  Calls only enqueue work on it and return; they never
+ *           synchronise.  Results are visible to later work on that stream.
+ * Errors.   Every call returns a tgemm_status_t.  Argument errors are found
+ *           before anything is enqueued, and C is then left untouched.
+ *           TGEMM_ERR_LAUNCH reports a HIP error raised by the launch itself;
+ *           faults inside a kernel surface at the caller's next
+ *           synchronisation, as usual for asynchronous HIP work.
+ * Sizes.    M, N, K >= 0.  M == 0 or N == 0 is a no-op returning TGEMM_OK.
+ *           K == 0 is an empty sum: C = epilogue(0 + bias).  Each of M, N, K
+ *           must be below 2^31, and every element offset (i * ld + j) must
+ *           fit in 63 bits.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TGEMM_ABI_VERSION 1
+
+typedef enum {
+    TGEMM_OK = 0,
+    TGEMM_ERR_INVALID = 1,      /* bad pointer, size, stride or enum value      */
+    TGEMM_ERR_UNSUPPORTED = 2,  /* valid request this build cannot run          */
+    TGEMM_ERR_LAUNCH = 3        /* the HIP runtime refused the kernel launch    */
+} tgemm_status_t;
+
+/* Epilogue applied to the fp32 accumulator before the single output rounding.
+ * Order follows the GEMM compute-cost page, section 5.1: add the bias, then
+ * the activation, then write back.  The activation is the tanh form of GeLU,
+ * 0.5*y*(1 + tanh(sqrt(2/pi)*(y + 0.044715*y^3))).  The DeepGEMM page
+ * (section 5.1) asks for a hook before the output is written; an enum is the
+ * ahead-of-time-compiled form of that hook. */
+typedef enum {
+    TGEMM_EPI_NONE = 0,
+    TGEMM_EPI_BIAS = 1,            /* y = acc + bias[j]                          */
+    TGEMM_EPI_BIAS_GELU_TANH = 2   /* y = gelu_tanh(acc + bias[j])               */
+} tgemm_epilogue_t;
+
+typedef enum {
+    TGEMM_OUT_F32 = 0,   /* C holds float32                                     */
+    TGEMM_OUT_BF16 = 1   /* C holds bfloat16, rounded to nearest even            */
+} tgemm_out_t;
+
+/* Kernel family choice for gemm_bf16_ex. */
+typedef enum {
+    TGEMM_ALGO_AUTO = 0,   /* thin-M kernel for M <= 64, tiled kernel otherwise */
+    TGEMM_ALGO_TILED = 1,  /* LDS-tiled MFMA kernel, any shape                  */
+    TGEMM_ALGO_THIN = 2    /* bandwidth-bound small-M kernel, requires M <= 64  */
+} tgemm_algo_t;
+
+/*
+ * gemm_bf16 -- C[M,N] = epilogue(A[M,K] . B[K,N] + bias[N])
+ *
+ * The linear layer of the GEMM compute-cost page (section 3.1, Y = X W + b;
+ * section 2.1 lists its uses: Q/K/V/O projections, the FFN pair, the LM
+ * head) with bf16 inputs and fp32 accumulation.
+ *
+ *   A      bf16 [M, K], row stride lda (elements), lda >= K
+ *   B      bf16 [K, N], row stride ldb, ldb >= N   (N-contiguous, "row-major B")
+ *   bias   bf16 [N], contiguous; required (non-NULL) for the two bias
+ *          epilogues and ignored for TGEMM_EPI_NONE
+ *   C      out_dtype [M, N], row stride ldc, ldc >= N
+ *   epilogue   a tgemm_epilogue_t value
+ *   out_dtype  a tgemm_out_t value
+ *   stream     hipStream_t or NULL
+ *
+ * Pointers must be non-NULL when the matrix they point to is non-empty.
+ * Any alignment is accepted; 16-byte aligned base pointers with strides that
+ * are multiples of 8 elements take the vectorised load path.
+ * Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
+ */
+int gemm_bf16(const void* A, const void* B, const void* bias, void* C,
+              int64_t M, int64_t N, int64_t K,
+              int64_t lda, int64_t ldb, int64_t ldc,
+              int epilogue, int out_dtype, void* stream);
+
+/*
+ * gemm_bf16_ex -- gemm_bf16 with an explicit kernel family (tgemm_algo_t).
+ * TGEMM_ALGO_THIN with M > 64 returns TGEMM_ERR_UNSUPPORTED.  Used by tests
+ * that cross-check the two kernel families and by the benchmark.
+ */
+int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C,
+                 int64_t M, int64_t N, int64_t K,
+                 int64_t lda, int64_t ldb, int64_t ldc,
+                 int epilogue, int out_dtype, int algo, void* stream);
+
+/*
+ * gemm_fp8_blockscaled -- C[i,j] = sum_g sA[i,g] * sB[g, j/128] *
+ *                                  sum_{k in group g} A[i,k] * B[k,j]
+ *
+ * FP8 inputs with per-group fp32 scale factors and fp32 accumulation, the
+ * low-precision scheme of the DeepGEMM page, section 2.4: groups of 128
+ * elements along K for each row of A, 128 x 128 blocks for B, products
+ * accumulated in fp32, scales applied per K group, bf16 output.
+ *
+ *   A    OCP e4m3fn bytes [M, K], packed row-major (row stride K)
+ *   sA   fp32 [M, ceil(K/128)], packed row-major; group g covers columns
+ *        [128g, min(K, 128g+128))
+ *   B    e4m3fn bytes [K, N], packed row-major (row stride N)
+ *   sB   fp32 [ceil(K/128), ceil(N/128)], packed row-major
+ *   C    bf16 [M, N], packed row-major
+ *
+ * Dequantised value = decode(code) * scale.  Scales must be finite; NaN
+ * codes (0x7F, 0xFF) propagate to the outputs they touch.
+ * Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
+ */
+int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
+                         void* C, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Name of the kernel configuration gemm_bf16_ex would launch for a problem
+ * (no launch, no validation of pointers).  Returns a static string, or NULL
+ * when the request is invalid. */
+const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue,
+                                  int out_dtype, int algo);
+
+/* Name of the kernel configuration gemm_fp8_blockscaled launches. */
+const char* gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K);
+
+/* Static, human-readable text for a status code. */
+const char* gemm_status_string(int status);
+
+/* TGEMM_ABI_VERSION of the built library. */
+int gemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

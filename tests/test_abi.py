@@ -1,0 +1,89 @@
+"""The C ABI library on the host: it loads, exports what include/tgemm.h
+declares, and rejects bad arguments before any HIP call (no GPU needed:
+every call here returns during validation, so nothing is enqueued).
+"""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from tiled_gemm_04_amd import binding
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libtgemm.so not built (python -m tiled_gemm_04_amd.build)")
+
+INV, UNS, OK = binding.TGEMM_ERR_INVALID, binding.TGEMM_ERR_UNSUPPORTED, binding.TGEMM_OK
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails or M/N is 0 first
+NULL = ctypes.c_void_p(0)
+
+
+def test_every_declared_function_is_exported():
+    names = binding.header_functions()
+    assert {"gemm_bf16", "gemm_fp8_blockscaled", "gemm_bf16_ex"} <= set(names)
+    L = binding.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert binding.gemm_abi_version() == 1
+    assert binding.gemm_status_string(0) == "ok"
+    assert "invalid" in binding.gemm_status_string(INV)
+    assert binding.gemm_status_string(99) == "unknown status"
+
+
+def _bf16(A=FAKE, B=FAKE, bias=FAKE, C=FAKE, M=64, N=64, K=64, lda=64, ldb=64, ldc=64, epi=0,
+          out=1, algo=None):
+    L = binding.lib()
+    if algo is None:
+        return L.gemm_bf16(A, B, bias, C, M, N, K, lda, ldb, ldc, epi, out, NULL)
+    return L.gemm_bf16_ex(A, B, bias, C, M, N, K, lda, ldb, ldc, epi, out, algo, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INV), (dict(N=-5), INV), (dict(K=-1), INV),
+    (dict(M=1 << 31, lda=64), INV),
+    (dict(C=NULL), INV), (dict(A=NULL), INV), (dict(B=NULL), INV),
+    (dict(epi=3), INV), (dict(epi=-1), INV), (dict(out=2), INV),
+    (dict(epi=1, bias=NULL), INV), (dict(epi=2, bias=NULL), INV),
+    (dict(lda=63), INV), (dict(ldb=10), INV), (dict(ldc=0), INV),
+    (dict(algo=3), INV), (dict(algo=2, M=65), UNS),
+    (dict(M=0), OK), (dict(N=0, ldb=1, ldc=1), OK), (dict(M=0, A=NULL, C=NULL), OK),
+])
+def test_bf16_validation(kw, status):
+    assert _bf16(**kw) == status
+
+
+def test_bf16_k_zero_needs_no_operands_but_needs_c():
+    # K == 0 with NULL A/B is valid (empty sum); C must still be given.
+    assert _bf16(A=NULL, B=NULL, C=NULL, K=0, lda=1) == INV
+
+
+def test_fp8_validation():
+    L = binding.lib()
+    f = ctypes.c_void_p
+    assert L.gemm_fp8_blockscaled(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 4, NULL) == INV
+    assert L.gemm_fp8_blockscaled(FAKE, NULL, FAKE, FAKE, FAKE, 4, 4, 4, NULL) == INV
+    assert L.gemm_fp8_blockscaled(FAKE, FAKE, FAKE, NULL, FAKE, 4, 4, 4, NULL) == INV
+    assert L.gemm_fp8_blockscaled(FAKE, FAKE, FAKE, FAKE, NULL, 4, 4, 4, NULL) == INV
+    assert L.gemm_fp8_blockscaled(NULL, NULL, NULL, NULL, NULL, 0, 4, 4, NULL) == OK
+    del f
+
+
+def test_kernel_selection_table():
+    name = binding.gemm_bf16_kernel_name
+    assert name(4096, 4096, 4096) == "tgemm_bf16_tiled_256x256x64"
+    assert name(2048, 16384, 4096) == "tgemm_bf16_tiled_256x256x64"
+    assert name(2048, 4096, 16384) == "tgemm_bf16_tiled_256x128x64"
+    assert name(64, 128256, 4096) == "tgemm_bf16_thin_m64"
+    assert name(1, 128256, 4096) == "tgemm_bf16_thin_m16"
+    assert name(64, 64, 64, algo=binding.ALGO_TILED).startswith("tgemm_bf16_tiled")
+    assert name(65, 64, 64, algo=binding.ALGO_THIN) is None
+    assert name(-1, 64, 64) is None
+    assert binding.gemm_fp8_kernel_name(4096, 14336, 4096) == "tgemm_fp8_bs_256x128x128"

@@ -1,0 +1,12 @@
+"""tgemm: bf16 and FP8 block-scaled GEMM for AMD MI355X (gfx950).
+
+The compute path is the HIP library libtgemm.so (sources in csrc/, C ABI in
+include/tgemm.h); this package only builds it and marshals torch tensors into
+its calls.
+"""
+
+from .binding import (  # noqa: F401
+    ALGO_AUTO, ALGO_THIN, ALGO_TILED, EPI_BIAS, EPI_BIAS_GELU_TANH, EPI_NONE, OUT_BF16, OUT_F32,
+    TgemmError, gemm_abi_version, gemm_bf16, gemm_bf16_ex, gemm_bf16_kernel_name,
+    gemm_fp8_blockscaled, gemm_fp8_kernel_name, gemm_status_string, lib,
+)

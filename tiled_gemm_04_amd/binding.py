@@ -1,0 +1,185 @@
+"""ctypes binding of libtgemm.so (argument marshalling only).
+
+The functions here carry the C ABI's names.  Each takes torch tensors that
+already live on the GPU, checks dtype / device / layout, derives sizes and
+row strides, passes raw device pointers and the current HIP stream to the
+library, and raises on a non-zero status.  No arithmetic of the GEMM happens
+here; torch is used only for device memory and streams.
+
+If libtgemm.so has not been built, every call raises -- there is no fallback.
+"""
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtgemm.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tgemm.h")
+
+TGEMM_OK = 0
+TGEMM_ERR_INVALID = 1
+TGEMM_ERR_UNSUPPORTED = 2
+TGEMM_ERR_LAUNCH = 3
+
+EPI_NONE = 0
+EPI_BIAS = 1
+EPI_BIAS_GELU_TANH = 2
+
+OUT_F32 = 0
+OUT_BF16 = 1
+
+ALGO_AUTO = 0
+ALGO_TILED = 1
+ALGO_THIN = 2
+
+_lib = None
+
+
+class TgemmError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().gemm_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+def lib():
+    """Load libtgemm.so once; raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m tiled_gemm_04_amd.build` "
+            "(the HIP library is required; there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.gemm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.gemm_bf16.restype = i32
+    L.gemm_bf16_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp]
+    L.gemm_bf16_ex.restype = i32
+    L.gemm_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    L.gemm_fp8_blockscaled.restype = i32
+    L.gemm_bf16_kernel_name.argtypes = [i64, i64, i64, i32, i32, i32]
+    L.gemm_bf16_kernel_name.restype = ctypes.c_char_p
+    L.gemm_fp8_kernel_name.argtypes = [i64, i64, i64]
+    L.gemm_fp8_kernel_name.restype = ctypes.c_char_p
+    L.gemm_status_string.argtypes = [i32]
+    L.gemm_status_string.restype = ctypes.c_char_p
+    L.gemm_abi_version.argtypes = []
+    L.gemm_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def header_functions():
+    """Names of the functions include/tgemm.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _row_major(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError(f"{name} must have unit inner stride")
+    return max(t.stride(0), t.shape[1], 1)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def gemm_bf16_ex(A, B, bias, C, epilogue=EPI_NONE, algo=ALGO_AUTO, stream=None):
+    """C[M,N] = epilogue(A[M,K] @ B[K,N] + bias[N]) on the GPU (writes C in place).
+
+    A, B: bfloat16, row-major (unit inner stride, any row stride).
+    bias: bfloat16 [N] contiguous, or None for EPI_NONE.
+    C: float32 or bfloat16 [M, N], row-major.
+    """
+    _check_cuda(A, B, bias, C)
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("A and B must be bfloat16")
+    if C.dtype == torch.float32:
+        out = OUT_F32
+    elif C.dtype == torch.bfloat16:
+        out = OUT_BF16
+    else:
+        raise ValueError("C must be float32 or bfloat16")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N) or (bias is not None and bias.numel() != N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    st = lib().gemm_bf16_ex(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K,
+                            _row_major(A, "A"), _row_major(B, "B"), _row_major(C, "C"),
+                            int(epilogue), out, int(algo), _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_bf16_ex")
+    return C
+
+
+def gemm_bf16(A, B, bias, C, epilogue=EPI_NONE, stream=None):
+    """gemm_bf16 of the C ABI: the library picks the kernel family."""
+    return gemm_bf16_ex(A, B, bias, C, epilogue, ALGO_AUTO, stream)
+
+
+def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
+    """C[M,N] (bf16) = sum_g sA[:,g] sB[g,n/128] (A_g @ B_g) with e4m3fn A, B.
+
+    A: float8_e4m3fn [M, K] contiguous; sA: float32 [M, ceil(K/128)] contiguous;
+    B: float8_e4m3fn [K, N] contiguous; sB: float32 [ceil(K/128), ceil(N/128)];
+    C: bfloat16 [M, N] contiguous.
+    """
+    _check_cuda(A, sA, B, sB, C)
+    if A.dtype != torch.float8_e4m3fn or B.dtype != torch.float8_e4m3fn:
+        raise ValueError("A and B must be float8_e4m3fn")
+    if sA.dtype != torch.float32 or sB.dtype != torch.float32 or C.dtype != torch.bfloat16:
+        raise ValueError("scales must be float32 and C bfloat16")
+    for t, n in ((A, "A"), (B, "B"), (sA, "sA"), (sB, "sB"), (C, "C")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous (packed row-major)")
+    M, K = A.shape
+    K2, N = B.shape
+    G, H = (K + 127) // 128, (N + 127) // 128
+    if K2 != K or tuple(C.shape) != (M, N) or tuple(sA.shape) != (M, G) or tuple(sB.shape) != (G, H):
+        raise ValueError("shape mismatch")
+    st = lib().gemm_fp8_blockscaled(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
+                                    _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_fp8_blockscaled")
+    return C
+
+
+def gemm_bf16_kernel_name(M, N, K, epilogue=EPI_NONE, out_dtype=OUT_BF16, algo=ALGO_AUTO):
+    r = lib().gemm_bf16_kernel_name(M, N, K, epilogue, out_dtype, algo)
+    return None if r is None else r.decode()
+
+
+def gemm_fp8_kernel_name(M, N, K):
+    r = lib().gemm_fp8_kernel_name(M, N, K)
+    return None if r is None else r.decode()
+
+
+def gemm_status_string(status):
+    return lib().gemm_status_string(status).decode()
+
+
+def gemm_abi_version():
+    return lib().gemm_abi_version()

@@ -1,0 +1,182 @@
+// C ABI of libtgemm.so: argument validation, kernel selection, launch.
+//
+// The interface follows the DeepGEMM page, section 1.3 (a plain function a
+// framework or an inference engine can call directly) and the linear layer
+// Y = X W + b of the GEMM compute-cost page, section 3.1.  Validation happens
+// before any HIP call, so a rejected request enqueues nothing and leaves C
+// untouched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tgemm.h"
+#include "launch.h"
+
+using tgemm::Bf16Args;
+using tgemm::Fp8Args;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+constexpr int64_t kThinMaxM = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+// The largest element offset (rows-1)*ld + cols-1 must stay below 2^62.
+bool extent_ok(int64_t rows, int64_t cols, int64_t ld) {
+  if (rows == 0 || cols == 0) return true;
+  constexpr int64_t kLimit = int64_t{1} << 62;
+  if (ld <= 0 || cols > kLimit) return false;
+  return rows - 1 <= (kLimit - cols) / ld;
+}
+
+int validate_bf16(const void* A, const void* B, const void* bias, const void* C, int64_t M,
+                  int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue,
+                  int out_dtype, int algo) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return TGEMM_ERR_INVALID;
+  if (epilogue < TGEMM_EPI_NONE || epilogue > TGEMM_EPI_BIAS_GELU_TANH) return TGEMM_ERR_INVALID;
+  if (out_dtype != TGEMM_OUT_F32 && out_dtype != TGEMM_OUT_BF16) return TGEMM_ERR_INVALID;
+  if (algo < TGEMM_ALGO_AUTO || algo > TGEMM_ALGO_THIN) return TGEMM_ERR_INVALID;
+  if (lda < K || ldb < N || ldc < N) return TGEMM_ERR_INVALID;
+  if (lda < 1 || ldb < 1 || ldc < 1) return TGEMM_ERR_INVALID;
+  if (!extent_ok(M, K, lda) || !extent_ok(K, N, ldb) || !extent_ok(M, N, ldc))
+    return TGEMM_ERR_INVALID;
+  if (M == 0 || N == 0) return TGEMM_OK;
+  if (C == nullptr) return TGEMM_ERR_INVALID;
+  if (K > 0 && (A == nullptr || B == nullptr)) return TGEMM_ERR_INVALID;
+  if (epilogue != TGEMM_EPI_NONE && bias == nullptr) return TGEMM_ERR_INVALID;
+  if (algo == TGEMM_ALGO_THIN && M > kThinMaxM) return TGEMM_ERR_UNSUPPORTED;
+  return TGEMM_OK;
+}
+
+// Shape-to-kernel table for the tiled family.  A launch wants at least one
+// full round of 256 workgroups (one per compute unit) and few idle units in
+// its last round; bigger tiles re-read less and run closer to the MFMA peak.
+int pick_tiled_shape(int64_t M, int64_t N) {
+  static const double kTileEfficiency[tgemm::kNumTiledShapes] = {1.0, 0.86, 0.62};
+  constexpr int64_t kCUs = 256;
+  int best = tgemm::kTile128x128;
+  double best_score = -1.0;
+  for (int s = 0; s < tgemm::kNumTiledShapes; ++s) {
+    const tgemm::TiledShapeInfo info = tgemm::tiled_shape_info(s);
+    const int64_t tiles = ((M + info.bm - 1) / info.bm) * ((N + info.bn - 1) / info.bn);
+    const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+    const double fill = static_cast<double>(tiles) / static_cast<double>(rounds * kCUs);
+    const double score = fill * kTileEfficiency[s];
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = s;
+    }
+  }
+  return best;
+}
+
+bool use_thin(int64_t M, int algo) {
+  if (algo == TGEMM_ALGO_THIN) return true;
+  if (algo == TGEMM_ALGO_TILED) return false;
+  return M <= kThinMaxM;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
+                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
+                 int algo, void* stream) {
+  const int st = validate_bf16(A, B, bias, C, M, N, K, lda, ldb, ldc, epilogue, out_dtype, algo);
+  if (st != TGEMM_OK) return st;
+  if (M == 0 || N == 0) return TGEMM_OK;
+
+  Bf16Args a;
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.vec_a = (K == 0 || (aligned16(A) && lda % 8 == 0)) ? 1 : 0;
+  a.vec_b = (K == 0 || (aligned16(B) && ldb % 8 == 0)) ? 1 : 0;
+  const int64_t out_align = out_dtype == TGEMM_OUT_BF16 ? 8 : 4;
+  a.vec_c = (aligned16(C) && ldc % out_align == 0) ? 1 : 0;
+
+  const int out_bf16 = out_dtype == TGEMM_OUT_BF16 ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (use_thin(M, algo)) {
+    e = tgemm::launch_bf16_thin(a, epilogue, out_bf16, s);
+  } else {
+    e = tgemm::launch_bf16_tiled(a, pick_tiled_shape(M, N), epilogue, out_bf16, s);
+  }
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+int gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
+              int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
+              void* stream) {
+  return gemm_bf16_ex(A, B, bias, C, M, N, K, lda, ldb, ldc, epilogue, out_dtype,
+                      TGEMM_ALGO_AUTO, stream);
+}
+
+int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB, void* C,
+                         int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return TGEMM_ERR_INVALID;
+  if (M == 0 || N == 0) return TGEMM_OK;
+  if (C == nullptr) return TGEMM_ERR_INVALID;
+  if (K > 0 && (A == nullptr || B == nullptr || sA == nullptr || sB == nullptr))
+    return TGEMM_ERR_INVALID;
+  if (!extent_ok(M, K, K) || !extent_ok(K, N, N) || !extent_ok(M, N, N)) return TGEMM_ERR_INVALID;
+
+  Fp8Args a;
+  a.A = static_cast<const uint8_t*>(A);
+  a.sA = sA;
+  a.B = static_cast<const uint8_t*>(B);
+  a.sB = sB;
+  a.C = static_cast<uint16_t*>(C);
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.G = static_cast<int>((K + 127) / 128);
+  a.H = static_cast<int>((N + 127) / 128);
+  a.vec_a = (aligned16(A) && K % 16 == 0) ? 1 : 0;
+  a.vec_b = (aligned8(B) && N % 8 == 0) ? 1 : 0;
+  const hipError_t e = tgemm::launch_fp8_blockscaled(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue, int out_dtype,
+                                  int algo) {
+  // Pointers play no part in the choice; pass dummies so only sizes are checked.
+  static const int kDummy = 0;
+  const void* d = &kDummy;
+  if (validate_bf16(d, d, d, d, M, N, K, K > 0 ? K : 1, N > 0 ? N : 1, N > 0 ? N : 1, epilogue,
+                    out_dtype, algo) != TGEMM_OK)
+    return nullptr;
+  if (use_thin(M, algo)) return tgemm::thin_kernel_name(static_cast<int>(M));
+  return tgemm::tiled_shape_info(pick_tiled_shape(M, N)).name;
+}
+
+const char* gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return nullptr;
+  return tgemm::fp8_kernel_name();
+}
+
+const char* gemm_status_string(int status) {
+  switch (status) {
+    case TGEMM_OK: return "ok";
+    case TGEMM_ERR_INVALID: return "invalid argument";
+    case TGEMM_ERR_UNSUPPORTED: return "unsupported request";
+    case TGEMM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gemm_abi_version(void) { return TGEMM_ABI_VERSION; }
+
+}  // extern "C"

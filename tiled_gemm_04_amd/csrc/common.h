@@ -1,0 +1,141 @@
+// Device-side helpers shared by the gfx950 GEMM kernels.
+//
+// Everything here is written for CDNA4 (gfx950, wave64, MFMA matrix cores,
+// 160 KB of LDS per compute unit).  Sources cited by short name:
+// "DeepGEMM page" = zwxr.cn/news/240083, "GEMM compute-cost page" =
+// kwkr.cn/news/191298, "tensor-core page" = llmtrend.com, 大语言模型（LLM）
+// 推理加速的秘诀：矩阵乘法、tensor-core.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tgemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies, 32 CUs each
+
+enum Epilogue { kEpiNone = 0, kEpiBias = 1, kEpiBiasGelu = 2 };
+
+// ---------------------------------------------------------------- bf16 ---
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16; the hardware conversion
+// (v_cvt_pk_bf16_f32) is what a plain __bf16 cast lowers to on gfx950.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+// -------------------------------------------------------------- epilogue ---
+
+// tanh-form GeLU.  0.5*(1 + tanh(u)) equals the logistic function at 2u, so
+// gelu(y) = y / (1 + exp(-2u)) with u = sqrt(2/pi) * (y + 0.044715 y^3); this
+// form has no cancellation for large negative y.  exp is taken as 2^x with
+// the hardware v_exp_f32.
+__device__ __forceinline__ float gelu_tanh(float y) {
+  constexpr float kSqrt2OverPi = 0.7978845608028654f;
+  constexpr float kCubic = 0.044715f;
+  constexpr float kLog2e = 1.4426950408889634f;
+  float u = kSqrt2OverPi * (y + kCubic * y * y * y);
+  float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * u);
+  return y / (1.0f + e);
+}
+
+template <int EPI>
+__device__ __forceinline__ float apply_epilogue(float acc, float bias) {
+  if constexpr (EPI == kEpiNone) {
+    return acc;
+  } else if constexpr (EPI == kEpiBias) {
+    return acc + bias;
+  } else {
+    return gelu_tanh(acc + bias);
+  }
+}
+
+// ----------------------------------------------------------- scheduling ---
+
+// Workgroups are dealt round-robin to the 8 dies (workgroup w runs on die
+// w % 8), and each die has its own L2.  Renumber so that each die receives a
+// contiguous run of logical tile ids; neighbouring logical tiles share rows
+// of A or columns of B and so hit the same L2.  Bijective on [0, total).
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  int per = total / kNumXcd;
+  int rem = total % kNumXcd;
+  int xcd = w % kNumXcd;
+  int idx = w / kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// Grouped ordering of a tiles_m x tiles_n grid: runs of `group` tile-rows are
+// walked column by column, so consecutive logical ids form compact blocks.
+__device__ __forceinline__ void tile_coords(int logical, int tiles_m, int tiles_n, int group,
+                                            int& tm, int& tn) {
+  int per_group = group * tiles_n;
+  int gid = logical / per_group;
+  int first_m = gid * group;
+  int gsize = tiles_m - first_m < group ? tiles_m - first_m : group;
+  int in_group = logical - gid * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+// ------------------------------------------------------------------- LDS ---
+
+// Operand tiles live in LDS as "chunk planes": for a tile of R rows whose
+// K extent is 8 chunks of 16 bytes, chunk c of row r sits at 16-byte slot
+//   c * R + (r ^ c)            (c < 8, so the XOR only permutes r's low 3 bits).
+// Eight lanes that read one chunk of eight consecutive rows, or write eight
+// different chunks of one row, always hit eight different 16-byte bank groups;
+// and because the XOR never touches bits 3 and up, rows 16 or 32 apart keep a
+// constant slot distance, so every MFMA block of a wave is addressed from a
+// single base register with immediate offsets.
+__device__ __forceinline__ int plane_slot(int rows, int r, int c) { return c * rows + (r ^ c); }
+
+// ------------------------------------------------------------- buffers ---
+
+// Buffer resource over [base, base + bytes), bytes clamped to 2^31 - 1.
+// Raw buffer loads whose offset falls outside the range return zero instead
+// of touching memory; the kernels use that for the edge rows of a tile and
+// pass kOutOfRange as the offset of any chunk that lies past M, N or K.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr uint32_t kBufferFlags = 0x00020000u;  // dword 3: 32-bit data format, no swizzle
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_window(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           static_cast<int>(kBufferFlags));
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// ------------------------------------------------------------ byte moves ---
+
+// v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value
+// (hi:lo).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+}  // namespace tgemm

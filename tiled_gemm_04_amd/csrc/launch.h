@@ -1,0 +1,54 @@
+// Host-side launch interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tgemm {
+
+// Problem description for the bf16 kernels.  Sizes are validated by the ABI
+// layer (each below 2^31); strides are in elements.
+struct Bf16Args {
+  const uint16_t* A;
+  const uint16_t* B;
+  const uint16_t* bias;
+  void* C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  int vec_a;  // 1: A rows may be read with 16-byte loads (aligned base, lda % 8 == 0)
+  int vec_b;  // 1: same for B
+  int vec_c;  // 1: C rows may be written with 16-byte stores
+};
+
+struct Fp8Args {
+  const uint8_t* A;
+  const float* sA;
+  const uint8_t* B;
+  const float* sB;
+  uint16_t* C;
+  int M, N, K;
+  int G;      // ceil(K / 128): A-scale columns, B-scale rows
+  int H;      // ceil(N / 128): B-scale columns
+  int vec_a;  // 1: A rows are 16-byte aligned (K % 16 == 0 and aligned base)
+  int vec_b;  // 1: B rows are 8-byte aligned (N % 8 == 0 and aligned base)
+};
+
+// Tiled bf16 kernel shapes (BM x BN output tile, 4 waves).
+enum TiledShape { kTile256x256 = 0, kTile256x128 = 1, kTile128x128 = 2, kNumTiledShapes = 3 };
+
+struct TiledShapeInfo {
+  int bm, bn;
+  const char* name;
+};
+TiledShapeInfo tiled_shape_info(int shape);
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epilogue, int out_bf16,
+                             hipStream_t stream);
+hipError_t launch_bf16_thin(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream);
+hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
+
+const char* thin_kernel_name(int M);
+const char* fp8_kernel_name();
+
+}  // namespace tgemm
