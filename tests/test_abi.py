@@ -78,8 +78,8 @@ def test_fp8_validation():
 
 def test_kernel_selection_table():
     name = binding.gemm_bf16_kernel_name
-    assert name(4096, 4096, 4096) == "tgemm_bf16_tiled_256x256x64"
-    assert name(2048, 16384, 4096) == "tgemm_bf16_tiled_256x256x64"
+    assert name(4096, 4096, 4096) == "tgemm_bf16_tiled_256x256x32"
+    assert name(2048, 16384, 4096) == "tgemm_bf16_tiled_256x256x32"
     assert name(2048, 4096, 16384) == "tgemm_bf16_tiled_256x128x64"
     assert name(64, 128256, 4096) == "tgemm_bf16_thin_m64"
     assert name(1, 128256, 4096) == "tgemm_bf16_thin_m16"

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace tgemm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -126,6 +128,27 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// The same window as a plain 4-dword descriptor, for inline assembly.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_window_words(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes));
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int32_t>(a & 0xffffffffu), static_cast<int32_t>((a >> 32) & 0xffffu), n,
+               static_cast<int32_t>(kBufferFlags)};
+}
+
+// 16-byte buffer load written straight into LDS: lane l's 16 bytes land at
+// LDS byte address lds_base + 16 l (lds_base must be wave-uniform), offsets
+// outside the window write zeros.  Emitted as inline assembly so the compiler
+// does not guard every later LDS read with a wait for all outstanding loads;
+// callers order these loads themselves with vmcnt waits and barriers.
+__device__ __forceinline__ void buf_load16_lds(i32x4 window, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(window)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
@@ -136,6 +159,30 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 // (hi:lo).
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ------------------------------------------------------------ scheduling ---
+
+// LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its
+// outstanding global loads (those are the prefetch of a later slice).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+#define TGEMM_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Slot of item k when n items are spread evenly over slots [a, b).
+__host__ __device__ constexpr int spread(int k, int n, int a, int b) { return a + (k * (b - a)) / n; }
+
+// f(std::integral_constant<int, 0>) ... f(std::integral_constant<int, N-1>),
+// expanded at compile time so every index is a constant.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace tgemm

@@ -1,27 +1,37 @@
-// LDS-tiled bf16 GEMM for gfx950: C = epilogue(A . B + bias), fp32 accumulate.
+// Direct-to-LDS bf16 GEMM for gfx950: C = epilogue(A . B + bias), fp32 accumulate.
 //
-// Structure (DeepGEMM page, sections 2.1-2.3 and 3.3; tensor-core page,
-// "Chunking" and "Registers与Tensor Cores"):
+// The method (DeepGEMM page, sections 2.1-2.3 and 3.3; tensor-core page,
+// "Chunking" and "Registers与Tensor Cores") maps onto CDNA4 as follows:
 //   * tiling -- each workgroup owns one BM x BN output tile and walks K in
-//     slices of BK = 64; four waves split the tile 2 x 2, so each wave owns
-//     a (BM/2) x (BN/2) block of 32 x 32 MFMA accumulators in registers;
-//   * staging -- every K slice of A (BM x 64) and B (64 x BN) is fetched with
-//     16-byte buffer loads into registers and written to LDS.  B arrives
-//     N-contiguous and is transposed 8 x 8 in registers on the way, so both
-//     operands sit K-contiguous in LDS, which is the layout the MFMA operand
-//     registers take;
-//   * pipelining -- two LDS stages; the global loads of slice t+1 are in
-//     flight while the MFMAs of slice t run, with one barrier per slice;
-//   * bank conflicts -- chunk-plane LDS layout with an XOR of the row's low
-//     bits (see plane_slot);
-//   * epilogue -- bias, tanh-GeLU and the output rounding are applied to the
-//     fp32 accumulators before the single store (GEMM compute-cost page,
-//     section 5.1); rows and columns past M, N are masked, and the K tail is
-//     zero-filled on both operands (DeepGEMM page, section 4.1).
+//     slices of BK; four waves split the tile 2 x 2, each owning a
+//     (BM/2) x (BN/2) block of 32 x 32 MFMA accumulators (AGPRs);
+//   * global -> LDS -- 16-byte buffer loads write straight into LDS (no
+//     register staging, no LDS store instructions).  Each wave instruction
+//     fills one contiguous KiB of LDS, lane l owning bytes 16l .. 16l+15, so
+//     the layout is chosen by which global chunk each lane fetches.  A rows
+//     (K-contiguous) and B rows (N-contiguous) are kept as they are in memory,
+//     with the 16-byte chunks of each row permuted by an XOR of the row index
+//     so that the MFMA operand reads below hit distinct LDS banks;
+//   * LDS -> registers -- A operands with one 16-byte read per lane; B
+//     operands with the gfx950 transposed read (ds_read_b64_tr_b16): within
+//     each group of 16 lanes, lane 4e+q supplies 4 consecutive columns of K
+//     row e and lane i receives column i of those 4 rows, i.e. 4 consecutive
+//     k of one n -- the K-contiguous operand layout MFMA wants, read from an
+//     N-contiguous tile (two reads per 8-k operand);
+//   * pipelining -- NS LDS stages: the loads of slice t+NS-1 are issued while
+//     slice t is multiplied, MFMA operands are double-buffered in registers,
+//     and every non-MFMA instruction is placed between MFMAs by a
+//     compile-time slot schedule, because with one wave per SIMD any burst of
+//     other instructions leaves the matrix unit idle;
+//   * epilogue -- bias, tanh-GeLU and output rounding applied to the fp32
+//     accumulators (GEMM compute-cost page, section 5.1), the tile routed
+//     through LDS so each lane stores 16 contiguous bytes; stores past M, N
+//     are masked, and loads past M, N, K read zero through the buffer range
+//     check (DeepGEMM page, section 4.1).
 //
-// Two instantiations per shape: VEC (aligned operands whose inner extents are
-// multiples of 8; edges handled by out-of-range buffer offsets, which read as
-// zero) and a general one that assembles edge chunks element by element.
+// Requirements (checked by the launcher, otherwise the general kernel runs):
+// A, B 16-byte aligned; lda, ldb multiples of 8; K, N multiples of 8; all
+// per-lane byte offsets below 2^31.
 #include "common.h"
 #include "launch.h"
 
@@ -30,192 +40,124 @@ namespace tgemm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;
 constexpr int kGroupM = 4;  // tile-rows per scheduling group
 
-template <int BM_, int BN_>
-struct Tiled {
-  static constexpr int BM = BM_;
-  static constexpr int BN = BN_;
-  static constexpr int WTM = BM / 2;  // wave tile (2 x 2 waves)
-  static constexpr int WTN = BN / 2;
-  static constexpr int FM = WTM / 32;  // 32 x 32 MFMA blocks per wave
-  static constexpr int FN = WTN / 32;
-  static constexpr int A_PER_THREAD = BM * 8 / kThreads;  // 16-byte chunks of A per thread
-  static constexpr int B_THREADS = BN;                     // threads owning an 8 x 8 B block
-  static constexpr int A_STAGE = BM * 8;                   // 16-byte slots per LDS stage
-  static constexpr int B_STAGE = BN * 8;
-  static constexpr int LDS_SLOTS = 2 * (A_STAGE + B_STAGE);
-  static_assert((BM * 8) % kThreads == 0, "A slice must split evenly over the threads");
-  static_assert(BN <= kThreads, "one thread per 8 x 8 block of the B slice");
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+template <int BM_, int BN_, int BK_, int NS_, int SPREAD_ = 1>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
+  // Loads of a slice are spread over the first KS*FM*FN/SPREAD MFMA slots.
+  static constexpr int SPREAD = SPREAD_;
+  static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile (2 x 2 waves)
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int KS = BK / 16;  // MFMA sub-steps per slice
+  // A stage: BM rows of BK bf16 (A_CPR chunks of 16 bytes each).
+  static constexpr int A_ROW = BK * 2;
+  static constexpr int A_CPR = BK / 8;
+  static constexpr int A_STAGE = BM * A_ROW;
+  // B stage: BK rows of BN bf16.
+  static constexpr int B_ROW = BN * 2;
+  static constexpr int B_CPR = BN / 8;
+  static constexpr int B_STAGE = BK * B_ROW;
+  static constexpr int STAGE = A_STAGE + B_STAGE;
+  static constexpr int LDS_BYTES = NS * STAGE;
+  // 1 KiB load blocks per wave and slice.
+  static constexpr int APW = A_STAGE / 1024 / 4;
+  static constexpr int BPW = B_STAGE / 1024 / 4;
+  static constexpr int LPS = APW + BPW;  // loads per thread per slice
+  // Epilogue staging: one 32-row strip of a wave's tile in fp32, rows padded by 16 bytes.
+  static constexpr int EPI_PITCH = WTN + 4;
+  static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+  static_assert(BN >= 128, "the B-row swizzle needs at least 16 chunks per row");
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32 x 32 block");
+  static_assert(A_STAGE % 4096 == 0 && B_STAGE % 4096 == 0, "stages must split into 4 waves x 1 KiB");
+  static_assert(NS >= 2, "at least two stages");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
+  static_assert(4 * 32 * EPI_PITCH * 4 <= LDS_BYTES, "epilogue staging must fit in LDS");
 };
 
-// 16-byte chunk (8 bf16) of row `row`, columns col .. col+7, zero outside
-// rows x cols; element by element (general instantiation).
-__device__ __forceinline__ u32x4 load16_checked(const uint16_t* base, int64_t ld, int row, int rows,
-                                                int col, int cols) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (row < rows) {
-    const uint16_t* p = base + static_cast<int64_t>(row) * ld + col;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (col + e < cols) v[e >> 1] |= static_cast<uint32_t>(p[e]) << (16 * (e & 1));
-    }
-  }
-  return v;
+// XOR applied to the 16-byte chunk index of A row r: consecutive rows that
+// share a 256-byte LDS bank row get different permutations, so 16 lanes
+// reading one chunk column of 16 consecutive rows touch 16 distinct bank
+// groups.
+template <class C>
+__device__ __forceinline__ int a_swz(int r) {
+  return (r / (16 / C::A_CPR)) % C::A_CPR;
 }
+// XOR applied to the chunk index of B row k: the four K rows read together by
+// a transposed read land in four different 64-byte bank segments.
+__device__ __forceinline__ int b_swz(int k) { return 4 * (k & 3); }
 
-// Column j of an 8 x 8 bf16 block given as 8 rows (k) of 8 columns (n): the 8
-// k-values of that column, two per dword, low half first.
-__device__ __forceinline__ u32x4 transpose_col(const u32x4 (&r)[8], int j) {
-  const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-  const int d = j >> 1;
-  u32x4 o;
-  o[0] = perm(r[1][d], r[0][d], sel);
-  o[1] = perm(r[3][d], r[2][d], sel);
-  o[2] = perm(r[5][d], r[4][d], sel);
-  o[3] = perm(r[7][d], r[6][d], sel);
-  return o;
-}
-
-template <class T, int EPI, bool OUT_BF16, bool VEC>
-__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
-                                                                int tiles_n) {
-  __shared__ u32x4 smem[T::LDS_SLOTS];
-  u32x4* sA = smem;                   // [2][8 chunks][BM]
-  u32x4* sB = smem + 2 * T::A_STAGE;  // [2][8 chunks][BN]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-
-  int tm, tn;
-  tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, kGroupM, tm, tn);
-  const int m0 = tm * T::BM;
-  const int n0 = tn * T::BN;
-
-  f32x16 acc[T::FM][T::FN];
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x16{};
-
-  // A: thread owns chunk a_c of rows a_r + 32 i.  B: thread (b_kb, b_nb) owns
-  // K rows 8 b_kb .. +7 and columns 8 b_nb .. +7 of the slice.
-  const int a_c = tid & 7;
-  const int a_r = tid >> 3;
-  const int b_kb = tid & 7;
-  const int b_nb = tid >> 3;
-  const bool b_owner = tid < T::B_THREADS;
-  const int64_t lda2 = p.lda * 2, ldb2 = p.ldb * 2;
-  const uint32_t a_voff = static_cast<uint32_t>(a_r * lda2 + 16 * a_c);
-  const uint32_t b_voff_ok = static_cast<uint32_t>(8 * b_kb * ldb2 + 16 * b_nb);
-  const uint32_t b_voff = (b_owner && n0 + 8 * b_nb < p.N) ? b_voff_ok : kOutOfRange;
-
-  u32x4 ra[T::A_PER_THREAD];
-  u32x4 rb[8];
-
-  auto gload = [&](int k0) {
-    if constexpr (VEC) {
-      const __amdgpu_buffer_rsrc_t wa = make_window(
-          p.A + static_cast<int64_t>(m0) * p.lda + k0,
-          (static_cast<int64_t>(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
-      const uint32_t av = (k0 + 8 * a_c < p.K) ? a_voff : kOutOfRange;
-#pragma unroll
-      for (int i = 0; i < T::A_PER_THREAD; ++i)
-        ra[i] = buf_load16(wa, av, static_cast<uint32_t>(32 * i * lda2));
-      const __amdgpu_buffer_rsrc_t wb = make_window(
-          p.B + static_cast<int64_t>(k0) * p.ldb + n0,
-          (static_cast<int64_t>(p.K - k0 - 1) * p.ldb + (p.N - n0)) * 2);
-      if (b_owner) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) rb[r] = buf_load16(wb, b_voff, static_cast<uint32_t>(r * ldb2));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < T::A_PER_THREAD; ++i)
-        ra[i] = load16_checked(p.A, p.lda, m0 + a_r + 32 * i, p.M, k0 + 8 * a_c, p.K);
-      if (b_owner) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          rb[r] = load16_checked(p.B, p.ldb, k0 + 8 * b_kb + r, p.K, n0 + 8 * b_nb, p.N);
-      }
-    }
-  };
-
-  auto sstore = [&](int stage) {
-    u32x4* a = sA + stage * T::A_STAGE + a_c * T::BM + (a_r ^ a_c);
-#pragma unroll
-    for (int i = 0; i < T::A_PER_THREAD; ++i) a[32 * i] = ra[i];
-    if (b_owner) {
-      u32x4* b = sB + stage * T::B_STAGE + b_kb * T::BN + 8 * b_nb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) b[j ^ b_kb] = transpose_col(rb, j);
-    }
-  };
-
+// Epilogue of one wave: its FM x FN accumulator blocks (transposed 32 x 32
+// layout, see the kernels) go through a private LDS strip of 32 rows, one
+// strip at a time, so that every lane stores 8 consecutive outputs (16 bytes
+// of bf16); bias, tanh-GeLU and rounding are applied on the way out
+// (GEMM compute-cost page, section 5.1).  row0 / col0: the wave tile's first
+// output row / column.  Rows >= M and columns >= N are not stored.
+template <int EPI, bool OUT_BF16, int FM, int FN>
+__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], float* strip, int lane,
+                                                int row0, int col0, const Bf16Args& p) {
+  constexpr int WTN = 32 * FN;
+  constexpr int PITCH = WTN + 4;  // floats; 16 bytes of padding per row
+  constexpr int LANES_PER_ROW = WTN / 8;
+  constexpr int ROWS_PER_PASS = kWave / LANES_PER_ROW;
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
-  auto compute = [&](int stage) {
+  const int erow = lane / LANES_PER_ROW;
+  const int ecol = 8 * (lane % LANES_PER_ROW);
+  const int gcol = col0 + ecol;
+  float bias[8];
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int c = 2 * ks + lhalf;
-      const u32x4* a = sA + stage * T::A_STAGE + c * T::BM + ((wm * T::WTM + lrow) ^ c);
-      const u32x4* b = sB + stage * T::B_STAGE + c * T::BN + ((wn * T::WTN + lrow) ^ c);
-      bf16x8 fa[T::FM], fb[T::FN];
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) fa[i] = __builtin_bit_cast(bf16x8, a[32 * i]);
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) fb[j] = __builtin_bit_cast(bf16x8, b[32 * j]);
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  const int KT = (p.K + kBK - 1) / kBK;
-  if (KT > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int t = 0; t < KT; ++t) {
-    if (t + 1 < KT) gload((t + 1) * kBK);
-    compute(t & 1);
-    if (t + 1 < KT) sstore((t + 1) & 1);
-    __syncthreads();
-  }
-
-  // Epilogue: MFMA 32x32 accumulator element 4*g + e of lane l is row
-  // 8*g + 4*(l/32) + e, column l%32 of its block.
-#pragma unroll
-  for (int j = 0; j < T::FN; ++j) {
-    const int col = n0 + wn * T::WTN + 32 * j + lrow;
-    float bias = 0.0f;
+  for (int e = 0; e < 8; ++e) {
+    bias[e] = 0.0f;
     if constexpr (EPI != kEpiNone) {
-      if (col < p.N) bias = bf16_bits_to_f32(p.bias[col]);
+      if (gcol + e < p.N) bias[e] = bf16_bits_to_f32(p.bias[gcol + e]);
     }
+  }
+  const bool full_cols = p.vec_c && gcol + 8 <= p.N;
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      const int rbase = m0 + wm * T::WTM + 32 * i + 4 * lhalf;
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = rbase + 8 * g + e;
-          if (row < p.M && col < p.N) {
-            const float v = apply_epilogue<EPI>(acc[i][j][4 * g + e], bias);
-            const int64_t off = static_cast<int64_t>(row) * p.ldc + col;
-            if constexpr (OUT_BF16) {
-              static_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
-            } else {
-              static_cast<float*>(p.C)[off] = v;
-            }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(strip + lrow * PITCH + 32 * j + 8 * g + 4 * lhalf) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                  acc[i][j][4 * g + 3]};
+#pragma unroll
+    for (int pass = 0; pass < 32 / ROWS_PER_PASS; ++pass) {
+      const int rr = erow + ROWS_PER_PASS * pass;
+      const float* src = strip + rr * PITCH + ecol;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = apply_epilogue<EPI>(v[e], bias[e]);
+      const int row = row0 + 32 * i + rr;
+      if (row < p.M) {
+        const int64_t off = static_cast<int64_t>(row) * p.ldc + gcol;
+        if constexpr (OUT_BF16) {
+          uint16_t* out = static_cast<uint16_t*>(p.C) + off;
+          if (full_cols) {
+            *reinterpret_cast<u32x4*>(out) =
+                u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7])};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (gcol + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
+          }
+        } else {
+          float* out = static_cast<float*>(p.C) + off;
+          if (full_cols) {
+            *reinterpret_cast<f32x4*>(out) = f32x4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4*>(out + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (gcol + e < p.N) out[e] = v[e];
           }
         }
       }
@@ -223,51 +165,257 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_tiled(Bf16Args p, int 
   }
 }
 
-template <class T, int EPI, bool OUT_BF16>
-hipError_t launch_t(const Bf16Args& a, hipStream_t s) {
-  const int tiles_m = (a.M + T::BM - 1) / T::BM;
-  const int tiles_n = (a.N + T::BN - 1) / T::BN;
-  const int total = tiles_m * tiles_n;
-  const bool vec = a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
-                   a.lda * 2 * T::BM < (int64_t{1} << 31) && a.ldb * 2 * kBK < (int64_t{1} << 31);
-  if (vec) {
-    hipLaunchKernelGGL((tgemm_bf16_tiled<T, EPI, OUT_BF16, true>), dim3(total), dim3(kThreads), 0,
-                       s, a, tiles_m, tiles_n);
-  } else {
-    hipLaunchKernelGGL((tgemm_bf16_tiled<T, EPI, OUT_BF16, false>), dim3(total), dim3(kThreads), 0,
-                       s, a, tiles_m, tiles_n);
+template <class C, int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
+                                                                int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (LDS load bases)
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+
+  int tm, tn;
+  tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, kGroupM, tm, tn);
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+
+  // acc[i][j] holds the transposed 32 x 32 block (MFMA operands swapped):
+  // element 4*g + e of lane l is row 32*i + l%32, column 32*j + 8*g + 4*(l/32) + e.
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+
+  // ---- global -> LDS: per-lane offsets inside the slice windows ----
+  // A block i of this wave covers 16-byte slots S = 64*blk + lane; slot S is
+  // chunk (S % A_CPR) ^ a_swz(row) of row S / A_CPR.  B likewise with b_swz.
+  // Every byte offset is carried in the per-lane offset so the buffer range
+  // check sees all of it; OR-ing in kOutOfRange (offsets stay below 2^31)
+  // turns a load into zeros.
+  const int64_t lda2 = p.lda * 2, ldb2 = p.ldb * 2;
+  uint32_t a_goff[C::APW];
+  int a_kc[C::APW];
+#pragma unroll
+  for (int i = 0; i < C::APW; ++i) {
+    const int s = 64 * (wave * C::APW + i) + lane;
+    const int r = s / C::A_CPR;
+    const int c = (s % C::A_CPR) ^ a_swz<C>(r);
+    a_goff[i] = static_cast<uint32_t>(r * lda2 + 16 * c);
+    a_kc[i] = 8 * c;
   }
+  uint32_t b_goff[C::BPW];
+#pragma unroll
+  for (int i = 0; i < C::BPW; ++i) {
+    const int s = 64 * (wave * C::BPW + i) + lane;
+    const int k = s / C::B_CPR;
+    const int c = (s % C::B_CPR) ^ b_swz(k);
+    b_goff[i] = static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange);
+  }
+  auto window_a = [&](int k0) {
+    return make_window_words(p.A + static_cast<int64_t>(m0) * p.lda + k0,
+                       (static_cast<int64_t>(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
+  };
+  auto window_b = [&](int k0) {
+    return make_window_words(p.B + static_cast<int64_t>(k0) * p.ldb + n0,
+                       (static_cast<int64_t>(p.K - k0 - 1) * p.ldb + (p.N - n0)) * 2);
+  };
+  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+  auto issue_a = [&](i32x4 w, int stage, int k0, int i) {
+    const uint32_t off = a_goff[i] | (k0 + a_kc[i] < p.K ? 0u : kOutOfRange);
+    buf_load16_lds(w, smem_base + stage * C::STAGE + (wave * C::APW + i) * 1024, off);
+  };
+  auto issue_b = [&](i32x4 w, int stage, int i) {
+    buf_load16_lds(w, smem_base + stage * C::STAGE + C::A_STAGE + (wave * C::BPW + i) * 1024,
+                   b_goff[i]);
+  };
+
+  // ---- LDS -> registers ----
+  const int lrow = lane & 31;
+  const int lhalf = lane >> 5;
+  // A operand of block i, sub-step ks: row wm*WTM + 32i + lrow, chunk 2ks + lhalf.
+  // The swizzle depends only on lrow (32i and wm*WTM are multiples of 16).
+  const int a_rd = (wm * C::WTM + lrow) * C::A_ROW;
+  const int a_x = a_swz<C>(lrow);
+  // B operand of block j: transposed reads; lane L = 16g + 4e + q supplies
+  // K row 8(g>>1) + e (+4 for the second half) and columns 16(g&1) + 4q .. +3
+  // of the block, and receives 4 k of column 16(g&1) + (L%16).
+  const int bg = lane >> 4, be = (lane >> 2) & 3, bq = lane & 3;
+  int b_rd[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    const int chunk = (((wn * C::WTN / 32) + j) ^ be) * 4 + 2 * (bg & 1) + (bq >> 1);
+    b_rd[j] = C::A_STAGE + (8 * (bg >> 1) + be) * C::B_ROW + chunk * 16 + 8 * (bq & 1);
+  }
+  constexpr int kNR = C::FM + C::FN;
+  bf16x8 fa[2][C::FM], fb[2][C::FN];
+  // Fragment f < FM is A block f, the rest are B blocks.
+  auto lds_read = [&](int buf, int stage, int ks, int f) {
+    const uint8_t* base = smem + stage * C::STAGE;
+    if (f < C::FM) {
+      const int off = a_rd + 32 * f * C::A_ROW + (((2 * ks + lhalf) ^ a_x) * 16);
+      fa[buf][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
+    } else {
+      const int j = f - C::FM;
+      const uint8_t* q = base + b_rd[j] + 16 * ks * C::B_ROW;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, q));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, q + 4 * C::B_ROW));
+      fb[buf][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  constexpr int kQ = C::FM * C::FN;
+  auto mfma_one = [&](int buf, int q) {
+    const int i = q / C::FN, j = q % C::FN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+
+  // Slot schedule of slice t (stage t % NS holds it; the loads of slice
+  // t+NS-1 go to the stage slice t-1 occupied).  Slots 0 .. KS*kQ-1 are the
+  // slice's MFMAs, sub-step u = slot / kQ using operand buffer u & 1:
+  //   loads of slice t+NS-1           spread over [0, kLoadEnd), at most one
+  //                                   per slot, so the vector memory path is
+  //                                   not flooded in bursts
+  //   operands of sub-step u+1        [u*kQ, u*kQ + kQ/2)   (u < KS-1)
+  //   wait for slice t+1, barrier     before slot kBar
+  //   operands of sub-step 0, t+1     [kBar, kBar + kQ/4)
+  // The barrier also certifies that every wave has finished reading the
+  // stage the next iteration's loads overwrite.
+  constexpr int kSlots = C::KS * kQ;
+  constexpr int kBar = (C::NS == 2) ? kSlots - kQ / 2 : (C::KS - 1) * kQ;
+  // With two stages slice t+1 is loaded in this very iteration, so all of
+  // its loads must precede the barrier.
+  constexpr int kLoadEnd = (C::NS == 2) ? (kBar < kSlots / C::SPREAD ? kBar : kSlots / C::SPREAD)
+                                       : kSlots / C::SPREAD;
+  static_assert(kLoadEnd >= C::LPS || C::LPS > kSlots, "one load per slot");
+  auto load_slot = [](int l) { return spread(l, C::LPS, 0, kLoadEnd); };
+  // Loads younger than slice t+1 when the barrier waits: the NS-3 slices
+  // issued in earlier iterations after it, plus this iteration's loads
+  // issued before the barrier.
+  constexpr int kBefore = [] {
+    int n = 0;
+    for (int l = 0; l < C::LPS; ++l) n += (spread(l, C::LPS, 0, kLoadEnd) < kBar) ? 1 : 0;
+    return n;
+  }();
+  constexpr int kAhead = (C::NS == 2) ? 0 : (C::NS - 3) * C::LPS + kBefore;
+  static_assert(kBar + kQ / 4 <= kSlots, "slot schedule");
+
+  const int KT = (p.K + C::BK - 1) / C::BK;
+  if (KT > 0) {
+    // Slices 0 .. NS-2 into stages 0 .. NS-2 (past K the loads read zeros).
+    static_for<C::NS - 1>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const i32x4 wa = window_a(s * C::BK), wb = window_b(s * C::BK);
+#pragma unroll
+      for (int i = 0; i < C::APW; ++i) issue_a(wa, s, s * C::BK, i);
+#pragma unroll
+      for (int i = 0; i < C::BPW; ++i) issue_b(wb, s, i);
+    });
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * C::LPS) : "memory");
+    lds_barrier();
+#pragma unroll
+    for (int f = 0; f < kNR; ++f) lds_read(0, 0, 0, f);
+
+    int cur = 0;
+    int lst = C::NS - 1;  // stage receiving slice t+NS-1
+    for (int t = 0; t < KT; ++t) {
+      const int nxt = cur + 1 == C::NS ? 0 : cur + 1;
+      const int kl = (t + C::NS - 1) * C::BK;
+      const i32x4 wa = window_a(kl), wb = window_b(kl);
+      static_for<kSlots>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int u = s / kQ;
+        if constexpr (s == kBar) {
+          TGEMM_SCHED_FENCE();
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAhead) : "memory");
+          lds_barrier();
+        }
+        TGEMM_SCHED_FENCE();
+        mfma_one(u & 1, s % kQ);
+        TGEMM_SCHED_FENCE();
+        static_for<kNR>([&](auto fc) {
+          constexpr int f = decltype(fc)::value;
+          if constexpr (u + 1 < C::KS && spread(f, kNR, u * kQ, u * kQ + kQ / 2) == s)
+            lds_read((u + 1) & 1, cur, u + 1, f);
+          if constexpr (spread(f, kNR, kBar, kBar + kQ / 4) == s) lds_read(0, nxt, 0, f);
+        });
+        static_for<C::APW>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (load_slot(i) == s) issue_a(wa, lst, kl, i);
+        });
+        static_for<C::BPW>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (load_slot(C::APW + i) == s) issue_b(wb, lst, i);
+        });
+      });
+      TGEMM_SCHED_FENCE();
+      lst = cur;
+      cur = nxt;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
+  lds_barrier();  // every wave is done with the operand stages
+
+  // ---- epilogue ----
+  store_wave_tile<EPI, OUT_BF16, C::FM, C::FN>(
+      acc, reinterpret_cast<float*>(smem) + wave * 32 * C::EPI_PITCH, lane, m0 + wm * C::WTM,
+      n0 + wn * C::WTN, p);
+}
+
+
+template <class C, int EPI, bool OUT_BF16>
+hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
+  const int tiles_m = (a.M + C::BM - 1) / C::BM;
+  const int tiles_n = (a.N + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL((tgemm_bf16_tiled<C, EPI, OUT_BF16>), dim3(tiles_m * tiles_n),
+                     dim3(kThreads), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <class T>
+template <class C>
 hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s) {
   if (out_bf16) {
-    if (epi == kEpiNone) return launch_t<T, kEpiNone, true>(a, s);
-    if (epi == kEpiBias) return launch_t<T, kEpiBias, true>(a, s);
-    return launch_t<T, kEpiBiasGelu, true>(a, s);
+    if (epi == kEpiNone) return launch_c<C, kEpiNone, true>(a, s);
+    if (epi == kEpiBias) return launch_c<C, kEpiBias, true>(a, s);
+    return launch_c<C, kEpiBiasGelu, true>(a, s);
   }
-  if (epi == kEpiNone) return launch_t<T, kEpiNone, false>(a, s);
-  if (epi == kEpiBias) return launch_t<T, kEpiBias, false>(a, s);
-  return launch_t<T, kEpiBiasGelu, false>(a, s);
+  if (epi == kEpiNone) return launch_c<C, kEpiNone, false>(a, s);
+  if (epi == kEpiBias) return launch_c<C, kEpiBias, false>(a, s);
+  return launch_c<C, kEpiBiasGelu, false>(a, s);
 }
+
+// Per tile shape: BK = 32 with four stages keeps three slices of loads in
+// flight for the large tiles (measured faster on MI355X than BK = 64 with two
+// stages, which keeps less than one slice in flight).
+using Cfg256x256 = Cfg<256, 256, 32, 4>;
+using Cfg256x128 = Cfg<256, 128, 64, 3>;
+using Cfg128x128 = Cfg<128, 128, 64, 4>;
 
 }  // namespace
 
 TiledShapeInfo tiled_shape_info(int shape) {
   switch (shape) {
-    case kTile256x256: return {256, 256, "tgemm_bf16_tiled_256x256x64"};
+    case kTile256x256: return {256, 256, "tgemm_bf16_tiled_256x256x32"};
     case kTile256x128: return {256, 128, "tgemm_bf16_tiled_256x128x64"};
     default: return {128, 128, "tgemm_bf16_tiled_128x128x64"};
   }
 }
 
+bool bf16_direct_ok(const Bf16Args& a, int shape) {
+  const TiledShapeInfo info = tiled_shape_info(shape);
+  // Largest per-lane offsets: a tile's rows of A, a slice's rows of B.
+  return a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
+         a.lda * 2 * info.bm < (int64_t{1} << 31) && a.ldb * 2 * 64 < (int64_t{1} << 31);
+}
+
 hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epi, int out_bf16,
                              hipStream_t s) {
+  if (!bf16_direct_ok(a, shape)) return launch_bf16_general(a, shape, epi, out_bf16, s);
   switch (shape) {
-    case kTile256x256: return dispatch_epi<Tiled<256, 256>>(a, epi, out_bf16, s);
-    case kTile256x128: return dispatch_epi<Tiled<256, 128>>(a, epi, out_bf16, s);
-    default: return dispatch_epi<Tiled<128, 128>>(a, epi, out_bf16, s);
+    case kTile256x256: return dispatch_epi<Cfg256x256>(a, epi, out_bf16, s);
+    case kTile256x128: return dispatch_epi<Cfg256x128>(a, epi, out_bf16, s);
+    default: return dispatch_epi<Cfg128x128>(a, epi, out_bf16, s);
   }
 }
 

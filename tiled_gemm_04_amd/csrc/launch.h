@@ -45,6 +45,9 @@ TiledShapeInfo tiled_shape_info(int shape);
 // Each returns hipSuccess or the launch error.
 hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                              hipStream_t stream);
+// Register-staged kernel for operands the direct-to-LDS kernel cannot take.
+hipError_t launch_bf16_general(const Bf16Args& a, int shape, int epilogue, int out_bf16,
+                               hipStream_t stream);
 hipError_t launch_bf16_thin(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream);
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
 
