@@ -4,28 +4,38 @@
 //
 // DeepGEMM page, section 2.4: low-precision inputs carry a scale per row
 // group or small block (here 1 x 128 along K for A, 128 x 128 for B), the
-// products are accumulated in fp32, and the scales bring the sum back to
-// the output format (bf16).
+// products are accumulated in fp32, and the scales bring the sum back to the
+// output format (bf16).
 //
-// One K slice is exactly one scale group (BK = 128).  For every 16 x 16
-// output block a wave issues one v_mfma_scale_f32_16x16x128_f8f6f4 with
-// neutral block exponents (E8M0 127 = 2^0) into a zeroed temporary, which
-// holds the group's exact partial sum, and then folds it into the fp32
-// accumulator with a single FMA per element: acc += P_g * (sA[i, g] * sB[g, J]).
-// A wave's columns lie inside one 128-column scale block of B (wave tiles
-// are at most 128 wide and start on multiples of their width, which divides
-// 128), so sB is one scalar per wave and slice and the row factor sA * sB is
-// formed once per row.
+// Mapping onto CDNA4:
+//   * one K slice is exactly one scale group (128 bytes of K), and one
+//     v_mfma_scale_f32_16x16x128_f8f6f4 (neutral E8M0 exponents 127 = 2^0)
+//     computes a 16 x 16 block's exact partial sum of the group into a
+//     short-lived temporary; one FMA per element folds it into the fp32
+//     accumulator: acc += P_g * (sA[i, g] * sB[g, J]).  The E8M0 block
+//     exponents of the instruction cannot hold arbitrary fp32 scales, hence
+//     the FMA;
+//   * the MFMA operands are swapped (B as the first operand) so each lane's
+//     accumulators belong to one output row: the row scale sA is one value
+//     per lane and 16-row block, and the column scale sB one value per wave
+//     (a wave's 64 columns lie inside one 128-column scale block);
+//   * the accumulators are updated by vector FMAs, so they live in
+//     architectural VGPRs; with two waves per SIMD (8 waves, 512 threads)
+//     each wave has 256 of them and owns a 128 x 64 block of a 256 x 256 tile
+//     (128 accumulator registers), and the second wave on the SIMD hides the
+//     other's LDS waits and FMA work;
+//   * A, B and the tile's column of A-scales go global -> LDS with direct
+//     buffer loads (no register staging); B stays N-contiguous in LDS and the
+//     K-contiguous B operand is read with ds_read_b64_tr_b8 (within each 16
+//     lanes, lane 2e+h supplies 8 columns of K row e and lane i receives
+//     column i of the 8 rows), four reads per 32-byte operand; 16-byte chunks
+//     of every LDS row are XOR-permuted by the row index so operand reads
+//     touch distinct LDS banks;
+//   * two LDS stages: slice g+1 is loaded while slice g is multiplied.
 //
-// Because the accumulators are updated by vector FMAs they must live in the
-// 256 architectural VGPRs (the MFMA-only AGPRs cannot be read by VALU
-// instructions), so a wave owns 128 x 64 outputs (128 fp32 per lane) and a
-// 256 x 128 tile is split over four waves (2 x 2), one per SIMD, which
-// leaves the AGPR file free as cheap spill space.  At 4096 x 14336 that is
-// 16 x 112 = 1792 tiles, exactly seven rounds of 256 compute units.  Data
-// movement is the same as the bf16 tiled kernel: two LDS stages, chunk-plane
-// LDS layout, and B transposed in registers (8 x 8 byte blocks) so that both
-// operands are K-contiguous in LDS.
+// Requirements (checked by the launcher, otherwise the general kernel runs):
+// A and B 16-byte aligned, K and N multiples of 16, per-lane byte offsets
+// below 2^31.
 #include "common.h"
 #include "launch.h"
 
@@ -33,81 +43,53 @@ namespace tgemm {
 
 namespace {
 
-constexpr int kWM = 2;  // waves along M
-constexpr int kWN = 2;  // waves along N
-constexpr int kThreads = 64 * kWM * kWN;
+constexpr int kThreads = 512;
 constexpr int kBM = 256;
-constexpr int kBN = 128;
+constexpr int kBN = 256;
 constexpr int kBK = 128;  // bytes of K per slice == one scale group
-constexpr int kWTM = kBM / kWM;
-constexpr int kWTN = kBN / kWN;
+constexpr int kWTM = 128;  // wave tile: 2 (M) x 4 (N) waves
+constexpr int kWTN = 64;
 constexpr int kFM = kWTM / 16;
 constexpr int kFN = kWTN / 16;
-constexpr int kAStage = kBM * 8;  // 16-byte chunks
-constexpr int kBStage = kBN * 8;
-constexpr int kAPerThread = kAStage / kThreads;
-constexpr int kRowsPerPass = kThreads / 8;  // A rows covered by one pass of the threads
-constexpr int kBBlocks = (kBK / 8) * (kBN / 8);  // 8 x 8 byte blocks per B slice
+constexpr int kAStage = kBM * kBK;
+constexpr int kBStage = kBK * kBN;
+constexpr int kStage = kAStage + kBStage;
+constexpr int kBlocksPerWave = kStage / 1024 / 8;  // 1 KiB direct loads per wave and slice
 constexpr int kGroupM = 4;
+constexpr int kScaleOne = 127;  // E8M0 exponent of 1.0
+constexpr int kFmtE4M3 = 0;     // f8f6f4 operand format code for FP8 E4M3
+constexpr int kEpiPitch = kWTN + 4;  // floats per row of the epilogue strip
 static_assert(128 % kWTN == 0, "a wave's columns must sit inside one 128-column scale block");
-static_assert(kAStage % kThreads == 0 && kBBlocks == kThreads && kBM <= kThreads, "thread split");
-static_assert(kBN / 8 * 16 == kThreads, "B mapping: 16 row groups x BN/8 column groups");
-constexpr int kScaleOne = 127;    // E8M0 exponent of 1.0
-constexpr int kFmtE4M3 = 0;       // f8f6f4 operand format code for FP8 E4M3
+static_assert(kAStage / 1024 == 4 * kBlocksPerWave, "waves 0-3 load A, waves 4-7 load B");
 
-// Byte-by-byte loads of one 16-byte chunk of an A row / one 8-byte chunk of
-// a B row, zero outside the matrix (general instantiation for unaligned
-// rows).
-__device__ __forceinline__ u32x4 load_a16_checked(const uint8_t* A, int K, int row, int M, int k) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (row < M) {
-    const uint8_t* p = A + static_cast<int64_t>(row) * K + k;
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (k + e < K) v[e >> 2] |= static_cast<uint32_t>(p[e]) << (8 * (e & 3));
-  }
-  return v;
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+#define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Chunk permutations.  A rows are 128 bytes (8 chunks, two rows per 256-byte
+// bank row): 16 consecutive rows read at one chunk land in 16 bank groups.
+// B rows are 256 bytes (16 chunks): the 16 K rows k0+e and k0+32+e (e < 8)
+// read together by one transposed read land in 16 bank groups.
+__device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int b_swz(int k) { return (k & 7) | (((k >> 5) & 1) << 3); }
+
+// 4-byte buffer load written straight into LDS (lane l -> lds_base + 4 l).
+__device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(window)
+               : "memory", "m0");
 }
 
-__device__ __forceinline__ u32x2 load_b8_checked(const uint8_t* B, int N, int row, int K, int col) {
-  u32x2 v = {0u, 0u};
-  if (row < K) {
-    const uint8_t* p = B + static_cast<int64_t>(row) * N + col;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (col + e < N) v[e >> 2] |= static_cast<uint32_t>(p[e]) << (8 * (e & 3));
-  }
-  return v;
-}
-
-// 4 x 4 byte transpose: x[q] holds row q (bytes = columns 0..3); returns the
-// four columns, each as one dword with row 0 in the low byte.
-__device__ __forceinline__ void transpose4x4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
-                                             uint32_t& y0, uint32_t& y1, uint32_t& y2,
-                                             uint32_t& y3) {
-  const uint32_t t0 = perm(x1, x0, 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
-  const uint32_t t1 = perm(x1, x0, 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
-  const uint32_t t2 = perm(x3, x2, 0x05010400u);
-  const uint32_t t3 = perm(x3, x2, 0x07030602u);
-  y0 = perm(t2, t0, 0x05040100u);
-  y1 = perm(t2, t0, 0x07060302u);
-  y2 = perm(t3, t1, 0x05040100u);
-  y3 = perm(t3, t1, 0x07060302u);
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x128x128(Fp8Args p, int tiles_m,
-                                                                    int tiles_n) {
-  __shared__ u32x4 smem[2 * (kAStage + kBStage)];
-  __shared__ __attribute__((aligned(16))) float s_scale_a[2][kBM];
-  u32x4* sA = smem;                 // [2][8 chunks][BM]
-  u32x4* sB = smem + 2 * kAStage;   // [2][8 chunks][BN]
+__global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args p, int tiles_m,
+                                                                     int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(256))) float s_sa[2][kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / kWN;
-  const int wn = wave % kWN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2;
+  const int wn = wave & 3;
 
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, kGroupM, tm, tn);
@@ -115,145 +97,171 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x128x128(Fp8Args 
   const int n0 = tn * kBN;
   const int hb = (n0 + wn * kWTN) / 128;  // this wave's B-scale column
 
+  // acc[i][j]: 16 x 16 block, transposed by the operand swap: element e of
+  // lane l is row 16*i + l%16, column 16*j + 4*(l/16) + e of the wave tile.
   f32x4 acc[kFM][kFN];
 #pragma unroll
   for (int i = 0; i < kFM; ++i)
 #pragma unroll
     for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4{};
 
-  // A: thread owns chunk a_c of rows a_r + 32 i.  B: thread (b_k8, b_nb) owns
-  // K rows 8 b_k8 .. +7 and columns 8 b_nb .. +7; transposed, they fill half
-  // (b_k8 & 1) of chunk b_k8 / 2 of eight LDS columns.
-  const int a_c = tid & 7;
-  const int a_r = tid >> 3;
-  const int b_k8 = tid & 15;
-  const int b_nb = tid >> 4;  // 0 .. BN/8 - 1
-  const uint32_t a_voff = static_cast<uint32_t>(a_r * p.K + 16 * a_c);
-  const uint32_t b_voff =
-      (n0 + 8 * b_nb < p.N) ? static_cast<uint32_t>(8 * b_k8 * p.N + 8 * b_nb) : kOutOfRange;
-
-  u32x4 ra[kAPerThread];
-  u32x2 rb[8];
-  float rs = 0.0f;
-
-  auto gload = [&](int g) {
-    const int k0 = g * kBK;
-    if constexpr (VEC) {
-      const __amdgpu_buffer_rsrc_t wa = make_window(
-          p.A + static_cast<int64_t>(m0) * p.K + k0,
-          static_cast<int64_t>(p.M - m0 - 1) * p.K + (p.K - k0));
-      const uint32_t av = (k0 + 16 * a_c < p.K) ? a_voff : kOutOfRange;
+  // ---- global -> LDS.  Block b < 32 holds A rows 8b .. 8b+7, block
+  // 32 + b holds B rows 4b .. 4b+3; slot 64b + lane holds chunk
+  // (slot % chunks-per-row) ^ swizzle(row) of its row. ----
+  const bool loads_a = wave < 4;
+  const int blk0 = (wave & 3) * kBlocksPerWave;
+  // A block blk (rows 8 blk .. +7): slot 64 blk + lane is row 8 blk + lane/8,
+  // physical chunk lane % 8, logical chunk (lane % 8) ^ a_swz(row), and
+  // a_swz(row) = (4 blk + lane/16) % 8 takes two forms by the parity of blk.
+  // B block blk (K rows 4 blk .. +3): row 4 blk + lane/16, physical chunk
+  // lane % 16, and b_swz(row) likewise has two forms by the parity of blk
+  // (bit 3 of it is (wave & 3) & 1 for every block of this wave).  The row
+  // offset of the block goes into the buffer base, so a lane keeps only its
+  // two in-block offsets.
+  int lc[2];      // logical chunk for even / odd blocks
+  uint32_t vo[2];  // in-block byte offset for even / odd blocks
 #pragma unroll
-      for (int i = 0; i < kAPerThread; ++i)
-        ra[i] = buf_load16(wa, av, static_cast<uint32_t>(kRowsPerPass * i * p.K));
-      const __amdgpu_buffer_rsrc_t wb = make_window(
-          p.B + static_cast<int64_t>(k0) * p.N + n0,
-          static_cast<int64_t>(p.K - k0 - 1) * p.N + (p.N - n0));
-#pragma unroll
-      for (int r = 0; r < 8; ++r) rb[r] = buf_load8(wb, b_voff, static_cast<uint32_t>(r * p.N));
+  for (int par = 0; par < 2; ++par) {
+    if (loads_a) {
+      lc[par] = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+      vo[par] = static_cast<uint32_t>((lane >> 3) * p.K + 16 * lc[par]);
     } else {
-#pragma unroll
-      for (int i = 0; i < kAPerThread; ++i)
-        ra[i] = load_a16_checked(p.A, p.K, m0 + a_r + kRowsPerPass * i, p.M, k0 + 16 * a_c);
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        rb[r] = load_b8_checked(p.B, p.N, k0 + 8 * b_k8 + r, p.K, n0 + 8 * b_nb);
+      lc[par] = (lane & 15) ^ (((4 * par + (lane >> 4)) & 7) | (((wave & 3) & 1) << 3));
+      vo[par] = static_cast<uint32_t>((lane >> 4) * p.N + 16 * lc[par]) |
+                (n0 + 16 * lc[par] < p.N ? 0u : kOutOfRange);
     }
-    if (tid < kBM) {
-      const int row = m0 + tid;
-      rs = row < p.M ? p.sA[static_cast<int64_t>(row) * p.G + g] : 0.0f;
+  }
+  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+  const uint32_t ssa_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(float, &s_sa[0][0])));
+  // Waves 0-3 also fetch the scale column sA[m0 + 64*wave + lane, g].
+  const uint32_t sa_off = static_cast<uint32_t>((64 * (wave & 3) + lane) * p.G * 4);
+  // This wave's i-th block of slice g (past K the loads read zeros).
+  auto issue = [&](int g, int i) {
+    const int stage = g & 1;
+    const int k0 = g * kBK;
+    const int blk = blk0 + i;
+    if (loads_a) {
+      const int r0 = m0 + 8 * blk;
+      const i32x4 w = make_window_words(p.A + static_cast<int64_t>(r0) * p.K + k0,
+                                        static_cast<int64_t>(p.M - r0 - 1) * p.K + (p.K - k0));
+      buf_load16_lds(w, smem_base + stage * kStage + blk * 1024,
+                     vo[i & 1] | (k0 + 16 * lc[i & 1] < p.K ? 0u : kOutOfRange));
+    } else {
+      const int k = k0 + 4 * blk;
+      const i32x4 w = make_window_words(p.B + static_cast<int64_t>(k) * p.N + n0,
+                                        static_cast<int64_t>(p.K - k - 1) * p.N + (p.N - n0));
+      buf_load16_lds(w, smem_base + stage * kStage + kAStage + blk * 1024, vo[i & 1]);
     }
+  };
+  auto issue_scales = [&](int g) {
+    if (loads_a) {
+      const i32x4 w = make_window_words(
+          p.sA + static_cast<int64_t>(m0) * p.G + g,
+          (g < p.G ? (static_cast<int64_t>(p.M - m0 - 1) * p.G + 1) * 4 : 0));
+      buf_load4_lds(w, ssa_base + ((g & 1) * kBM + 64 * (wave & 3)) * 4, sa_off);
+    }
+  };
+  auto issue_slice = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < kBlocksPerWave; ++i) issue(g, i);
+    issue_scales(g);
   };
 
-  auto sstore = [&](int stage) {
-    u32x4* a = sA + stage * kAStage + a_c * kBM + (a_r ^ a_c);
+  // ---- LDS -> registers ----
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
+  // A operand of block i: row wm*128 + 16i + l16, K bytes 32 lq .. +31
+  // (chunks 2 lq and 2 lq + 1).  The swizzle depends only on l16.
+  const int a_row = wm * kWTM + l16;
+  const int a_off0 = a_row * kBK + (((2 * lq) ^ a_swz(l16)) * 16);
+  const int a_off1 = a_row * kBK + (((2 * lq + 1) ^ a_swz(l16)) * 16);
+  // B operand of block j: column chunk cj = 4 wn + j; transposed read s
+  // covers K rows 32 lq + 8 s + e for lane 16 lq + 2 e + h, columns 8 h .. +7.
+  const int be = l16 >> 1, bh = l16 & 1;
+  int b_off[kFN];
 #pragma unroll
-    for (int i = 0; i < kAPerThread; ++i) a[kRowsPerPass * i] = ra[i];
-    if (tid < kBM) s_scale_a[stage][tid] = rs;
-    // Column j of the 8 x 8 byte block gets its 8 K-bytes, rows 0..3 in the
-    // low dword and rows 4..7 in the high dword.
-    uint32_t col[8][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        uint32_t y0, y1, y2, y3;
-        transpose4x4(rb[4 * h][d], rb[4 * h + 1][d], rb[4 * h + 2][d], rb[4 * h + 3][d], y0, y1,
-                     y2, y3);
-        col[4 * d + 0][h] = y0;
-        col[4 * d + 1][h] = y1;
-        col[4 * d + 2][h] = y2;
-        col[4 * d + 3][h] = y3;
-      }
-    }
-    const int chunk = b_k8 >> 1;
-    u32x2* b = reinterpret_cast<u32x2*>(sB + stage * kBStage + chunk * kBN + 8 * b_nb) + (b_k8 & 1);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[2 * (j ^ chunk)] = u32x2{col[j][0], col[j][1]};
-  };
-
-  const int lrow = lane & 15;
-  const int c = 2 * (lane >> 4);  // this lane's two 16-byte chunks of the 128-byte K slice
-  auto compute = [&](int stage, int g) {
-    const float sb = hb < p.H ? p.sB[static_cast<int64_t>(g) * p.H + hb] : 0.0f;
-    const u32x4* a_lo = sA + stage * kAStage + c * kBM + ((wm * kWTM + lrow) ^ c);
-    const u32x4* a_hi = sA + stage * kAStage + (c + 1) * kBM + ((wm * kWTM + lrow) ^ (c + 1));
-    const u32x4* b_lo = sB + stage * kBStage + c * kBN + ((wn * kWTN + lrow) ^ c);
-    const u32x4* b_hi = sB + stage * kBStage + (c + 1) * kBN + ((wn * kWTN + lrow) ^ (c + 1));
-    i32x8 fb[kFN];
-#pragma unroll
-    for (int j = 0; j < kFN; ++j) {  // B operands stay in registers for the slice
-      const u32x4 lo = b_lo[16 * j];
-      const u32x4 hi = b_hi[16 * j];
-      fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-#pragma unroll
-    for (int i = 0; i < kFM; ++i) {
-      const u32x4 lo = a_lo[16 * i];
-      const u32x4 hi = a_hi[16 * i];
-      const i32x8 fa = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      // Rows of this lane in block i: 4*(lane/16) + e.
-      const f32x4 sa = *reinterpret_cast<const f32x4*>(
-          &s_scale_a[stage][wm * kWTM + 16 * i + 4 * (lane >> 4)]);
-      const f32x4 s = sa * sb;
-#pragma unroll
-      for (int j = 0; j < kFN; ++j) {
-        const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            fa, fb[j], f32x4{}, kFmtE4M3, kFmtE4M3, 0, kScaleOne, 0, kScaleOne);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(part[e], s[e], acc[i][j][e]);
-      }
-    }
-  };
+  for (int j = 0; j < kFN; ++j) {
+    const int k = 32 * lq + be;
+    b_off[j] = kAStage + k * kBN + (((4 * wn + j) ^ b_swz(k)) * 16) + 8 * bh;
+  }
 
   const int G = p.G;
   if (G > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    if (g + 1 < G) gload(g + 1);
-    compute(g & 1, g);
-    if (g + 1 < G) sstore((g + 1) & 1);
-    __syncthreads();
+    issue_slice(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    // B scales of this wave's column block, 64 groups per register: lane l
+    // holds sB[g0 + l, hb] and each group's value is taken with readlane.
+    float sb_lanes = 0.0f;
+    for (int g = 0; g < G; ++g) {
+      const int stage = g & 1;
+      const uint8_t* base = smem + stage * kStage;
+      if ((g & 63) == 0) {
+        const int gl = g + lane;
+        sb_lanes = (gl < G && hb < p.H) ? p.sB[static_cast<int64_t>(gl) * p.H + hb] : 0.0f;
+      }
+      const float sb = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sb_lanes), g & 63));
+      i32x8 fb[kFN];
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) {
+        i32x2 q[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          q[s] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j] + s * 8 * kBN));
+        fb[j] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+      }
+#pragma unroll
+      for (int i = 0; i < kFM; ++i) {
+        if (i < kBlocksPerWave) issue(g + 1, i);  // slice g+1 into the idle stage
+        if (i == kFM - 1) issue_scales(g + 1);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + a_off0 + 16 * i * kBK);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + a_off1 + 16 * i * kBK);
+        const i32x8 fa = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const float s = s_sa[stage][a_row + 16 * i] * sb;
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) {
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              fb[j], fa, f32x4{}, kFmtE4M3, kFmtE4M3, 0, kScaleOne, 0, kScaleOne);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(part[e], s, acc[i][j][e]);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // slice g+1 has landed
+      lds_barrier();                                     // and slice g is no longer read
+    }
   }
 
-  // Epilogue: MFMA 16x16 accumulator element e of lane l is row 4*(l/16)+e,
-  // column l%16 of its block.
-  const int row_off = 4 * (lane >> 4);
+  // ---- epilogue: 16-row strips through this wave's LDS area, 16-byte stores ----
+  float* strip = reinterpret_cast<float*>(smem) + wave * 16 * kEpiPitch;
+  const int erow = lane >> 3;       // 8 rows per pass
+  const int ecol = 8 * (lane & 7);  // 8 columns per lane
+  const int gcol = n0 + wn * kWTN + ecol;
+  const bool full_cols = gcol + 8 <= p.N;
 #pragma unroll
-  for (int j = 0; j < kFN; ++j) {
-    const int col = n0 + wn * kWTN + 16 * j + lrow;
+  for (int i = 0; i < kFM; ++i) {
 #pragma unroll
-    for (int i = 0; i < kFM; ++i) {
+    for (int j = 0; j < kFN; ++j)
+      *reinterpret_cast<f32x4*>(strip + l16 * kEpiPitch + 16 * j + 4 * lq) = acc[i][j];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * kWTM + 16 * i + row_off + e;
-        if (row < p.M && col < p.N)
-          p.C[static_cast<int64_t>(row) * p.N + col] = f32_to_bf16_bits(acc[i][j][e]);
+    for (int pass = 0; pass < 2; ++pass) {
+      const int rr = erow + 8 * pass;
+      const float* src = strip + rr * kEpiPitch + ecol;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+      const int row = m0 + wm * kWTM + 16 * i + rr;
+      if (row < p.M) {
+        uint16_t* out = p.C + static_cast<int64_t>(row) * p.N + gcol;
+        if (full_cols) {
+          *reinterpret_cast<u32x4*>(out) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                 pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+        } else {
+          const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gcol + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
+        }
       }
     }
   }
@@ -261,20 +269,19 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x128x128(Fp8Args 
 
 }  // namespace
 
-const char* fp8_kernel_name() { return "tgemm_fp8_bs_256x128x128"; }
+const char* fp8_kernel_name() { return "tgemm_fp8_bs_256x256x128"; }
 
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t s) {
+  const bool direct = a.vec_a && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0 && a.K % 16 == 0 &&
+                      a.N % 16 == 0 &&
+                      static_cast<int64_t>(a.K) * kBM < (int64_t{1} << 31) &&
+                      static_cast<int64_t>(a.N) * kBK < (int64_t{1} << 31) &&
+                      static_cast<int64_t>(kBM) * a.G * 4 < (int64_t{1} << 31);
+  if (!direct) return launch_fp8_general(a, s);
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.N + kBN - 1) / kBN;
-  const bool vec = a.vec_a && a.vec_b && static_cast<int64_t>(a.K) * kBM < (int64_t{1} << 31) &&
-                   static_cast<int64_t>(a.N) * kBK < (int64_t{1} << 31);
-  if (vec) {
-    hipLaunchKernelGGL(tgemm_fp8_bs_256x128x128<true>, dim3(tiles_m * tiles_n), dim3(kThreads), 0,
-                       s, a, tiles_m, tiles_n);
-  } else {
-    hipLaunchKernelGGL(tgemm_fp8_bs_256x128x128<false>, dim3(tiles_m * tiles_n), dim3(kThreads), 0,
-                       s, a, tiles_m, tiles_n);
-  }
+  hipLaunchKernelGGL(tgemm_fp8_bs_256x256x128, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
+                     tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -50,6 +50,8 @@ hipError_t launch_bf16_general(const Bf16Args& a, int shape, int epilogue, int o
                                hipStream_t stream);
 hipError_t launch_bf16_thin(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream);
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
+// Register-staged kernel for FP8 operands the direct-to-LDS kernel cannot take.
+hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
 const char* thin_kernel_name(int M);
 const char* fp8_kernel_name();
