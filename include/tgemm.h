@@ -139,12 +139,16 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
                          void* C, int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Name of the kernel configuration gemm_bf16_ex would launch for a problem
- * (no launch, no validation of pointers).  Returns a static string, or NULL
- * when the request is invalid. */
+ * with 16-byte aligned operands (no launch, no validation of pointers;
+ * operands that are not 16-byte aligned, or whose row strides are not
+ * multiples of 8, run the register-staged kernel of the same tile shape).
+ * Returns a static string, or NULL when the request is invalid. */
 const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue,
                                   int out_dtype, int algo);
 
-/* Name of the kernel configuration gemm_fp8_blockscaled launches. */
+/* Name of the kernel configuration gemm_fp8_blockscaled launches for these
+ * sizes (the direct-to-LDS kernel when K is a multiple of 16, the general
+ * kernel otherwise).  No launch. */
 const char* gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K);
 
 /* Static, human-readable text for a status code. */

@@ -87,3 +87,5 @@ def test_kernel_selection_table():
     assert name(65, 64, 64, algo=binding.ALGO_THIN) is None
     assert name(-1, 64, 64) is None
     assert binding.gemm_fp8_kernel_name(4096, 14336, 4096) == "tgemm_fp8_bs_256x256x128"
+    assert binding.gemm_fp8_kernel_name(4097, 14335, 4096) == "tgemm_fp8_bs_256x256x128"
+    assert binding.gemm_fp8_kernel_name(64, 64, 200).startswith("tgemm_fp8_bs_general")

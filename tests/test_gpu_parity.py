@@ -215,6 +215,31 @@ def test_fp8_small_shapes(shape):
     run_and_check_fp8(qa, sa, qb, sb, label="small")
 
 
+@pytest.mark.parametrize("shape", [(300, 264, 384), (97, 131, 256)])
+def test_fp8_unaligned_operands(shape):
+    """A and B at odd byte offsets, C at an odd element offset: the direct
+    kernel's byte-addressed loads and 2-byte stores."""
+    dev = _dev()
+    M, N, K = shape
+    qa, sa, qb, sb = wl.fp8_inputs(wl.WORKLOADS["fp8"], device=dev, M=M, N=N, K=K)
+    ra = torch.zeros(M * K + 3, dtype=torch.uint8, device=dev)
+    ra[3:].copy_(qa.view(torch.uint8).reshape(-1))
+    rb = torch.zeros(K * N + 1, dtype=torch.uint8, device=dev)
+    rb[1:].copy_(qb.view(torch.uint8).reshape(-1))
+    a_u = ra[3:].view(torch.float8_e4m3fn).view(M, K)
+    b_u = rb[1:].view(torch.float8_e4m3fn).view(K, N)
+    cbuf = torch.full((M * N + 2,), CANARY_BF16, dtype=torch.int16, device=dev)
+    c = cbuf[1:M * N + 1].view(torch.bfloat16).view(M, N)
+    print(f"[gpu] fp8 unaligned M={M} N={N} K={K}", flush=True)
+    tg.gemm_fp8_blockscaled(a_u, sa, b_u, sb, c)
+    torch.cuda.synchronize()
+    assert int(cbuf[0]) == CANARY_BF16 and int(cbuf[M * N + 1]) == CANARY_BF16
+    y, d = og.gemm_fp8_blockscaled_bits(wl.bits_u8(qa), sa.cpu().numpy(), wl.bits_u8(qb),
+                                        sb.cpu().numpy())
+    r = og.compare(c.float().cpu().double().numpy(), y, d, TOL_FP8)
+    assert r["ok"], r
+
+
 def test_fp8_integer_codes_exact():
     dev = _dev()
     M, N, K = 64, 128, 256

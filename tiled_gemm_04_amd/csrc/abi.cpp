@@ -146,6 +146,7 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
   a.H = static_cast<int>((N + 127) / 128);
   a.vec_a = (aligned16(A) && K % 16 == 0) ? 1 : 0;
   a.vec_b = (aligned8(B) && N % 8 == 0) ? 1 : 0;
+  a.vec_c = (aligned16(C) && N % 8 == 0) ? 1 : 0;
   const hipError_t e = tgemm::launch_fp8_blockscaled(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
@@ -164,7 +165,7 @@ const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue,
 
 const char* gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return nullptr;
-  return tgemm::fp8_kernel_name();
+  return tgemm::fp8_kernel_name(M, N, K);
 }
 
 const char* gemm_status_string(int status) {

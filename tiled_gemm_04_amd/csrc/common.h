@@ -142,10 +142,16 @@ __device__ __forceinline__ i32x4 make_window_words(const void* base, int64_t byt
 // outside the window write zeros.  Emitted as inline assembly so the compiler
 // does not guard every later LDS read with a wait for all outstanding loads;
 // callers order these loads themselves with vmcnt waits and barriers.
+// The descriptor and base must be wave-uniform; readfirstlane makes that
+// explicit to the compiler (and costs nothing for values already scalar).
+__device__ __forceinline__ i32x4 uniform_words(i32x4 w) {
+  return i32x4{__builtin_amdgcn_readfirstlane(w[0]), __builtin_amdgcn_readfirstlane(w[1]),
+               __builtin_amdgcn_readfirstlane(w[2]), __builtin_amdgcn_readfirstlane(w[3])};
+}
 __device__ __forceinline__ void buf_load16_lds(i32x4 window, uint32_t lds_base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds_base), "v"(voff), "s"(window)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_words(window))
                : "memory", "m0");
 }
 

@@ -34,8 +34,12 @@
 //   * two LDS stages: slice g+1 is loaded while slice g is multiplied.
 //
 // Requirements (checked by the launcher, otherwise the general kernel runs):
-// A and B 16-byte aligned, K and N multiples of 16, per-lane byte offsets
-// below 2^31.
+// K a multiple of 16 (whole 16-byte chunks of A along K) and per-lane byte
+// offsets below 2^31.  Rows of A, B and C need no particular alignment: the
+// 16-byte buffer loads are byte-addressed (gfx9 unaligned access mode; on
+// MI355X they return the exact bytes at any offset), B columns past N only
+// reach accumulators of columns that are never stored, and the stores fall
+// back to 2-byte writes when C rows are not 16-byte aligned.
 #include "common.h"
 #include "launch.h"
 
@@ -76,7 +80,7 @@ __device__ __forceinline__ int b_swz(int k) { return (k & 7) | (((k >> 5) & 1) <
 __device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
-               : "s"(lds_base), "v"(voff), "s"(window)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_words(window))
                : "memory", "m0");
 }
 
@@ -135,22 +139,51 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   const uint32_t ssa_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(float, &s_sa[0][0])));
   // Waves 0-3 also fetch the scale column sA[m0 + 64*wave + lane, g].
   const uint32_t sa_off = static_cast<uint32_t>((64 * (wave & 3) + lane) * p.G * 4);
+  int tail_lds = -1;  // LDS byte offset of a straddling B chunk to fix up, or -1
+  // Buffer windows of slice g: A rows m0 .. M-1 from column k0, B rows
+  // k0 .. K-1 from column n0 (one window per matrix and slice; a block's row
+  // offset goes into the per-lane offset).
+  auto window_a = [&](int g) {
+    const int k0 = g * kBK;
+    return make_window_words(p.A + static_cast<int64_t>(m0) * p.K + k0,
+                             static_cast<int64_t>(p.M - m0 - 1) * p.K + (p.K - k0));
+  };
+  auto window_b = [&](int g) {
+    const int k0 = g * kBK;
+    return make_window_words(p.B + static_cast<int64_t>(k0) * p.N + n0,
+                             static_cast<int64_t>(p.K - k0 - 1) * p.N + (p.N - n0));
+  };
   // This wave's i-th block of slice g (past K the loads read zeros).
-  auto issue = [&](int g, int i) {
+  auto issue = [&](i32x4 w, int g, int i) {
     const int stage = g & 1;
     const int k0 = g * kBK;
     const int blk = blk0 + i;
     if (loads_a) {
-      const int r0 = m0 + 8 * blk;
-      const i32x4 w = make_window_words(p.A + static_cast<int64_t>(r0) * p.K + k0,
-                                        static_cast<int64_t>(p.M - r0 - 1) * p.K + (p.K - k0));
       buf_load16_lds(w, smem_base + stage * kStage + blk * 1024,
-                     vo[i & 1] | (k0 + 16 * lc[i & 1] < p.K ? 0u : kOutOfRange));
+                     (vo[i & 1] + static_cast<uint32_t>(8 * blk * p.K)) |
+                         (k0 + 16 * lc[i & 1] < p.K ? 0u : kOutOfRange));
     } else {
-      const int k = k0 + 4 * blk;
-      const i32x4 w = make_window_words(p.B + static_cast<int64_t>(k) * p.N + n0,
-                                        static_cast<int64_t>(p.K - k - 1) * p.N + (p.N - n0));
-      buf_load16_lds(w, smem_base + stage * kStage + kAStage + blk * 1024, vo[i & 1]);
+      // The range check works per requested dword, so when N % 4 != 0 the
+      // chunk holding the last bytes of B (last row, last columns) would
+      // come back with its final valid bytes zeroed.  That lane loads zeros
+      // and copies the bytes itself once the loads have landed (tail_fix).
+      const int col = n0 + 16 * lc[i & 1];
+      const bool straddle =
+          (p.N & 3) != 0 && k0 + 4 * blk + (lane >> 4) == p.K - 1 && col < p.N && col + 16 > p.N;
+      const uint32_t dst = smem_base + stage * kStage + kAStage + blk * 1024;
+      if (straddle) tail_lds = static_cast<int>(dst - smem_base) + 16 * lane;
+      buf_load16_lds(w, dst,
+                     straddle ? kOutOfRange : vo[i & 1] + static_cast<uint32_t>(4 * blk * p.N));
+    }
+  };
+  // Copy the valid bytes of the straddling chunk (see issue) into LDS; call
+  // after this wave's loads have landed and before the barrier.
+  auto tail_fix = [&]() {
+    if (tail_lds >= 0) {
+      const int col = n0 + 16 * lc[(((tail_lds - kAStage) % kStage) / 1024) & 1];
+      const uint8_t* src = p.B + static_cast<int64_t>(p.K - 1) * p.N;
+      for (int e = 0; e < 16 && col + e < p.N; ++e) smem[tail_lds + e] = src[col + e];
+      tail_lds = -1;
     }
   };
   auto issue_scales = [&](int g) {
@@ -162,8 +195,9 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     }
   };
   auto issue_slice = [&](int g) {
+    const i32x4 w = loads_a ? window_a(g) : window_b(g);
 #pragma unroll
-    for (int i = 0; i < kBlocksPerWave; ++i) issue(g, i);
+    for (int i = 0; i < kBlocksPerWave; ++i) issue(w, g, i);
     issue_scales(g);
   };
 
@@ -189,6 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   if (G > 0) {
     issue_slice(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    tail_fix();
     lds_barrier();
     // B scales of this wave's column block, 64 groups per register: lane l
     // holds sB[g0 + l, hb] and each group's value is taken with readlane.
@@ -211,9 +246,10 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
           q[s] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j] + s * 8 * kBN));
         fb[j] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
       }
+      const i32x4 wnext = loads_a ? window_a(g + 1) : window_b(g + 1);
 #pragma unroll
       for (int i = 0; i < kFM; ++i) {
-        if (i < kBlocksPerWave) issue(g + 1, i);  // slice g+1 into the idle stage
+        if (i < kBlocksPerWave) issue(wnext, g + 1, i);  // slice g+1 into the idle stage
         if (i == kFM - 1) issue_scales(g + 1);
         const u32x4 lo = *reinterpret_cast<const u32x4*>(base + a_off0 + 16 * i * kBK);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(base + a_off1 + 16 * i * kBK);
@@ -229,6 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
         }
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // slice g+1 has landed
+      tail_fix();
       lds_barrier();                                     // and slice g is no longer read
     }
   }
@@ -238,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   const int erow = lane >> 3;       // 8 rows per pass
   const int ecol = 8 * (lane & 7);  // 8 columns per lane
   const int gcol = n0 + wn * kWTN + ecol;
-  const bool full_cols = gcol + 8 <= p.N;
+  const bool full_cols = p.vec_c && gcol + 8 <= p.N;
 #pragma unroll
   for (int i = 0; i < kFM; ++i) {
 #pragma unroll
@@ -269,15 +306,18 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
 
 }  // namespace
 
-const char* fp8_kernel_name() { return "tgemm_fp8_bs_256x256x128"; }
+bool fp8_direct_ok(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  return K % 16 == 0 && K * kBM < (int64_t{1} << 31) && N * kBK < (int64_t{1} << 31) &&
+         static_cast<int64_t>(kBM) * ((K + 127) / 128) * 4 < (int64_t{1} << 31);
+}
+
+const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K) {
+  return fp8_direct_ok(M, N, K) ? "tgemm_fp8_bs_256x256x128" : "tgemm_fp8_bs_general_256x128x128";
+}
 
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t s) {
-  const bool direct = a.vec_a && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0 && a.K % 16 == 0 &&
-                      a.N % 16 == 0 &&
-                      static_cast<int64_t>(a.K) * kBM < (int64_t{1} << 31) &&
-                      static_cast<int64_t>(a.N) * kBK < (int64_t{1} << 31) &&
-                      static_cast<int64_t>(kBM) * a.G * 4 < (int64_t{1} << 31);
-  if (!direct) return launch_fp8_general(a, s);
+  if (!fp8_direct_ok(a.M, a.N, a.K)) return launch_fp8_general(a, s);
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.N + kBN - 1) / kBN;
   hipLaunchKernelGGL(tgemm_fp8_bs_256x256x128, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,

@@ -31,6 +31,7 @@ struct Fp8Args {
   int H;      // ceil(N / 128): B-scale columns
   int vec_a;  // 1: A rows are 16-byte aligned (K % 16 == 0 and aligned base)
   int vec_b;  // 1: B rows are 8-byte aligned (N % 8 == 0 and aligned base)
+  int vec_c;  // 1: C rows may be written with 16-byte stores (N % 8 == 0, aligned base)
 };
 
 // Tiled bf16 kernel shapes (BM x BN output tile, 4 waves).
@@ -54,6 +55,6 @@ hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
 hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
 const char* thin_kernel_name(int M);
-const char* fp8_kernel_name();
+const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K);
 
 }  // namespace tgemm
