@@ -1,25 +1,26 @@
-// Small-M bf16 GEMM for gfx950, tuned as a bandwidth-bound kernel.
+// Small-M bf16 GEMM for gfx950, written as a bandwidth-bound kernel.
 //
 // The LM head of the GEMM compute-cost page (section 7.2; also section 2.1,
 // embedding and output layers, and section 3.2 on decode) multiplies a few
 // rows X[M, K] (M = batch, often 1) by a weight W[K, N] with N in the tens
-// or hundreds of thousands.  Each weight element is used M times only, so
-// the kernel's job is to stream W from HBM exactly once at full bandwidth;
-// the arithmetic still goes to the MFMA units (16 x 16 x 32 bf16, M padded
-// up to a multiple of 16) because at M = 64 it would otherwise swamp the
-// vector ALUs.
+// or hundreds of thousands.  Each weight element is used M times only, so the
+// kernel's job is to stream W from HBM exactly once at full bandwidth; the
+// arithmetic still goes to the MFMA units (16 x 16 x 32 bf16, M padded to a
+// multiple of 16) because at M = 64 it would otherwise swamp the vector ALUs.
 //
 // Layout of the work:
-//   * a workgroup owns 128 consecutive columns; its four waves split K into
-//     four contiguous ranges and add their partial sums through LDS at the
-//     end;
-//   * per step a wave covers 32 rows of K: lane l reads 8 rows x 8 columns
-//     of W (eight 16-byte loads; rows 8*(l/16) .. +7, columns 8*(l%16) .. +7)
-//     and transposes them in registers.  Column c of that block becomes the
-//     B operand of MFMA number c, so MFMA c computes the 16 columns
-//     8*j + c (j = 0..15) and every lane ends up owning 8 consecutive output
-//     columns -- W needs no trip through LDS;
-//   * the loads for step s + 1 are issued before the MFMAs of step s.
+//   * a workgroup owns 512 consecutive columns, so every row of its W stripe
+//     is one contiguous KiB; measured on MI355X, KiB-wide row stripes read
+//     at about 6.4 TB/s against about 6.0 TB/s for 256-byte stripes;
+//   * the stripe is walked in slices of 32 rows that go global -> LDS with
+//     direct buffer loads (one load instruction = one row), four LDS stages
+//     deep (three slices, 96 KiB, in flight per compute unit); the matching
+//     16-row blocks of X come the same way;
+//   * each wave owns 128 columns over the whole of K (no cross-wave
+//     reduction); its MFMA B operands are read from the N-contiguous rows
+//     with ds_read_b64_tr_b16, exactly as in the tiled kernel, and the
+//     16-byte chunks of each LDS row are XOR-permuted so those reads are
+//     bank-conflict free.
 #include "common.h"
 #include "launch.h"
 
@@ -28,183 +29,162 @@ namespace tgemm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCols = 128;     // columns per workgroup
-constexpr int kStepK = 32;     // K rows per wave step
-constexpr int kRedStride = 132;  // floats per row of the LDS reduction buffer (padded)
+constexpr int kBN = 512;        // columns per workgroup
+constexpr int kWTN = 128;       // columns per wave
+constexpr int kFN = kWTN / 16;  // 16-column MFMA blocks per wave
+constexpr int kBK = 32;         // K rows per slice
+constexpr int kNS = 4;          // LDS stages
+constexpr int kWRow = kBN * 2;  // bytes per W row of the stripe (1 KiB)
+constexpr int kWStage = kBK * kWRow;
+constexpr int kXStage = 4 * 1024;  // four 16-row blocks of X, 64 bytes per row
+constexpr int kStage = kWStage + kXStage;
+constexpr int kLoadsPerSlice = kBK / 4 + 1;  // per wave: 8 W rows and one X block
+static_assert(kNS * kStage <= 160 * 1024, "LDS capacity");
 
-// 8 bf16 of row `row`, columns col .. col+7, zero outside rows x cols,
-// element by element (general instantiation).
-__device__ __forceinline__ u32x4 load_row8(const uint16_t* base, int64_t ld, int row, int rows,
-                                           int col, int cols) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (row < rows) {
-    const uint16_t* p = base + static_cast<int64_t>(row) * ld + col;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (col + e < cols) v[e >> 1] |= static_cast<uint32_t>(p[e]) << (16 * (e & 1));
-  }
-  return v;
-}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-__device__ __forceinline__ u32x4 transpose_col(const u32x4 (&r)[8], int j) {
-  const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-  const int d = j >> 1;
-  u32x4 o;
-  o[0] = perm(r[1][d], r[0][d], sel);
-  o[1] = perm(r[3][d], r[2][d], sel);
-  o[2] = perm(r[5][d], r[4][d], sel);
-  o[3] = perm(r[7][d], r[6][d], sel);
-  return o;
-}
+// XOR on the chunk index of W row k (even, so 32-byte pairs stay together):
+// the 8 rows one transposed read touches in a half-wave land in 8 different
+// 32-byte bank segments.
+__device__ __forceinline__ int w_swz(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+// XOR on the chunk index of row r of an X block (4 chunks of 16 bytes).
+__device__ __forceinline__ int x_swz(int r) { return (r >> 2) & 3; }
 
-template <int MB>
-struct Stage {
-  u32x4 w[8];
-  u32x4 x[MB];
-};
-
-template <int MB, int EPI, bool OUT_BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void tgemm_bf16_thin(Bf16Args p) {
-  __shared__ float red[4 * 16 * kRedStride];
+template <int MB, int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n0 = blockIdx.x * kCols;
-  const int lc = lane & 15;   // column chunk / A row within a 16-row block
-  const int kg = lane >> 4;   // 8-row K group inside a step
-  const int col = n0 + 8 * lc;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * kBN;
 
-  // Contiguous K range of this wave, in whole steps.
-  const int steps = (p.K + kStepK - 1) / kStepK;
-  const int s_begin = (steps * wave) / 4;
-  const int s_end = (steps * (wave + 1)) / 4;
-
-  f32x4 acc[MB][8];
+  // acc[mb][j]: 16 x 16 block, transposed by the operand swap: element e of
+  // lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the wave's 128.
+  f32x4 acc[MB][kFN];
 #pragma unroll
-  for (int m = 0; m < MB; ++m)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[m][c] = f32x4{};
+    for (int j = 0; j < kFN; ++j) acc[mb][j] = f32x4{};
 
-  // VEC: W rows k .. k+31 of this workgroup's columns, and X columns
-  // k .. k+31, are read through buffer windows rebased every step; rows past
-  // K or M fall outside the window and read as zero.
+  // ---- global -> LDS: wave w loads W rows 8w .. 8w+7 of a slice (lane l ->
+  // physical chunk l, logical chunk l ^ w_swz(row)) and X block w (rows
+  // 16w .. 16w+15, lane l -> row l/4, physical chunk l%4). ----
   const int64_t lda2 = p.lda * 2, ldb2 = p.ldb * 2;
-  const uint32_t w_voff = (col < p.N) ? static_cast<uint32_t>(8 * kg * ldb2 + 16 * lc) : kOutOfRange;
-  const uint32_t x_voff = static_cast<uint32_t>(lc * lda2 + 16 * kg);
-
-  auto load = [&](Stage<MB>& st, int s) {
-    const int k = s * kStepK;
-    if constexpr (VEC) {
-      const __amdgpu_buffer_rsrc_t ww = make_window(
-          p.B + static_cast<int64_t>(k) * p.ldb + n0,
-          (static_cast<int64_t>(p.K - k - 1) * p.ldb + (p.N - n0)) * 2);
+  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+  const int xr = lane >> 2;
+  const int xc = (lane & 3) ^ x_swz(xr);
+  const uint32_t x_off = static_cast<uint32_t>((16 * wave + xr) * lda2 + 16 * xc);
+  auto issue_slice = [&](int t) {
+    const int stage = t % kNS;
+    const int k0 = t * kBK;
+    const i32x4 ww = make_window_words(p.B + static_cast<int64_t>(k0) * p.ldb + n0,
+                                       (static_cast<int64_t>(p.K - k0 - 1) * p.ldb + (p.N - n0)) * 2);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) st.w[r] = buf_load16(ww, w_voff, static_cast<uint32_t>(r * ldb2));
-      const __amdgpu_buffer_rsrc_t wx = make_window(
-          p.A + k, (static_cast<int64_t>(p.M - 1) * p.lda + (p.K - k)) * 2);
-      const uint32_t xv = (k + 8 * kg < p.K) ? x_voff : kOutOfRange;
-#pragma unroll
-      for (int m = 0; m < MB; ++m) st.x[m] = buf_load16(wx, xv, static_cast<uint32_t>(16 * m * lda2));
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) st.w[r] = load_row8(p.B, p.ldb, k + 8 * kg + r, p.K, col, p.N);
-#pragma unroll
-      for (int m = 0; m < MB; ++m) st.x[m] = load_row8(p.A, p.lda, 16 * m + lc, p.M, k + 8 * kg, p.K);
+    for (int i = 0; i < kBK / 4; ++i) {
+      const int k = 8 * wave + i;
+      const int c = lane ^ w_swz(k);
+      buf_load16_lds(ww, smem_base + stage * kStage + k * kWRow,
+                     static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange));
     }
+    const i32x4 wx = make_window_words(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (p.K - k0)) * 2);
+    buf_load16_lds(wx, smem_base + stage * kStage + kWStage + wave * 1024,
+                   x_off | (k0 + 8 * xc < p.K ? 0u : kOutOfRange));
   };
 
-  auto compute = [&](const Stage<MB>& st) {
+  // ---- LDS -> registers ----
+  // B operand of block j (columns 16 j .. +15 of the wave): lane L = 16g +
+  // 4e + q supplies K row 8g + e (+4 for the second read) and columns 4q ..
+  // 4q+3 of the block; it receives 4 k of column L % 16.
+  const int bg = lane >> 4, be = (lane >> 2) & 3, bq = lane & 3;
+  int b_off[kFN];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, transpose_col(st.w, c));
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-        acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, st.x[m]), b, acc[m][c], 0, 0, 0);
-    }
-  };
+  for (int j = 0; j < kFN; ++j) {
+    const int k = 8 * bg + be;
+    const int chunk = (2 * (8 * wave + j) + (bq >> 1)) ^ w_swz(k);
+    b_off[j] = k * kWRow + chunk * 16 + 8 * (bq & 1);
+  }
+  // X operand of block mb: row l%16, K 8*(l/16) .. +7 of the slice.
+  const int xrow = lane & 15;
+  const int x_rd = kWStage + xrow * 64 + (((lane >> 4) ^ x_swz(xrow)) * 16);
 
-  Stage<MB> s0, s1;
-  if (s_begin < s_end) load(s0, s_begin);
-  for (int s = s_begin; s < s_end; s += 2) {
-    if (s + 1 < s_end) load(s1, s + 1);
-    compute(s0);
-    if (s + 2 < s_end) load(s0, s + 2);
-    if (s + 1 < s_end) compute(s1);
+  const int KT = (p.K + kBK - 1) / kBK;
+  if (KT > 0) {
+    for (int t = 0; t < kNS - 1; ++t) issue_slice(t);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kNS - 2) * kLoadsPerSlice) : "memory");
+    lds_barrier();
+    for (int t = 0; t < KT; ++t) {
+      issue_slice(t + kNS - 1);  // into the stage slice t-1 occupied
+      const uint8_t* base = smem + (t % kNS) * kStage;
+      bf16x8 fb[kFN], fx[MB];
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, base + b_off[j]));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, base + b_off[j] + 4 * kWRow));
+        fb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        fx[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd + mb * 1024));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < kFN; ++j)
+          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fx[mb], acc[mb][j], 0, 0, 0);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kNS - 2) * kLoadsPerSlice) : "memory");
+      lds_barrier();  // slice t+1 landed everywhere; slice t no longer read
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
   }
 
-  // Cross-wave reduction, one 16-row block at a time.  MFMA 16x16 accumulator
-  // element i of lane l is row 4*(l/16) + i, column l%16 of its block; in
-  // MFMA c that column is 8*(l%16) + c of the workgroup's 128.
+  // ---- epilogue: lane holds 4 consecutive columns of one row per block ----
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    float* mine = red + wave * 16 * kRedStride;
+  for (int j = 0; j < kFN; ++j) {
+    const int col = n0 + kWTN * wave + 16 * j + 4 * (lane >> 4);
+    float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (EPI != kEpiNone) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* dst = mine + (4 * kg + i) * kRedStride + 8 * lc;
-      *reinterpret_cast<f32x4*>(dst) =
-          f32x4{acc[m][0][i], acc[m][1][i], acc[m][2][i], acc[m][3][i]};
-      *reinterpret_cast<f32x4*>(dst + 4) =
-          f32x4{acc[m][4][i], acc[m][5][i], acc[m][6][i], acc[m][7][i]};
+      for (int e = 0; e < 4; ++e)
+        if (col + e < p.N) bias[e] = bf16_bits_to_f32(p.bias[col + e]);
     }
-    __syncthreads();
-    // Thread t finishes row t/16, columns 8*(t%16) .. +7 of this block.
-    const int r = tid >> 4;
-    const int cc = 8 * (tid & 15);
-    float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float s = 0.0f;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = 16 * mb + (lane & 15);
+      if (row >= p.M) continue;
+      float v[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) s += red[(w * 16 + r) * kRedStride + cc + e];
-      v[e] = s;
-    }
-    const int row = 16 * m + r;
-    const int c0 = n0 + cc;
-    if (row < p.M) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float bias = 0.0f;
-        if constexpr (EPI != kEpiNone) {
-          if (c0 + e < p.N) bias = bf16_bits_to_f32(p.bias[c0 + e]);
-        }
-        v[e] = apply_epilogue<EPI>(v[e], bias);
-      }
-      const int64_t off = static_cast<int64_t>(row) * p.ldc + c0;
+      for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<EPI>(acc[mb][j][e], bias[e]);
+      const int64_t off = static_cast<int64_t>(row) * p.ldc + col;
+      const bool full = p.vec_c && col + 4 <= p.N;
       if constexpr (OUT_BF16) {
         uint16_t* out = static_cast<uint16_t*>(p.C) + off;
-        if (c0 + 8 <= p.N && p.vec_c) {
-          *reinterpret_cast<u32x4*>(out) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                 pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+        if (full) {
+          *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (c0 + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
         }
       } else {
         float* out = static_cast<float*>(p.C) + off;
+        if (full) {
+          *reinterpret_cast<f32x4*>(out) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (c0 + e < p.N) out[e] = v[e];
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.N) out[e] = v[e];
+        }
       }
     }
-    __syncthreads();
   }
 }
 
 template <int MB, int EPI, bool OUT_BF16>
 hipError_t launch_m(const Bf16Args& a, hipStream_t s) {
-  const int grid = (a.N + kCols - 1) / kCols;
-  const bool vec = a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
-                   a.lda * 2 * 64 < (int64_t{1} << 31) && a.ldb * 2 * kStepK < (int64_t{1} << 31);
-  if (vec) {
-    hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16, true>), dim3(grid), dim3(kThreads), 0, s,
-                       a);
-  } else {
-    hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16, false>), dim3(grid), dim3(kThreads), 0,
-                       s, a);
-  }
+  hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16>), dim3((a.N + kBN - 1) / kBN),
+                     dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -230,6 +210,11 @@ const char* thin_kernel_name(int M) {
 }
 
 hipError_t launch_bf16_thin(const Bf16Args& a, int epi, int out_bf16, hipStream_t s) {
+  // Direct loads need 16-byte aligned rows and per-lane offsets below 2^31
+  // (a slice's 32 rows of W, 64 rows of X).
+  const bool direct = a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
+                      a.ldb * 2 * kBK < (int64_t{1} << 31) && a.lda * 2 * 64 < (int64_t{1} << 31);
+  if (!direct) return launch_bf16_thin_general(a, epi, out_bf16, s);
   if (a.M <= 16) return dispatch_epi<1>(a, epi, out_bf16, s);
   if (a.M <= 32) return dispatch_epi<2>(a, epi, out_bf16, s);
   if (a.M <= 48) return dispatch_epi<3>(a, epi, out_bf16, s);

@@ -50,6 +50,9 @@ hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epilogue, int out
 hipError_t launch_bf16_general(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                                hipStream_t stream);
 hipError_t launch_bf16_thin(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream);
+// Register-transposing thin kernel for operands the direct-to-LDS one cannot take.
+hipError_t launch_bf16_thin_general(const Bf16Args& a, int epilogue, int out_bf16,
+                                    hipStream_t stream);
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
 // Register-staged kernel for FP8 operands the direct-to-LDS kernel cannot take.
 hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
