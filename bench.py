@@ -51,7 +51,24 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (the reference kernel for "
+                         "scaling HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(steps=5):
+    """A plain copy of known size: 2^30 bytes read and 2^30 bytes written per call."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_call": n,
+                      "bytes_written_per_call": n, "calls": steps}), flush=True)
 
 
 def source_digest(files):
@@ -217,6 +234,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     head = Case(args.workload, dev)
     ms_step, kern_ms, kern_med = head.time(args.steps, args.warmup)
