@@ -39,18 +39,21 @@ namespace tgemm {
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kGroupM = 4;  // tile-rows per scheduling group
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-template <int BM_, int BN_, int BK_, int NS_, int SPREAD_ = 1>
+template <int BM_, int BN_, int BK_, int NS_, int SPREAD_ = 1, int WN_ = 2>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
+  // Waves: 2 along M times WN along N (WN = 4: two waves per SIMD).
+  static constexpr int WN = WN_;
+  static constexpr int WAVES = 2 * WN;
+  static constexpr int THREADS = 64 * WAVES;
   // Loads of a slice are spread over the first KS*FM*FN/SPREAD MFMA slots.
   static constexpr int SPREAD = SPREAD_;
-  static constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile (2 x 2 waves)
+  static constexpr int WTM = BM / 2, WTN = BN / WN;  // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int KS = BK / 16;  // MFMA sub-steps per slice
   // A stage: BM rows of BK bf16 (A_CPR chunks of 16 bytes each).
@@ -64,18 +67,19 @@ struct Cfg {
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int LDS_BYTES = NS * STAGE;
   // 1 KiB load blocks per wave and slice.
-  static constexpr int APW = A_STAGE / 1024 / 4;
-  static constexpr int BPW = B_STAGE / 1024 / 4;
+  static constexpr int APW = A_STAGE / 1024 / WAVES;
+  static constexpr int BPW = B_STAGE / 1024 / WAVES;
   static constexpr int LPS = APW + BPW;  // loads per thread per slice
   // Epilogue staging: one 32-row strip of a wave's tile in fp32, rows padded by 16 bytes.
   static constexpr int EPI_PITCH = WTN + 4;
   static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
   static_assert(BN >= 128, "the B-row swizzle needs at least 16 chunks per row");
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32 x 32 block");
-  static_assert(A_STAGE % 4096 == 0 && B_STAGE % 4096 == 0, "stages must split into 4 waves x 1 KiB");
+  static_assert(A_STAGE % (1024 * WAVES) == 0 && B_STAGE % (1024 * WAVES) == 0,
+                "stages must split into 1 KiB loads per wave");
   static_assert(NS >= 2, "at least two stages");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
-  static_assert(4 * 32 * EPI_PITCH * 4 <= LDS_BYTES, "epilogue staging must fit in LDS");
+  static_assert(WAVES * 32 * EPI_PITCH * 4 <= LDS_BYTES, "epilogue staging must fit in LDS");
 };
 
 // XOR applied to the 16-byte chunk index of A row r: consecutive rows that
@@ -166,15 +170,15 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], flo
 }
 
 template <class C, int EPI, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
+__global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
                                                                 int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (LDS load bases)
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / C::WN;
+  const int wn = wave % C::WN;
 
   int tm, tn;
   tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, kGroupM, tm, tn);
@@ -369,7 +373,7 @@ hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
   const int tiles_n = (a.N + C::BN - 1) / C::BN;
   hipLaunchKernelGGL((tgemm_bf16_tiled<C, EPI, OUT_BF16>), dim3(tiles_m * tiles_n),
-                     dim3(kThreads), 0, s, a, tiles_m, tiles_n);
+                     dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -385,10 +389,11 @@ hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s)
   return launch_c<C, kEpiBiasGelu, false>(a, s);
 }
 
-// Per tile shape: BK = 32 with four stages keeps three slices of loads in
-// flight for the large tiles (measured faster on MI355X than BK = 64 with two
-// stages, which keeps less than one slice in flight).
-using Cfg256x256 = Cfg<256, 256, 32, 4>;
+// Per tile shape (measured on MI355X): BK = 32 with four stages keeps three
+// slices of loads in flight; the 256 x 256 tile runs 8 waves (two per SIMD,
+// each 128 x 64 outputs), which hides one wave's LDS and memory waits behind
+// the other's MFMAs (about 10 % faster than 4 waves of 128 x 128).
+using Cfg256x256 = Cfg<256, 256, 32, 4, 1, 4>;
 using Cfg256x128 = Cfg<256, 128, 64, 3>;
 using Cfg128x128 = Cfg<128, 128, 64, 4>;
 
