@@ -89,3 +89,4 @@ def test_kernel_selection_table():
     assert binding.gemm_fp8_kernel_name(4096, 14336, 4096) == "tgemm_fp8_bs_256x256x128"
     assert binding.gemm_fp8_kernel_name(4097, 14335, 4096) == "tgemm_fp8_bs_256x256x128"
     assert binding.gemm_fp8_kernel_name(64, 64, 200).startswith("tgemm_fp8_bs_general")
+    assert binding.gemm_fp8_kernel_name(64, 3, 256).startswith("tgemm_fp8_bs_general")

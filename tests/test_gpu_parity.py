@@ -207,7 +207,11 @@ def run_and_check_fp8(qa, sa, qb, sb, rows=None, label=""):
 
 
 @pytest.mark.parametrize("shape", [(256, 128, 128), (300, 264, 384), (300, 260, 200),
-                                   (17, 129, 136), (513, 1000, 1024), (1, 8, 16)])
+                                   (17, 129, 136), (513, 1000, 1024), (1, 8, 16),
+                                   # N % 4 != 0: the last B row's final bytes (1, 2, 3 of them)
+                                   (40, 5, 128), (33, 130, 96), (70, 67, 208), (300, 323, 256),
+                                   # N < 4 runs on the general kernel
+                                   (19, 3, 160), (7, 1, 48), (9, 2, 16)])
 def test_fp8_small_shapes(shape):
     dev = _dev()
     M, N, K = shape

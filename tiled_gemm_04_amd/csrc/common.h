@@ -131,7 +131,13 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 // The same window as a plain 4-dword descriptor, for inline assembly.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 make_window_words(const void* base, int64_t bytes) {
-  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int32_t>(bytes));
+  // Clamp to [0, 2^31 - 1] with 32-bit compares only (the scalar unit has no
+  // 64-bit signed compare; a vector compare would move the descriptor into
+  // vector registers).
+  const uint64_t u = static_cast<uint64_t>(bytes);
+  const int32_t hi = static_cast<int32_t>(u >> 32);
+  const uint32_t lo = static_cast<uint32_t>(u);
+  const int32_t n = hi < 0 ? 0 : ((hi > 0 || lo > 0x7fffffffu) ? 0x7fffffff : static_cast<int32_t>(lo));
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return i32x4{static_cast<int32_t>(a & 0xffffffffu), static_cast<int32_t>((a >> 32) & 0xffffu), n,
                static_cast<int32_t>(kBufferFlags)};

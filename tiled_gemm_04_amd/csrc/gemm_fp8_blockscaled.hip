@@ -14,16 +14,15 @@
 //     short-lived temporary; one FMA per element folds it into the fp32
 //     accumulator: acc += P_g * (sA[i, g] * sB[g, J]).  The E8M0 block
 //     exponents of the instruction cannot hold arbitrary fp32 scales, hence
-//     the FMA;
+//     the FMA (a 64-byte slice would need it twice per group);
 //   * the MFMA operands are swapped (B as the first operand) so each lane's
 //     accumulators belong to one output row: the row scale sA is one value
 //     per lane and 16-row block, and the column scale sB one value per wave
 //     (a wave's 64 columns lie inside one 128-column scale block);
 //   * the accumulators are updated by vector FMAs, so they live in
-//     architectural VGPRs; with two waves per SIMD (8 waves, 512 threads)
-//     each wave has 256 of them and owns a 128 x 64 block of a 256 x 256 tile
-//     (128 accumulator registers), and the second wave on the SIMD hides the
-//     other's LDS waits and FMA work;
+//     architectural VGPRs; two waves per SIMD (8 waves, 512 threads) give
+//     each wave 256 of them, and each wave owns a 128 x 64 block of a
+//     256 x 256 tile (128 accumulator registers);
 //   * A, B and the tile's column of A-scales go global -> LDS with direct
 //     buffer loads (no register staging); B stays N-contiguous in LDS and the
 //     K-contiguous B operand is read with ds_read_b64_tr_b8 (within each 16
@@ -31,7 +30,15 @@
 //     column i of the 8 rows), four reads per 32-byte operand; 16-byte chunks
 //     of every LDS row are XOR-permuted by the row index so operand reads
 //     touch distinct LDS banks;
-//   * two LDS stages: slice g+1 is loaded while slice g is multiplied.
+//   * two LDS stages, and a fixed slot schedule per slice (one MFMA per
+//     slot, 8 rows x 4 columns of 16 x 16 blocks): the A operand of row i+1
+//     is read during row i; the FMAs of row i run between the MFMAs of row
+//     i+1 (those of the last row at the start of the next slice), so no FMA
+//     waits on a fresh MFMA result; the barrier sits before the last row,
+//     whose operands are already in registers, and the next slice's B
+//     operands replace the current ones one by one behind its MFMAs; the
+//     loads of slice g+2 start right after that barrier (every wave is done
+//     with the stage) and finish early in slice g+1, one per slot.
 //
 // Requirements (checked by the launcher, otherwise the general kernel runs):
 // K a multiple of 16 (whole 16-byte chunks of A along K) and per-lane byte
@@ -66,6 +73,12 @@ constexpr int kEpiPitch = kWTN + 4;  // floats per row of the epilogue strip
 static_assert(128 % kWTN == 0, "a wave's columns must sit inside one 128-column scale block");
 static_assert(kAStage / 1024 == 4 * kBlocksPerWave, "waves 0-3 load A, waves 4-7 load B");
 
+// Slot schedule of one slice (slot s runs MFMA (s / kFN, s % kFN)).
+constexpr int kSlots = kFM * kFN;
+constexpr int kBar = kSlots - kFN;  // barrier before the last row
+constexpr int kEarly = 4;           // loads of slice g+2 issued after the barrier of slice g
+static_assert(kBar + kEarly <= kSlots && kBlocksPerWave - kEarly <= kBar, "load slots");
+
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 #define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -75,6 +88,21 @@ typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 // read together by one transposed read land in 16 bank groups.
 __device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int b_swz(int k) { return (k & 7) | (((k >> 5) & 1) << 3); }
+
+// Value of an OCP FP8 E4M3 (e4m3fn) byte: sign, 4 exponent bits with bias
+// 7, 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6), and
+// S.1111.111 is NaN (the format has no infinities).
+__device__ __forceinline__ float e4m3_value(uint8_t b) {
+  const uint32_t em = b & 0x7fu;
+  float v;
+  if (em == 0x7fu)
+    v = __builtin_nanf("");
+  else if (em < 8u)
+    v = static_cast<float>(em) * 0x1p-9f;
+  else
+    v = __builtin_bit_cast(float, (((em >> 3) + 120u) << 23) | ((em & 7u) << 20));
+  return (b & 0x80u) ? -v : v;
+}
 
 // 4-byte buffer load written straight into LDS (lane l -> lds_base + 4 l).
 __device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, uint32_t voff) {
@@ -120,9 +148,9 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   // B block blk (K rows 4 blk .. +3): row 4 blk + lane/16, physical chunk
   // lane % 16, and b_swz(row) likewise has two forms by the parity of blk
   // (bit 3 of it is (wave & 3) & 1 for every block of this wave).  The row
-  // offset of the block goes into the buffer base, so a lane keeps only its
+  // offset of the block is a wave-uniform addend, so a lane keeps only its
   // two in-block offsets.
-  int lc[2];      // logical chunk for even / odd blocks
+  int lc[2];       // logical chunk for even / odd blocks
   uint32_t vo[2];  // in-block byte offset for even / odd blocks
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -137,80 +165,59 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   }
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
   const uint32_t ssa_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(float, &s_sa[0][0])));
+  // The wave's own matrix, slice by slice: the buffer window of slice g
+  // starts at win0 + g * wstep and spans wsize0 - g * wstep bytes (A rows
+  // m0 .. M-1 from column 128 g; B rows 128 g .. K-1 from column n0), so
+  // bytes past M or K read as zeros.
+  const uint8_t* win0 = loads_a ? p.A + static_cast<int64_t>(m0) * p.K : p.B + n0;
+  const int64_t wsize0 = loads_a ? static_cast<int64_t>(p.M - m0 - 1) * p.K + p.K
+                                 : static_cast<int64_t>(p.K - 1) * p.N + (p.N - n0);
+  const int64_t wstep = loads_a ? int64_t{kBK} : int64_t{kBK} * p.N;
+  const uint32_t blk_stride = loads_a ? 8u * p.K : 4u * p.N;  // bytes per block of rows
+  auto window = [&](int g) {
+    return make_window_words(win0 + g * wstep, wsize0 - g * wstep);
+  };
   // Waves 0-3 also fetch the scale column sA[m0 + 64*wave + lane, g].
   const uint32_t sa_off = static_cast<uint32_t>((64 * (wave & 3) + lane) * p.G * 4);
-  int tail_lds = -1;  // LDS byte offset of a straddling B chunk to fix up, or -1
-  // Buffer windows of slice g: A rows m0 .. M-1 from column k0, B rows
-  // k0 .. K-1 from column n0 (one window per matrix and slice; a block's row
-  // offset goes into the per-lane offset).
-  auto window_a = [&](int g) {
-    const int k0 = g * kBK;
-    return make_window_words(p.A + static_cast<int64_t>(m0) * p.K + k0,
-                             static_cast<int64_t>(p.M - m0 - 1) * p.K + (p.K - k0));
-  };
-  auto window_b = [&](int g) {
-    const int k0 = g * kBK;
-    return make_window_words(p.B + static_cast<int64_t>(k0) * p.N + n0,
-                             static_cast<int64_t>(p.K - k0 - 1) * p.N + (p.N - n0));
-  };
-  // This wave's i-th block of slice g (past K the loads read zeros).
+  const int64_t sa_size = (static_cast<int64_t>(p.M - m0 - 1) * p.G + 1) * 4;
+  // A loads past K read zeros: kc is the chunk's first column for A waves
+  // and a large negative number for B waves (no column check).
+  int kc[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) kc[par] = loads_a ? 16 * lc[par] : -(1 << 30);
+  const uint32_t dst0 = smem_base + (loads_a ? 0u : static_cast<uint32_t>(kAStage)) +
+                        static_cast<uint32_t>(blk0) * 1024u;
+  const uint32_t off0 = static_cast<uint32_t>(blk0) * blk_stride;
+  // This wave's i-th block of slice g.  Slices g >= G are allowed (they read
+  // zeros: their windows are empty past K) so the schedule needs no branch.
   auto issue = [&](i32x4 w, int g, int i) {
-    const int stage = g & 1;
-    const int k0 = g * kBK;
-    const int blk = blk0 + i;
-    if (loads_a) {
-      buf_load16_lds(w, smem_base + stage * kStage + blk * 1024,
-                     (vo[i & 1] + static_cast<uint32_t>(8 * blk * p.K)) |
-                         (k0 + 16 * lc[i & 1] < p.K ? 0u : kOutOfRange));
-    } else {
-      // The range check works per requested dword, so when N % 4 != 0 the
-      // chunk holding the last bytes of B (last row, last columns) would
-      // come back with its final valid bytes zeroed.  That lane loads zeros
-      // and copies the bytes itself once the loads have landed (tail_fix).
-      const int col = n0 + 16 * lc[i & 1];
-      const bool straddle =
-          (p.N & 3) != 0 && k0 + 4 * blk + (lane >> 4) == p.K - 1 && col < p.N && col + 16 > p.N;
-      const uint32_t dst = smem_base + stage * kStage + kAStage + blk * 1024;
-      if (straddle) tail_lds = static_cast<int>(dst - smem_base) + 16 * lane;
-      buf_load16_lds(w, dst,
-                     straddle ? kOutOfRange : vo[i & 1] + static_cast<uint32_t>(4 * blk * p.N));
-    }
-  };
-  // Copy the valid bytes of the straddling chunk (see issue) into LDS; call
-  // after this wave's loads have landed and before the barrier.
-  auto tail_fix = [&]() {
-    if (tail_lds >= 0) {
-      const int col = n0 + 16 * lc[(((tail_lds - kAStage) % kStage) / 1024) & 1];
-      const uint8_t* src = p.B + static_cast<int64_t>(p.K - 1) * p.N;
-      for (int e = 0; e < 16 && col + e < p.N; ++e) smem[tail_lds + e] = src[col + e];
-      tail_lds = -1;
-    }
+    const uint32_t off = (vo[i & 1] + off0 + static_cast<uint32_t>(i) * blk_stride) |
+                         (g * kBK + kc[i & 1] < p.K ? 0u : kOutOfRange);
+    buf_load16_lds(w, dst0 + static_cast<uint32_t>((g & 1) * kStage + i * 1024), off);
   };
   auto issue_scales = [&](int g) {
     if (loads_a) {
-      const i32x4 w = make_window_words(
-          p.sA + static_cast<int64_t>(m0) * p.G + g,
-          (g < p.G ? (static_cast<int64_t>(p.M - m0 - 1) * p.G + 1) * 4 : 0));
-      buf_load4_lds(w, ssa_base + ((g & 1) * kBM + 64 * (wave & 3)) * 4, sa_off);
+      const i32x4 w = make_window_words(p.sA + static_cast<int64_t>(m0) * p.G + g, g < p.G ? sa_size : 0);
+      buf_load4_lds(w, ssa_base + ((g & 1) * kBM + 64 * wave) * 4, sa_off);
     }
   };
-  auto issue_slice = [&](int g) {
-    const i32x4 w = loads_a ? window_a(g) : window_b(g);
-#pragma unroll
-    for (int i = 0; i < kBlocksPerWave; ++i) issue(w, g, i);
-    issue_scales(g);
-  };
+  // The range check works per requested dword, so when N % 4 != 0 the
+  // 16-byte load holding the last columns of B's last row returns its final
+  // N % 4 valid bytes as zeros (they share a dword with bytes past the
+  // window).  The tile holding column N-1 adds those products after the
+  // main loop (tail_products).
+  const bool tail_tile = (p.N & 3) != 0 && n0 + kBN >= p.N;
 
   // ---- LDS -> registers ----
   const int l16 = lane & 15;
   const int lq = lane >> 4;
-  // A operand of block i: row wm*128 + 16i + l16, K bytes 32 lq .. +31
+  // A operand of row block i: row wm*128 + 16i + l16, K bytes 32 lq .. +31
   // (chunks 2 lq and 2 lq + 1).  The swizzle depends only on l16.
   const int a_row = wm * kWTM + l16;
   const int a_off0 = a_row * kBK + (((2 * lq) ^ a_swz(l16)) * 16);
   const int a_off1 = a_row * kBK + (((2 * lq + 1) ^ a_swz(l16)) * 16);
-  // B operand of block j: column chunk cj = 4 wn + j; transposed read s
-  // covers K rows 32 lq + 8 s + e for lane 16 lq + 2 e + h, columns 8 h .. +7.
+  // B operand of column block j: column chunk cj = 4 wn + j; transposed read
+  // s covers K rows 32 lq + 8 s + e for lane 16 lq + 2 e + h, columns 8 h .. +7.
   const int be = l16 >> 1, bh = l16 & 1;
   int b_off[kFN];
 #pragma unroll
@@ -218,57 +225,149 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     const int k = 32 * lq + be;
     b_off[j] = kAStage + k * kBN + (((4 * wn + j) ^ b_swz(k)) * 16) + 8 * bh;
   }
+  i32x8 fb[kFN];
+  i32x8 fa[2];
+  float srow[2];  // sA of the row block whose FMAs are pending / next (times sB at fold)
+  f32x4 part[kFN];
+  auto read_b = [&](int stage, int j) {
+    const uint8_t* base = smem + stage * kStage + b_off[j];
+    i32x2 q[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) q[s] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + s * 8 * kBN));
+    fb[j] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+  };
+  auto read_a = [&](int stage, int i) {
+    const uint8_t* base = smem + stage * kStage + 16 * i * kBK;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + a_off0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + a_off1);
+    fa[i & 1] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto read_scale = [&](int stage, int i) { srow[i & 1] = s_sa[stage][a_row + 16 * i]; };
+  // FMAs of block (i, j) from the partial sum of its last MFMA.
+  auto fold = [&](int i, int j, float scale) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(part[j][e], scale, acc[i][j][e]);
+  };
+
+  // Products of B's last row with its last N % 4 columns (see tail_tile):
+  // columns c = N - N%4 .. N-1 all sit in one 4-column group, held by lanes
+  // with lq == (c - n0) % 16 / 4 of block j == (c - n0) % 64 / 16 of wave
+  // column (c - n0) / 64, as elements e = c % 4 of each of their 8 rows.
+  auto tail_products = [&]() {
+    const int c0 = p.N - (p.N & 3) - n0;  // first missing column in the tile
+    if (wn != c0 / 64 || lq != (c0 % 16) / 4) return;
+    const int jt = (c0 % 64) / 16;
+    const int g = p.G - 1;
+    const uint8_t* brow = p.B + static_cast<int64_t>(p.K - 1) * p.N + n0 + c0;
+    float bv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[e] = e < (p.N & 3) ? e4m3_value(brow[e]) : 0.0f;
+    const float sb = hb < p.H ? p.sB[static_cast<int64_t>(g) * p.H + hb] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) {
+      const int row = m0 + a_row + 16 * i;
+      if (row >= p.M) continue;
+      const float a = e4m3_value(p.A[static_cast<int64_t>(row) * p.K + p.K - 1]) *
+                      p.sA[static_cast<int64_t>(row) * p.G + g] * sb;
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+        if (j == jt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(a, bv[e], acc[i][j][e]);
+    }
+  };
 
   const int G = p.G;
   if (G > 0) {
-    issue_slice(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    tail_fix();
-    lds_barrier();
     // B scales of this wave's column block, 64 groups per register: lane l
     // holds sB[g0 + l, hb] and each group's value is taken with readlane.
-    float sb_lanes = 0.0f;
+    auto sb_fetch = [&](int g0) {
+      const int gl = g0 + lane;
+      return (gl < G && hb < p.H) ? p.sB[static_cast<int64_t>(gl) * p.H + hb] : 0.0f;
+    };
+    auto sb_of = [&](float lanes, int g) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lanes), g & 63));
+    };
+    // The first slice folds a zero "previous row".
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) part[j] = f32x4{};
+    srow[1] = 0.0f;
+    float sb_lanes = sb_fetch(0);
+    float sb_cur = sb_of(sb_lanes, 0);
+    // Prologue: slice 0, then the first kEarly blocks of slice 1.
+    {
+      const i32x4 w = window(0);
+#pragma unroll
+      for (int i = 0; i < kBlocksPerWave; ++i) issue(w, 0, i);
+      issue_scales(0);
+    }
+    if (G > 1) {
+      const i32x4 w = window(1);
+#pragma unroll
+      for (int i = 0; i < kEarly; ++i) issue(w, 1, i);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEarly) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) read_b(0, j);
+    read_a(0, 0);
+    read_scale(0, 0);
+
+    float sb_prev = 0.0f;  // sB of the slice whose last row is pending
+    float scale = 0.0f;    // sA * sB of the row being folded
     for (int g = 0; g < G; ++g) {
       const int stage = g & 1;
-      const uint8_t* base = smem + stage * kStage;
-      if ((g & 63) == 0) {
-        const int gl = g + lane;
-        sb_lanes = (gl < G && hb < p.H) ? p.sB[static_cast<int64_t>(gl) * p.H + hb] : 0.0f;
-      }
-      const float sb = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sb_lanes), g & 63));
-      i32x8 fb[kFN];
-#pragma unroll
-      for (int j = 0; j < kFN; ++j) {
-        i32x2 q[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          q[s] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j] + s * 8 * kBN));
-        fb[j] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
-      }
-      const i32x4 wnext = loads_a ? window_a(g + 1) : window_b(g + 1);
-#pragma unroll
-      for (int i = 0; i < kFM; ++i) {
-        if (i < kBlocksPerWave) issue(wnext, g + 1, i);  // slice g+1 into the idle stage
-        if (i == kFM - 1) issue_scales(g + 1);
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + a_off0 + 16 * i * kBK);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + a_off1 + 16 * i * kBK);
-        const i32x8 fa = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        const float s = s_sa[stage][a_row + 16 * i] * sb;
-#pragma unroll
-        for (int j = 0; j < kFN; ++j) {
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              fb[j], fa, f32x4{}, kFmtE4M3, kFmtE4M3, 0, kScaleOne, 0, kScaleOne);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(part[e], s, acc[i][j][e]);
+      if (((g + 1) & 63) == 0) sb_lanes = sb_fetch(g + 1);
+      const i32x4 w1 = window(g + 1);
+      const i32x4 w2 = window(g + 2);
+      float sb_next = 0.0f;
+      static_for<kSlots>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int i = s / kFN, j = s % kFN;
+        if constexpr (s == kBar) {
+          // Slice g+1 has landed and every wave is done reading slice g's
+          // stage (all its operands for this last row are in registers).
+          TGEMM_SCHED_FENCE();
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          lds_barrier();
+          sb_next = sb_of(sb_lanes, g + 1);
         }
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // slice g+1 has landed
-      tail_fix();
-      lds_barrier();                                     // and slice g is no longer read
+        TGEMM_SCHED_FENCE();
+        // FMAs of the previous row (row kFM-1 of the previous slice at i == 0).
+        if constexpr (j == 0) scale = srow[(i + 1) & 1] * (i == 0 ? sb_prev : sb_cur);
+        fold(i == 0 ? kFM - 1 : i - 1, j, scale);
+        part[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            fb[j], fa[i & 1], f32x4{}, kFmtE4M3, kFmtE4M3, 0, kScaleOne, 0, kScaleOne);
+        TGEMM_SCHED_FENCE();
+        // Operand reads.
+        if constexpr (i + 1 < kFM) {
+          if constexpr (j == 0) read_a(stage, i + 1);
+          if constexpr (j == 1) read_scale(stage, i + 1);
+        } else {
+          read_b(stage ^ 1, j);  // fb[j] of slice g+1 replaces the one just used
+          if constexpr (j == 0) read_a(stage ^ 1, 0);
+          if constexpr (j == 1) read_scale(stage ^ 1, 0);
+        }
+        // Global -> LDS: blocks kEarly.. of slice g+1 in the first slots,
+        // blocks 0 .. kEarly-1 of slice g+2 right after the barrier.
+        if constexpr (s < kBlocksPerWave - kEarly) issue(w1, g + 1, kEarly + s);
+        if constexpr (s == kBlocksPerWave - kEarly) issue_scales(g + 1);
+        if constexpr (s >= kBar && s < kBar + kEarly) issue(w2, g + 2, s - kBar);
+      });
+      TGEMM_SCHED_FENCE();
+      sb_prev = sb_cur;
+      sb_cur = sb_next;
     }
+    // FMAs of the last row of the last slice.
+    scale = srow[1] * sb_prev;
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) fold(kFM - 1, j, scale);
+    if (tail_tile) tail_products();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();  // every wave is done with the operand stages
 
   // ---- epilogue: 16-row strips through this wave's LDS area, 16-byte stores ----
   float* strip = reinterpret_cast<float*>(smem) + wave * 16 * kEpiPitch;
@@ -308,7 +407,9 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
 
 bool fp8_direct_ok(int64_t M, int64_t N, int64_t K) {
   (void)M;
-  return K % 16 == 0 && K * kBM < (int64_t{1} << 31) && N * kBK < (int64_t{1} << 31) &&
+  // N >= 4: below that one 4-byte word of B spans more than two rows, and
+  // the last-row patch would not cover every zeroed byte.
+  return K % 16 == 0 && N >= 4 && K * kBM < (int64_t{1} << 31) && N * kBK < (int64_t{1} << 31) &&
          static_cast<int64_t>(kBM) * ((K + 127) / 128) * 4 < (int64_t{1} << 31);
 }
 
