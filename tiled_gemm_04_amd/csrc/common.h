@@ -39,24 +39,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two values in one v_cvt_pk_bf16_f32 (lo in bits 15:0).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 // -------------------------------------------------------------- epilogue ---
 
 // tanh-form GeLU.  0.5*(1 + tanh(u)) equals the logistic function at 2u, so
 // gelu(y) = y / (1 + exp(-2u)) with u = sqrt(2/pi) * (y + 0.044715 y^3); this
-// form has no cancellation for large negative y.  exp is taken as 2^x with
-// the hardware v_exp_f32.
+// form has no cancellation for large negative y (exp overflows to +inf and
+// the reciprocal to 0).  exp is taken as 2^x with the hardware v_exp_f32 and
+// the division as a product with v_rcp_f32 (both about 1 ulp, far below
+// the bf16 output's rounding).
 __device__ __forceinline__ float gelu_tanh(float y) {
   constexpr float kSqrt2OverPi = 0.7978845608028654f;
   constexpr float kCubic = 0.044715f;
   constexpr float kLog2e = 1.4426950408889634f;
-  float u = kSqrt2OverPi * (y + kCubic * y * y * y);
-  float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * u);
-  return y / (1.0f + e);
+  constexpr float kA = -2.0f * kLog2e * kSqrt2OverPi;  // exponent = y * (kA + kB y^2)
+  constexpr float kB = kA * kCubic;
+  const float e = __builtin_amdgcn_exp2f(y * __builtin_fmaf(kB, y * y, kA));
+  return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 template <int EPI>

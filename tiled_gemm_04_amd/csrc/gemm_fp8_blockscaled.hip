@@ -70,6 +70,9 @@ constexpr int kGroupM = 4;
 constexpr int kScaleOne = 127;  // E8M0 exponent of 1.0
 constexpr int kFmtE4M3 = 0;     // f8f6f4 operand format code for FP8 E4M3
 constexpr int kEpiPitch = kWTN + 4;  // floats per row of the epilogue strip
+// s_waitcnt immediate for vmcnt(0) with the other counters unconstrained
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
 static_assert(128 % kWTN == 0, "a wave's columns must sit inside one 128-column scale block");
 static_assert(kAStage / 1024 == 4 * kBlocksPerWave, "waves 0-3 load A, waves 4-7 load B");
 
@@ -110,6 +113,78 @@ __device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, u
                :
                : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_words(window))
                : "memory", "m0");
+}
+
+// Stores a wave's kFMxkFN blocks of 16 x 16 accumulators (rows row0 + 16 i
+// + l%16, columns col0 + 16 j + 4 (l/16) + e) as bf16, through a 16-row
+// strip of LDS per wave so that each lane writes 8 consecutive columns.
+template <int FM>
+__device__ __forceinline__ void store_wave(const f32x4 (&acc)[FM][kFN], float* strip, int lane,
+                                           int row0, int col0, const Fp8Args& p) {
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int erow = lane >> 3;       // 8 rows per pass
+  const int ecol = 8 * (lane & 7);  // 8 columns per lane
+  const int gcol = col0 + ecol;
+  const bool full_cols = p.vec_c && gcol + 8 <= p.N;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+      *reinterpret_cast<f32x4*>(strip + l16 * kEpiPitch + 16 * j + 4 * lq) = acc[i][j];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int rr = erow + 8 * pass;
+      const float* src = strip + rr * kEpiPitch + ecol;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+      const int row = row0 + 16 * i + rr;
+      if (row < p.M) {
+        uint16_t* out = p.C + static_cast<int64_t>(row) * p.N + gcol;
+        if (full_cols) {
+          *reinterpret_cast<u32x4*>(out) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                 pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+        } else {
+          const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gcol + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
+        }
+      }
+    }
+  }
+}
+
+// The buffer range check works per requested dword, so when N % 4 != 0 the
+// 16-byte load holding the last columns of B's last row returns its final
+// N % 4 valid bytes as zeros (they share a dword with bytes past the
+// window).  The tile holding column N-1 adds those products afterwards:
+// columns c = N - N%4 .. N-1 sit in one 4-column group, held by the lanes
+// with l/16 == (c - n0) % 16 / 4 of block j == (c - n0) % 64 / 16 of wave
+// column (c - n0) / 64, as elements e = c % 4 of each of their rows.
+template <int FM>
+__device__ __forceinline__ void add_tail_products(f32x4 (&acc)[FM][kFN], const Fp8Args& p, int row0,
+                                                  int n0, int wn, int lane, int hb) {
+  const int c0 = p.N - (p.N & 3) - n0;  // first column of the group, within the tile
+  if (wn != c0 / 64 || (lane >> 4) != (c0 % 16) / 4) return;
+  const int jt = (c0 % 64) / 16;
+  const int g = p.G - 1;
+  const uint8_t* brow = p.B + static_cast<int64_t>(p.K - 1) * p.N + n0 + c0;
+  float bv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bv[e] = e < (p.N & 3) ? e4m3_value(brow[e]) : 0.0f;
+  const float sb = hb < p.H ? p.sB[static_cast<int64_t>(g) * p.H + hb] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int row = row0 + (lane & 15) + 16 * i;
+    if (row >= p.M) continue;
+    const float a = e4m3_value(p.A[static_cast<int64_t>(row) * p.K + p.K - 1]) *
+                    p.sA[static_cast<int64_t>(row) * p.G + g] * sb;
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+      if (j == jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(a, bv[e], acc[i][j][e]);
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args p, int tiles_m,
@@ -201,11 +276,8 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
       buf_load4_lds(w, ssa_base + ((g & 1) * kBM + 64 * wave) * 4, sa_off);
     }
   };
-  // The range check works per requested dword, so when N % 4 != 0 the
-  // 16-byte load holding the last columns of B's last row returns its final
-  // N % 4 valid bytes as zeros (they share a dword with bytes past the
-  // window).  The tile holding column N-1 adds those products after the
-  // main loop (tail_products).
+  // The tile holding column N-1 adds the products that the range check
+  // drops from B's last row (add_tail_products).
   const bool tail_tile = (p.N & 3) != 0 && n0 + kBN >= p.N;
 
   // ---- LDS -> registers ----
@@ -249,34 +321,6 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(part[j][e], scale, acc[i][j][e]);
   };
 
-  // Products of B's last row with its last N % 4 columns (see tail_tile):
-  // columns c = N - N%4 .. N-1 all sit in one 4-column group, held by lanes
-  // with lq == (c - n0) % 16 / 4 of block j == (c - n0) % 64 / 16 of wave
-  // column (c - n0) / 64, as elements e = c % 4 of each of their 8 rows.
-  auto tail_products = [&]() {
-    const int c0 = p.N - (p.N & 3) - n0;  // first missing column in the tile
-    if (wn != c0 / 64 || lq != (c0 % 16) / 4) return;
-    const int jt = (c0 % 64) / 16;
-    const int g = p.G - 1;
-    const uint8_t* brow = p.B + static_cast<int64_t>(p.K - 1) * p.N + n0 + c0;
-    float bv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bv[e] = e < (p.N & 3) ? e4m3_value(brow[e]) : 0.0f;
-    const float sb = hb < p.H ? p.sB[static_cast<int64_t>(g) * p.H + hb] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < kFM; ++i) {
-      const int row = m0 + a_row + 16 * i;
-      if (row >= p.M) continue;
-      const float a = e4m3_value(p.A[static_cast<int64_t>(row) * p.K + p.K - 1]) *
-                      p.sA[static_cast<int64_t>(row) * p.G + g] * sb;
-#pragma unroll
-      for (int j = 0; j < kFN; ++j)
-        if (j == jt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(a, bv[e], acc[i][j][e]);
-    }
-  };
-
   const int G = p.G;
   if (G > 0) {
     // B scales of this wave's column block, 64 groups per register: lane l
@@ -310,16 +354,24 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     lds_barrier();
+    // Same order as the reads of the next slice in the last row of the loop.
 #pragma unroll
-    for (int j = 0; j < kFN; ++j) read_b(0, j);
-    read_a(0, 0);
-    read_scale(0, 0);
+    for (int j = 0; j < kFN; ++j) {
+      read_b(0, j);
+      if (j == 0) read_a(0, 0);
+      if (j == 1) read_scale(0, 0);
+    }
 
     float sb_prev = 0.0f;  // sB of the slice whose last row is pending
     float scale = 0.0f;    // sA * sB of the row being folded
     for (int g = 0; g < G; ++g) {
       const int stage = g & 1;
-      if (((g + 1) & 63) == 0) sb_lanes = sb_fetch(g + 1);
+      if (((g + 1) & 63) == 0) {
+        // Next 64 B scales; wait here (rarely) rather than at their use,
+        // where the wait would also cover the slices in flight.
+        sb_lanes = sb_fetch(g + 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
       const i32x4 w1 = window(g + 1);
       const i32x4 w2 = window(g + 2);
       float sb_next = 0.0f;
@@ -364,44 +416,16 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     scale = srow[1] * sb_prev;
 #pragma unroll
     for (int j = 0; j < kFN; ++j) fold(kFM - 1, j, scale);
-    if (tail_tile) tail_products();
+    if (tail_tile) add_tail_products(acc, p, m0 + wm * kWTM, n0, wn, lane, hb);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();  // every wave is done with the operand stages
 
-  // ---- epilogue: 16-row strips through this wave's LDS area, 16-byte stores ----
-  float* strip = reinterpret_cast<float*>(smem) + wave * 16 * kEpiPitch;
-  const int erow = lane >> 3;       // 8 rows per pass
-  const int ecol = 8 * (lane & 7);  // 8 columns per lane
-  const int gcol = n0 + wn * kWTN + ecol;
-  const bool full_cols = p.vec_c && gcol + 8 <= p.N;
-#pragma unroll
-  for (int i = 0; i < kFM; ++i) {
-#pragma unroll
-    for (int j = 0; j < kFN; ++j)
-      *reinterpret_cast<f32x4*>(strip + l16 * kEpiPitch + 16 * j + 4 * lq) = acc[i][j];
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int rr = erow + 8 * pass;
-      const float* src = strip + rr * kEpiPitch + ecol;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-      const int row = m0 + wm * kWTM + 16 * i + rr;
-      if (row < p.M) {
-        uint16_t* out = p.C + static_cast<int64_t>(row) * p.N + gcol;
-        if (full_cols) {
-          *reinterpret_cast<u32x4*>(out) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                                                 pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
-        } else {
-          const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (gcol + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
-        }
-      }
-    }
-  }
+  // ---- epilogue ----
+  store_wave(acc, reinterpret_cast<float*>(smem) + wave * 16 * kEpiPitch, lane, m0 + wm * kWTM,
+             n0 + wn * kWTN, p);
 }
+
 
 }  // namespace
 
