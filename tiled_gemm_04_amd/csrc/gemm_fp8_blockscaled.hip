@@ -85,11 +85,16 @@ static_assert(kBar + kEarly <= kSlots && kBlocksPerWave - kEarly <= kBar, "load 
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 #define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// Chunk permutations.  A rows are 128 bytes (8 chunks, two rows per 256-byte
-// bank row): 16 consecutive rows read at one chunk land in 16 bank groups.
+// Chunk permutations (physical chunk = logical chunk ^ swizzle(row)).
+// A rows are 128 bytes (8 chunks).  An A operand read has lane 16q + r take
+// chunks 2q and 2q+1 of row r (r < 16).  Measured with SQ_LDS_BANK_CONFLICT
+// on gfx950, r & 7 flipped by bit 3 of r serves all four lane groups without
+// conflicts; the plainer (r >> 1) & 7, though it puts each 16-lane group on
+// 16 distinct 16-byte bank slots, costs a second cycle on half of the reads.
+// The permutation depends on r mod 16 only, so row blocks 16 apart share it.
 // B rows are 256 bytes (16 chunks): the 16 K rows k0+e and k0+32+e (e < 8)
 // read together by one transposed read land in 16 bank groups.
-__device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int b_swz(int k) { return (k & 7) | (((k >> 5) & 1) << 3); }
 
 // Value of an OCP FP8 E4M3 (e4m3fn) byte: sign, 4 exponent bits with bias
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   const int blk0 = (wave & 3) * kBlocksPerWave;
   // A block blk (rows 8 blk .. +7): slot 64 blk + lane is row 8 blk + lane/8,
   // physical chunk lane % 8, logical chunk (lane % 8) ^ a_swz(row), and
-  // a_swz(row) = (4 blk + lane/16) % 8 takes two forms by the parity of blk.
+  // a_swz(row) = (lane/8) ^ (blk & 1) takes two forms by the parity of blk.
   // B block blk (K rows 4 blk .. +3): row 4 blk + lane/16, physical chunk
   // lane % 16, and b_swz(row) likewise has two forms by the parity of blk
   // (bit 3 of it is (wave & 3) & 1 for every block of this wave).  The row
@@ -230,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
     if (loads_a) {
-      lc[par] = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+      lc[par] = (lane & 7) ^ a_swz(8 * par + (lane >> 3));
       vo[par] = static_cast<uint32_t>((lane >> 3) * p.K + 16 * lc[par]);
     } else {
       lc[par] = (lane & 15) ^ (((4 * par + (lane >> 4)) & 7) | (((wave & 3) & 1) << 3));
