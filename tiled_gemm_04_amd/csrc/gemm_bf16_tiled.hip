@@ -218,13 +218,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
     const int c = (s % C::B_CPR) ^ b_swz(k);
     b_goff[i] = static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange);
   }
-  auto window_a = [&](int k0) {
-    return make_window_words(p.A + static_cast<int64_t>(m0) * p.lda + k0,
-                       (static_cast<int64_t>(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
-  };
+  // Windows of the slice at column k0: A rows m0 .. M-1 from column k0, B
+  // rows k0 .. K-1 from column n0 (bytes past M or K read as zeros).  They
+  // move by one slice per iteration, so the loop steps a pointer and a size
+  // instead of recomputing them.
+  const uint16_t* const a_base0 = p.A + static_cast<int64_t>(m0) * p.lda;
+  const int64_t a_size0 = (static_cast<int64_t>(p.M - m0 - 1) * p.lda + p.K) * 2;
+  const uint16_t* const b_base0 = p.B + n0;
+  const int64_t b_size0 = (static_cast<int64_t>(p.K - 1) * p.ldb + (p.N - n0)) * 2;
+  const int64_t b_step = static_cast<int64_t>(C::BK) * p.ldb;  // elements per slice
+  auto window_a = [&](int k0) { return make_window_words(a_base0 + k0, a_size0 - 2 * k0); };
   auto window_b = [&](int k0) {
-    return make_window_words(p.B + static_cast<int64_t>(k0) * p.ldb + n0,
-                       (static_cast<int64_t>(p.K - k0 - 1) * p.ldb + (p.N - n0)) * 2);
+    return make_window_words(b_base0 + static_cast<int64_t>(k0) * p.ldb,
+                             b_size0 - 2 * static_cast<int64_t>(k0) * p.ldb);
   };
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
   auto issue_a = [&](i32x4 w, int stage, int k0, int i) {
@@ -323,10 +329,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 
     int cur = 0;
     int lst = C::NS - 1;  // stage receiving slice t+NS-1
+    // Windows of slice t+NS-1, stepped once per iteration.
+    const uint16_t* a_ptr = a_base0 + (C::NS - 1) * C::BK;
+    int64_t a_left = a_size0 - 2 * (C::NS - 1) * C::BK;
+    const uint16_t* b_ptr = b_base0 + (C::NS - 1) * b_step;
+    int64_t b_left = b_size0 - 2 * (C::NS - 1) * b_step;
     for (int t = 0; t < KT; ++t) {
       const int nxt = cur + 1 == C::NS ? 0 : cur + 1;
       const int kl = (t + C::NS - 1) * C::BK;
-      const i32x4 wa = window_a(kl), wb = window_b(kl);
+      const i32x4 wa = make_window_words(a_ptr, a_left), wb = make_window_words(b_ptr, b_left);
+      a_ptr += C::BK;
+      a_left -= 2 * C::BK;
+      b_ptr += b_step;
+      b_left -= 2 * b_step;
       static_for<kSlots>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         constexpr int u = s / kQ;
