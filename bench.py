@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
-                    help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged)")
+                    help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
+                         "tiny, quant_a, quant_b)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -83,7 +84,13 @@ KERNEL_SOURCES = {
     "tiled": ["common.h", "launch.h", "gemm_bf16_tiled.hip"],
     "thin": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
     "fp8": ["common.h", "launch.h", "gemm_fp8_blockscaled.hip"],
+    "quant": ["common.h", "launch.h", "quant_fp8.hip"],
 }
+
+# FP8 quantisers, timed on the FP8 workload's unquantised operands (bf16):
+# activations A [4096, 4096] in 1 x 128 groups, weights B [4096, 14336] in
+# 128 x 128 blocks.
+QUANT_CASES = {"quant_a": ("a", "tgemm_quant_fp8_1x128"), "quant_b": ("b", "tgemm_quant_fp8_128x128")}
 
 
 def committed_traffic(workload, family):
@@ -114,6 +121,9 @@ class Case:
         import workloads as wl
 
         self.name = name
+        if name in QUANT_CASES:
+            self._init_quant(name, dev)
+            return
         w = wl.WORKLOADS[name]
         self.w = w
         self.M, self.N, self.K = w.M, w.N, w.K
@@ -147,6 +157,39 @@ class Case:
             self.peak = PEAK_HBM_GBS if thin else PEAK_BF16_TFLOPS
             self.dtype = "bf16"
         self.inputs_for_oracle = None if w.fp8 else (a, b)
+
+    def describe(self):
+        if self.family == "quant":
+            grouping = "1x128" if self.name == "quant_a" else "128x128"
+            return f"{self.name}: Q, S = quantize_fp8_{grouping}(X[{self.M},{self.N}] bf16)"
+        return f"{self.name}: C[{self.M},{self.N}] = A[{self.M},{self.K}] . B[{self.K},{self.N}]"
+
+    def _init_quant(self, name, dev):
+        import torch
+
+        import tiled_gemm_04_amd as tg
+        import workloads as wl
+
+        operand, self.kernel = QUANT_CASES[name]
+        a, b = wl.fp8_sources_bf16(wl.WORKLOADS["fp8"], device=dev)
+        x = a if operand == "a" else b
+        del a, b
+        R, C = x.shape
+        q = torch.empty(R, C, dtype=torch.float8_e4m3fn, device=dev)
+        if operand == "a":
+            s = torch.empty(R, (C + 127) // 128, dtype=torch.float32, device=dev)
+            self.launch = lambda: tg.quantize_fp8_1x128(x, q, s)
+        else:
+            s = torch.empty((R + 127) // 128, (C + 127) // 128, dtype=torch.float32, device=dev)
+            self.launch = lambda: tg.quantize_fp8_128x128(x, q, s)
+        self.w = None
+        self.M, self.N, self.K = R, C, 0
+        self.flops = 0
+        self.bytes = 2 * R * C + R * C + 4 * s.numel()  # read bf16, write codes and scales
+        self.family = "quant"
+        self.bound, self.peak = "hbm", PEAK_HBM_GBS
+        self.dtype = "bf16->fp8_e4m3"
+        self.inputs_for_oracle = None
 
     def time(self, steps, warmup):
         """(ms per step from the bracketing synchronisations, mean kernel ms).
@@ -256,8 +299,7 @@ def main():
         "vs_baseline": None,
         "dtype": head.dtype,
         "data": "synthetic (seeded, shapes and distributions of the source pages' workloads)",
-        "config": {"workload": f"{head.name}: C[{head.M},{head.N}] = A[{head.M},{head.K}] . "
-                               f"B[{head.K},{head.N}]", "M": head.M, "N": head.N, "K": head.K,
+        "config": {"workload": head.describe(), "M": head.M, "N": head.N, "K": head.K,
                    "kernel": head.kernel},
         "roofline": head.roofline(kern_ms),
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
@@ -268,7 +310,7 @@ def main():
     if not args.no_secondary:
         sec = {}
         for name in ("ffn_up", "ffn_down", "thin_m1", "thin_m8", "thin_m32", "thin_m64", "fp8",
-                     "fp8_ragged", "tiny"):
+                     "fp8_ragged", "tiny", "quant_a", "quant_b"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

@@ -138,6 +138,52 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C,
 int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
                          void* C, int64_t M, int64_t N, int64_t K, void* stream);
 
+/*
+ * quantize_fp8_1x128 -- FP8 codes and scales for the A operand of
+ * gemm_fp8_blockscaled: one scale per (row, 128-wide column group).
+ *
+ * The producer side of the DeepGEMM page's low-precision scheme (section
+ * 2.4): each group of consecutive values shares one fp32 scale that maps it
+ * into the e4m3 range.  For the group of row i, columns [128g, min(K,128g+128)):
+ *
+ *   scale     = amax / 448 in fp32 (rounded to nearest), amax = max |x| over
+ *               the group; 1 when the group is all zero
+ *   Q[i, k]   = e4m3fn( clamp(X[i, k] / scale, -448, 448) ), the division in
+ *               fp32 (rounded to nearest), the cast to nearest, ties to even;
+ *               zero keeps its sign
+ *
+ *   X    bf16 [M, K], row-major with row stride ldx >= K
+ *   Q    e4m3fn bytes [M, K], packed row-major (row stride K); may be passed
+ *        straight to gemm_fp8_blockscaled as A
+ *   S    fp32 [M, ceil(K/128)], packed row-major (gemm_fp8_blockscaled's sA)
+ *
+ * X must be finite (a NaN or infinity gives unspecified codes and scales in
+ * its group).  Q and S must not overlap X.  M == 0 or K == 0 is a no-op.
+ * Returns TGEMM_OK, TGEMM_ERR_INVALID (null pointer, negative size,
+ * ldx < K), TGEMM_ERR_UNSUPPORTED (more than 2^33 rows x 512-column
+ * chunks) or TGEMM_ERR_LAUNCH.
+ */
+int quantize_fp8_1x128(const void* X, void* Q, float* S, int64_t M, int64_t K, int64_t ldx,
+                       void* stream);
+
+/*
+ * quantize_fp8_128x128 -- FP8 codes and scales for the B operand of
+ * gemm_fp8_blockscaled: one scale per 128 x 128 block.
+ *
+ * Same rule as quantize_fp8_1x128 with the group being the block of rows
+ * [128g, min(K,128g+128)) and columns [128h, min(N,128h+128)) (DeepGEMM
+ * page, section 2.4: a small block of the weight matrix shares one scale).
+ *
+ *   W    bf16 [K, N], row-major with row stride ldw >= N
+ *   Q    e4m3fn bytes [K, N], packed row-major (gemm_fp8_blockscaled's B)
+ *   S    fp32 [ceil(K/128), ceil(N/128)], packed row-major (its sB)
+ *
+ * Same error behaviour as quantize_fp8_1x128 (TGEMM_ERR_UNSUPPORTED beyond
+ * 2^31 - 1 blocks).
+ */
+int quantize_fp8_128x128(const void* W, void* Q, float* S, int64_t K, int64_t N, int64_t ldw,
+                         void* stream);
+
 /* Name of the kernel configuration gemm_bf16_ex would launch for a problem
  * with 16-byte aligned operands (no launch, no validation of pointers;
  * operands that are not 16-byte aligned, or whose row strides are not
@@ -147,8 +193,8 @@ const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue,
                                   int out_dtype, int algo);
 
 /* Name of the kernel configuration gemm_fp8_blockscaled launches for these
- * sizes (the direct-to-LDS kernel when K is a multiple of 16, the general
- * kernel otherwise).  No launch. */
+ * sizes (the direct-to-LDS kernel when K is a multiple of 16 and N >= 4, the
+ * general kernel otherwise).  No launch. */
 const char* gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K);
 
 /* Static, human-readable text for a status code. */

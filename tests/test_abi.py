@@ -21,7 +21,8 @@ NULL = ctypes.c_void_p(0)
 
 def test_every_declared_function_is_exported():
     names = binding.header_functions()
-    assert {"gemm_bf16", "gemm_fp8_blockscaled", "gemm_bf16_ex"} <= set(names)
+    assert {"gemm_bf16", "gemm_fp8_blockscaled", "gemm_bf16_ex", "quantize_fp8_1x128",
+            "quantize_fp8_128x128"} <= set(names)
     L = binding.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -74,6 +75,20 @@ def test_fp8_validation():
     assert L.gemm_fp8_blockscaled(FAKE, FAKE, FAKE, FAKE, NULL, 4, 4, 4, NULL) == INV
     assert L.gemm_fp8_blockscaled(NULL, NULL, NULL, NULL, NULL, 0, 4, 4, NULL) == OK
     del f
+
+
+@pytest.mark.parametrize("fn", ["quantize_fp8_1x128", "quantize_fp8_128x128"])
+def test_quantize_validation(fn):
+    q = getattr(binding.lib(), fn)
+    assert q(FAKE, FAKE, FAKE, -1, 8, 8, NULL) == INV
+    assert q(FAKE, FAKE, FAKE, 8, -1, 8, NULL) == INV
+    assert q(FAKE, FAKE, FAKE, 1 << 31, 8, 8, NULL) == INV
+    assert q(NULL, FAKE, FAKE, 8, 8, 8, NULL) == INV
+    assert q(FAKE, NULL, FAKE, 8, 8, 8, NULL) == INV
+    assert q(FAKE, FAKE, NULL, 8, 8, 8, NULL) == INV
+    assert q(FAKE, FAKE, FAKE, 8, 8, 7, NULL) == INV  # row stride below the row length
+    assert q(NULL, NULL, NULL, 0, 8, 8, NULL) == OK
+    assert q(NULL, NULL, NULL, 8, 0, 8, NULL) == OK
 
 
 def test_kernel_selection_table():

@@ -62,6 +62,10 @@ def lib():
     L.gemm_bf16_ex.restype = i32
     L.gemm_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.gemm_fp8_blockscaled.restype = i32
+    L.quantize_fp8_1x128.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    L.quantize_fp8_1x128.restype = i32
+    L.quantize_fp8_128x128.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    L.quantize_fp8_128x128.restype = i32
     L.gemm_bf16_kernel_name.argtypes = [i64, i64, i64, i32, i32, i32]
     L.gemm_bf16_kernel_name.restype = ctypes.c_char_p
     L.gemm_fp8_kernel_name.argtypes = [i64, i64, i64]
@@ -78,7 +82,7 @@ def header_functions():
     """Names of the functions include/tgemm.h declares."""
     text = open(HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:gemm|quantize)_\w+)\s*\(", text)))
 
 
 def _stream_ptr(stream):
@@ -165,6 +169,44 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_fp8_blockscaled")
     return C
+
+
+def _quantize(name, X, Q, S, group_rows, stream):
+    _check_cuda(X, Q, S)
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    if Q.dtype not in (torch.float8_e4m3fn, torch.uint8) or S.dtype != torch.float32:
+        raise ValueError("Q must be float8_e4m3fn (or uint8 codes) and S float32")
+    ld = _row_major(X, "X")
+    R, Cn = X.shape
+    if not Q.is_contiguous() or not S.is_contiguous():
+        raise ValueError("Q and S must be contiguous (packed row-major)")
+    G = (R + 127) // 128 if group_rows else R
+    if tuple(Q.shape) != (R, Cn) or tuple(S.shape) != (G, (Cn + 127) // 128):
+        raise ValueError("shape mismatch")
+    st = getattr(lib(), name)(_ptr(X), _ptr(Q), _ptr(S), R, Cn, ld, _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, name)
+    return Q, S
+
+
+def quantize_fp8_1x128(X, Q, S, stream=None):
+    """FP8 codes and per-(row, 128-column group) scales of X on the GPU.
+
+    X: bfloat16 [M, K] with unit inner stride; Q: float8_e4m3fn (or uint8)
+    [M, K] contiguous; S: float32 [M, ceil(K/128)] contiguous.  Written in
+    place; returns (Q, S).
+    """
+    return _quantize("quantize_fp8_1x128", X, Q, S, False, stream)
+
+
+def quantize_fp8_128x128(W, Q, S, stream=None):
+    """FP8 codes and per-128x128-block scales of W on the GPU.
+
+    W: bfloat16 [K, N] with unit inner stride; Q: float8_e4m3fn (or uint8)
+    [K, N] contiguous; S: float32 [ceil(K/128), ceil(N/128)] contiguous.
+    """
+    return _quantize("quantize_fp8_128x128", W, Q, S, True, stream)
 
 
 def gemm_bf16_kernel_name(M, N, K, epilogue=EPI_NONE, out_dtype=OUT_BF16, algo=ALGO_AUTO):

@@ -78,6 +78,29 @@ bool use_thin(int64_t M, int algo) {
   return M <= kThinMaxM;
 }
 
+// Shared validation and launch of the two FP8 quantisers.
+int quantize_fp8(const void* X, void* Q, float* S, int64_t rows, int64_t cols, int64_t ldx,
+                 void* stream, bool blocks) {
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return TGEMM_ERR_INVALID;
+  if (rows == 0 || cols == 0) return TGEMM_OK;
+  if (X == nullptr || Q == nullptr || S == nullptr || ldx < cols) return TGEMM_ERR_INVALID;
+  if (!extent_ok(rows, cols, ldx) || !extent_ok(rows, cols, cols)) return TGEMM_ERR_INVALID;
+  tgemm::QuantArgs a;
+  a.X = static_cast<const uint16_t*>(X);
+  a.Q = static_cast<uint8_t*>(Q);
+  a.S = S;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ldx;
+  a.groups_per_row = (cols + 127) / 128;
+  a.vec_in = (aligned16(X) && ldx % 8 == 0) ? 1 : 0;
+  a.vec_out = (aligned8(Q) && cols % 8 == 0) ? 1 : 0;
+  const hipError_t e = blocks ? tgemm::launch_quant_fp8_128x128(a, static_cast<hipStream_t>(stream))
+                              : tgemm::launch_quant_fp8_1x128(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidConfiguration) return TGEMM_ERR_UNSUPPORTED;
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,6 +172,16 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
   a.vec_c = (aligned16(C) && N % 8 == 0) ? 1 : 0;
   const hipError_t e = tgemm::launch_fp8_blockscaled(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+int quantize_fp8_1x128(const void* X, void* Q, float* S, int64_t M, int64_t K, int64_t ldx,
+                       void* stream) {
+  return quantize_fp8(X, Q, S, M, K, ldx, stream, false);
+}
+
+int quantize_fp8_128x128(const void* W, void* Q, float* S, int64_t K, int64_t N, int64_t ldw,
+                         void* stream) {
+  return quantize_fp8(W, Q, S, K, N, ldw, stream, true);
 }
 
 const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue, int out_dtype,

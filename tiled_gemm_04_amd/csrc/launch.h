@@ -34,6 +34,18 @@ struct Fp8Args {
   int vec_c;  // 1: C rows may be written with 16-byte stores (N % 8 == 0, aligned base)
 };
 
+// FP8 quantiser problem: bf16 X [rows, cols] (row stride ldx) -> e4m3fn
+// codes Q [rows, cols] (packed) and fp32 scales S [.., groups_per_row].
+struct QuantArgs {
+  const uint16_t* X;
+  uint8_t* Q;
+  float* S;
+  int64_t rows, cols, ldx;
+  int64_t groups_per_row;  // ceil(cols / 128)
+  int vec_in;   // 1: X rows may be read with 16-byte loads (aligned base, ldx % 8 == 0)
+  int vec_out;  // 1: Q rows may be written with 8-byte stores (aligned base, cols % 8 == 0)
+};
+
 // Tiled bf16 kernel shapes (BM x BN output tile, 4 waves).
 enum TiledShape { kTile256x256 = 0, kTile256x128 = 1, kTile128x128 = 2, kNumTiledShapes = 3 };
 
@@ -57,6 +69,8 @@ hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
 // Register-staged kernel for FP8 operands the direct-to-LDS kernel cannot take.
 hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
+hipError_t launch_quant_fp8_1x128(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_quant_fp8_128x128(const QuantArgs& a, hipStream_t stream);
 const char* thin_kernel_name(int M);
 const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K);
 

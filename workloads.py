@@ -172,6 +172,20 @@ def fp8_inputs(w: Workload, device="cpu", M=None, N=None, K=None):
     return qa, sa, qb, sb
 
 
+def fp8_sources_bf16(w: Workload, device="cpu", M=None, N=None, K=None):
+    """(A bf16 [M,K], B bf16 [K,N]): the FP8 workload's unquantised operands
+    (same draws and outliers as ``fp8_inputs``) rounded to bf16, the inputs
+    of the GPU quantisers."""
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    a = draw((M, K), "normal", w.a_sigma, w.seed, T_A, device)
+    u = draw((M, K), "uniform", 1.0, w.seed, T_OUTLIER, device)
+    a = torch.where((u + 1.0) * 0.5 < 0.001, a * 20.0, a)
+    b = draw((K, N), "normal", w.b_sigma, w.seed, T_B, device)
+    return a.to(torch.bfloat16), b.to(torch.bfloat16)
+
+
 def bits_u16(t):
     """bf16 tensor -> numpy uint16 codes (on CPU)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")
