@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
                     help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
-                         "tiny, quant_a, quant_b)")
+                         "tiny, quant_a, quant_b, w8_m1..64)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -85,7 +85,12 @@ KERNEL_SOURCES = {
     "thin": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
     "fp8": ["common.h", "launch.h", "gemm_fp8_blockscaled.hip"],
     "quant": ["common.h", "launch.h", "quant_fp8.hip"],
+    "w8": ["common.h", "launch.h", "gemm_w8_thin.hip"],
 }
+
+# Weight-only int8 LM head: the thin-M workloads' X [M, 4096] times int8
+# codes Q [4096, 128256] with fp32 scales per (128 rows, column).
+W8_CASES = {"w8_m1": 1, "w8_m8": 8, "w8_m32": 32, "w8_m64": 64}
 
 # FP8 quantisers, timed on the FP8 workload's unquantised operands (bf16):
 # activations A [4096, 4096] in 1 x 128 groups, weights B [4096, 14336] in
@@ -123,6 +128,9 @@ class Case:
         self.name = name
         if name in QUANT_CASES:
             self._init_quant(name, dev)
+            return
+        if name in W8_CASES:
+            self._init_w8(name, dev)
             return
         w = wl.WORKLOADS[name]
         self.w = w
@@ -162,7 +170,32 @@ class Case:
         if self.family == "quant":
             grouping = "1x128" if self.name == "quant_a" else "128x128"
             return f"{self.name}: Q, S = quantize_fp8_{grouping}(X[{self.M},{self.N}] bf16)"
+        if self.family == "w8":
+            return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
+                    f"(Q[{self.K},{self.N}] int8 * S[{(self.K + 127) // 128},{self.N}])")
         return f"{self.name}: C[{self.M},{self.N}] = A[{self.M},{self.K}] . B[{self.K},{self.N}]"
+
+    def _init_w8(self, name, dev):
+        import torch
+
+        import tiled_gemm_04_amd as tg
+        import workloads as wl
+
+        w = wl.WORKLOADS["thin_m64"]
+        M, N, K = W8_CASES[name], w.N, w.K
+        x = wl.thin_x(w, M, dev)
+        q, s = wl.w8_weights(K, N, w.seed, dev)
+        c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        self.launch = lambda: tg.gemm_bf16_w8(x, q, s, None, c)
+        self.w = None
+        self.M, self.N, self.K = M, N, K
+        self.flops = 2 * M * N * K
+        self.bytes = 2 * M * K + K * N + 4 * s.numel() + 2 * M * N
+        self.kernel = tg.gemm_w8_kernel_name(M, N, K)
+        self.family = "w8"
+        self.bound, self.peak = "hbm", PEAK_HBM_GBS
+        self.dtype = "bf16 x int8"
+        self.inputs_for_oracle = None
 
     def _init_quant(self, name, dev):
         import torch
@@ -310,7 +343,8 @@ def main():
     if not args.no_secondary:
         sec = {}
         for name in ("ffn_up", "ffn_down", "thin_m1", "thin_m8", "thin_m32", "thin_m64", "fp8",
-                     "fp8_ragged", "tiny", "quant_a", "quant_b"):
+                     "fp8_ragged", "tiny", "quant_a", "quant_b", "w8_m1", "w8_m8", "w8_m32",
+                     "w8_m64"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

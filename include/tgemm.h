@@ -139,6 +139,38 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
                          void* C, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * gemm_bf16_w8 -- C[i,n] = epilogue( sum_k X[i,k] * (Q[k,n] * S[k/128, n]) + bias[n] )
+ *
+ * Weight-only int8 GEMM for the small-M, memory-bound case: the LM head of
+ * the GEMM compute-cost page (section 7.2, its first remedy: keep the large
+ * weight in a low-precision integer format so fewer bytes are streamed).
+ * Scales follow the per-group scheme of the DeepGEMM page, section 2.4: one
+ * fp32 scale per (group of 128 consecutive rows of Q, column).
+ *
+ *   X     bf16 [M, K], row stride ldx >= K (elements)
+ *   Q     int8 [K, N] two's-complement codes, row stride ldq >= N (bytes)
+ *   S     fp32 [ceil(K/128), N], packed row-major; row g scales Q rows
+ *         [128g, min(K, 128g+128))
+ *   bias  bf16 [N] or NULL (required when epilogue != TGEMM_EPI_NONE)
+ *   C     [M, N] bf16 or fp32 (out_dtype), row stride ldc >= N
+ *
+ * Epilogue, output rounding and conventions as gemm_bf16.  Products X * Q
+ * are exact and summed in fp32 per 128-row group, and each group's sum is
+ * scaled by S in fp32 (no weight is rounded), so the result carries the
+ * rounding of an fp32-accumulated GEMM.
+ * Supported: M <= 64, K % 8 == 0, N % 4 == 0, ldq % 4 == 0 (others return
+ * TGEMM_ERR_UNSUPPORTED).  Returns TGEMM_OK, TGEMM_ERR_INVALID,
+ * TGEMM_ERR_UNSUPPORTED or TGEMM_ERR_LAUNCH.
+ */
+int gemm_bf16_w8(const void* X, const void* Q, const float* S, const void* bias, void* C,
+                 int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                 int epilogue, int out_dtype, void* stream);
+
+/* Name of the kernel gemm_bf16_w8 launches for packed operands of these
+ * sizes, or NULL when they are unsupported or invalid.  No launch. */
+const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K);
+
+/*
  * quantize_fp8_1x128 -- FP8 codes and scales for the A operand of
  * gemm_fp8_blockscaled: one scale per (row, 128-wide column group).
  *

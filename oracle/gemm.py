@@ -20,6 +20,12 @@ What is computed (all in float64 on exactly decoded inputs):
   block of B.  Each element is dequantised as ``decode(q) * scale`` before the
   same contraction; both factors are exact in float64, so the dequantised
   operands are exact.
+* Weight-only int8.  The LM head's first remedy on the GEMM compute-cost page
+  (section 7.2) keeps the weight in a low-precision integer format; with the
+  per-group scales of the DeepGEMM page (section 2.4) each weight is
+  ``q[k, n] * s[k // 128, n]`` (int8 code times the fp32 scale of its
+  128-row group and column), exact in float64, before the same contraction
+  with the bf16 activations.
 * FLOP count.  A multiply-add counts as two operations, so an ``[M,K]x[K,N]``
   product costs ``2*M*N*K`` (GEMM compute-cost page, section 3.1); the bias is
   not counted.
@@ -40,6 +46,7 @@ EPI_BIAS = 1
 EPI_BIAS_GELU_TANH = 2
 
 FP8_GROUP = 128  # K-group width of the A scales; B scales cover 128 x 128 blocks
+W8_GROUP = 128   # rows of Q sharing one scale per column (weight-only int8)
 
 GELU_C = math.sqrt(2.0 / math.pi)
 GELU_A = 0.044715
@@ -111,6 +118,24 @@ def dequant_fp8_b(qb_bits, sb):
     if sb.shape != ((K + FP8_GROUP - 1) // FP8_GROUP, (N + FP8_GROUP - 1) // FP8_GROUP):
         raise ValueError(f"sB shape {sb.shape} for B {qb.shape}")
     return qb * sb[gk][:, gn]
+
+
+def dequant_w8(q, s):
+    """W[k, n] = q[k, n] * s[k // 128, n] for int8 codes q [K, N] and fp32
+    scales s [ceil(K/128), N] (exact in float64)."""
+    q = np.asarray(q, dtype=np.int8).astype(np.float64)
+    s = np.asarray(s, dtype=np.float32).astype(np.float64)
+    K, N = q.shape
+    if s.shape != ((K + W8_GROUP - 1) // W8_GROUP, N):
+        raise ValueError(f"scale shape {s.shape} for codes {q.shape}")
+    return q * s[np.arange(K) // W8_GROUP, :]
+
+
+def gemm_bf16_w8_bits(x_bits, q, s, bias_bits=None, epilogue=EPI_NONE):
+    """Oracle for the weight-only int8 path: bf16 activations times the
+    dequantised weights, then bias and epilogue."""
+    bias = None if bias_bits is None else bf16_decode(bias_bits)
+    return gemm_f64(bf16_decode(x_bits), dequant_w8(q, s), bias, epilogue)
 
 
 def gemm_fp8_blockscaled_bits(qa_bits, sa, qb_bits, sb):

@@ -14,6 +14,14 @@ matrix B.  The readings used for the points the page leaves open:
   cast rounding to nearest, ties to even (saturating before the cast);
 * dequantised value ``decode(q) * s``;
 * groups at ragged edges cover only the elements inside the matrix.
+
+Weight-only int8 (the GEMM compute-cost page, section 7.2: store the LM-head
+weight in a low-precision integer format), round to nearest per group: one
+scale per (128 consecutive rows, column) of W [K, N]:
+
+* ``s = amax / 127`` in fp32 (round to nearest), 1 for an all-zero group;
+* ``q = rint(clamp(w / s, -127, 127))`` with ``w / s`` in fp32 and ties to
+  even, stored as int8 (the code -128 is never produced).
 """
 
 import numpy as np
@@ -58,4 +66,25 @@ def quantise_blocks_128x128(x):
             rs = slice(g * GROUP, min(K, (g + 1) * GROUP))
             cs = slice(h * GROUP, min(N, (h + 1) * GROUP))
             q[rs, cs], s[g, h] = _quantise_group(x[rs, cs])
+    return q, s
+
+
+INT8_MAX = 127.0
+
+
+def quantise_int8_k128(w):
+    """W [K, N] fp32 -> (int8 codes [K, N], fp32 scales [ceil(K/128), N])."""
+    w = np.asarray(w, dtype=np.float32)
+    K, N = w.shape
+    G = (K + GROUP - 1) // GROUP
+    q = np.zeros((K, N), dtype=np.int8)
+    s = np.zeros((G, N), dtype=np.float32)
+    for g in range(G):
+        rs = slice(g * GROUP, min(K, (g + 1) * GROUP))
+        amax = np.max(np.abs(w[rs]), axis=0).astype(np.float32)
+        sg = np.where(amax == 0, np.float32(1.0), (amax / np.float32(INT8_MAX)).astype(np.float32))
+        sg = sg.astype(np.float32)
+        scaled = (w[rs] / sg[None, :]).astype(np.float32)
+        q[rs] = np.rint(np.clip(scaled, -INT8_MAX, INT8_MAX)).astype(np.int8)
+        s[g] = sg
     return q, s

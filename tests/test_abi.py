@@ -22,7 +22,7 @@ NULL = ctypes.c_void_p(0)
 def test_every_declared_function_is_exported():
     names = binding.header_functions()
     assert {"gemm_bf16", "gemm_fp8_blockscaled", "gemm_bf16_ex", "quantize_fp8_1x128",
-            "quantize_fp8_128x128"} <= set(names)
+            "quantize_fp8_128x128", "gemm_bf16_w8", "gemm_w8_kernel_name"} <= set(names)
     L = binding.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -75,6 +75,30 @@ def test_fp8_validation():
     assert L.gemm_fp8_blockscaled(FAKE, FAKE, FAKE, FAKE, NULL, 4, 4, 4, NULL) == INV
     assert L.gemm_fp8_blockscaled(NULL, NULL, NULL, NULL, NULL, 0, 4, 4, NULL) == OK
     del f
+
+
+def _w8(X=FAKE, Q=FAKE, S=FAKE, bias=FAKE, C=FAKE, M=8, N=64, K=64, ldx=64, ldq=64, ldc=64, epi=0,
+        out=1):
+    return binding.lib().gemm_bf16_w8(X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epi, out, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INV), (dict(K=-1), INV), (dict(C=NULL), INV), (dict(X=NULL), INV),
+    (dict(Q=NULL), INV), (dict(S=NULL), INV), (dict(epi=1, bias=NULL), INV), (dict(out=2), INV),
+    (dict(ldx=63), INV), (dict(ldq=10), INV),
+    (dict(M=65), UNS), (dict(N=66, ldq=66, ldc=66), UNS), (dict(K=60, ldx=64), UNS),
+    (dict(ldq=66), UNS),
+    (dict(M=0), OK), (dict(N=0, ldq=1, ldc=1), OK),
+])
+def test_w8_validation(kw, status):
+    assert _w8(**kw) == status
+
+
+def test_w8_kernel_names():
+    assert binding.gemm_w8_kernel_name(1, 128256, 4096) == "tgemm_w8_thin_m16"
+    assert binding.gemm_w8_kernel_name(64, 128256, 4096) == "tgemm_w8_thin_m64"
+    assert binding.gemm_w8_kernel_name(65, 128256, 4096) is None
+    assert binding.gemm_w8_kernel_name(8, 130, 4096) is None
 
 
 @pytest.mark.parametrize("fn", ["quantize_fp8_1x128", "quantize_fp8_128x128"])

@@ -349,3 +349,94 @@ def test_fp8_generator_outlier_rate_and_scale_shapes():
     assert qb.shape == (512, 384) and sb.shape == (4, 3)
     dec = formats.e4m3_decode(wl.bits_u8(qa))
     assert np.all(np.max(np.abs(dec.reshape(256, 4, 128)), axis=2) == 448.0)
+
+
+# ---------------------------------------------------------- weight-only int8 ----
+
+def _w8_small(K, N, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-127, 128, (K, N)).astype(np.int8)
+    s = (rng.uniform(0.5, 2.0, ((K + 127) // 128, N)) * 1e-3).astype(np.float32)
+    return q, s
+
+
+def test_w8_dequantisation_indexing_brute_force():
+    q, s = _w8_small(300, 37, 21)
+    w = gemm.dequant_w8(q, s)
+    for k in range(0, 300, 7):
+        for n in range(37):
+            assert w[k, n] == float(q[k, n]) * float(s[k // 128, n])
+
+
+def test_w8_integer_codes_unit_scales_exact():
+    rng = np.random.default_rng(22)
+    M, K, N = 3, 260, 9
+    x = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    q = rng.integers(-127, 128, (K, N)).astype(np.int8)
+    xb = formats.bf16_encode_rne(x)
+    y, d = gemm.gemm_bf16_w8_bits(xb, q, np.ones((3, N), np.float32))
+    assert np.array_equal(y, x.astype(np.float64) @ q.astype(np.float64))
+    assert np.array_equal(d, np.abs(x.astype(np.float64)) @ np.abs(q.astype(np.float64)))
+
+
+def test_w8_power_of_two_scale_changes_one_group():
+    rng = np.random.default_rng(23)
+    M, K, N = 4, 384, 12
+    xb = formats.bf16_encode_rne(rng.standard_normal((M, K)).astype(np.float32))
+    q, s = _w8_small(K, N, 24)
+    y, _ = gemm.gemm_bf16_w8_bits(xb, q, s)
+    s2 = s.copy()
+    s2[1, 5] *= 0.25
+    y2, _ = gemm.gemm_bf16_w8_bits(xb, q, s2)
+    x = formats.bf16_decode(xb)
+    part = x[:, 128:256] @ (q[128:256, 5].astype(np.float64) * float(s[1, 5]))
+    assert np.array_equal(np.delete(y2, 5, 1), np.delete(y, 5, 1))
+    assert np.allclose(y2[:, 5], y[:, 5] - 0.75 * part, rtol=0, atol=1e-12)
+
+
+def test_w8_equals_bf16_path_when_weights_are_bf16_exact():
+    """With power-of-two scales every q * s (|q| <= 127) is exact in bf16, so
+    the int8 oracle must equal the bf16 oracle on those weights."""
+    rng = np.random.default_rng(25)
+    M, K, N = 5, 200, 33
+    xb = formats.bf16_encode_rne(rng.standard_normal((M, K)).astype(np.float32))
+    q = rng.integers(-127, 128, (K, N)).astype(np.int8)
+    s = np.ldexp(1.0, rng.integers(-12, -4, (2, N))).astype(np.float32)
+    w = gemm.dequant_w8(q, s)
+    wb = formats.bf16_encode_rne(w.astype(np.float32))
+    assert np.array_equal(formats.bf16_decode(wb), w)
+    y8, d8 = gemm.gemm_bf16_w8_bits(xb, q, s)
+    yb, db = gemm.gemm_bf16_bits(xb, wb)
+    assert np.array_equal(y8, yb) and np.array_equal(d8, db)
+
+
+def test_int8_quantiser_invariants_and_ties():
+    rng = np.random.default_rng(26)
+    w = rng.standard_normal((300, 6)).astype(np.float32)
+    w[128:256, 2] = 0.0                      # an all-zero group
+    w[0, 4] = 127.0                          # group (0, 4): scale exactly 1 ...
+    w[1, 4], w[2, 4], w[3, 4] = 2.5, 3.5, -0.5   # ... so these are exact ties
+    q, s = quant.quantise_int8_k128(w)
+    assert q.dtype == np.int8 and s.shape == (3, 6)
+    assert s[1, 2] == 1.0 and np.all(q[128:256, 2] == 0)
+    assert s[0, 4] == 1.0 and (q[1, 4], q[2, 4], q[3, 4]) == (2, 4, 0)
+    for g in range(3):
+        rs = slice(128 * g, min(300, 128 * (g + 1)))
+        for n in range(6):
+            col = w[rs, n].astype(np.float64)
+            if np.all(col == 0):
+                continue
+            amax = np.float32(np.max(np.abs(w[rs, n])))
+            assert s[g, n] == np.float32(amax / np.float32(127.0))
+            assert np.max(np.abs(q[rs, n].astype(np.int64))) == 127
+            assert np.all(np.abs(col - q[rs, n] * float(s[g, n])) <= 0.5 * float(s[g, n]) * (1 + 1e-6))
+
+
+def test_w8_generator_shapes_and_ranges():
+    q, s = wl.w8_weights(300, 40, 4)
+    assert q.dtype == torch.int8 and tuple(q.shape) == (300, 40)
+    assert s.dtype == torch.float32 and tuple(s.shape) == (3, 40)
+    assert int(q.min()) >= -127 and int(q.max()) <= 127
+    assert float(s.min()) > 0
+    q2, s2 = wl.w8_weights(300, 40, 4)
+    assert torch.equal(q, q2) and torch.equal(s, s2)

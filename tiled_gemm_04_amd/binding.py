@@ -62,6 +62,10 @@ def lib():
     L.gemm_bf16_ex.restype = i32
     L.gemm_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.gemm_fp8_blockscaled.restype = i32
+    L.gemm_bf16_w8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.gemm_bf16_w8.restype = i32
+    L.gemm_w8_kernel_name.argtypes = [i64, i64, i64]
+    L.gemm_w8_kernel_name.restype = ctypes.c_char_p
     L.quantize_fp8_1x128.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     L.quantize_fp8_1x128.restype = i32
     L.quantize_fp8_128x128.argtypes = [vp, vp, vp, i64, i64, i64, vp]
@@ -169,6 +173,40 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_fp8_blockscaled")
     return C
+
+
+def gemm_bf16_w8(X, Q, S, bias, C, epilogue=EPI_NONE, stream=None):
+    """C[M,N] = epilogue(X[M,K] @ (Q[K,N] * S[k/128, N]) + bias[N]) on the GPU.
+
+    X: bfloat16 [M, K] (unit inner stride); Q: int8 [K, N] (unit inner stride);
+    S: float32 [ceil(K/128), N] contiguous; bias: bfloat16 [N] or None;
+    C: bfloat16 or float32 [M, N] (unit inner stride), written in place.
+    """
+    _check_cuda(X, Q, S, bias, C)
+    if X.dtype != torch.bfloat16 or Q.dtype != torch.int8 or S.dtype != torch.float32:
+        raise ValueError("X must be bfloat16, Q int8 and S float32")
+    if C.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("C must be bfloat16 or float32")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    ldx, ldq, ldc = _row_major(X, "X"), _row_major(Q, "Q"), _row_major(C, "C")
+    M, K = X.shape
+    K2, N = Q.shape
+    if K2 != K or tuple(C.shape) != (M, N) or tuple(S.shape) != ((K + 127) // 128, N):
+        raise ValueError("shape mismatch")
+    if not S.is_contiguous():
+        raise ValueError("S must be contiguous")
+    out = OUT_BF16 if C.dtype == torch.bfloat16 else OUT_F32
+    st = lib().gemm_bf16_w8(_ptr(X), _ptr(Q), _ptr(S), _ptr(bias), _ptr(C), M, N, K, ldx, ldq, ldc,
+                            int(epilogue), out, _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_bf16_w8")
+    return C
+
+
+def gemm_w8_kernel_name(M, N, K):
+    r = lib().gemm_w8_kernel_name(M, N, K)
+    return None if r is None else r.decode()
 
 
 def _quantize(name, X, Q, S, group_rows, stream):

@@ -174,6 +174,40 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
+int gemm_bf16_w8(const void* X, const void* Q, const float* S, const void* bias, void* C,
+                 int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                 int epilogue, int out_dtype, void* stream) {
+  // Same argument rules as gemm_bf16 (Q in place of B, row stride in bytes).
+  const int v = validate_bf16(X, Q, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype,
+                              TGEMM_ALGO_AUTO);
+  if (v != TGEMM_OK || M == 0 || N == 0) return v;
+  if (K > 0 && S == nullptr) return TGEMM_ERR_INVALID;
+  if (!tgemm::w8_supported(M, N, K, ldx, ldq)) return TGEMM_ERR_UNSUPPORTED;
+  tgemm::W8Args a;
+  a.X = static_cast<const uint16_t*>(X);
+  a.Q = static_cast<const uint8_t*>(Q);
+  a.S = S;
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.ldx = ldx;
+  a.ldq = ldq;
+  a.ldc = ldc;
+  // A lane stores 4 consecutive outputs: 8 bytes of bf16 or 16 bytes of fp32.
+  a.vec_c = ((out_dtype == TGEMM_OUT_BF16 ? aligned8(C) : aligned16(C)) && ldc % 4 == 0) ? 1 : 0;
+  const hipError_t e = tgemm::launch_w8_thin(a, epilogue, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return nullptr;
+  if (!tgemm::w8_supported(M, N, K, K, N)) return nullptr;
+  return tgemm::w8_kernel_name(static_cast<int>(M));
+}
+
 int quantize_fp8_1x128(const void* X, void* Q, float* S, int64_t M, int64_t K, int64_t ldx,
                        void* stream) {
   return quantize_fp8(X, Q, S, M, K, ldx, stream, false);

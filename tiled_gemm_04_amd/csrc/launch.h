@@ -46,6 +46,20 @@ struct QuantArgs {
   int vec_out;  // 1: Q rows may be written with 8-byte stores (aligned base, cols % 8 == 0)
 };
 
+// Weight-only int8 GEMM: bf16 X [M, K] (row stride ldx) times int8 codes
+// Q [K, N] (row stride ldq bytes) with fp32 scales S [ceil(K/128), N]
+// (packed), + bias, epilogue, into C [M, N] (row stride ldc).
+struct W8Args {
+  const uint16_t* X;
+  const uint8_t* Q;
+  const float* S;
+  const uint16_t* bias;
+  void* C;
+  int M, N, K;
+  int64_t ldx, ldq, ldc;
+  int vec_c;  // 1: C rows may be written with 8- / 16-byte stores
+};
+
 // Tiled bf16 kernel shapes (BM x BN output tile, 4 waves).
 enum TiledShape { kTile256x256 = 0, kTile256x128 = 1, kTile128x128 = 2, kNumTiledShapes = 3 };
 
@@ -69,6 +83,9 @@ hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
 // Register-staged kernel for FP8 operands the direct-to-LDS kernel cannot take.
 hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
+hipError_t launch_w8_thin(const W8Args& a, int epilogue, int out_bf16, hipStream_t stream);
+bool w8_supported(int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq);
+const char* w8_kernel_name(int M);
 hipError_t launch_quant_fp8_1x128(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quant_fp8_128x128(const QuantArgs& a, hipStream_t stream);
 const char* thin_kernel_name(int M);

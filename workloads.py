@@ -37,6 +37,7 @@ E4M3_MAX = 448.0
 
 # tensor indices inside one workload's seed space
 T_A, T_B, T_BIAS, T_OUTLIER = 1, 2, 3, 4
+T_W8_CODES, T_W8_SCALES = 6, 7
 
 
 @dataclass(frozen=True)
@@ -107,6 +108,11 @@ def bf16_inputs(w: Workload, device="cpu", rows=None):
     if w.bias_sigma > 0:
         bias = bf16((w.N,), "normal", w.bias_sigma, w.seed, T_BIAS, device)
     return a, b, bias
+
+
+def thin_x(w: Workload, M, device="cpu"):
+    """The first M rows of a thin-M workload's X (the same draws bf16_inputs uses)."""
+    return bf16((64, w.K), w.a_dist, w.a_sigma, w.seed, T_A, device)[:M].contiguous()
 
 
 def ffn_hidden(M, N, seed, device="cpu"):
@@ -184,6 +190,21 @@ def fp8_sources_bf16(w: Workload, device="cpu", M=None, N=None, K=None):
     a = torch.where((u + 1.0) * 0.5 < 0.001, a * 20.0, a)
     b = draw((K, N), "normal", w.b_sigma, w.seed, T_B, device)
     return a.to(torch.bfloat16), b.to(torch.bfloat16)
+
+
+def w8_weights(K, N, seed, device="cpu"):
+    """Synthetic operands of a weight-only int8 LM head: int8 codes Q [K, N]
+    and fp32 scales S [ceil(K/128), N].
+
+    Drawn directly rather than quantised: codes follow N(0, 32) rounded and
+    clipped to [-127, 127] (the shape of round-to-nearest codes of Gaussian
+    weights under a per-group max scaling) and scales are 4.6e-4 * (1 + 0.2 u),
+    u ~ U[-1, 1] (about the max of 128 draws of N(0, 0.02), over 127).
+    """
+    q = draw((K, N), "normal", 32.0, seed, T_W8_CODES, device).round().clamp(-127, 127)
+    G = (K + 127) // 128
+    u = draw((G, N), "uniform", 1.0, seed, T_W8_SCALES, device)
+    return q.to(torch.int8), (4.6e-4 * (1.0 + 0.2 * u)).to(torch.float32).contiguous()
 
 
 def bits_u16(t):
