@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
                     help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
-                         "tiny, quant_a, quant_b, w8_m1..64)")
+                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -85,12 +85,14 @@ KERNEL_SOURCES = {
     "thin": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
     "fp8": ["common.h", "launch.h", "gemm_fp8_blockscaled.hip"],
     "quant": ["common.h", "launch.h", "quant_fp8.hip"],
-    "w8": ["common.h", "launch.h", "gemm_w8_thin.hip"],
+    "w8": ["common.h", "launch.h", "gemm_wq_thin.hip"],
+    "w4": ["common.h", "launch.h", "gemm_wq_thin.hip"],
 }
 
 # Weight-only int8 LM head: the thin-M workloads' X [M, 4096] times int8
 # codes Q [4096, 128256] with fp32 scales per (128 rows, column).
-W8_CASES = {"w8_m1": 1, "w8_m8": 8, "w8_m32": 32, "w8_m64": 64}
+W8_CASES = {"w8_m1": 1, "w8_m8": 8, "w8_m32": 32, "w8_m64": 64,
+            "w4_m1": 1, "w4_m8": 8, "w4_m32": 32, "w4_m64": 64}
 
 # FP8 quantisers, timed on the FP8 workload's unquantised operands (bf16):
 # activations A [4096, 4096] in 1 x 128 groups, weights B [4096, 14336] in
@@ -173,6 +175,9 @@ class Case:
         if self.family == "w8":
             return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
                     f"(Q[{self.K},{self.N}] int8 * S[{(self.K + 127) // 128},{self.N}])")
+        if self.family == "w4":
+            return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
+                    f"(Q[{self.K},{self.N}] int4, two per byte * S[{(self.K + 127) // 128},{self.N}])")
         return f"{self.name}: C[{self.M},{self.N}] = A[{self.M},{self.K}] . B[{self.K},{self.N}]"
 
     def _init_w8(self, name, dev):
@@ -184,17 +189,20 @@ class Case:
         w = wl.WORKLOADS["thin_m64"]
         M, N, K = W8_CASES[name], w.N, w.K
         x = wl.thin_x(w, M, dev)
-        q, s = wl.w8_weights(K, N, w.seed, dev)
+        bits = 8 if name.startswith("w8") else 4
+        q, s = (wl.w8_weights if bits == 8 else wl.w4_weights)(K, N, w.seed, dev)
         c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        self.launch = lambda: tg.gemm_bf16_w8(x, q, s, None, c)
+        fn = tg.gemm_bf16_w8 if bits == 8 else tg.gemm_bf16_w4
+        self.launch = lambda: fn(x, q, s, None, c)
         self.w = None
         self.M, self.N, self.K = M, N, K
         self.flops = 2 * M * N * K
-        self.bytes = 2 * M * K + K * N + 4 * s.numel() + 2 * M * N
-        self.kernel = tg.gemm_w8_kernel_name(M, N, K)
-        self.family = "w8"
+        # X, the codes (K*N*bits/8 bytes), the scales and C, each once.
+        self.bytes = 2 * M * K + q.numel() + 4 * s.numel() + 2 * M * N
+        self.kernel = (tg.gemm_w8_kernel_name if bits == 8 else tg.gemm_w4_kernel_name)(M, N, K)
+        self.family = "w8" if bits == 8 else "w4"
         self.bound, self.peak = "hbm", PEAK_HBM_GBS
-        self.dtype = "bf16 x int8"
+        self.dtype = "bf16 x int8" if bits == 8 else "bf16 x int4"
         self.inputs_for_oracle = None
 
     def _init_quant(self, name, dev):
@@ -344,7 +352,7 @@ def main():
         sec = {}
         for name in ("ffn_up", "ffn_down", "thin_m1", "thin_m8", "thin_m32", "thin_m64", "fp8",
                      "fp8_ragged", "tiny", "quant_a", "quant_b", "w8_m1", "w8_m8", "w8_m32",
-                     "w8_m64"):
+                     "w8_m64", "w4_m1", "w4_m8", "w4_m32", "w4_m64"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

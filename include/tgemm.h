@@ -171,6 +171,35 @@ int gemm_bf16_w8(const void* X, const void* Q, const float* S, const void* bias,
 const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K);
 
 /*
+ * gemm_bf16_w4 -- C[i,n] = epilogue( sum_k X[i,k] * (q[k,n] * S[k/128, n]) + bias[n] )
+ *
+ * Weight-only int4 GEMM: gemm_bf16_w8 with 4-bit codes, a quarter of the
+ * bf16 weight's bytes (the GEMM compute-cost page, section 4.3, lists int4
+ * beside int8 as the low-precision integer weight formats; section 7.2 is
+ * the LM-head use).
+ *
+ *   X     bf16 [M, K], row stride ldx >= K (elements)
+ *   Q     bytes [K/2, N], row stride ldq >= N (bytes): byte (r, n) holds
+ *         q[2r, n] in bits 0-3 and q[2r+1, n] in bits 4-7, each a 4-bit
+ *         two's-complement code in [-8, 7]
+ *   S     fp32 [ceil(K/128), N], packed row-major; row g scales K rows
+ *         [128g, min(K, 128g+128)) (Q byte rows [64g, 64g+64))
+ *   bias, C, epilogue, out_dtype, stream as gemm_bf16_w8
+ *
+ * Numerics as gemm_bf16_w8: products are exact and each 128-row group's
+ * fp32 sum is scaled once.  Supported: M <= 64, K % 8 == 0, N % 4 == 0,
+ * ldq % 4 == 0 (others return TGEMM_ERR_UNSUPPORTED).  Returns TGEMM_OK,
+ * TGEMM_ERR_INVALID, TGEMM_ERR_UNSUPPORTED or TGEMM_ERR_LAUNCH.
+ */
+int gemm_bf16_w4(const void* X, const void* Q, const float* S, const void* bias, void* C,
+                 int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                 int epilogue, int out_dtype, void* stream);
+
+/* Name of the kernel gemm_bf16_w4 launches for packed operands of these
+ * sizes, or NULL when they are unsupported or invalid.  No launch. */
+const char* gemm_w4_kernel_name(int64_t M, int64_t N, int64_t K);
+
+/*
  * quantize_fp8_1x128 -- FP8 codes and scales for the A operand of
  * gemm_fp8_blockscaled: one scale per (row, 128-wide column group).
  *

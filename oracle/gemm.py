@@ -26,6 +26,11 @@ What is computed (all in float64 on exactly decoded inputs):
   ``q[k, n] * s[k // 128, n]`` (int8 code times the fp32 scale of its
   128-row group and column), exact in float64, before the same contraction
   with the bf16 activations.
+* Weight-only int4.  The same with 4-bit codes (the GEMM compute-cost page,
+  section 4.3, names int4 beside int8).  Storage: byte ``(r, n)`` of the
+  packed matrix holds the codes of K rows ``2r`` (bits 0-3) and ``2r + 1``
+  (bits 4-7) of column ``n``, each a 4-bit two's-complement number, so a
+  nibble ``v`` is the code ``v - 16`` when ``v >= 8`` and ``v`` otherwise.
 * FLOP count.  A multiply-add counts as two operations, so an ``[M,K]x[K,N]``
   product costs ``2*M*N*K`` (GEMM compute-cost page, section 3.1); the bias is
   not counted.
@@ -136,6 +141,28 @@ def gemm_bf16_w8_bits(x_bits, q, s, bias_bits=None, epilogue=EPI_NONE):
     dequantised weights, then bias and epilogue."""
     bias = None if bias_bits is None else bf16_decode(bias_bits)
     return gemm_f64(bf16_decode(x_bits), dequant_w8(q, s), bias, epilogue)
+
+
+def unpack_int4(packed):
+    """Packed bytes [K/2, N] -> int4 codes as int8 [K, N] (values -8 .. 7):
+    row 2r from the low nibble of byte row r, row 2r + 1 from the high one."""
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int16)
+    half, N = p.shape
+    q = np.zeros((2 * half, N), dtype=np.int8)
+    for h, nib in ((0, p & 0x0F), (1, p >> 4)):
+        q[h::2] = np.where(nib >= 8, nib - 16, nib).astype(np.int8)
+    return q
+
+
+def dequant_w4(packed, s):
+    """W[k, n] = q[k, n] * s[k // 128, n] for packed int4 codes (exact)."""
+    return dequant_w8(unpack_int4(packed), s)
+
+
+def gemm_bf16_w4_bits(x_bits, packed, s, bias_bits=None, epilogue=EPI_NONE):
+    """Oracle for the weight-only int4 path (as gemm_bf16_w8_bits)."""
+    bias = None if bias_bits is None else bf16_decode(bias_bits)
+    return gemm_f64(bf16_decode(x_bits), dequant_w4(packed, s), bias, epilogue)
 
 
 def gemm_fp8_blockscaled_bits(qa_bits, sa, qb_bits, sb):

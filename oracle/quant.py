@@ -22,6 +22,12 @@ scale per (128 consecutive rows, column) of W [K, N]:
 * ``s = amax / 127`` in fp32 (round to nearest), 1 for an all-zero group;
 * ``q = rint(clamp(w / s, -127, 127))`` with ``w / s`` in fp32 and ties to
   even, stored as int8 (the code -128 is never produced).
+
+Weight-only int4 (section 4.3 of the same page lists int4 beside int8), the
+same scheme with 4-bit codes: ``s = amax / 7``, ``q = rint(clamp(w / s, -7,
+7))`` (the code -8 is never produced), packed two per byte along K: byte
+``(r, n)`` holds ``q[2r, n]`` in bits 0-3 and ``q[2r + 1, n]`` in bits 4-7,
+two's complement.
 """
 
 import numpy as np
@@ -72,8 +78,10 @@ def quantise_blocks_128x128(x):
 INT8_MAX = 127.0
 
 
-def quantise_int8_k128(w):
-    """W [K, N] fp32 -> (int8 codes [K, N], fp32 scales [ceil(K/128), N])."""
+INT4_MAX = 7.0
+
+
+def _quantise_int_k128(w, qmax):
     w = np.asarray(w, dtype=np.float32)
     K, N = w.shape
     G = (K + GROUP - 1) // GROUP
@@ -82,9 +90,32 @@ def quantise_int8_k128(w):
     for g in range(G):
         rs = slice(g * GROUP, min(K, (g + 1) * GROUP))
         amax = np.max(np.abs(w[rs]), axis=0).astype(np.float32)
-        sg = np.where(amax == 0, np.float32(1.0), (amax / np.float32(INT8_MAX)).astype(np.float32))
+        sg = np.where(amax == 0, np.float32(1.0), (amax / np.float32(qmax)).astype(np.float32))
         sg = sg.astype(np.float32)
         scaled = (w[rs] / sg[None, :]).astype(np.float32)
-        q[rs] = np.rint(np.clip(scaled, -INT8_MAX, INT8_MAX)).astype(np.int8)
+        q[rs] = np.rint(np.clip(scaled, -qmax, qmax)).astype(np.int8)
         s[g] = sg
     return q, s
+
+
+def quantise_int8_k128(w):
+    """W [K, N] fp32 -> (int8 codes [K, N], fp32 scales [ceil(K/128), N])."""
+    return _quantise_int_k128(w, INT8_MAX)
+
+
+def quantise_int4_k128(w):
+    """W [K, N] fp32 (K even) -> (int4 codes as int8 [K, N], fp32 scales
+    [ceil(K/128), N]); pack_int4 gives the stored bytes."""
+    if np.asarray(w).shape[0] % 2:
+        raise ValueError("int4 codes pair up along K: K must be even")
+    return _quantise_int_k128(w, INT4_MAX)
+
+
+def pack_int4(q):
+    """int4 codes [K, N] (K even, values -8 .. 7) -> bytes [K/2, N]: the
+    two's-complement nibble of row 2r in bits 0-3, of row 2r + 1 in 4-7."""
+    q = np.asarray(q, dtype=np.int16)
+    if q.shape[0] % 2 or q.min(initial=0) < -8 or q.max(initial=0) > 7:
+        raise ValueError("int4 codes must be in [-8, 7] with an even row count")
+    nib = (q & 0x0F).astype(np.uint8)
+    return (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)

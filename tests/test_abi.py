@@ -22,7 +22,8 @@ NULL = ctypes.c_void_p(0)
 def test_every_declared_function_is_exported():
     names = binding.header_functions()
     assert {"gemm_bf16", "gemm_fp8_blockscaled", "gemm_bf16_ex", "quantize_fp8_1x128",
-            "quantize_fp8_128x128", "gemm_bf16_w8", "gemm_w8_kernel_name"} <= set(names)
+            "quantize_fp8_128x128", "gemm_bf16_w8", "gemm_w8_kernel_name", "gemm_bf16_w4",
+            "gemm_w4_kernel_name"} <= set(names)
     L = binding.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -78,8 +79,8 @@ def test_fp8_validation():
 
 
 def _w8(X=FAKE, Q=FAKE, S=FAKE, bias=FAKE, C=FAKE, M=8, N=64, K=64, ldx=64, ldq=64, ldc=64, epi=0,
-        out=1):
-    return binding.lib().gemm_bf16_w8(X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epi, out, NULL)
+        out=1, fn="gemm_bf16_w8"):
+    return getattr(binding.lib(), fn)(X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epi, out, NULL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -90,8 +91,9 @@ def _w8(X=FAKE, Q=FAKE, S=FAKE, bias=FAKE, C=FAKE, M=8, N=64, K=64, ldx=64, ldq=
     (dict(ldq=66), UNS),
     (dict(M=0), OK), (dict(N=0, ldq=1, ldc=1), OK),
 ])
-def test_w8_validation(kw, status):
-    assert _w8(**kw) == status
+@pytest.mark.parametrize("fn", ["gemm_bf16_w8", "gemm_bf16_w4"])
+def test_w8_validation(kw, status, fn):
+    assert _w8(fn=fn, **kw) == status
 
 
 def test_w8_kernel_names():
@@ -99,6 +101,11 @@ def test_w8_kernel_names():
     assert binding.gemm_w8_kernel_name(64, 128256, 4096) == "tgemm_w8_thin_m64"
     assert binding.gemm_w8_kernel_name(65, 128256, 4096) is None
     assert binding.gemm_w8_kernel_name(8, 130, 4096) is None
+    assert binding.gemm_w4_kernel_name(1, 128256, 4096) == "tgemm_w4_thin_m16"
+    assert binding.gemm_w4_kernel_name(33, 128256, 4096) == "tgemm_w4_thin_m48"
+    assert binding.gemm_w4_kernel_name(64, 128256, 4096) == "tgemm_w4_thin_m64"
+    assert binding.gemm_w4_kernel_name(65, 128256, 4096) is None
+    assert binding.gemm_w4_kernel_name(8, 128256, 4092) is None
 
 
 @pytest.mark.parametrize("fn", ["quantize_fp8_1x128", "quantize_fp8_128x128"])

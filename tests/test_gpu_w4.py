@@ -1,0 +1,177 @@
+"""GPU parity of the weight-only int4 GEMM (gemm_bf16_w4) against the fp64
+oracle on the dequantised weights (needs an MI355X).
+
+Codes are stored two per byte along K (low nibble = even row).  The kernel
+turns each code into 16 q exactly in bf16, sums the exact products in fp32
+per 128-row group and scales the group sum by s / 16 (an exact power-of-two
+rescaling), so its error is that of an fp32-accumulated GEMM: the bf16
+path's tolerances, max |c - y| / (sum_k |x||q s| + |bias|) <= 1e-5 for fp32
+output and 8e-3 for bf16 output.  The same codes through the int8 kernel
+give the same bits, since every partial sum is exactly 16 times the int8
+one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import tiled_gemm_04_amd as tg
+import workloads as wl
+from oracle import gemm as og
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32, TOL_BF16 = 1e-5, 8e-3
+CANARY_BF16 = 0x7FC1
+CANARY_F32 = 0x7FC00001
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda")
+
+
+def _guarded_out(M, N, dtype, dev, pad_cols=6):
+    ldc = N + pad_cols
+    if dtype == torch.bfloat16:
+        big = torch.full((M + 2, ldc), CANARY_BF16, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    else:
+        big = torch.full((M + 2, ldc), CANARY_F32, dtype=torch.int32, device=dev).view(torch.float32)
+    return big, big[1:M + 1, :N]
+
+
+def _guards_intact(big, M, N):
+    raw = big.view(torch.int16 if big.dtype == torch.bfloat16 else torch.int32)
+    canary = CANARY_BF16 if big.dtype == torch.bfloat16 else CANARY_F32
+    return bool((raw[0] == canary).all()) and bool((raw[M + 1] == canary).all()) and \
+        bool((raw[1:M + 1, N:] == canary).all())
+
+
+def _inputs(M, N, K, seed, dev, bias=False):
+    x = wl.bf16((M, K), "normal", 1.0, seed, 1, dev)
+    p, s = wl.w4_weights(K, N, seed, dev)
+    b = wl.bf16((N,), "normal", 0.02, seed, 3, dev) if bias else None
+    return x, p, s, b
+
+
+def _check(x, p, s, b, epi, out_dtype, label, cols=None):
+    dev = x.device
+    M, N = x.shape[0], p.shape[1]
+    big, c = _guarded_out(M, N, out_dtype, dev)
+    print(f"[gpu] w4 {label} M={M} N={N} K={x.shape[1]} epi={epi} out={out_dtype}", flush=True)
+    tg.gemm_bf16_w4(x, p, s, b, c, epilogue=epi)
+    torch.cuda.synchronize()
+    assert _guards_intact(big, M, N)
+    pc, sc = (p, s) if cols is None else (p[:, cols], s[:, cols])
+    y, d = og.gemm_bf16_w4_bits(wl.bits_u16(x), pc.cpu().numpy(), sc.cpu().numpy(),
+                                None if b is None else wl.bits_u16(b if cols is None else b[cols]), epi)
+    got = c if cols is None else c[:, cols]
+    tol = TOL_F32 if out_dtype == torch.float32 else TOL_BF16
+    r = og.compare(got.float().cpu().double().numpy(), y, d, tol)
+    assert r["ok"], f"{label}: {r}"
+    return c
+
+
+@pytest.mark.parametrize("shape", [(1, 512, 4096), (5, 100, 200), (16, 1000, 256), (17, 1028, 136),
+                                   (33, 2048, 1000), (64, 516, 384), (64, 4, 8), (48, 1536, 64),
+                                   (3, 520, 72)])
+def test_w4_shapes(shape):
+    M, N, K = shape
+    x, p, s, _ = _inputs(M, N, K, 41, _dev())
+    _check(x, p, s, None, tg.EPI_NONE, torch.bfloat16, "shape")
+
+
+@pytest.mark.parametrize("epi", [tg.EPI_NONE, tg.EPI_BIAS, tg.EPI_BIAS_GELU_TANH])
+@pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
+def test_w4_epilogues_and_outputs(epi, out):
+    x, p, s, b = _inputs(8, 700, 512, 42, _dev(), bias=True)
+    _check(x, p, s, b, epi, out, "epilogue")
+
+
+def test_w4_every_nibble_value_including_minus_eight():
+    """Uniform random bytes: all 16 codes, -8 included, in both nibbles."""
+    dev = _dev()
+    M, N, K = 7, 640, 384
+    x = wl.bf16((M, K), "normal", 1.0, 43, 1, dev)
+    g = torch.Generator(device=dev).manual_seed(43 * 256 + 8)
+    p = torch.randint(0, 256, (K // 2, N), generator=g, device=dev, dtype=torch.int32).to(torch.uint8)
+    s = (torch.rand((K // 128, N), generator=g, device=dev) + 0.5) * 1e-2
+    _check(x, p, s, None, tg.EPI_NONE, torch.float32, "all nibbles")
+
+
+def test_w4_matches_int8_kernel_bit_for_bit():
+    """The same codes through gemm_bf16_w8 (as int8) give identical bits."""
+    dev = _dev()
+    M, N, K = 12, 1024, 640
+    x, p, s, b = _inputs(M, N, K, 44, dev, bias=True)
+    q8 = torch.from_numpy(og.unpack_int4(p.cpu().numpy())).to(dev)
+    for out in (torch.float32, torch.bfloat16):
+        c4 = _check(x, p, s, b, tg.EPI_BIAS, out, "vs int8")
+        c8 = torch.empty(M, N, dtype=out, device=dev)
+        tg.gemm_bf16_w8(x, q8, s, b, c8, epilogue=tg.EPI_BIAS)
+        torch.cuda.synchronize()
+        assert torch.equal(c4.contiguous().view(torch.uint8), c8.view(torch.uint8))
+
+
+def test_w4_strided_and_unaligned():
+    """X with row stride K + 3 starting one element into its buffer, packed
+    Q with row stride N + 4 bytes starting 4 bytes in, C at an odd element
+    offset."""
+    dev = _dev()
+    M, N, K = 9, 600, 264
+    xb = wl.bf16((M * (K + 3) + 1,), "normal", 1.0, 45, 1, dev)
+    x = xb[1:].view(M, K + 3)[:, :K]
+    p0, s = wl.w4_weights(K, N, 45, dev)
+    pbuf = torch.zeros((K // 2) * (N + 4) + 4, dtype=torch.uint8, device=dev)
+    p = pbuf[4:].view(K // 2, N + 4)[:, :N]
+    p.copy_(p0)
+    cbuf = torch.full((M * N + 2,), CANARY_BF16, dtype=torch.int16, device=dev)
+    c = cbuf[1:M * N + 1].view(torch.bfloat16).view(M, N)
+    print(f"[gpu] w4 strided M={M} N={N} K={K}", flush=True)
+    tg.gemm_bf16_w4(x, p, s, None, c)
+    torch.cuda.synchronize()
+    assert int(cbuf[0]) == CANARY_BF16 and int(cbuf[M * N + 1]) == CANARY_BF16
+    y, d = og.gemm_bf16_w4_bits(wl.bits_u16(x.contiguous()), p.cpu().numpy(), s.cpu().numpy())
+    r = og.compare(c.float().cpu().double().numpy(), y, d, TOL_BF16)
+    assert r["ok"], r
+
+
+def test_w4_k_zero_is_epilogue_of_bias():
+    dev = _dev()
+    M, N = 3, 64
+    x = torch.empty(M, 0, dtype=torch.bfloat16, device=dev)
+    p = torch.empty(0, N, dtype=torch.uint8, device=dev)
+    s = torch.empty(0, N, dtype=torch.float32, device=dev)
+    b = wl.bf16((N,), "normal", 1.0, 46, 3, dev)
+    c = torch.empty(M, N, dtype=torch.float32, device=dev)
+    tg.gemm_bf16_w4(x, p, s, b, c, epilogue=tg.EPI_BIAS)
+    torch.cuda.synchronize()
+    assert torch.equal(c.cpu(), b.float().cpu().expand(M, N))
+
+
+def test_w4_unsupported_shapes_raise():
+    dev = _dev()
+    x, p, s, _ = _inputs(65, 64, 64, 47, dev)
+    c = torch.empty(65, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(tg.TgemmError):
+        tg.gemm_bf16_w4(x, p, s, None, c)           # M > 64
+    x, p, s, _ = _inputs(4, 66, 64, 47, dev)
+    c = torch.empty(4, 66, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(tg.TgemmError):
+        tg.gemm_bf16_w4(x, p, s, None, c)           # N % 4 != 0
+
+
+def test_full_size_lm_head_w4():
+    """The LM head [M, 4096] x [4096, 128256] with int4 weights at M = 1, 8,
+    32, 64 (the thin-M workloads' X), checked on 2,048 sampled columns
+    including both edges."""
+    dev = _dev()
+    w = wl.WORKLOADS["thin_m64"]
+    x, _, _ = wl.bf16_inputs(w, device=dev)
+    p, s = wl.w4_weights(w.K, w.N, w.seed, dev)
+    g = torch.Generator().manual_seed(93)
+    cols = torch.cat([torch.arange(0, 256), torch.randint(256, w.N - 256, (1536,), generator=g),
+                      torch.arange(w.N - 256, w.N)]).to(dev)
+    for M in (1, 8, 32, 64):
+        _check(x[:M].contiguous(), p, s, None, tg.EPI_NONE, torch.bfloat16, f"lm_head M={M}", cols=cols)

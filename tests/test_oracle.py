@@ -440,3 +440,104 @@ def test_w8_generator_shapes_and_ranges():
     assert float(s.min()) > 0
     q2, s2 = wl.w8_weights(300, 40, 4)
     assert torch.equal(q, q2) and torch.equal(s, s2)
+
+
+# ---------------------------------------------------------- weight-only int4 ----
+
+def test_int4_unpack_hand_decoded_bytes():
+    """Bytes decoded by hand from the storage rule (low nibble = even K row,
+    high nibble = odd K row, 4-bit two's complement)."""
+    packed = np.array([[0x9F, 0x70], [0x08, 0x80], [0x00, 0xFF]], dtype=np.uint8)
+    q = gemm.unpack_int4(packed)
+    expect = np.array([[-1, 0], [-7, 7], [-8, 0], [0, -8], [0, -1], [0, -1]], dtype=np.int8)
+    assert np.array_equal(q, expect)
+
+
+def test_int4_unpack_every_byte_closed_form_and_pack_round_trip():
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    q = gemm.unpack_int4(b).astype(np.int64)
+    lo, hi = q[0], q[1]
+    assert lo.min() == -8 and lo.max() == 7 and hi.min() == -8 and hi.max() == 7
+    assert np.array_equal(np.mod(lo, 16) + 16 * np.mod(hi, 16), np.arange(256))
+    assert np.array_equal(quant.pack_int4(q.astype(np.int8)), b)
+
+
+def _w4_small(K, N, seed):
+    rng = np.random.default_rng(seed)
+    packed = rng.integers(0, 256, (K // 2, N)).astype(np.uint8)
+    s = (rng.uniform(0.5, 2.0, ((K + 127) // 128, N)) * 1e-2).astype(np.float32)
+    return packed, s
+
+
+def test_w4_dequantisation_indexing_brute_force():
+    packed, s = _w4_small(300, 37, 31)
+    w = gemm.dequant_w4(packed, s)
+    for k in range(0, 300, 5):
+        for n in range(37):
+            byte = int(packed[k // 2, n])
+            nib = (byte >> 4) if k % 2 else (byte & 15)
+            code = nib - 16 if nib >= 8 else nib
+            assert w[k, n] == code * float(s[k // 128, n])
+
+
+def test_w4_integer_codes_unit_scales_exact():
+    rng = np.random.default_rng(32)
+    M, K, N = 3, 260, 9
+    x = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    q = rng.integers(-8, 8, (K, N)).astype(np.int8)
+    xb = formats.bf16_encode_rne(x)
+    y, d = gemm.gemm_bf16_w4_bits(xb, quant.pack_int4(q), np.ones((3, N), np.float32))
+    assert np.array_equal(y, x.astype(np.float64) @ q.astype(np.float64))
+    assert np.array_equal(d, np.abs(x.astype(np.float64)) @ np.abs(q.astype(np.float64)))
+
+
+def test_w4_equals_w8_oracle_on_the_same_codes():
+    """int4 codes are valid int8 codes: both oracles must agree bit for bit,
+    bias and epilogue included."""
+    rng = np.random.default_rng(33)
+    M, K, N = 4, 392, 21
+    xb = formats.bf16_encode_rne(rng.standard_normal((M, K)).astype(np.float32))
+    bb = formats.bf16_encode_rne(rng.standard_normal(N).astype(np.float32))
+    packed, s = _w4_small(K, N, 34)
+    for epi in (gemm.EPI_NONE, gemm.EPI_BIAS, gemm.EPI_BIAS_GELU_TANH):
+        y4, d4 = gemm.gemm_bf16_w4_bits(xb, packed, s, None if epi == gemm.EPI_NONE else bb, epi)
+        y8, d8 = gemm.gemm_bf16_w8_bits(xb, gemm.unpack_int4(packed), s,
+                                        None if epi == gemm.EPI_NONE else bb, epi)
+        assert np.array_equal(y4, y8) and np.array_equal(d4, d8)
+
+
+def test_int4_quantiser_invariants_and_ties():
+    rng = np.random.default_rng(35)
+    w = rng.standard_normal((300, 6)).astype(np.float32)
+    w[128:256, 2] = 0.0                          # an all-zero group
+    w[0, 4] = 7.0                                # group (0, 4): scale exactly 1 ...
+    w[1, 4], w[2, 4], w[3, 4] = 2.5, 3.5, -0.5   # ... so these are exact ties
+    q, s = quant.quantise_int4_k128(w)
+    assert q.dtype == np.int8 and s.shape == (3, 6)
+    assert s[1, 2] == 1.0 and np.all(q[128:256, 2] == 0)
+    assert s[0, 4] == 1.0 and (q[1, 4], q[2, 4], q[3, 4]) == (2, 4, 0)
+    assert q.min() >= -7 and q.max() <= 7
+    for g in range(3):
+        rs = slice(128 * g, min(300, 128 * (g + 1)))
+        for n in range(6):
+            col = w[rs, n].astype(np.float64)
+            if np.all(col == 0):
+                continue
+            amax = np.float32(np.max(np.abs(w[rs, n])))
+            assert s[g, n] == np.float32(amax / np.float32(7.0))
+            assert np.max(np.abs(q[rs, n].astype(np.int64))) == 7
+            assert np.all(np.abs(col - q[rs, n] * float(s[g, n])) <= 0.5 * float(s[g, n]) * (1 + 1e-6))
+    assert np.array_equal(gemm.unpack_int4(quant.pack_int4(q)), q)
+    with pytest.raises(ValueError):
+        quant.quantise_int4_k128(w[:299])
+
+
+def test_w4_generator_shapes_and_ranges():
+    p, s = wl.w4_weights(300, 40, 4)
+    assert p.dtype == torch.uint8 and tuple(p.shape) == (150, 40)
+    assert s.dtype == torch.float32 and tuple(s.shape) == (3, 40)
+    q = gemm.unpack_int4(p.numpy())
+    assert q.min() >= -7 and q.max() <= 7 and 1.5 < q.std() < 3.0
+    assert float(s.min()) > 0
+    p2, s2 = wl.w4_weights(300, 40, 4)
+    assert torch.equal(p, p2) and torch.equal(s, s2)

@@ -66,6 +66,10 @@ def lib():
     L.gemm_bf16_w8.restype = i32
     L.gemm_w8_kernel_name.argtypes = [i64, i64, i64]
     L.gemm_w8_kernel_name.restype = ctypes.c_char_p
+    L.gemm_bf16_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.gemm_bf16_w4.restype = i32
+    L.gemm_w4_kernel_name.argtypes = [i64, i64, i64]
+    L.gemm_w4_kernel_name.restype = ctypes.c_char_p
     L.quantize_fp8_1x128.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     L.quantize_fp8_1x128.restype = i32
     L.quantize_fp8_128x128.argtypes = [vp, vp, vp, i64, i64, i64, vp]
@@ -175,6 +179,33 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
     return C
 
 
+def _weight_only(name, bits, X, Q, S, bias, C, epilogue, stream):
+    _check_cuda(X, Q, S, bias, C)
+    qdt = torch.int8 if bits == 8 else torch.uint8
+    if X.dtype != torch.bfloat16 or Q.dtype != qdt or S.dtype != torch.float32:
+        raise ValueError(f"X must be bfloat16, Q {qdt} and S float32")
+    if C.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("C must be bfloat16 or float32")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    ldx, ldq, ldc = _row_major(X, "X"), _row_major(Q, "Q"), _row_major(C, "C")
+    M, K = X.shape
+    Kq, N = Q.shape
+    if bits == 4 and K % 2:
+        raise ValueError("int4 codes pair up along K: K must be even")
+    if Kq != (K if bits == 8 else K // 2) or tuple(C.shape) != (M, N) \
+            or tuple(S.shape) != ((K + 127) // 128, N):
+        raise ValueError("shape mismatch")
+    if not S.is_contiguous():
+        raise ValueError("S must be contiguous")
+    out = OUT_BF16 if C.dtype == torch.bfloat16 else OUT_F32
+    st = getattr(lib(), name)(_ptr(X), _ptr(Q), _ptr(S), _ptr(bias), _ptr(C), M, N, K, ldx, ldq, ldc,
+                              int(epilogue), out, _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, name)
+    return C
+
+
 def gemm_bf16_w8(X, Q, S, bias, C, epilogue=EPI_NONE, stream=None):
     """C[M,N] = epilogue(X[M,K] @ (Q[K,N] * S[k/128, N]) + bias[N]) on the GPU.
 
@@ -182,30 +213,23 @@ def gemm_bf16_w8(X, Q, S, bias, C, epilogue=EPI_NONE, stream=None):
     S: float32 [ceil(K/128), N] contiguous; bias: bfloat16 [N] or None;
     C: bfloat16 or float32 [M, N] (unit inner stride), written in place.
     """
-    _check_cuda(X, Q, S, bias, C)
-    if X.dtype != torch.bfloat16 or Q.dtype != torch.int8 or S.dtype != torch.float32:
-        raise ValueError("X must be bfloat16, Q int8 and S float32")
-    if C.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("C must be bfloat16 or float32")
-    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
-        raise ValueError("bias must be a contiguous bfloat16 vector")
-    ldx, ldq, ldc = _row_major(X, "X"), _row_major(Q, "Q"), _row_major(C, "C")
-    M, K = X.shape
-    K2, N = Q.shape
-    if K2 != K or tuple(C.shape) != (M, N) or tuple(S.shape) != ((K + 127) // 128, N):
-        raise ValueError("shape mismatch")
-    if not S.is_contiguous():
-        raise ValueError("S must be contiguous")
-    out = OUT_BF16 if C.dtype == torch.bfloat16 else OUT_F32
-    st = lib().gemm_bf16_w8(_ptr(X), _ptr(Q), _ptr(S), _ptr(bias), _ptr(C), M, N, K, ldx, ldq, ldc,
-                            int(epilogue), out, _stream_ptr(stream))
-    if st != TGEMM_OK:
-        raise TgemmError(st, "gemm_bf16_w8")
-    return C
+    return _weight_only("gemm_bf16_w8", 8, X, Q, S, bias, C, epilogue, stream)
+
+
+def gemm_bf16_w4(X, Q, S, bias, C, epilogue=EPI_NONE, stream=None):
+    """gemm_bf16_w8 with int4 codes: Q is uint8 [K/2, N], byte (r, n) holding
+    code (2r, n) in its low nibble and (2r+1, n) in its high nibble, each a
+    4-bit two's-complement value."""
+    return _weight_only("gemm_bf16_w4", 4, X, Q, S, bias, C, epilogue, stream)
 
 
 def gemm_w8_kernel_name(M, N, K):
     r = lib().gemm_w8_kernel_name(M, N, K)
+    return None if r is None else r.decode()
+
+
+def gemm_w4_kernel_name(M, N, K):
+    r = lib().gemm_w4_kernel_name(M, N, K)
     return None if r is None else r.decode()
 
 

@@ -79,6 +79,41 @@ bool use_thin(int64_t M, int algo) {
 }
 
 // Shared validation and launch of the two FP8 quantisers.
+// Weight-only integer GEMM (bits = 8 or 4): the argument rules of gemm_bf16
+// with Q in place of B (row stride in bytes; int4 rows hold two K rows each).
+int gemm_weight_only(int bits, const void* X, const void* Q, const float* S, const void* bias,
+                     void* C, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                     int epilogue, int out_dtype, void* stream) {
+  const int v = validate_bf16(X, Q, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype,
+                              TGEMM_ALGO_AUTO);
+  if (v != TGEMM_OK || M == 0 || N == 0) return v;
+  if (K > 0 && S == nullptr) return TGEMM_ERR_INVALID;
+  if (!tgemm::wq_supported(bits, M, N, K, ldx, ldq)) return TGEMM_ERR_UNSUPPORTED;
+  tgemm::W8Args a;
+  a.X = static_cast<const uint16_t*>(X);
+  a.Q = static_cast<const uint8_t*>(Q);
+  a.S = S;
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.ldx = ldx;
+  a.ldq = ldq;
+  a.ldc = ldc;
+  // A lane stores 4 consecutive outputs: 8 bytes of bf16 or 16 bytes of fp32.
+  a.vec_c = ((out_dtype == TGEMM_OUT_BF16 ? aligned8(C) : aligned16(C)) && ldc % 4 == 0) ? 1 : 0;
+  const hipError_t e = tgemm::launch_wq_thin(bits, a, epilogue, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+const char* weight_only_name(int bits, int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return nullptr;
+  if (!tgemm::wq_supported(bits, M, N, K, K, N)) return nullptr;
+  return tgemm::wq_kernel_name(bits, static_cast<int>(M));
+}
+
 int quantize_fp8(const void* X, void* Q, float* S, int64_t rows, int64_t cols, int64_t ldx,
                  void* stream, bool blocks) {
   if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return TGEMM_ERR_INVALID;
@@ -177,36 +212,18 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
 int gemm_bf16_w8(const void* X, const void* Q, const float* S, const void* bias, void* C,
                  int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
                  int epilogue, int out_dtype, void* stream) {
-  // Same argument rules as gemm_bf16 (Q in place of B, row stride in bytes).
-  const int v = validate_bf16(X, Q, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype,
-                              TGEMM_ALGO_AUTO);
-  if (v != TGEMM_OK || M == 0 || N == 0) return v;
-  if (K > 0 && S == nullptr) return TGEMM_ERR_INVALID;
-  if (!tgemm::w8_supported(M, N, K, ldx, ldq)) return TGEMM_ERR_UNSUPPORTED;
-  tgemm::W8Args a;
-  a.X = static_cast<const uint16_t*>(X);
-  a.Q = static_cast<const uint8_t*>(Q);
-  a.S = S;
-  a.bias = static_cast<const uint16_t*>(bias);
-  a.C = C;
-  a.M = static_cast<int>(M);
-  a.N = static_cast<int>(N);
-  a.K = static_cast<int>(K);
-  a.ldx = ldx;
-  a.ldq = ldq;
-  a.ldc = ldc;
-  // A lane stores 4 consecutive outputs: 8 bytes of bf16 or 16 bytes of fp32.
-  a.vec_c = ((out_dtype == TGEMM_OUT_BF16 ? aligned8(C) : aligned16(C)) && ldc % 4 == 0) ? 1 : 0;
-  const hipError_t e = tgemm::launch_w8_thin(a, epilogue, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
-                                             static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+  return gemm_weight_only(8, X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype, stream);
 }
 
-const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 1 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return nullptr;
-  if (!tgemm::w8_supported(M, N, K, K, N)) return nullptr;
-  return tgemm::w8_kernel_name(static_cast<int>(M));
+int gemm_bf16_w4(const void* X, const void* Q, const float* S, const void* bias, void* C,
+                 int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                 int epilogue, int out_dtype, void* stream) {
+  return gemm_weight_only(4, X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype, stream);
 }
+
+const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K) { return weight_only_name(8, M, N, K); }
+
+const char* gemm_w4_kernel_name(int64_t M, int64_t N, int64_t K) { return weight_only_name(4, M, N, K); }
 
 int quantize_fp8_1x128(const void* X, void* Q, float* S, int64_t M, int64_t K, int64_t ldx,
                        void* stream) {

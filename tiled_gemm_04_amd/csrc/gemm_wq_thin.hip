@@ -1,0 +1,400 @@
+// Small-M GEMMs with integer weights and per-group fp32 scales (weight-only
+// quantisation) for gfx950, written as bandwidth-bound kernels.
+//
+//   C[i, n] = epilogue( sum_k X[i, k] * (q[k, n] * S[k / 128, n]) + bias[n] )
+//
+// The GEMM compute-cost page (section 7.2, the LM head) names keeping the
+// large output projection in a low-precision integer format as the first
+// remedy for its memory-bound cost: the weight W[K, N] is streamed once per
+// call, so halving its bytes halves the time (section 4.3 of the same page
+// lists int8 and int4 as the usual formats).  W is stored as integer codes
+// q with one fp32 scale per (128-row group along K, column), the
+// round-to-nearest per-group scheme of the DeepGEMM page's section 2.4
+// applied to integers; activations X stay bf16.  Two code widths:
+//   * int8: Q [K, N] bytes, one signed code per byte;
+//   * int4: Q [K/2, N] bytes, two signed 4-bit codes per byte along K (byte
+//     (r, n) holds q[2r, n] in its low nibble and q[2r+1, n] in its high
+//     nibble, two's complement, codes -8 .. 7).
+//
+// Layout of the work (the bf16 thin-M kernel's, with byte rows):
+//   * a workgroup owns 512 consecutive columns: a byte row of its stripe is
+//     512 contiguous bytes; the stripe is walked in slices of 32 byte rows
+//     (32 K rows of int8, 64 of int4) that go global -> LDS with direct
+//     buffer loads (one load = two byte rows), six LDS stages deep, together
+//     with the matching 16-row blocks of X and the 512 scales of the slice's
+//     group;
+//   * eight waves (two per SIMD, so one wave's conversions overlap the
+//     other's MFMAs and loads) each own 64 columns over the whole of K.  A
+//     wave's MFMA operand for 16 columns comes from one ds_read_b64_tr_b8
+//     (lane i receives column i of 8 byte rows: the 8 K values one
+//     16 x 16 x 32 MFMA takes per lane for int8, those of two MFMAs for
+//     int4); every code becomes a bf16 exactly (a sign-extending byte to fp32
+//     conversion, then the upper half; int4 codes are first moved to the top
+//     nibble of their byte, which gives 16 q, and the 1/16 goes into the
+//     group scale);
+//   * the MFMAs of a 128-row group accumulate sum_k x * q exactly as an fp32
+//     GEMM would; at the end of the group one FMA per accumulator folds it
+//     in with the column's scale, acc += s * partial -- the same grouped
+//     dequantisation as the FP8 path, so no weight is rounded.
+#include "common.h"
+#include "launch.h"
+
+namespace tgemm {
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kBN = 512;        // columns per workgroup
+constexpr int kWTN = 64;        // columns per wave
+constexpr int kFN = kWTN / 16;  // 16-column MFMA blocks per wave
+constexpr int kRows = 32;       // byte rows of Q per slice
+constexpr int kGroupK = 128;    // K rows per scale group
+constexpr int kNS = 6;          // LDS stages
+constexpr int kWRow = kBN;      // bytes per Q row of the stripe
+constexpr int kWStage = kRows * kWRow;   // 16 KiB
+constexpr int kSStage = kBN * 4;         // the slice group's 512 fp32 scales
+constexpr int kLoadsPerSlice = 2 + 1 + 1;  // per wave: 4 Q rows, one KiB of X, 64 scales
+
+// Per code width: K rows per slice (kBK), bytes of one 16-row X block of a
+// slice, the X part of a stage (four blocks) and the stage size.
+template <int BITS>
+struct WqShape {
+  static_assert(BITS == 8 || BITS == 4, "int8 or int4 codes");
+  static constexpr int kBK = kRows * 8 / BITS;
+  static constexpr int kXBlock = 16 * kBK * 2;
+  static constexpr int kXStage = 4 * kXBlock;
+  static constexpr int kStage = kWStage + kXStage + kSStage;
+  static constexpr int kSlicesPerGroup = kGroupK / kBK;
+  // Slices between barriers: int4 slices carry twice the conversion work
+  // of int8 ones, and two per barrier let a wave's conversions of one run
+  // into the other's (measured 5-10 % faster for int4, 0-5 % slower for
+  // int8).
+  static constexpr int kPerBar = BITS == 4 ? 2 : 1;
+  static_assert(kNS * kStage <= 160 * 1024, "LDS capacity");
+};
+
+#define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+
+// XOR on the 16-byte chunk index of byte row k of a Q slice, so that the 16
+// byte rows one transposed read covers per 32 lanes land in 16 different
+// 16-byte bank slots of a 256-byte bank row.  int8: rows 8g + e (g < 2,
+// e < 8).  int4: rows 4g + e and 16 + 4g + e (g < 2, e < 4) -- the K values
+// 8g .. 8g+7 of the slice's two 32-wide MFMA steps.
+template <int BITS>
+__device__ __forceinline__ int q_swz(int k) {
+  if constexpr (BITS == 8) return k & 15;
+  else return (k & 7) | (((k >> 4) & 1) << 3);
+}
+// XOR on the chunk index of row r of an X block: 4 chunks per row (int8
+// slices, 64-byte rows) or 8 (int4 slices, 128-byte rows); the 16 rows one
+// operand read covers land in distinct 16-byte slots.
+template <int BITS>
+__device__ __forceinline__ int x_swz(int r) {
+  if constexpr (BITS == 8) return (r >> 2) & 3;
+  else return (r >> 1) & 7;
+}
+
+// 4-byte buffer load written straight into LDS (lane l -> lds_base + 4 l).
+__device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_words(window))
+               : "memory", "m0");
+}
+
+// Eight int8 codes (two dwords, K order) as 8 bf16, exactly.
+__device__ __forceinline__ bf16x8 codes_to_bf16(i32x2 codes) {
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = static_cast<float>(static_cast<int8_t>(static_cast<uint32_t>(codes[0]) >> (8 * e)));
+    f[4 + e] = static_cast<float>(static_cast<int8_t>(static_cast<uint32_t>(codes[1]) >> (8 * e)));
+  }
+  // Upper halves of two fp32 words into one (bytes 2, 3 of a then of b).
+  auto hi2 = [](float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  };
+  return __builtin_bit_cast(bf16x8, u32x4{hi2(f[0], f[1]), hi2(f[2], f[3]), hi2(f[4], f[5]), hi2(f[6], f[7])});
+}
+
+// Four bytes of int4 codes (byte e = K values 2e (low nibble), 2e + 1 (high
+// nibble)) as 8 bf16 holding 16 q, exactly: each nibble is moved to the top
+// of its byte, whose sign-extended value is then 16 times the code.
+__device__ __forceinline__ bf16x8 nibbles_to_bf16(uint32_t codes) {
+  const uint32_t lo = (codes << 4) & 0xf0f0f0f0u;
+  const uint32_t hi = codes & 0xf0f0f0f0u;
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = static_cast<float>(static_cast<int8_t>(lo >> (8 * e)));
+    f[2 * e + 1] = static_cast<float>(static_cast<int8_t>(hi >> (8 * e)));
+  }
+  auto hi2 = [](float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  };
+  return __builtin_bit_cast(bf16x8, u32x4{hi2(f[0], f[1]), hi2(f[2], f[3]), hi2(f[4], f[5]), hi2(f[6], f[7])});
+}
+
+template <int BITS, int MB, int EPI, bool OUT_BF16>
+__device__ __forceinline__ void wq_thin_body(const W8Args& p, uint8_t* smem) {
+  using Sh = WqShape<BITS>;
+  constexpr int kBK = Sh::kBK;
+  constexpr int kStage = Sh::kStage;
+  constexpr int kXStage = Sh::kXStage;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * kBN;
+
+  // acc[mb][j]: 16 x 16 block, transposed by the operand swap: element e of
+  // lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the wave's 64.
+  f32x4 acc[MB][kFN];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) acc[mb][j] = f32x4{};
+
+  // ---- global -> LDS.  Q: load i of wave w covers slice byte rows 4w + 2i
+  // (lanes 0-31) and 4w + 2i + 1 (lanes 32-63), lane -> physical chunk
+  // lane % 32, logical chunk (lane % 32) ^ q_swz(row).  X, int8 (64-byte
+  // rows): block w % 4 (rows 16(w%4) .. +15), lane -> row l/4, physical
+  // chunk l%4 (waves 4-7 write the same bytes as waves 0-3, which keeps
+  // every wave's load count equal).  X, int4 (128-byte rows): block w / 2,
+  // rows 8(w%2) + l/8, physical chunk l%8.  Scales: wave w fetches columns
+  // 64w .. 64w+63 of the group. ----
+  const int64_t ldx2 = p.ldx * 2;
+  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+  uint32_t w_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k = 4 * wave + 2 * i + (lane >> 5);
+    const int c = (lane & 31) ^ q_swz<BITS>(k);
+    w_off[i] = static_cast<uint32_t>(k * p.ldq + 16 * c) | (n0 + 16 * c < p.N ? 0u : kOutOfRange);
+  }
+  // Row (within the four blocks) and logical chunk this lane loads of X.
+  const int xr = BITS == 8 ? 16 * (wave & 3) + (lane >> 2) : 8 * wave + (lane >> 3);
+  const int xc = BITS == 8 ? (lane & 3) ^ x_swz<BITS>(xr & 15) : (lane & 7) ^ x_swz<BITS>(xr & 15);
+  const uint32_t x_off = static_cast<uint32_t>(xr * ldx2 + 16 * xc);
+  const uint32_t x_dst = kWStage + (BITS == 8 ? (wave & 3) : wave) * 1024;
+  const int G = (p.K + kGroupK - 1) / kGroupK;
+  const int64_t q_rows = BITS == 8 ? p.K : p.K / 2;  // byte rows of Q
+  auto issue_slice = [&](int t) {
+    const uint32_t stage = smem_base + static_cast<uint32_t>((t % kNS) * kStage);
+    const int k0 = t * kBK;
+    const int64_t r0 = static_cast<int64_t>(t) * kRows;
+    const i32x4 ww = make_window_words(p.Q + r0 * p.ldq + n0, (q_rows - r0 - 1) * p.ldq + (p.N - n0));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) buf_load16_lds(ww, stage + (4 * wave + 2 * i) * kWRow, w_off[i]);
+    const i32x4 wx = make_window_words(p.X + k0, (static_cast<int64_t>(p.M - 1) * p.ldx + (p.K - k0)) * 2);
+    buf_load16_lds(wx, stage + x_dst, x_off | (k0 + 8 * xc < p.K ? 0u : kOutOfRange));
+    const int g = k0 / kGroupK;
+    const i32x4 ws = make_window_words(p.S + static_cast<int64_t>(g) * p.N + n0,
+                                       g < G ? static_cast<int64_t>(p.N - n0) * 4 : 0);
+    buf_load4_lds(ws, stage + kWStage + kXStage + 64 * wave * 4, static_cast<uint32_t>((64 * wave + lane) * 4));
+  };
+
+  // ---- LDS -> registers ----
+  // Q operand of block j (columns 16 j .. +15 of the wave): within each
+  // 16-lane group g, lane 2e + h supplies bytes 8h .. 8h+7 of the block in
+  // byte row k(g, e) and receives column (lane % 16) of those 8 rows:
+  // int8 rows 8g + e (K values 8g .. 8g+7); int4 rows 4g + e for e < 4 and
+  // 16 + 4g + e - 4 for e >= 4 (K values 8g .. 8g+7 of MFMA steps 0 and 1).
+  const int bg = lane >> 4, be = (lane >> 1) & 7, bh = lane & 1;
+  int b_off[kFN];
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int k = BITS == 8 ? 8 * bg + be : 4 * bg + (be & 3) + 16 * (be >> 2);
+    b_off[j] = k * kWRow + (((4 * wave + j) ^ q_swz<BITS>(k)) * 16) + 8 * bh;
+  }
+  // Scales of this lane's accumulator columns 16 j + 4 (lane / 16) .. +3.
+  const int s_rd = kWStage + kXStage + (kWTN * wave + 4 * (lane >> 4)) * 4;
+  // X operand of block mb and MFMA step u: row l%16, K 32u + 8*(l/16) .. +7
+  // of the slice.
+  const int xrow = lane & 15;
+  int x_rd[kBK / 32];
+#pragma unroll
+  for (int u = 0; u < kBK / 32; ++u)
+    x_rd[u] = kWStage + xrow * (kBK * 2) + (((4 * u + (lane >> 4)) ^ x_swz<BITS>(xrow)) * 16);
+  // int4 operands carry 16 q.
+  constexpr float kCodeScale = BITS == 8 ? 1.0f : 1.0f / 16.0f;
+
+  const int KT = (p.K + kBK - 1) / kBK;
+  if (KT > 0) {
+    f32x4 part[MB][kFN];  // sum over the current 128-row group of x * q
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) part[mb][j] = f32x4{};
+    // One slice's operand reads, conversions and MFMAs, and the group fold
+    // when it ends a 128-row group.  A slice at or past KT (the partner of
+    // an odd last slice of a pair) reads zeros and adds nothing.
+    auto process = [&](int t) {
+      const uint8_t* base = smem + (t % kNS) * kStage;
+      constexpr int kSteps = kBK / 32;  // 16 x 16 x 32 MFMA steps per slice
+      bf16x8 fb[kSteps][kFN], fx[kSteps][MB];
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) {
+        const i32x2 q = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
+        if constexpr (BITS == 8) {
+          fb[0][j] = codes_to_bf16(q);
+        } else {
+          fb[0][j] = nibbles_to_bf16(static_cast<uint32_t>(q[0]));
+          fb[1][j] = nibbles_to_bf16(static_cast<uint32_t>(q[1]));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          fx[u][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[u] + mb * Sh::kXBlock));
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < kFN; ++j)
+            part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fx[u][mb], part[mb][j], 0, 0, 0);
+      if ((t % Sh::kSlicesPerGroup) == Sh::kSlicesPerGroup - 1 || t == KT - 1) {
+        // End of a scale group: acc += s * partial, per column.
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) {
+          f32x4 sc = *reinterpret_cast<const f32x4*>(base + s_rd + 64 * j);
+          if constexpr (BITS == 4) sc *= kCodeScale;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[mb][j][e] = __builtin_fmaf(part[mb][j][e], sc[e], acc[mb][j][e]);
+            part[mb][j] = f32x4{};
+          }
+        }
+      }
+    };
+    // kPerBar slices per barrier; their loads go kAhead slices ahead, into
+    // the stages the previous group of slices occupied.
+    constexpr int kPerBar = Sh::kPerBar;
+    constexpr int kAhead = kNS - kPerBar;
+    for (int t = 0; t < kAhead; ++t) issue_slice(t);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
+    lds_barrier();
+    for (int t = 0; t < KT; t += kPerBar) {
+#pragma unroll
+      for (int h = 0; h < kPerBar; ++h) issue_slice(t + kAhead + h);
+#pragma unroll
+      for (int h = 0; h < kPerBar; ++h) process(t + h);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
+      lds_barrier();  // the next slices landed everywhere; these are no longer read
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
+  }
+
+  // ---- epilogue: lane holds 4 consecutive columns of one row per block ----
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int col = n0 + kWTN * wave + 16 * j + 4 * (lane >> 4);
+    float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (EPI != kEpiNone) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < p.N) bias[e] = bf16_bits_to_f32(p.bias[col + e]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = 16 * mb + (lane & 15);
+      if (row >= p.M) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<EPI>(acc[mb][j][e], bias[e]);
+      const int64_t off = static_cast<int64_t>(row) * p.ldc + col;
+      const bool full = p.vec_c && col + 4 <= p.N;
+      if constexpr (OUT_BF16) {
+        uint16_t* out = static_cast<uint16_t*>(p.C) + off;
+        if (full) {
+          *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
+        }
+      } else {
+        float* out = static_cast<float*>(p.C) + off;
+        if (full) {
+          *reinterpret_cast<f32x4*>(out) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.N) out[e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+template <int MB, int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_w8_thin(W8Args p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * WqShape<8>::kStage];
+  wq_thin_body<8, MB, EPI, OUT_BF16>(p, smem);
+}
+
+template <int MB, int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_w4_thin(W8Args p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * WqShape<4>::kStage];
+  wq_thin_body<4, MB, EPI, OUT_BF16>(p, smem);
+}
+
+template <int BITS, int MB, int EPI, bool OUT_BF16>
+hipError_t launch_m(const W8Args& a, hipStream_t s) {
+  const dim3 grid((a.N + kBN - 1) / kBN);
+  if constexpr (BITS == 8)
+    hipLaunchKernelGGL((tgemm_w8_thin<MB, EPI, OUT_BF16>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((tgemm_w4_thin<MB, EPI, OUT_BF16>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int MB>
+hipError_t dispatch_epi(const W8Args& a, int epi, int out_bf16, hipStream_t s) {
+  if (out_bf16) {
+    if (epi == kEpiNone) return launch_m<BITS, MB, kEpiNone, true>(a, s);
+    if (epi == kEpiBias) return launch_m<BITS, MB, kEpiBias, true>(a, s);
+    return launch_m<BITS, MB, kEpiBiasGelu, true>(a, s);
+  }
+  if (epi == kEpiNone) return launch_m<BITS, MB, kEpiNone, false>(a, s);
+  if (epi == kEpiBias) return launch_m<BITS, MB, kEpiBias, false>(a, s);
+  return launch_m<BITS, MB, kEpiBiasGelu, false>(a, s);
+}
+
+template <int BITS>
+hipError_t dispatch_m(const W8Args& a, int epi, int out_bf16, hipStream_t s) {
+  if (a.M <= 16) return dispatch_epi<BITS, 1>(a, epi, out_bf16, s);
+  if (a.M <= 32) return dispatch_epi<BITS, 2>(a, epi, out_bf16, s);
+  if (a.M <= 48) return dispatch_epi<BITS, 3>(a, epi, out_bf16, s);
+  return dispatch_epi<BITS, 4>(a, epi, out_bf16, s);
+}
+
+}  // namespace
+
+bool wq_supported(int bits, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq) {
+  // Whole 16-byte X chunks along K (K even, so int4 rows pair up), dword-
+  // aligned Q rows (no dword of Q straddles a window end), per-lane offsets
+  // below 2^31 (a slice's 32 byte rows of Q, 64 rows of X), and at most 64
+  // rows.
+  return (bits == 8 || bits == 4) && M <= 64 && K % 8 == 0 && N % 4 == 0 && ldq % 4 == 0 &&
+         ldq * kRows < (int64_t{1} << 31) && ldx * 2 * 64 < (int64_t{1} << 31);
+}
+
+const char* wq_kernel_name(int bits, int M) {
+  static const char* const kNames[2][4] = {
+      {"tgemm_w8_thin_m16", "tgemm_w8_thin_m32", "tgemm_w8_thin_m48", "tgemm_w8_thin_m64"},
+      {"tgemm_w4_thin_m16", "tgemm_w4_thin_m32", "tgemm_w4_thin_m48", "tgemm_w4_thin_m64"}};
+  const int m = M <= 16 ? 0 : M <= 32 ? 1 : M <= 48 ? 2 : 3;
+  return kNames[bits == 8 ? 0 : 1][m];
+}
+
+hipError_t launch_wq_thin(int bits, const W8Args& a, int epi, int out_bf16, hipStream_t s) {
+  if (bits == 8) return dispatch_m<8>(a, epi, out_bf16, s);
+  return dispatch_m<4>(a, epi, out_bf16, s);
+}
+
+}  // namespace tgemm

@@ -46,9 +46,10 @@ struct QuantArgs {
   int vec_out;  // 1: Q rows may be written with 8-byte stores (aligned base, cols % 8 == 0)
 };
 
-// Weight-only int8 GEMM: bf16 X [M, K] (row stride ldx) times int8 codes
-// Q [K, N] (row stride ldq bytes) with fp32 scales S [ceil(K/128), N]
-// (packed), + bias, epilogue, into C [M, N] (row stride ldc).
+// Weight-only integer GEMM: bf16 X [M, K] (row stride ldx) times integer
+// codes Q (int8: [K, N]; int4: [K/2, N], two codes per byte along K; row
+// stride ldq bytes) with fp32 scales S [ceil(K/128), N] (packed), + bias,
+// epilogue, into C [M, N] (row stride ldc).
 struct W8Args {
   const uint16_t* X;
   const uint8_t* Q;
@@ -83,9 +84,10 @@ hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
 // Register-staged kernel for FP8 operands the direct-to-LDS kernel cannot take.
 hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
-hipError_t launch_w8_thin(const W8Args& a, int epilogue, int out_bf16, hipStream_t stream);
-bool w8_supported(int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq);
-const char* w8_kernel_name(int M);
+// bits: 8 or 4 (the code width).
+hipError_t launch_wq_thin(int bits, const W8Args& a, int epilogue, int out_bf16, hipStream_t stream);
+bool wq_supported(int bits, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq);
+const char* wq_kernel_name(int bits, int M);
 hipError_t launch_quant_fp8_1x128(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quant_fp8_128x128(const QuantArgs& a, hipStream_t stream);
 const char* thin_kernel_name(int M);

@@ -38,6 +38,7 @@ E4M3_MAX = 448.0
 # tensor indices inside one workload's seed space
 T_A, T_B, T_BIAS, T_OUTLIER = 1, 2, 3, 4
 T_W8_CODES, T_W8_SCALES = 6, 7
+T_W4_CODES, T_W4_SCALES = 8, 9
 
 
 @dataclass(frozen=True)
@@ -205,6 +206,26 @@ def w8_weights(K, N, seed, device="cpu"):
     G = (K + 127) // 128
     u = draw((G, N), "uniform", 1.0, seed, T_W8_SCALES, device)
     return q.to(torch.int8), (4.6e-4 * (1.0 + 0.2 * u)).to(torch.float32).contiguous()
+
+
+def w4_weights(K, N, seed, device="cpu"):
+    """Synthetic operands of a weight-only int4 LM head: packed bytes
+    [K/2, N] (byte (r, n) = code (2r, n) in bits 0-3, code (2r+1, n) in bits
+    4-7, two's complement) and fp32 scales S [ceil(K/128), N].
+
+    Codes follow N(0, 2.4) rounded and clipped to [-7, 7] (round-to-nearest
+    codes of Gaussian weights under a per-group max scaling: 7 * sigma / amax
+    with amax about 2.9 sigma over 128 draws); scales are 8.3e-3 * (1 + 0.2 u),
+    u ~ U[-1, 1] (about the max of 128 draws of N(0, 0.02), over 7).
+    """
+    if K % 2:
+        raise ValueError("K must be even")
+    q = draw((K, N), "normal", 2.4, seed, T_W4_CODES, device).round().clamp(-7, 7).to(torch.int16)
+    nib = (q & 0x0F).to(torch.uint8)
+    packed = (nib[0::2] | (nib[1::2] << 4)).contiguous()
+    G = (K + 127) // 128
+    u = draw((G, N), "uniform", 1.0, seed, T_W4_SCALES, device)
+    return packed, (8.3e-3 * (1.0 + 0.2 * u)).to(torch.float32).contiguous()
 
 
 def bits_u16(t):
