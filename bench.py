@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
                     help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
-                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64)")
+                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -87,6 +87,7 @@ KERNEL_SOURCES = {
     "quant": ["common.h", "launch.h", "quant_fp8.hip"],
     "w8": ["common.h", "launch.h", "gemm_wq_thin.hip"],
     "w4": ["common.h", "launch.h", "gemm_wq_thin.hip"],
+    "lsm": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
 }
 
 # Weight-only int8 LM head: the thin-M workloads' X [M, 4096] times int8
@@ -97,6 +98,7 @@ W8_CASES = {"w8_m1": 1, "w8_m8": 8, "w8_m32": 32, "w8_m64": 64,
 # FP8 quantisers, timed on the FP8 workload's unquantised operands (bf16):
 # activations A [4096, 4096] in 1 x 128 groups, weights B [4096, 14336] in
 # 128 x 128 blocks.
+LSM_CASES = {"lsm_m1": 1, "lsm_m8": 8, "lsm_m32": 32, "lsm_m64": 64}
 QUANT_CASES = {"quant_a": ("a", "tgemm_quant_fp8_1x128"), "quant_b": ("b", "tgemm_quant_fp8_128x128")}
 
 
@@ -133,6 +135,9 @@ class Case:
             return
         if name in W8_CASES:
             self._init_w8(name, dev)
+            return
+        if name in LSM_CASES:
+            self._init_lsm(name, dev)
             return
         w = wl.WORKLOADS[name]
         self.w = w
@@ -175,6 +180,9 @@ class Case:
         if self.family == "w8":
             return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
                     f"(Q[{self.K},{self.N}] int8 * S[{(self.K + 127) // 128},{self.N}])")
+        if self.family == "lsm":
+            return (f"{self.name}: C[{self.M},{self.N}] = log_softmax(X[{self.M},{self.K}] . "
+                    f"W[{self.K},{self.N}] + bias[{self.N}]) over each row")
         if self.family == "w4":
             return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
                     f"(Q[{self.K},{self.N}] int4, two per byte * S[{(self.K + 127) // 128},{self.N}])")
@@ -203,6 +211,32 @@ class Case:
         self.family = "w8" if bits == 8 else "w4"
         self.bound, self.peak = "hbm", PEAK_HBM_GBS
         self.dtype = "bf16 x int8" if bits == 8 else "bf16 x int4"
+        self.inputs_for_oracle = None
+
+    def _init_lsm(self, name, dev):
+        import torch
+
+        import tiled_gemm_04_amd as tg
+        import workloads as wl
+
+        w = wl.WORKLOADS["thin_m64"]
+        M, N, K = LSM_CASES[name], w.N, w.K
+        x = wl.thin_x(w, M, dev)
+        _, wt, _ = wl.bf16_inputs(w, device=dev, rows=1)
+        b = wl.bf16((N,), "normal", 0.02, w.seed, wl.T_BIAS, dev)
+        c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(tg.gemm_logsoftmax_workspace_size(M, N), dtype=torch.uint8, device=dev)
+        self.launch = lambda: tg.gemm_bf16_logsoftmax(x, wt, b, c, workspace=ws)
+        self.w = None
+        self.M, self.N, self.K = M, N, K
+        self.flops = 2 * M * N * K
+        # X, W, bias and the log-probabilities, each once (the logits never
+        # leave the chip).
+        self.bytes = 2 * M * K + 2 * K * N + 2 * N + 2 * M * N
+        self.kernel = "tgemm_bf16_thin_lsm"
+        self.family = "lsm"
+        self.bound, self.peak = "hbm", PEAK_HBM_GBS
+        self.dtype = "bf16"
         self.inputs_for_oracle = None
 
     def _init_quant(self, name, dev):
@@ -352,7 +386,8 @@ def main():
         sec = {}
         for name in ("ffn_up", "ffn_down", "thin_m1", "thin_m8", "thin_m32", "thin_m64", "fp8",
                      "fp8_ragged", "tiny", "quant_a", "quant_b", "w8_m1", "w8_m8", "w8_m32",
-                     "w8_m64", "w4_m1", "w4_m8", "w4_m32", "w4_m64"):
+                     "w8_m64", "w4_m1", "w4_m8", "w4_m32", "w4_m64", "lsm_m1", "lsm_m8", "lsm_m32",
+                     "lsm_m64"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

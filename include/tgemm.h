@@ -139,6 +139,47 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
                          void* C, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * gemm_bf16_logsoftmax -- C[i,n] = y[i,n] - log sum_n' exp(y[i,n']),
+ *                         y = X W + bias
+ *
+ * The LM head with its bias add and the LogSoftmax that follows it fused
+ * (the GEMM compute-cost page, section 7.2: merging the output projection,
+ * the bias and LogSoftmax so no separate passes read the logits back):
+ * each row of C is the log-probability distribution over the N columns.
+ * Shapes and strides as gemm_bf16 (X in place of A, W of B); bias bf16 [N]
+ * or NULL (no bias); C bf16 or fp32 (out_dtype).
+ *
+ *   workspace        device memory of at least
+ *                    gemm_logsoftmax_workspace_size(M, N, out_dtype) bytes,
+ *                    16-byte aligned, owned by the caller; scratch (its
+ *                    contents on entry do not matter and are clobbered)
+ *   workspace_bytes  its size
+ *
+ * Two kernels on the stream: the thin GEMM, whose epilogue adds the bias,
+ * forms per 512-column stripe each row's maximum and sum of exponentials
+ * and writes the fp32 logits (into C for fp32 output, else into the
+ * workspace); then a normalisation that merges each row's stripe pairs into
+ * log sum exp and writes logit - lse.  Logits and the row statistics are
+ * fp32 and each output is rounded once.  Calls on one stream serialise;
+ * concurrent calls must not share a workspace.
+ * Supported: M <= 64, K % 8 == 0, N % 8 == 0, X and W 16-byte aligned with
+ * ldx, ldw multiples of 8 (others return TGEMM_ERR_UNSUPPORTED).  N == 0
+ * with M > 0, a NULL or short workspace return TGEMM_ERR_INVALID.
+ * Returns TGEMM_OK, TGEMM_ERR_INVALID, TGEMM_ERR_UNSUPPORTED or
+ * TGEMM_ERR_LAUNCH.
+ */
+int gemm_bf16_logsoftmax(const void* X, const void* W, const void* bias, void* C,
+                         int64_t M, int64_t N, int64_t K,
+                         int64_t ldx, int64_t ldw, int64_t ldc, int out_dtype,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gemm_bf16_logsoftmax needs: M * ceil(N/512) * 8
+ * rounded up to a multiple of 256, plus M * N * 4 when out_dtype is
+ * TGEMM_OUT_BF16; -1 for negative or oversized sizes or an unknown
+ * out_dtype. */
+int64_t gemm_logsoftmax_workspace_size(int64_t M, int64_t N, int out_dtype);
+
+/*
  * gemm_bf16_w8 -- C[i,n] = epilogue( sum_k X[i,k] * (Q[k,n] * S[k/128, n]) + bias[n] )
  *
  * Weight-only int8 GEMM for the small-M, memory-bound case: the LM head of

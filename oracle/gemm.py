@@ -31,6 +31,16 @@ What is computed (all in float64 on exactly decoded inputs):
   packed matrix holds the codes of K rows ``2r`` (bits 0-3) and ``2r + 1``
   (bits 4-7) of column ``n``, each a 4-bit two's-complement number, so a
   nibble ``v`` is the code ``v - 16`` when ``v >= 8`` and ``v`` otherwise.
+* Log-softmax head.  The LM head's second remedy on the GEMM compute-cost
+  page (section 7.2) fuses the output GEMM, the bias add and the LogSoftmax
+  that follows it.  Per row: ``out[i, n] = y[i, n] - lse_i`` with
+  ``y = x w + b`` and ``lse_i = m_i + log(sum_n exp(y[i, n] - m_i))``,
+  ``m_i = max_n y[i, n]`` (the textbook log-sum-exp, shifted by the maximum
+  so no exponential overflows).  Error metric: a logit error ``d_n`` moves
+  ``lse`` by at most ``max_n |d_n|``, so an output's error is at most twice
+  the largest logit error of its row; with logit errors bounded by
+  ``tol * D`` (``D`` as below) and output rounding relative to the output,
+  the denominator is ``2 * max_n D[i, n] + |out[i, n]|``.
 * FLOP count.  A multiply-add counts as two operations, so an ``[M,K]x[K,N]``
   product costs ``2*M*N*K`` (GEMM compute-cost page, section 3.1); the bias is
   not counted.
@@ -163,6 +173,24 @@ def gemm_bf16_w4_bits(x_bits, packed, s, bias_bits=None, epilogue=EPI_NONE):
     """Oracle for the weight-only int4 path (as gemm_bf16_w8_bits)."""
     bias = None if bias_bits is None else bf16_decode(bias_bits)
     return gemm_f64(bf16_decode(x_bits), dequant_w4(packed, s), bias, epilogue)
+
+
+def log_softmax_rows(y):
+    """Row-wise log-softmax of float64 logits: y - (m + log sum exp(y - m))."""
+    y = np.asarray(y, dtype=np.float64)
+    m = np.max(y, axis=1, keepdims=True)
+    return y - (m + np.log(np.sum(np.exp(y - m), axis=1, keepdims=True)))
+
+
+def gemm_bf16_logsoftmax_bits(x_bits, w_bits, bias_bits=None):
+    """Oracle for the fused LM head: (out, denominators) with out the
+    row-wise log-softmax of ``x w + b`` and denominators
+    ``2 * max_n D[i, n] + |out[i, n]|``."""
+    bias = None if bias_bits is None else bf16_decode(bias_bits)
+    y, d = gemm_f64(bf16_decode(x_bits), bf16_decode(w_bits), bias, EPI_BIAS if bias is not None
+                    else EPI_NONE)
+    out = log_softmax_rows(y)
+    return out, 2.0 * np.max(d, axis=1, keepdims=True) + np.abs(out)
 
 
 def gemm_fp8_blockscaled_bits(qa_bits, sa, qb_bits, sb):

@@ -23,7 +23,7 @@ def test_every_declared_function_is_exported():
     names = binding.header_functions()
     assert {"gemm_bf16", "gemm_fp8_blockscaled", "gemm_bf16_ex", "quantize_fp8_1x128",
             "quantize_fp8_128x128", "gemm_bf16_w8", "gemm_w8_kernel_name", "gemm_bf16_w4",
-            "gemm_w4_kernel_name"} <= set(names)
+            "gemm_w4_kernel_name", "gemm_bf16_logsoftmax", "gemm_logsoftmax_workspace_size"} <= set(names)
     L = binding.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -136,3 +136,28 @@ def test_kernel_selection_table():
     assert binding.gemm_fp8_kernel_name(4097, 14335, 4096) == "tgemm_fp8_bs_256x256x128"
     assert binding.gemm_fp8_kernel_name(64, 64, 200).startswith("tgemm_fp8_bs_general")
     assert binding.gemm_fp8_kernel_name(64, 3, 256).startswith("tgemm_fp8_bs_general")
+
+
+def test_logsoftmax_workspace_size_and_validation():
+    L = binding.lib()
+    assert L.gemm_logsoftmax_workspace_size(1, 128256, binding.OUT_F32) == 2048  # 251 * 8, to 256
+    assert L.gemm_logsoftmax_workspace_size(1, 128256, binding.OUT_BF16) == 2048 + 128256 * 4
+    assert L.gemm_logsoftmax_workspace_size(64, 512, binding.OUT_F32) == 512
+    assert L.gemm_logsoftmax_workspace_size(-1, 8, binding.OUT_F32) == -1
+    assert L.gemm_logsoftmax_workspace_size(1, 8, 7) == -1
+    ws = 256 + 4 * 512 * 4
+
+    def call(X=FAKE, W=FAKE, bias=NULL, C=FAKE, M=4, N=512, K=64, ldx=64, ldw=512, ldc=512, out=1,
+             work=FAKE, work_bytes=ws):
+        return L.gemm_bf16_logsoftmax(X, W, bias, C, M, N, K, ldx, ldw, ldc, out, work, work_bytes, NULL)
+
+    assert call(M=0) == OK
+    assert call(N=0, ldw=1, ldc=1) == INV              # empty distribution
+    assert call(M=-1) == INV
+    assert call(out=2) == INV
+    assert call(C=NULL) == INV
+    assert call(X=NULL) == INV
+    assert call(work=NULL) == INV
+    assert call(work_bytes=256 + 4 * 512 * 4 - 1) == INV
+    assert call(out=0, work_bytes=255) == INV
+    assert call(ldx=63) == INV

@@ -541,3 +541,63 @@ def test_w4_generator_shapes_and_ranges():
     assert float(s.min()) > 0
     p2, s2 = wl.w4_weights(300, 40, 4)
     assert torch.equal(p, p2) and torch.equal(s, s2)
+
+
+# ---------------------------------------------------------- log-softmax head ----
+
+def test_log_softmax_uniform_logits_is_minus_log_n():
+    """W = 0, no bias: every logit is 0, so every output is -log N."""
+    rng = np.random.default_rng(51)
+    x = formats.bf16_encode_rne(rng.standard_normal((3, 40)).astype(np.float32))
+    w = formats.bf16_encode_rne(np.zeros((40, 1000), np.float32))
+    out, _ = gemm.gemm_bf16_logsoftmax_bits(x, w)
+    assert np.allclose(out, -math.log(1000.0), rtol=0, atol=1e-15)
+
+
+def test_log_softmax_two_columns_closed_form():
+    """Two logits a, b: out = (-softplus(b - a), -softplus(a - b)), with
+    softplus(t) = max(t, 0) + log1p(exp(-|t|))."""
+    def softplus(t):
+        return max(t, 0.0) + math.log1p(math.exp(-abs(t)))
+
+    y = np.array([[0.0, 0.0], [1.0, 3.0], [-2.0, 5.0], [1000.0, 0.0]])
+    out = gemm.log_softmax_rows(y)
+    for (a, b), (oa, ob) in zip(y, out):
+        assert abs(oa + softplus(b - a)) < 1e-12
+        assert abs(ob + softplus(a - b)) < 1e-12
+    assert out[0, 0] == -math.log(2.0)
+
+
+def test_log_softmax_rows_normalised_shift_invariant_and_library():
+    rng = np.random.default_rng(52)
+    y = rng.standard_normal((5, 777)) * 7.0
+    out = gemm.log_softmax_rows(y)
+    assert np.allclose(np.sum(np.exp(out), axis=1), 1.0, rtol=0, atol=1e-13)
+    assert np.allclose(gemm.log_softmax_rows(y + 123.25), out, rtol=0, atol=1e-12)
+    ref = torch.log_softmax(torch.from_numpy(y), dim=1).numpy()
+    assert np.allclose(out, ref, rtol=0, atol=1e-13)
+    big = gemm.log_softmax_rows(np.array([[1e4, 0.0, -1e4]]))
+    assert np.all(np.isfinite(big)) and big[0, 0] == 0.0
+
+
+def test_logsoftmax_oracle_applies_bias_before_normalising():
+    """Bias enters the logits: a bias that is constant over columns changes
+    nothing; a bias on one column moves the distribution by its closed form."""
+    rng = np.random.default_rng(53)
+    M, K, N = 4, 64, 96
+    xb = formats.bf16_encode_rne(rng.standard_normal((M, K)).astype(np.float32))
+    wb = formats.bf16_encode_rne((rng.standard_normal((K, N)) * 0.05).astype(np.float32))
+    out0, d0 = gemm.gemm_bf16_logsoftmax_bits(xb, wb)
+    const = formats.bf16_encode_rne(np.full(N, 2.5, np.float32))
+    out1, _ = gemm.gemm_bf16_logsoftmax_bits(xb, wb, const)
+    assert np.allclose(out1, out0, rtol=0, atol=1e-12)
+    one = np.zeros(N, np.float32)
+    one[7] = 1.0
+    out2, _ = gemm.gemm_bf16_logsoftmax_bits(xb, wb, formats.bf16_encode_rne(one))
+    y = formats.bf16_decode(xb) @ formats.bf16_decode(wb)
+    y[:, 7] += 1.0
+    ref = y - np.log(np.sum(np.exp(y), axis=1, keepdims=True))
+    assert np.allclose(out2, ref, rtol=0, atol=1e-12)
+    # Denominators: twice the row's largest sum_k |x||w| plus |out|.
+    dk = np.abs(formats.bf16_decode(xb)) @ np.abs(formats.bf16_decode(wb))
+    assert np.allclose(d0, 2 * dk.max(axis=1, keepdims=True) + np.abs(out0), rtol=1e-15, atol=0)

@@ -66,6 +66,10 @@ def lib():
     L.gemm_bf16_w8.restype = i32
     L.gemm_w8_kernel_name.argtypes = [i64, i64, i64]
     L.gemm_w8_kernel_name.restype = ctypes.c_char_p
+    L.gemm_bf16_logsoftmax.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, i64, vp]
+    L.gemm_bf16_logsoftmax.restype = i32
+    L.gemm_logsoftmax_workspace_size.argtypes = [i64, i64, i32]
+    L.gemm_logsoftmax_workspace_size.restype = i64
     L.gemm_bf16_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
     L.gemm_bf16_w4.restype = i32
     L.gemm_w4_kernel_name.argtypes = [i64, i64, i64]
@@ -176,6 +180,44 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
                                     _stream_ptr(stream))
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_fp8_blockscaled")
+    return C
+
+
+def gemm_logsoftmax_workspace_size(M, N, out_dtype=OUT_BF16):
+    return int(lib().gemm_logsoftmax_workspace_size(M, N, out_dtype))
+
+
+def gemm_bf16_logsoftmax(X, W, bias, C, workspace=None, stream=None):
+    """C[M,N] = log_softmax(X[M,K] @ W[K,N] + bias[N], over N) on the GPU.
+
+    X, W: bfloat16 (unit inner stride); bias: bfloat16 [N] or None; C:
+    bfloat16 or float32 [M, N] (unit inner stride), written in place.
+    workspace: a 16-byte aligned device tensor of at least
+    gemm_logsoftmax_workspace_size(M, N, out dtype) bytes, or None to allocate
+    one here (torch's caching allocator).
+    """
+    _check_cuda(X, W, bias, C)
+    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("X and W must be bfloat16")
+    if C.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("C must be bfloat16 or float32")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    ldx, ldw, ldc = _row_major(X, "X"), _row_major(W, "W"), _row_major(C, "C")
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K or tuple(C.shape) != (M, N) or (bias is not None and bias.numel() != N):
+        raise ValueError("shape mismatch")
+    out = OUT_BF16 if C.dtype == torch.bfloat16 else OUT_F32
+    need = gemm_logsoftmax_workspace_size(M, N, out)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    _check_cuda(workspace)
+    st = lib().gemm_bf16_logsoftmax(_ptr(X), _ptr(W), _ptr(bias), _ptr(C), M, N, K, ldx, ldw, ldc,
+                                    out, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_bf16_logsoftmax")
     return C
 
 

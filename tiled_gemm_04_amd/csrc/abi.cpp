@@ -181,6 +181,58 @@ int gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M
                       TGEMM_ALGO_AUTO, stream);
 }
 
+int64_t gemm_logsoftmax_workspace_size(int64_t M, int64_t N, int out_dtype) {
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return -1;
+  if (out_dtype != TGEMM_OUT_F32 && out_dtype != TGEMM_OUT_BF16) return -1;
+  // Per-stripe pairs, rounded up to 256 bytes, then fp32 logits when the
+  // output is bf16.
+  const int64_t pairs = (M * tgemm::lsm_workgroups(N) * 8 + 255) / 256 * 256;
+  return pairs + (out_dtype == TGEMM_OUT_BF16 ? M * N * 4 : 0);
+}
+
+int gemm_bf16_logsoftmax(const void* X, const void* W, const void* bias, void* C, int64_t M,
+                         int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldc, int out_dtype,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  if (M > 0 && N == 0) return TGEMM_ERR_INVALID;  // no distribution over zero columns
+  const int st = validate_bf16(X, W, bias, C, M, N, K, ldx, ldw, ldc, TGEMM_EPI_NONE, out_dtype,
+                               TGEMM_ALGO_AUTO);
+  if (st != TGEMM_OK || M == 0) return st;
+  if (workspace == nullptr || workspace_bytes < gemm_logsoftmax_workspace_size(M, N, out_dtype))
+    return TGEMM_ERR_INVALID;
+  Bf16Args a;
+  a.A = static_cast<const uint16_t*>(X);
+  a.B = static_cast<const uint16_t*>(W);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.lda = ldx;
+  a.ldb = ldw;
+  a.ldc = ldc;
+  a.vec_a = (K == 0 || (aligned16(X) && ldx % 8 == 0)) ? 1 : 0;
+  a.vec_b = (K == 0 || (aligned16(W) && ldw % 8 == 0)) ? 1 : 0;
+  const int64_t out_align = out_dtype == TGEMM_OUT_BF16 ? 8 : 4;
+  a.vec_c = (aligned16(C) && ldc % out_align == 0) ? 1 : 0;
+  if (!tgemm::lsm_direct_ok(a)) return TGEMM_ERR_UNSUPPORTED;
+  tgemm::LsmArgs q;
+  q.part = static_cast<float2*>(workspace);
+  q.G = static_cast<int>(tgemm::lsm_workgroups(N));
+  if (out_dtype == TGEMM_OUT_F32) {
+    q.logits = static_cast<float*>(C);
+    q.ldl = ldc;
+    q.vec_l = a.vec_c;
+  } else {
+    q.logits = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        (M * q.G * 8 + 255) / 256 * 256);
+    q.ldl = N;
+    q.vec_l = aligned16(q.logits) ? 1 : 0;
+  }
+  const hipError_t e = tgemm::launch_bf16_thin_lsm(a, q, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
+                                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
 int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB, void* C,
                          int64_t M, int64_t N, int64_t K, void* stream) {
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)

@@ -51,18 +51,18 @@ __device__ __forceinline__ int w_swz(int k) { return 2 * ((k & 3) | (((k >> 3) &
 // XOR on the chunk index of row r of an X block (4 chunks of 16 bytes).
 __device__ __forceinline__ int x_swz(int r) { return (r >> 2) & 3; }
 
-template <int MB, int EPI, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
-
+// Streams the workgroup's 512-column stripe of W once and leaves the
+// products in acc[mb][j] (16 x 16 blocks, transposed by the operand swap:
+// element e of lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the
+// wave's 128).  Ends with every load landed; the caller synchronises the
+// workgroup before reusing smem.
+template <int MB>
+__device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem, f32x4 (&acc)[MB][kFN]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * kBN;
 
-  // acc[mb][j]: 16 x 16 block, transposed by the operand swap: element e of
-  // lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the wave's 128.
-  f32x4 acc[MB][kFN];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -138,6 +138,43 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
   }
+}
+
+// Stores 4 consecutive outputs v[0..3] of row `row` starting at column col
+// (columns past N skipped).
+template <bool OUT_BF16>
+__device__ __forceinline__ void store4(const Bf16Args& p, int row, int col, const float (&v)[4]) {
+  const int64_t off = static_cast<int64_t>(row) * p.ldc + col;
+  const bool full = p.vec_c && col + 4 <= p.N;
+  if constexpr (OUT_BF16) {
+    uint16_t* out = static_cast<uint16_t*>(p.C) + off;
+    if (full) {
+      *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
+    }
+  } else {
+    float* out = static_cast<float*>(p.C) + off;
+    if (full) {
+      *reinterpret_cast<f32x4*>(out) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < p.N) out[e] = v[e];
+    }
+  }
+}
+
+template <int MB, int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
+  f32x4 acc[MB][kFN];
+  thin_accumulate<MB>(p, smem, acc);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kBN;
 
   // ---- epilogue: lane holds 4 consecutive columns of one row per block ----
 #pragma unroll
@@ -156,27 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<EPI>(acc[mb][j][e], bias[e]);
-      const int64_t off = static_cast<int64_t>(row) * p.ldc + col;
-      const bool full = p.vec_c && col + 4 <= p.N;
-      if constexpr (OUT_BF16) {
-        uint16_t* out = static_cast<uint16_t*>(p.C) + off;
-        if (full) {
-          *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
-        }
-      } else {
-        float* out = static_cast<float*>(p.C) + off;
-        if (full) {
-          *reinterpret_cast<f32x4*>(out) = f32x4{v[0], v[1], v[2], v[3]};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < p.N) out[e] = v[e];
-        }
-      }
+      store4<OUT_BF16>(p, row, col, v);
     }
   }
 }
@@ -200,7 +217,207 @@ hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s)
   return launch_m<MB, kEpiBiasGelu, false>(a, s);
 }
 
+// ---- LM head with bias and log-softmax over each row (GEMM compute-cost
+// page, section 7.2: the output GEMM, its bias add and the LogSoftmax that
+// follows, fused) ----
+//
+//   out[i, n] = y[i, n] - lse_i,  y = X W + bias,  lse_i = log sum_n exp(y[i, n])
+//
+// Pass 1 (the thin GEMM's epilogue): each workgroup adds the bias to its
+// stripe's logits, forms per row the stripe maximum m_w and s_w =
+// sum exp(y - m_w) (the safe-softmax pair) and writes them to part[row * G +
+// w], and writes the fp32 logits (into C for fp32 output, else into the
+// workspace, so each output is rounded once).  Pass 2 (lsm_normalize) merges
+// the G pairs of a row, lse = m + log s with m = max_w m_w and s =
+// sum_w s_w exp(m_w - m), and writes y - lse.  The logits cross HBM once
+// each way (3-4 bytes per output per pass, small beside the weight the
+// first pass streams); a single pass would need a grid-wide barrier.
+
+// Merges the pair (m2, s2) into (m, s); m == -inf marks an empty pair.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  if (m2 == -__builtin_inff()) return;
+  if (m == -__builtin_inff()) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float mn = __builtin_fmaxf(m, m2);
+  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
+}
+
+template <int MB>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_lsm(Bf16Args p, LsmArgs q) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
+  f32x4 acc[MB][kFN];
+  thin_accumulate<MB>(p, smem, acc);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kBN;
+  constexpr float kNegInf = -__builtin_inff();
+
+  // Logits with bias; columns past N take -inf, which no maximum or sum sees.
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int col = n0 + kWTN * wave + 16 * j + 4 * (lane >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = col + e < p.N;
+      const float b = (in && p.bias != nullptr) ? bf16_bits_to_f32(p.bias[col + e]) : 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][j][e] = in ? acc[mb][j][e] + b : kNegInf;
+    }
+  }
+
+  // Row 16 mb + l%16 of the stripe: lanes l, l^16, l^32, l^48 of each wave
+  // hold its columns; the four waves meet in LDS.
+  float* red = reinterpret_cast<float*>(smem);  // [4 waves][64 rows]
+  __syncthreads();  // every wave's loads have landed: smem is free
+  float mrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float m = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = __builtin_fmaxf(m, acc[mb][j][e]);
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16, 64));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
+    if (lane < 16) red[wave * 64 + 16 * mb + lane] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = 16 * mb + (lane & 15);
+    mrow[mb] = __builtin_fmaxf(__builtin_fmaxf(red[r], red[64 + r]), __builtin_fmaxf(red[128 + r], red[192 + r]));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t += __expf(acc[mb][j][e] - mrow[mb]);
+    t += __shfl_xor(t, 16, 64);
+    t += __shfl_xor(t, 32, 64);
+    if (lane < 16) red[wave * 64 + 16 * mb + lane] = t;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < 16) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = 16 * mb + lane;
+      const float srow = (red[r] + red[64 + r]) + (red[128 + r] + red[192 + r]);
+      if (r < p.M) q.part[static_cast<int64_t>(r) * gridDim.x + blockIdx.x] = float2{mrow[mb], srow};
+    }
+  }
+
+  // fp32 logits to their buffer.
+  Bf16Args pl = p;
+  pl.C = q.logits;
+  pl.ldc = q.ldl;
+  pl.vec_c = q.vec_l;
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int col = n0 + kWTN * wave + 16 * j + 4 * (lane >> 4);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = 16 * mb + (lane & 15);
+      if (row >= p.M) continue;
+      const float v[4] = {acc[mb][j][0], acc[mb][j][1], acc[mb][j][2], acc[mb][j][3]};
+      store4<false>(pl, row, col, v);
+    }
+  }
+}
+
+// Pass 2: workgroup (x, y) normalises columns kChunk x .. + kChunk - 1 of
+// row y; each thread takes 16 columns, as four 4-column groups 1 KiB apart
+// per wave.
+constexpr int kChunk = 4096;
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void tgemm_lsm_normalize(LsmArgs q, void* C, int64_t ldc, int N,
+                                                           int vec_c) {
+  __shared__ float red[2][4];
+  const int r = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int G = q.G;
+  float m = -__builtin_inff(), s = 0.0f;
+  const float2* part = q.part + static_cast<int64_t>(r) * G;
+  for (int w = t; w < G; w += 256) {
+    const float2 v = part[w];
+    lse_merge(m, s, v.x, v.y);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float m2 = __shfl_xor(m, d, 64);
+    const float s2 = __shfl_xor(s, d, 64);
+    lse_merge(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    red[0][wave] = m;
+    red[1][wave] = s;
+  }
+  __syncthreads();
+  m = red[0][0];
+  s = red[1][0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) lse_merge(m, s, red[0][w], red[1][w]);
+  const float lse = m + __logf(s);
+
+  const float* lrow = q.logits + static_cast<int64_t>(r) * q.ldl;
+  Bf16Args po{};
+  po.C = C;
+  po.ldc = ldc;
+  po.N = N;
+  po.vec_c = vec_c;
+#pragma unroll
+  for (int i = 0; i < kChunk / 1024; ++i) {
+    const int col = blockIdx.x * kChunk + 1024 * i + 4 * t;
+    if (col >= N) break;
+    float v[4];
+    if (q.vec_l && col + 4 <= N) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(lrow + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = x[e] - lse;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = col + e < N ? lrow[col + e] - lse : 0.0f;
+    }
+    store4<OUT_BF16>(po, r, col, v);
+  }
+}
+
+template <int MB>
+hipError_t launch_lsm_m(const Bf16Args& a, const LsmArgs& q, hipStream_t s) {
+  hipLaunchKernelGGL((tgemm_bf16_thin_lsm<MB>), dim3(q.G), dim3(kThreads), 0, s, a, q);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int64_t lsm_workgroups(int64_t N) { return (N + kBN - 1) / kBN; }
+
+bool lsm_direct_ok(const Bf16Args& a) {
+  return a.M <= 64 && a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
+         a.ldb * 2 * kBK < (int64_t{1} << 31) && a.lda * 2 * 64 < (int64_t{1} << 31);
+}
+
+hipError_t launch_bf16_thin_lsm(const Bf16Args& a, const LsmArgs& q, int out_bf16, hipStream_t s) {
+  hipError_t e;
+  if (a.M <= 16) e = launch_lsm_m<1>(a, q, s);
+  else if (a.M <= 32) e = launch_lsm_m<2>(a, q, s);
+  else if (a.M <= 48) e = launch_lsm_m<3>(a, q, s);
+  else e = launch_lsm_m<4>(a, q, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>((a.N + kChunk - 1) / kChunk), static_cast<unsigned>(a.M));
+  if (out_bf16)
+    hipLaunchKernelGGL((tgemm_lsm_normalize<true>), grid, dim3(256), 0, s, q, a.C, a.ldc, a.N, a.vec_c);
+  else
+    hipLaunchKernelGGL((tgemm_lsm_normalize<false>), grid, dim3(256), 0, s, q, a.C, a.ldc, a.N, a.vec_c);
+  return hipGetLastError();
+}
 
 const char* thin_kernel_name(int M) {
   if (M <= 16) return "tgemm_bf16_thin_m16";

@@ -88,6 +88,20 @@ hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 hipError_t launch_wq_thin(int bits, const W8Args& a, int epilogue, int out_bf16, hipStream_t stream);
 bool wq_supported(int bits, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq);
 const char* wq_kernel_name(int bits, int M);
+// Thin-M GEMM + bias + row log-softmax, in two passes: the GEMM kernel
+// writes fp32 logits (row stride ldl) and per-stripe (max, sum exp) pairs
+// part [M, G] (G = lsm_workgroups(N)); the second kernel merges each row's
+// pairs and writes logits - lse into C.
+struct LsmArgs {
+  float2* part;
+  float* logits;  // C itself for fp32 output, else workspace
+  int64_t ldl;
+  int G;
+  int vec_l;  // 1: logit rows may be read and written with 16-byte accesses
+};
+hipError_t launch_bf16_thin_lsm(const Bf16Args& a, const LsmArgs& q, int out_bf16, hipStream_t stream);
+int64_t lsm_workgroups(int64_t N);
+bool lsm_direct_ok(const Bf16Args& a);
 hipError_t launch_quant_fp8_1x128(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quant_fp8_128x128(const QuantArgs& a, hipStream_t stream);
 const char* thin_kernel_name(int M);
