@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
                     help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
-                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64)")
+                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -88,6 +88,7 @@ KERNEL_SOURCES = {
     "w8": ["common.h", "launch.h", "gemm_wq_thin.hip"],
     "w4": ["common.h", "launch.h", "gemm_wq_thin.hip"],
     "lsm": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
+    "nt": ["common.h", "launch.h", "gemm_bf16_tiled.hip"],
 }
 
 # Weight-only int8 LM head: the thin-M workloads' X [M, 4096] times int8
@@ -98,6 +99,7 @@ W8_CASES = {"w8_m1": 1, "w8_m8": 8, "w8_m32": 32, "w8_m64": 64,
 # FP8 quantisers, timed on the FP8 workload's unquantised operands (bf16):
 # activations A [4096, 4096] in 1 x 128 groups, weights B [4096, 14336] in
 # 128 x 128 blocks.
+NT_CASES = {"square_nt": "square", "ffn_up_nt": "ffn_up", "ffn_down_nt": "ffn_down"}
 LSM_CASES = {"lsm_m1": 1, "lsm_m8": 8, "lsm_m32": 32, "lsm_m64": 64}
 QUANT_CASES = {"quant_a": ("a", "tgemm_quant_fp8_1x128"), "quant_b": ("b", "tgemm_quant_fp8_128x128")}
 
@@ -138,6 +140,9 @@ class Case:
             return
         if name in LSM_CASES:
             self._init_lsm(name, dev)
+            return
+        if name in NT_CASES:
+            self._init_nt(name, dev)
             return
         w = wl.WORKLOADS[name]
         self.w = w
@@ -180,6 +185,9 @@ class Case:
         if self.family == "w8":
             return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
                     f"(Q[{self.K},{self.N}] int8 * S[{(self.K + 127) // 128},{self.N}])")
+        if self.family == "nt":
+            return (f"{self.name}: C[{self.M},{self.N}] = A[{self.M},{self.K}] . Bt[{self.N},{self.K}]^T "
+                    f"(weight K-contiguous)")
         if self.family == "lsm":
             return (f"{self.name}: C[{self.M},{self.N}] = log_softmax(X[{self.M},{self.K}] . "
                     f"W[{self.K},{self.N}] + bias[{self.N}]) over each row")
@@ -211,6 +219,28 @@ class Case:
         self.family = "w8" if bits == 8 else "w4"
         self.bound, self.peak = "hbm", PEAK_HBM_GBS
         self.dtype = "bf16 x int8" if bits == 8 else "bf16 x int4"
+        self.inputs_for_oracle = None
+
+    def _init_nt(self, name, dev):
+        import torch
+
+        import tiled_gemm_04_amd as tg
+        import workloads as wl
+
+        w = wl.WORKLOADS[NT_CASES[name]]
+        a, b, bias = wl.bf16_inputs(w, device=dev)
+        bt = b.t().contiguous()  # the same weight, stored [N, K]
+        del b
+        c = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev)
+        self.launch = lambda: tg.gemm_bf16_nt(a, bt, bias, c, epilogue=w.epilogue)
+        self.w = None
+        self.M, self.N, self.K = w.M, w.N, w.K
+        self.flops = 2 * w.M * w.N * w.K
+        self.bytes = 2 * (w.M * w.K + w.K * w.N) + 2 * w.M * w.N + (2 * w.N if w.epilogue else 0)
+        self.kernel = tg.gemm_bf16_nt_kernel_name(w.M, w.N, w.K)
+        self.family = "nt"
+        self.bound, self.peak = "mfma", PEAK_BF16_TFLOPS
+        self.dtype = "bf16"
         self.inputs_for_oracle = None
 
     def _init_lsm(self, name, dev):
@@ -387,7 +417,7 @@ def main():
         for name in ("ffn_up", "ffn_down", "thin_m1", "thin_m8", "thin_m32", "thin_m64", "fp8",
                      "fp8_ragged", "tiny", "quant_a", "quant_b", "w8_m1", "w8_m8", "w8_m32",
                      "w8_m64", "w4_m1", "w4_m8", "w4_m32", "w4_m64", "lsm_m1", "lsm_m8", "lsm_m32",
-                     "lsm_m64"):
+                     "lsm_m64", "square_nt", "ffn_up_nt", "ffn_down_nt"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

@@ -106,6 +106,29 @@ int gemm_bf16(const void* A, const void* B, const void* bias, void* C,
               int epilogue, int out_dtype, void* stream);
 
 /*
+ * gemm_bf16_nt -- C = epilogue(A . Bt^T + bias): gemm_bf16 with the weight
+ * given K-contiguous, Bt [N, K] row-major (row stride ldb >= K elements),
+ * the layout nn.Linear keeps its weight in ([out_features, in_features]).
+ *
+ * The GEMM compute-cost page (section 5.2) asks that operands be laid out
+ * the way the kernel reads them, so that no implicit transpose (an extra
+ * pass and copy) precedes the product; this entry point reads [N, K] weights
+ * as they are.  Everything else (A, bias, C, epilogue, out_dtype, numerics,
+ * stream) as gemm_bf16.
+ * Supported: K % 8 == 0, A and Bt 16-byte aligned with lda, ldb multiples of
+ * 8 (others return TGEMM_ERR_UNSUPPORTED; N is free).  Returns TGEMM_OK,
+ * TGEMM_ERR_INVALID, TGEMM_ERR_UNSUPPORTED or TGEMM_ERR_LAUNCH.
+ */
+int gemm_bf16_nt(const void* A, const void* Bt, const void* bias, void* C,
+                 int64_t M, int64_t N, int64_t K,
+                 int64_t lda, int64_t ldb, int64_t ldc,
+                 int epilogue, int out_dtype, void* stream);
+
+/* Name of the kernel gemm_bf16_nt launches for aligned operands of these
+ * sizes, or NULL when they are unsupported or invalid.  No launch. */
+const char* gemm_bf16_nt_kernel_name(int64_t M, int64_t N, int64_t K);
+
+/*
  * gemm_bf16_ex -- gemm_bf16 with an explicit kernel family (tgemm_algo_t).
  * TGEMM_ALGO_THIN with M > 64 returns TGEMM_ERR_UNSUPPORTED.  Used by tests
  * that cross-check the two kernel families and by the benchmark.

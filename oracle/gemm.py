@@ -135,6 +135,15 @@ def dequant_fp8_b(qb_bits, sb):
     return qb * sb[gk][:, gn]
 
 
+def gemm_bf16_nt_bits(a_bits, bt_bits, bias_bits=None, epilogue=EPI_NONE):
+    """The same product with the weight given K-contiguous, bt [N, K]:
+    ``y[i, n] = sum_k a[i, k] * bt[n, k]``, i.e. the contraction with
+    ``b = bt`` transposed (decoding is elementwise, so it commutes with the
+    transpose)."""
+    bias = None if bias_bits is None else bf16_decode(bias_bits)
+    return gemm_f64(bf16_decode(a_bits), bf16_decode(bt_bits).T, bias, epilogue)
+
+
 def dequant_w8(q, s):
     """W[k, n] = q[k, n] * s[k // 128, n] for int8 codes q [K, N] and fp32
     scales s [ceil(K/128), N] (exact in float64)."""

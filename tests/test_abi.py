@@ -161,3 +161,20 @@ def test_logsoftmax_workspace_size_and_validation():
     assert call(work_bytes=256 + 4 * 512 * 4 - 1) == INV
     assert call(out=0, work_bytes=255) == INV
     assert call(ldx=63) == INV
+
+
+def test_nt_validation():
+    L = binding.lib()
+
+    def call(A=FAKE, B=FAKE, bias=FAKE, C=FAKE, M=64, N=64, K=64, lda=64, ldb=64, ldc=64, epi=0, out=1):
+        return L.gemm_bf16_nt(A, B, bias, C, M, N, K, lda, ldb, ldc, epi, out, NULL)
+
+    assert call(ldb=63) == INV                  # ldb < K for a [N, K] weight
+    assert call(K=60, lda=64, ldb=64) == UNS   # K % 8
+    assert call(lda=66) == UNS                 # lda % 8
+    assert call(M=0) == OK and call(N=0, ldc=1) == OK
+    assert call(C=NULL) == INV and call(B=NULL) == INV
+    assert call(epi=1, bias=NULL) == INV
+    assert binding.gemm_bf16_nt_kernel_name(4096, 4096, 4096) == "tgemm_bf16_tiled_bt_256x256x32"
+    assert binding.gemm_bf16_nt_kernel_name(2048, 4096, 16384) == "tgemm_bf16_tiled_bt_256x128x64"
+    assert binding.gemm_bf16_nt_kernel_name(64, 64, 60) is None

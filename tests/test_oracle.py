@@ -601,3 +601,25 @@ def test_logsoftmax_oracle_applies_bias_before_normalising():
     # Denominators: twice the row's largest sum_k |x||w| plus |out|.
     dk = np.abs(formats.bf16_decode(xb)) @ np.abs(formats.bf16_decode(wb))
     assert np.allclose(d0, 2 * dk.max(axis=1, keepdims=True) + np.abs(out0), rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------- K-contiguous weights ----
+
+def test_nt_oracle_brute_force_and_transpose_relation():
+    """y[i, n] = sum_k a[i, k] * bt[n, k] by explicit loops on a tiny case,
+    and equality with the [K, N] oracle on the transposed weight."""
+    rng = np.random.default_rng(71)
+    M, N, K = 3, 5, 7
+    ab = formats.bf16_encode_rne(rng.standard_normal((M, K)).astype(np.float32))
+    btb = formats.bf16_encode_rne(rng.standard_normal((N, K)).astype(np.float32))
+    y, d = gemm.gemm_bf16_nt_bits(ab, btb)
+    a, bt = formats.bf16_decode(ab), formats.bf16_decode(btb)
+    for i in range(M):
+        for n in range(N):
+            ref = math.fsum(float(a[i, k]) * float(bt[n, k]) for k in range(K))
+            assert abs(y[i, n] - ref) <= 1e-15 * max(1.0, abs(ref))
+            assert abs(d[i, n] - math.fsum(abs(float(a[i, k]) * float(bt[n, k])) for k in range(K))) < 1e-14
+    bias = formats.bf16_encode_rne(rng.standard_normal(N).astype(np.float32))
+    y1, d1 = gemm.gemm_bf16_nt_bits(ab, btb, bias, gemm.EPI_BIAS_GELU_TANH)
+    y2, d2 = gemm.gemm_bf16_bits(ab, np.ascontiguousarray(btb.T), bias, gemm.EPI_BIAS_GELU_TANH)
+    assert np.array_equal(y1, y2) and np.array_equal(d1, d2)

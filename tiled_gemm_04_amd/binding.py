@@ -66,6 +66,10 @@ def lib():
     L.gemm_bf16_w8.restype = i32
     L.gemm_w8_kernel_name.argtypes = [i64, i64, i64]
     L.gemm_w8_kernel_name.restype = ctypes.c_char_p
+    L.gemm_bf16_nt.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.gemm_bf16_nt.restype = i32
+    L.gemm_bf16_nt_kernel_name.argtypes = [i64, i64, i64]
+    L.gemm_bf16_nt_kernel_name.restype = ctypes.c_char_p
     L.gemm_bf16_logsoftmax.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, i64, vp]
     L.gemm_bf16_logsoftmax.restype = i32
     L.gemm_logsoftmax_workspace_size.argtypes = [i64, i64, i32]
@@ -181,6 +185,35 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_fp8_blockscaled")
     return C
+
+
+def gemm_bf16_nt(A, Bt, bias, C, epilogue=EPI_NONE, stream=None):
+    """C[M,N] = epilogue(A[M,K] @ Bt[N,K].T + bias[N]) on the GPU (writes C in
+    place); Bt is the K-contiguous weight, as nn.Linear stores it."""
+    _check_cuda(A, Bt, bias, C)
+    for t, nm in ((A, "A"), (Bt, "Bt")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    if C.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("C must be bfloat16 or float32")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    lda, ldb, ldc = _row_major(A, "A"), _row_major(Bt, "Bt"), _row_major(C, "C")
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    out = OUT_BF16 if C.dtype == torch.bfloat16 else OUT_F32
+    st = lib().gemm_bf16_nt(_ptr(A), _ptr(Bt), _ptr(bias), _ptr(C), M, N, K, lda, ldb, ldc,
+                            int(epilogue), out, _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_bf16_nt")
+    return C
+
+
+def gemm_bf16_nt_kernel_name(M, N, K):
+    r = lib().gemm_bf16_nt_kernel_name(M, N, K)
+    return None if r is None else r.decode()
 
 
 def gemm_logsoftmax_workspace_size(M, N, out_dtype=OUT_BF16):

@@ -174,6 +174,46 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C, int64_
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
+int gemm_bf16_nt(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
+                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
+                 void* stream) {
+  // validate_bf16 checks B as [K, N] with ldb >= N; here B is [N, K].
+  const int st = validate_bf16(A, B, bias, C, M, N, K, lda, N > 0 ? N : 1, ldc, epilogue, out_dtype,
+                               TGEMM_ALGO_AUTO);
+  if (st != TGEMM_OK) return st;
+  if (ldb < K || ldb < 1 || !extent_ok(N, K, ldb)) return TGEMM_ERR_INVALID;
+  if (M == 0 || N == 0) return TGEMM_OK;
+  Bf16Args a;
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.vec_a = (K == 0 || (aligned16(A) && lda % 8 == 0)) ? 1 : 0;
+  a.vec_b = (K == 0 || (aligned16(B) && ldb % 8 == 0)) ? 1 : 0;
+  const int64_t out_align = out_dtype == TGEMM_OUT_BF16 ? 8 : 4;
+  a.vec_c = (aligned16(C) && ldc % out_align == 0) ? 1 : 0;
+  const int shape = pick_tiled_shape(M, N);
+  if (!tgemm::bf16_bt_direct_ok(a, shape)) return TGEMM_ERR_UNSUPPORTED;
+  const hipError_t e = tgemm::launch_bf16_tiled_bt(a, shape, epilogue, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
+                                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+const char* gemm_bf16_nt_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return nullptr;
+  if (K % 8 != 0) return nullptr;
+  static const char* const kNames[tgemm::kNumTiledShapes] = {
+      "tgemm_bf16_tiled_bt_256x256x32", "tgemm_bf16_tiled_bt_256x128x64", "tgemm_bf16_tiled_bt_128x128x64"};
+  const int shape = pick_tiled_shape(M, N);
+  return shape >= 0 && shape < tgemm::kNumTiledShapes ? kNames[shape] : nullptr;
+}
+
 int gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
               int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
               void* stream) {

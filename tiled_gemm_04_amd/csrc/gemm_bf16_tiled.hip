@@ -29,8 +29,14 @@
 //     are masked, and loads past M, N, K read zero through the buffer range
 //     check (DeepGEMM page, section 4.1).
 //
-// Requirements (checked by the launcher, otherwise the general kernel runs):
-// A, B 16-byte aligned; lda, ldb multiples of 8; K, N multiples of 8; all
+// B comes in either layout: [K, N] (N-contiguous, read with the transposed
+// LDS reads above) or, with BT, [N, K] (K-contiguous, the nn.Linear weight
+// layout) -- then B tiles are stored and read exactly like A tiles (plain
+// 16-byte operand reads, the A swizzle).
+//
+// Requirements (checked by the launcher, otherwise the general kernel runs,
+// or for BT the call is unsupported): A, B 16-byte aligned; lda, ldb
+// multiples of 8; K multiple of 8 and (for [K, N] B) N multiple of 8; all
 // per-lane byte offsets below 2^31.
 #include "common.h"
 #include "launch.h"
@@ -169,7 +175,7 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], flo
   }
 }
 
-template <class C, int EPI, bool OUT_BF16>
+template <class C, bool BT, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
                                                                 int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
@@ -211,12 +217,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
     a_kc[i] = 8 * c;
   }
   uint32_t b_goff[C::BPW];
+  int b_kc[C::BPW];  // BT: first K column of the chunk
 #pragma unroll
   for (int i = 0; i < C::BPW; ++i) {
     const int s = 64 * (wave * C::BPW + i) + lane;
-    const int k = s / C::B_CPR;
-    const int c = (s % C::B_CPR) ^ b_swz(k);
-    b_goff[i] = static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange);
+    if constexpr (BT) {
+      const int n = s / C::A_CPR;
+      const int c = (s % C::A_CPR) ^ a_swz<C>(n);
+      b_goff[i] = static_cast<uint32_t>(n * ldb2 + 16 * c);
+      b_kc[i] = 8 * c;
+    } else {
+      const int k = s / C::B_CPR;
+      const int c = (s % C::B_CPR) ^ b_swz(k);
+      b_goff[i] = static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange);
+      b_kc[i] = 0;
+    }
   }
   // Windows of the slice at column k0: A rows m0 .. M-1 from column k0, B
   // rows k0 .. K-1 from column n0 (bytes past M or K read as zeros).  They
@@ -224,22 +239,24 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
   // instead of recomputing them.
   const uint16_t* const a_base0 = p.A + static_cast<int64_t>(m0) * p.lda;
   const int64_t a_size0 = (static_cast<int64_t>(p.M - m0 - 1) * p.lda + p.K) * 2;
-  const uint16_t* const b_base0 = p.B + n0;
-  const int64_t b_size0 = (static_cast<int64_t>(p.K - 1) * p.ldb + (p.N - n0)) * 2;
-  const int64_t b_step = static_cast<int64_t>(C::BK) * p.ldb;  // elements per slice
+  // BT: B rows n0 .. N-1 from column k0, stepping like A.
+  const uint16_t* const b_base0 = BT ? p.B + static_cast<int64_t>(n0) * p.ldb : p.B + n0;
+  const int64_t b_size0 = BT ? (static_cast<int64_t>(p.N - n0 - 1) * p.ldb + p.K) * 2
+                             : (static_cast<int64_t>(p.K - 1) * p.ldb + (p.N - n0)) * 2;
+  const int64_t b_step = BT ? int64_t{C::BK} : static_cast<int64_t>(C::BK) * p.ldb;  // elements per slice
   auto window_a = [&](int k0) { return make_window_words(a_base0 + k0, a_size0 - 2 * k0); };
   auto window_b = [&](int k0) {
-    return make_window_words(b_base0 + static_cast<int64_t>(k0) * p.ldb,
-                             b_size0 - 2 * static_cast<int64_t>(k0) * p.ldb);
+    const int64_t e = BT ? int64_t{k0} : static_cast<int64_t>(k0) * p.ldb;
+    return make_window_words(b_base0 + e, b_size0 - 2 * e);
   };
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
   auto issue_a = [&](i32x4 w, int stage, int k0, int i) {
     const uint32_t off = a_goff[i] | (k0 + a_kc[i] < p.K ? 0u : kOutOfRange);
     buf_load16_lds(w, smem_base + stage * C::STAGE + (wave * C::APW + i) * 1024, off);
   };
-  auto issue_b = [&](i32x4 w, int stage, int i) {
-    buf_load16_lds(w, smem_base + stage * C::STAGE + C::A_STAGE + (wave * C::BPW + i) * 1024,
-                   b_goff[i]);
+  auto issue_b = [&](i32x4 w, int stage, int k0, int i) {
+    const uint32_t off = BT ? (b_goff[i] | (k0 + b_kc[i] < p.K ? 0u : kOutOfRange)) : b_goff[i];
+    buf_load16_lds(w, smem_base + stage * C::STAGE + C::A_STAGE + (wave * C::BPW + i) * 1024, off);
   };
 
   // ---- LDS -> registers ----
@@ -253,11 +270,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
   // K row 8(g>>1) + e (+4 for the second half) and columns 16(g&1) + 4q .. +3
   // of the block, and receives 4 k of column 16(g&1) + (L%16).
   const int bg = lane >> 4, be = (lane >> 2) & 3, bq = lane & 3;
+  // BT: B operand of block j, sub-step ks: row wn*WTN + 32j + lrow of the
+  // K-contiguous tile, chunk 2ks + lhalf, as for A.
   int b_rd[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) {
-    const int chunk = (((wn * C::WTN / 32) + j) ^ be) * 4 + 2 * (bg & 1) + (bq >> 1);
-    b_rd[j] = C::A_STAGE + (8 * (bg >> 1) + be) * C::B_ROW + chunk * 16 + 8 * (bq & 1);
+    if constexpr (BT) {
+      b_rd[j] = C::A_STAGE + (wn * C::WTN + 32 * j + lrow) * C::A_ROW;
+    } else {
+      const int chunk = (((wn * C::WTN / 32) + j) ^ be) * 4 + 2 * (bg & 1) + (bq >> 1);
+      b_rd[j] = C::A_STAGE + (8 * (bg >> 1) + be) * C::B_ROW + chunk * 16 + 8 * (bq & 1);
+    }
   }
   constexpr int kNR = C::FM + C::FN;
   bf16x8 fa[2][C::FM], fb[2][C::FN];
@@ -267,6 +290,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
     if (f < C::FM) {
       const int off = a_rd + 32 * f * C::A_ROW + (((2 * ks + lhalf) ^ a_x) * 16);
       fa[buf][f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
+    } else if constexpr (BT) {
+      const int off = b_rd[f - C::FM] + (((2 * ks + lhalf) ^ a_x) * 16);
+      fb[buf][f - C::FM] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
     } else {
       const int j = f - C::FM;
       const uint8_t* q = base + b_rd[j] + 16 * ks * C::B_ROW;
@@ -320,7 +346,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 #pragma unroll
       for (int i = 0; i < C::APW; ++i) issue_a(wa, s, s * C::BK, i);
 #pragma unroll
-      for (int i = 0; i < C::BPW; ++i) issue_b(wb, s, i);
+      for (int i = 0; i < C::BPW; ++i) issue_b(wb, s, s * C::BK, i);
     });
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * C::LPS) : "memory");
     lds_barrier();
@@ -365,7 +391,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
         });
         static_for<C::BPW>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (load_slot(C::APW + i) == s) issue_b(wb, lst, i);
+          if constexpr (load_slot(C::APW + i) == s) issue_b(wb, lst, kl, i);
         });
       });
       TGEMM_SCHED_FENCE();
@@ -383,25 +409,25 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 }
 
 
-template <class C, int EPI, bool OUT_BF16>
+template <class C, bool BT, int EPI, bool OUT_BF16>
 hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
   const int tiles_n = (a.N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((tgemm_bf16_tiled<C, EPI, OUT_BF16>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16>), dim3(tiles_m * tiles_n),
                      dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, bool BT>
 hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s) {
   if (out_bf16) {
-    if (epi == kEpiNone) return launch_c<C, kEpiNone, true>(a, s);
-    if (epi == kEpiBias) return launch_c<C, kEpiBias, true>(a, s);
-    return launch_c<C, kEpiBiasGelu, true>(a, s);
+    if (epi == kEpiNone) return launch_c<C, BT, kEpiNone, true>(a, s);
+    if (epi == kEpiBias) return launch_c<C, BT, kEpiBias, true>(a, s);
+    return launch_c<C, BT, kEpiBiasGelu, true>(a, s);
   }
-  if (epi == kEpiNone) return launch_c<C, kEpiNone, false>(a, s);
-  if (epi == kEpiBias) return launch_c<C, kEpiBias, false>(a, s);
-  return launch_c<C, kEpiBiasGelu, false>(a, s);
+  if (epi == kEpiNone) return launch_c<C, BT, kEpiNone, false>(a, s);
+  if (epi == kEpiBias) return launch_c<C, BT, kEpiBias, false>(a, s);
+  return launch_c<C, BT, kEpiBiasGelu, false>(a, s);
 }
 
 // Per tile shape (measured on MI355X): BK = 32 with four stages keeps three
@@ -429,13 +455,30 @@ bool bf16_direct_ok(const Bf16Args& a, int shape) {
          a.lda * 2 * info.bm < (int64_t{1} << 31) && a.ldb * 2 * 64 < (int64_t{1} << 31);
 }
 
+bool bf16_bt_direct_ok(const Bf16Args& a, int shape) {
+  const TiledShapeInfo info = tiled_shape_info(shape);
+  // Largest per-lane offsets: a tile's rows of A and of B.
+  return a.vec_a && a.vec_b && a.K % 8 == 0 && a.lda * 2 * info.bm < (int64_t{1} << 31) &&
+         a.ldb * 2 * info.bn < (int64_t{1} << 31);
+}
+
 hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epi, int out_bf16,
                              hipStream_t s) {
   if (!bf16_direct_ok(a, shape)) return launch_bf16_general(a, shape, epi, out_bf16, s);
   switch (shape) {
-    case kTile256x256: return dispatch_epi<Cfg256x256>(a, epi, out_bf16, s);
-    case kTile256x128: return dispatch_epi<Cfg256x128>(a, epi, out_bf16, s);
-    default: return dispatch_epi<Cfg128x128>(a, epi, out_bf16, s);
+    case kTile256x256: return dispatch_epi<Cfg256x256, false>(a, epi, out_bf16, s);
+    case kTile256x128: return dispatch_epi<Cfg256x128, false>(a, epi, out_bf16, s);
+    default: return dispatch_epi<Cfg128x128, false>(a, epi, out_bf16, s);
+  }
+}
+
+hipError_t launch_bf16_tiled_bt(const Bf16Args& a, int shape, int epi, int out_bf16,
+                                hipStream_t s) {
+  if (!bf16_bt_direct_ok(a, shape)) return hipErrorInvalidValue;
+  switch (shape) {
+    case kTile256x256: return dispatch_epi<Cfg256x256, true>(a, epi, out_bf16, s);
+    case kTile256x128: return dispatch_epi<Cfg256x128, true>(a, epi, out_bf16, s);
+    default: return dispatch_epi<Cfg128x128, true>(a, epi, out_bf16, s);
   }
 }
 

@@ -73,6 +73,11 @@ TiledShapeInfo tiled_shape_info(int shape);
 // Each returns hipSuccess or the launch error.
 hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                              hipStream_t stream);
+// B given as [N, K] (K-contiguous, row stride ldb); hipErrorInvalidValue
+// when the operands do not meet bf16_bt_direct_ok.
+hipError_t launch_bf16_tiled_bt(const Bf16Args& a, int shape, int epilogue, int out_bf16,
+                                hipStream_t stream);
+bool bf16_bt_direct_ok(const Bf16Args& a, int shape);
 // Register-staged kernel for operands the direct-to-LDS kernel cannot take.
 hipError_t launch_bf16_general(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                                hipStream_t stream);
