@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
                     help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
-                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt)")
+                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt, thin_nt_m1..64)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -88,7 +88,7 @@ KERNEL_SOURCES = {
     "w8": ["common.h", "launch.h", "gemm_wq_thin.hip"],
     "w4": ["common.h", "launch.h", "gemm_wq_thin.hip"],
     "lsm": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
-    "nt": ["common.h", "launch.h", "gemm_bf16_tiled.hip"],
+    "nt": ["common.h", "launch.h", "gemm_bf16_tiled.hip", "gemm_bf16_thin.hip"],
 }
 
 # Weight-only int8 LM head: the thin-M workloads' X [M, 4096] times int8
@@ -99,7 +99,9 @@ W8_CASES = {"w8_m1": 1, "w8_m8": 8, "w8_m32": 32, "w8_m64": 64,
 # FP8 quantisers, timed on the FP8 workload's unquantised operands (bf16):
 # activations A [4096, 4096] in 1 x 128 groups, weights B [4096, 14336] in
 # 128 x 128 blocks.
-NT_CASES = {"square_nt": "square", "ffn_up_nt": "ffn_up", "ffn_down_nt": "ffn_down"}
+NT_CASES = {"square_nt": "square", "ffn_up_nt": "ffn_up", "ffn_down_nt": "ffn_down",
+            "thin_nt_m1": "thin_m1", "thin_nt_m8": "thin_m8", "thin_nt_m32": "thin_m32",
+            "thin_nt_m64": "thin_m64"}
 LSM_CASES = {"lsm_m1": 1, "lsm_m8": 8, "lsm_m32": 32, "lsm_m64": 64}
 QUANT_CASES = {"quant_a": ("a", "tgemm_quant_fp8_1x128"), "quant_b": ("b", "tgemm_quant_fp8_128x128")}
 
@@ -229,6 +231,8 @@ class Case:
 
         w = wl.WORKLOADS[NT_CASES[name]]
         a, b, bias = wl.bf16_inputs(w, device=dev)
+        if w.name.startswith("thin"):
+            a = wl.thin_x(w, w.M, dev)
         bt = b.t().contiguous()  # the same weight, stored [N, K]
         del b
         c = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev)
@@ -239,7 +243,8 @@ class Case:
         self.bytes = 2 * (w.M * w.K + w.K * w.N) + 2 * w.M * w.N + (2 * w.N if w.epilogue else 0)
         self.kernel = tg.gemm_bf16_nt_kernel_name(w.M, w.N, w.K)
         self.family = "nt"
-        self.bound, self.peak = "mfma", PEAK_BF16_TFLOPS
+        thin = w.name.startswith("thin")
+        self.bound, self.peak = ("hbm", PEAK_HBM_GBS) if thin else ("mfma", PEAK_BF16_TFLOPS)
         self.dtype = "bf16"
         self.inputs_for_oracle = None
 
@@ -417,7 +422,8 @@ def main():
         for name in ("ffn_up", "ffn_down", "thin_m1", "thin_m8", "thin_m32", "thin_m64", "fp8",
                      "fp8_ragged", "tiny", "quant_a", "quant_b", "w8_m1", "w8_m8", "w8_m32",
                      "w8_m64", "w4_m1", "w4_m8", "w4_m32", "w4_m64", "lsm_m1", "lsm_m8", "lsm_m32",
-                     "lsm_m64", "square_nt", "ffn_up_nt", "ffn_down_nt"):
+                     "lsm_m64", "square_nt", "ffn_up_nt", "ffn_down_nt", "thin_nt_m1",
+                     "thin_nt_m8", "thin_nt_m32", "thin_nt_m64"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

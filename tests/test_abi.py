@@ -178,3 +178,6 @@ def test_nt_validation():
     assert binding.gemm_bf16_nt_kernel_name(4096, 4096, 4096) == "tgemm_bf16_tiled_bt_256x256x32"
     assert binding.gemm_bf16_nt_kernel_name(2048, 4096, 16384) == "tgemm_bf16_tiled_bt_256x128x64"
     assert binding.gemm_bf16_nt_kernel_name(64, 64, 60) is None
+    assert binding.gemm_bf16_nt_kernel_name(1, 128256, 4096) == "tgemm_bf16_thin_nt_m16"
+    assert binding.gemm_bf16_nt_kernel_name(64, 128256, 4096) == "tgemm_bf16_thin_nt_m64"
+    assert binding.gemm_bf16_nt_kernel_name(65, 128256, 4096).startswith("tgemm_bf16_tiled_bt")

@@ -117,3 +117,48 @@ def test_nt_unsupported_and_invalid():
     c = torch.empty(4, 8, dtype=torch.bfloat16, device=dev)
     with pytest.raises(ValueError):
         tg.gemm_bf16_nt(a, bt[:, :8], None, c)   # K mismatch
+
+
+@pytest.mark.parametrize("shape", [(1, 512, 4096), (5, 1000, 200), (16, 130, 64), (17, 2056, 136),
+                                   (33, 4096, 1000), (48, 300, 8), (64, 768, 384), (64, 4, 64)])
+def test_nt_thin_m_shapes(shape):
+    """M <= 64 runs the thin kernel for K-contiguous weights."""
+    M, N, K = shape
+    assert tg.gemm_bf16_nt_kernel_name(M, N, K).startswith("tgemm_bf16_thin_nt")
+    a, bt, _ = _inputs(M, N, K, 86, _dev())
+    _check(a, bt, None, tg.EPI_NONE, torch.bfloat16, "thin")
+
+
+@pytest.mark.parametrize("epi", [tg.EPI_BIAS, tg.EPI_BIAS_GELU_TANH])
+@pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
+def test_nt_thin_epilogues(epi, out):
+    a, bt, b = _inputs(9, 700, 264, 87, _dev(), bias=True)
+    _check(a, bt, b, epi, out, "thin epilogue")
+
+
+def test_nt_thin_full_lm_head():
+    """The LM head 4096 x 128256 with the weight stored [vocab, d_model],
+    against the oracle on 2,048 sampled columns and within the same bound of
+    the [K, N] thin kernel on the transposed weight (the K-contiguous kernel
+    sums the slices in a rotated order, so the bits may differ), for M = 1,
+    8, 32, 64."""
+    dev = _dev()
+    w = wl.WORKLOADS["thin_m64"]
+    x, b_kn, _ = wl.bf16_inputs(w, device=dev)
+    bt = b_kn.t().contiguous()
+    g = torch.Generator().manual_seed(95)
+    cols = torch.cat([torch.arange(0, 256), torch.randint(256, w.N - 256, (1536,), generator=g),
+                      torch.arange(w.N - 256, w.N)]).to(dev)
+    for M in (1, 8, 32, 64):
+        xm = x[:M].contiguous()
+        c_nt = torch.empty(M, w.N, dtype=torch.float32, device=dev)
+        c_kn = torch.empty(M, w.N, dtype=torch.float32, device=dev)
+        print(f"[gpu] nt lm_head M={M}", flush=True)
+        tg.gemm_bf16_nt(xm, bt, None, c_nt)
+        tg.gemm_bf16(xm, b_kn, None, c_kn)
+        torch.cuda.synchronize()
+        y, d = og.gemm_bf16_nt_bits(wl.bits_u16(xm), wl.bits_u16(bt[cols]))
+        r = og.compare(c_nt[:, cols].cpu().double().numpy(), y, d, TOL_F32)
+        assert r["ok"], f"M={M}: {r}"
+        dfull = (xm.float().abs() @ b_kn.float().abs())
+        assert float(((c_nt - c_kn).abs() / dfull.clamp_min(1e-30)).max()) <= 2 * TOL_F32, f"M={M}"

@@ -198,16 +198,27 @@ int gemm_bf16_nt(const void* A, const void* B, const void* bias, void* C, int64_
   a.vec_b = (K == 0 || (aligned16(B) && ldb % 8 == 0)) ? 1 : 0;
   const int64_t out_align = out_dtype == TGEMM_OUT_BF16 ? 8 : 4;
   a.vec_c = (aligned16(C) && ldc % out_align == 0) ? 1 : 0;
-  const int shape = pick_tiled_shape(M, N);
-  if (!tgemm::bf16_bt_direct_ok(a, shape)) return TGEMM_ERR_UNSUPPORTED;
-  const hipError_t e = tgemm::launch_bf16_tiled_bt(a, shape, epilogue, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
-                                                   static_cast<hipStream_t>(stream));
+  const int out_bf16 = out_dtype == TGEMM_OUT_BF16 ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (use_thin(M, TGEMM_ALGO_AUTO) && tgemm::thin_nt_ok(a)) {
+    e = tgemm::launch_bf16_thin_nt(a, epilogue, out_bf16, s);
+  } else {
+    const int shape = pick_tiled_shape(M, N);
+    if (!tgemm::bf16_bt_direct_ok(a, shape)) return TGEMM_ERR_UNSUPPORTED;
+    e = tgemm::launch_bf16_tiled_bt(a, shape, epilogue, out_bf16, s);
+  }
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
 const char* gemm_bf16_nt_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return nullptr;
   if (K % 8 != 0) return nullptr;
+  if (use_thin(M, TGEMM_ALGO_AUTO)) {
+    static const char* const kThin[4] = {"tgemm_bf16_thin_nt_m16", "tgemm_bf16_thin_nt_m32",
+                                         "tgemm_bf16_thin_nt_m48", "tgemm_bf16_thin_nt_m64"};
+    return kThin[(M - 1) / 16];
+  }
   static const char* const kNames[tgemm::kNumTiledShapes] = {
       "tgemm_bf16_tiled_bt_256x256x32", "tgemm_bf16_tiled_bt_256x128x64", "tgemm_bf16_tiled_bt_128x128x64"};
   const int shape = pick_tiled_shape(M, N);

@@ -217,6 +217,187 @@ hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s)
   return launch_m<MB, kEpiBiasGelu, false>(a, s);
 }
 
+// ---- Small-M GEMM with K-contiguous weights, Wt [N, K] (the nn.Linear
+// layout of an LM head, [vocab, d_model]) ----
+//
+// Each output column is one contiguous weight row, so a workgroup owns 256
+// rows of Wt (256 columns of C) and walks K in slices of 64: a slice of a
+// row is one 128-byte cache line.  A load instruction brings 8 rows' lines
+// (1 KiB) straight into LDS, four stages deep (three slices, 120 KiB, in
+// flight).  Both MFMA operands are K-contiguous rows in LDS, read with one
+// 16-byte read per lane (8 consecutive k); the 16-byte chunks of each
+// 128-byte row are XOR-permuted by (row / 2) % 8 so the 16 rows one read
+// covers land in 16 distinct bank slots.  Four waves each own 64 columns
+// over all of K.
+//
+// Workgroup b walks its slices starting at slice 3b (mod the slice count).
+// Weight rows (2K bytes apart, 8 KiB at K = 4096) read at one K offset by
+// every workgroup at once concentrate on a few HBM channels; measured on
+// the 4096 x 128256 head, the staggered start takes the stream from 4.3 to
+// 6.0 TB/s (the sum is the same, in a rotated order).
+namespace nt {
+constexpr int kBN = 256;        // weight rows (output columns) per workgroup
+constexpr int kWTN = kBN / 4;   // per wave
+constexpr int kFN = kWTN / 16;  // 16-column MFMA blocks per wave
+constexpr int kBK = 64;         // K per slice
+constexpr int kNS = 4;          // LDS stages
+constexpr int kStagger = 3;     // first slice of workgroup b: kStagger * b (mod slices)
+constexpr int kRow = kBK * 2;   // bytes per LDS row (weight or X)
+constexpr int kChunks = kRow / 16;         // 16-byte chunks per row
+constexpr int kRowsPerLoad = 1024 / kRow;  // rows one 1 KiB load covers
+constexpr int kWStage = kBN * kRow;
+constexpr int kXStage = 64 * kRow;       // 64 rows of X
+constexpr int kStage = kWStage + kXStage;
+constexpr int kWLoads = kWStage / 1024 / 4;  // per wave and slice
+constexpr int kXLoads = kXStage / 1024 / 4;
+constexpr int kLoadsPerSlice = kWLoads + kXLoads;
+static_assert(kNS * kStage <= 160 * 1024, "LDS capacity");
+// 16 consecutive rows read at one logical chunk land in 16 distinct 16-byte
+// bank slots.
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (kChunks >= 16) return r & 15;
+  else return (r >> 1) & 7;
+}
+}  // namespace nt
+
+template <int MB, int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_nt(Bf16Args p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[nt::kNS * nt::kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * nt::kBN;
+
+  f32x4 acc[MB][nt::kFN];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < nt::kFN; ++j) acc[mb][j] = f32x4{};
+
+  // ---- global -> LDS: load i of wave w covers weight rows 64w + 8i ..
+  // +7 of the stripe (lane l -> row l/8, physical chunk l%8, logical chunk
+  // (l%8) ^ swz(row)); X loads cover rows 16w + 8i .. +7 the same way. ----
+  const int64_t lda2 = p.lda * 2, ldb2 = p.ldb * 2;
+  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+  const int lr = lane / nt::kChunks, lc = lane % nt::kChunks;
+  uint32_t w_off[nt::kWLoads];
+  int w_kc[nt::kWLoads];
+#pragma unroll
+  for (int i = 0; i < nt::kWLoads; ++i) {
+    const int r = nt::kWTN * wave + nt::kRowsPerLoad * i + lr;
+    const int c = lc ^ nt::swz(r);
+    w_off[i] = static_cast<uint32_t>(r * ldb2 + 16 * c);
+    w_kc[i] = 8 * c;
+  }
+  uint32_t x_off[nt::kXLoads];
+  int x_kc[nt::kXLoads];
+#pragma unroll
+  for (int i = 0; i < nt::kXLoads; ++i) {
+    const int r = 16 * wave + nt::kRowsPerLoad * i + lr;
+    const int c = lc ^ nt::swz(r);
+    x_off[i] = static_cast<uint32_t>(r * lda2 + 16 * c);
+    x_kc[i] = 8 * c;
+  }
+  const int KT = (p.K + nt::kBK - 1) / nt::kBK;
+  const int t0 = KT > 0 ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * nt::kStagger) % KT) : 0;
+  auto issue_slice = [&](int t) {
+    const uint32_t stage = smem_base + static_cast<uint32_t>((t % nt::kNS) * nt::kStage);
+    // The t-th slice walked is slice (t0 + t) mod KT; t >= KT loads nothing
+    // (k0 = K: empty windows).
+    const int k0 = t < KT ? (t0 + t < KT ? t0 + t : t0 + t - KT) * nt::kBK : p.K;
+    // Weight rows n0 .. N-1 and X rows 0 .. M-1 from column k0; rows past
+    // the ends and columns past K read zeros.
+    const i32x4 ww = make_window_words(p.B + static_cast<int64_t>(n0) * p.ldb + k0,
+                                       (static_cast<int64_t>(p.N - n0 - 1) * p.ldb + (p.K - k0)) * 2);
+#pragma unroll
+    for (int i = 0; i < nt::kWLoads; ++i)
+      buf_load16_lds(ww, stage + (nt::kWTN * wave + nt::kRowsPerLoad * i) * nt::kRow,
+                     w_off[i] | (k0 + w_kc[i] < p.K ? 0u : kOutOfRange));
+    const i32x4 wx = make_window_words(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (p.K - k0)) * 2);
+#pragma unroll
+    for (int i = 0; i < nt::kXLoads; ++i)
+      buf_load16_lds(wx, stage + nt::kWStage + (16 * wave + nt::kRowsPerLoad * i) * nt::kRow,
+                     x_off[i] | (k0 + x_kc[i] < p.K ? 0u : kOutOfRange));
+  };
+
+  // ---- LDS -> registers: operand of MFMA step u (K 32u .. 32u+31 of the
+  // slice): lane l reads row (l%16) of its block, logical chunk 4u + l/16. ----
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int w_rd = (nt::kWTN * wave + l16) * nt::kRow;  // + 16 j rows; swz(row) = swz(l16)
+  const int x_rd = nt::kWStage + l16 * nt::kRow;  // + 16 mb rows
+  const int sw = nt::swz(l16);
+
+  if (KT > 0) {
+    for (int t = 0; t < nt::kNS - 1; ++t) issue_slice(t);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((nt::kNS - 2) * nt::kLoadsPerSlice) : "memory");
+    lds_barrier();
+    for (int t = 0; t < KT; ++t) {
+      issue_slice(t + nt::kNS - 1);  // into the stage slice t-1 occupied
+      const uint8_t* base = smem + (t % nt::kNS) * nt::kStage;
+#pragma unroll
+      for (int u = 0; u < nt::kBK / 32; ++u) {
+        const int ch = ((4 * u + lq) ^ sw) * 16;
+        bf16x8 fw[nt::kFN], fx[MB];
+#pragma unroll
+        for (int j = 0; j < nt::kFN; ++j)
+          fw[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + w_rd + 16 * j * nt::kRow + ch));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          fx[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd + 16 * mb * nt::kRow + ch));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < nt::kFN; ++j)
+            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx[mb], acc[mb][j], 0, 0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((nt::kNS - 2) * nt::kLoadsPerSlice) : "memory");
+      lds_barrier();  // slice t+1 landed everywhere; slice t no longer read
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
+  }
+
+  // ---- epilogue: element e of lane l in block (mb, j) is row 16 mb + l%16,
+  // column 16 j + 4 (l/16) + e of the wave's 64 ----
+#pragma unroll
+  for (int j = 0; j < nt::kFN; ++j) {
+    const int col = n0 + nt::kWTN * wave + 16 * j + 4 * lq;
+    float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (EPI != kEpiNone) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < p.N) bias[e] = bf16_bits_to_f32(p.bias[col + e]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = 16 * mb + l16;
+      if (row >= p.M) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<EPI>(acc[mb][j][e], bias[e]);
+      store4<OUT_BF16>(p, row, col, v);
+    }
+  }
+}
+
+template <int MB, int EPI, bool OUT_BF16>
+hipError_t launch_nt_m(const Bf16Args& a, hipStream_t s) {
+  hipLaunchKernelGGL((tgemm_bf16_thin_nt<MB, EPI, OUT_BF16>), dim3((a.N + nt::kBN - 1) / nt::kBN),
+                     dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MB>
+hipError_t dispatch_nt_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s) {
+  if (out_bf16) {
+    if (epi == kEpiNone) return launch_nt_m<MB, kEpiNone, true>(a, s);
+    if (epi == kEpiBias) return launch_nt_m<MB, kEpiBias, true>(a, s);
+    return launch_nt_m<MB, kEpiBiasGelu, true>(a, s);
+  }
+  if (epi == kEpiNone) return launch_nt_m<MB, kEpiNone, false>(a, s);
+  if (epi == kEpiBias) return launch_nt_m<MB, kEpiBias, false>(a, s);
+  return launch_nt_m<MB, kEpiBiasGelu, false>(a, s);
+}
+
 // ---- LM head with bias and log-softmax over each row (GEMM compute-cost
 // page, section 7.2: the output GEMM, its bias add and the LogSoftmax that
 // follows, fused) ----
@@ -417,6 +598,18 @@ hipError_t launch_bf16_thin_lsm(const Bf16Args& a, const LsmArgs& q, int out_bf1
   else
     hipLaunchKernelGGL((tgemm_lsm_normalize<false>), grid, dim3(256), 0, s, q, a.C, a.ldc, a.N, a.vec_c);
   return hipGetLastError();
+}
+
+bool thin_nt_ok(const Bf16Args& a) {
+  return a.M <= 64 && a.vec_a && a.vec_b && a.K % 8 == 0 &&
+         a.ldb * 2 * nt::kBN < (int64_t{1} << 31) && a.lda * 2 * 64 < (int64_t{1} << 31);
+}
+
+hipError_t launch_bf16_thin_nt(const Bf16Args& a, int epi, int out_bf16, hipStream_t s) {
+  if (a.M <= 16) return dispatch_nt_epi<1>(a, epi, out_bf16, s);
+  if (a.M <= 32) return dispatch_nt_epi<2>(a, epi, out_bf16, s);
+  if (a.M <= 48) return dispatch_nt_epi<3>(a, epi, out_bf16, s);
+  return dispatch_nt_epi<4>(a, epi, out_bf16, s);
 }
 
 const char* thin_kernel_name(int M) {

@@ -78,6 +78,9 @@ hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epilogue, int out
 hipError_t launch_bf16_tiled_bt(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                                 hipStream_t stream);
 bool bf16_bt_direct_ok(const Bf16Args& a, int shape);
+// Small-M kernel for B given as [N, K] (M <= 64, aligned operands).
+hipError_t launch_bf16_thin_nt(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream);
+bool thin_nt_ok(const Bf16Args& a);
 // Register-staged kernel for operands the direct-to-LDS kernel cannot take.
 hipError_t launch_bf16_general(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                                hipStream_t stream);
