@@ -105,6 +105,37 @@ int gemm_bf16(const void* A, const void* B, const void* bias, void* C,
               int64_t lda, int64_t ldb, int64_t ldc,
               int epilogue, int out_dtype, void* stream);
 
+/* Layout of the B operand of gemm_bf16_strided_batched. */
+typedef enum {
+  TGEMM_B_KN = 0, /* B [K, N], row stride ldb >= N (as gemm_bf16) */
+  TGEMM_B_NK = 1  /* B [N, K], row stride ldb >= K (as gemm_bf16_nt) */
+} tgemm_b_layout_t;
+
+/*
+ * gemm_bf16_strided_batched -- C_z = epilogue(A_z . B_z + bias), z < batch,
+ * with A_z = A + z*stride_a, B_z = B + z*stride_b, C_z = C + z*stride_c
+ * (strides in elements; 0 shares an operand across the batch).
+ *
+ * Many same-shaped GEMMs in one launch, so that small problems together fill
+ * the GPU (the GEMM compute-cost page, section 5.3: packing independent
+ * small GEMMs into one batched call raised utilisation where single
+ * small-M calls left it low).  One bias [N] serves every problem.  Each
+ * problem follows gemm_bf16 (b_layout TGEMM_B_KN) or gemm_bf16_nt
+ * (TGEMM_B_NK) and gives the same result as that call.
+ * Invalid (TGEMM_ERR_INVALID): negative batch or strides, an unknown
+ * b_layout, batch > 1 with stride_c < (M-1)*ldc + N (outputs would
+ * overlap), and the per-problem errors.  batch > 65535, and for TGEMM_B_NK
+ * the operands gemm_bf16_nt does not support, return TGEMM_ERR_UNSUPPORTED.
+ * Vector loads are used only when strides keep every problem 16-byte
+ * aligned.  Returns TGEMM_OK, TGEMM_ERR_INVALID, TGEMM_ERR_UNSUPPORTED or
+ * TGEMM_ERR_LAUNCH.
+ */
+int gemm_bf16_strided_batched(const void* A, const void* B, const void* bias, void* C,
+                              int64_t M, int64_t N, int64_t K,
+                              int64_t lda, int64_t ldb, int64_t ldc,
+                              int64_t stride_a, int64_t stride_b, int64_t stride_c, int64_t batch,
+                              int b_layout, int epilogue, int out_dtype, void* stream);
+
 /*
  * gemm_bf16_nt -- C = epilogue(A . Bt^T + bias): gemm_bf16 with the weight
  * given K-contiguous, Bt [N, K] row-major (row stride ldb >= K elements),

@@ -181,3 +181,22 @@ def test_nt_validation():
     assert binding.gemm_bf16_nt_kernel_name(1, 128256, 4096) == "tgemm_bf16_thin_nt_m16"
     assert binding.gemm_bf16_nt_kernel_name(64, 128256, 4096) == "tgemm_bf16_thin_nt_m64"
     assert binding.gemm_bf16_nt_kernel_name(65, 128256, 4096).startswith("tgemm_bf16_tiled_bt")
+
+
+def test_strided_batched_validation():
+    L = binding.lib()
+
+    def call(A=FAKE, B=FAKE, bias=NULL, C=FAKE, M=64, N=64, K=64, lda=64, ldb=64, ldc=64, sa=4096,
+             sb=4096, sc=4096, batch=3, layout=0, epi=0, out=1):
+        return L.gemm_bf16_strided_batched(A, B, bias, C, M, N, K, lda, ldb, ldc, sa, sb, sc, batch,
+                                           layout, epi, out, NULL)
+
+    assert call(batch=-1) == INV
+    assert call(sa=-1) == INV and call(sb=-8) == INV and call(sc=-8) == INV
+    assert call(layout=2) == INV
+    assert call(sc=64 * 63) == INV                     # outputs of problems 0 and 1 overlap
+    assert call(batch=0) == OK and call(M=0) == OK
+    assert call(batch=70000) == UNS
+    assert call(layout=1, K=60, lda=64, ldb=64) == UNS  # [N, K] weights need K % 8 == 0
+    assert call(C=NULL) == INV
+    assert call(sa=1 << 61, batch=8) == INV            # whole-batch extent overflows

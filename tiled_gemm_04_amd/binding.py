@@ -31,6 +31,9 @@ EPI_BIAS_GELU_TANH = 2
 OUT_F32 = 0
 OUT_BF16 = 1
 
+B_KN = 0  # B [K, N]
+B_NK = 1  # B [N, K]
+
 ALGO_AUTO = 0
 ALGO_TILED = 1
 ALGO_THIN = 2
@@ -66,6 +69,9 @@ def lib():
     L.gemm_bf16_w8.restype = i32
     L.gemm_w8_kernel_name.argtypes = [i64, i64, i64]
     L.gemm_w8_kernel_name.restype = ctypes.c_char_p
+    L.gemm_bf16_strided_batched.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                            i64, i32, i32, i32, vp]
+    L.gemm_bf16_strided_batched.restype = i32
     L.gemm_bf16_nt.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
     L.gemm_bf16_nt.restype = i32
     L.gemm_bf16_nt_kernel_name.argtypes = [i64, i64, i64]
@@ -184,6 +190,44 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
                                     _stream_ptr(stream))
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_fp8_blockscaled")
+    return C
+
+
+def _batch_stride(t):
+    return t.stride(0) if t.shape[0] > 1 else 0
+
+
+def gemm_bf16_strided_batched(A, B, bias, C, b_layout=B_KN, epilogue=EPI_NONE, stream=None):
+    """C[z] = epilogue(A[z] @ B[z] + bias) for every z of a batch, one launch.
+
+    A: bfloat16 [batch, M, K]; B: bfloat16 [batch, K, N] (b_layout B_KN) or
+    [batch, N, K] (B_NK, the product is then A[z] @ B[z].T); C: bfloat16 or
+    float32 [batch, M, N]; each matrix with unit inner stride, any row and
+    batch strides (an expanded tensor, batch stride 0, shares an operand).
+    """
+    _check_cuda(A, B, bias, C)
+    if A.dim() != 3 or B.dim() != 3 or C.dim() != 3:
+        raise ValueError("A, B and C must be 3-D [batch, rows, cols]")
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("A and B must be bfloat16")
+    if C.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("C must be bfloat16 or float32")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    batch, M, K = A.shape
+    if b_layout == B_KN:
+        K2, N = B.shape[1:]
+    else:
+        N, K2 = B.shape[1:]
+    if K2 != K or tuple(C.shape) != (batch, M, N) or B.shape[0] != batch:
+        raise ValueError("shape mismatch")
+    lda, ldb, ldc = _row_major(A[0], "A"), _row_major(B[0], "B"), _row_major(C[0], "C")
+    out = OUT_BF16 if C.dtype == torch.bfloat16 else OUT_F32
+    st = lib().gemm_bf16_strided_batched(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K, lda, ldb, ldc,
+                                         _batch_stride(A), _batch_stride(B), _batch_stride(C), batch,
+                                         int(b_layout), int(epilogue), out, _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_bf16_strided_batched")
     return C
 
 

@@ -225,6 +225,72 @@ const char* gemm_bf16_nt_kernel_name(int64_t M, int64_t N, int64_t K) {
   return shape >= 0 && shape < tgemm::kNumTiledShapes ? kNames[shape] : nullptr;
 }
 
+int gemm_bf16_strided_batched(const void* A, const void* B, const void* bias, void* C, int64_t M,
+                              int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                              int64_t stride_a, int64_t stride_b, int64_t stride_c, int64_t batch,
+                              int b_layout, int epilogue, int out_dtype, void* stream) {
+  if (b_layout != TGEMM_B_KN && b_layout != TGEMM_B_NK) return TGEMM_ERR_INVALID;
+  const bool nk = b_layout == TGEMM_B_NK;
+  // One problem's rules (B as [K, N] or [N, K]).
+  const int st = validate_bf16(A, B, bias, C, M, N, K, lda, nk ? (N > 0 ? N : 1) : ldb, ldc, epilogue,
+                               out_dtype, TGEMM_ALGO_AUTO);
+  if (st != TGEMM_OK) return st;
+  if (nk && (ldb < K || ldb < 1 || !extent_ok(N, K, ldb))) return TGEMM_ERR_INVALID;
+  if (batch < 0 || stride_a < 0 || stride_b < 0 || stride_c < 0) return TGEMM_ERR_INVALID;
+  if (batch == 0 || M == 0 || N == 0) return TGEMM_OK;
+  // Whole-batch extents, and no two problems writing the same output.
+  constexpr int64_t kLimit = int64_t{1} << 62;
+  const int64_t ext_a = (M - 1) * lda + K, ext_b = nk ? (N - 1) * ldb + K : (K - 1) * ldb + N;
+  const int64_t ext_c = (M - 1) * ldc + N;
+  auto fits = [&](int64_t stride, int64_t ext) {
+    return stride == 0 || batch - 1 <= (kLimit - ext) / stride;
+  };
+  if (!fits(stride_a, K > 0 ? ext_a : 0) || !fits(stride_b, K > 0 ? ext_b : 0) || !fits(stride_c, ext_c))
+    return TGEMM_ERR_INVALID;
+  if (batch > 1 && stride_c < ext_c) return TGEMM_ERR_INVALID;
+  if (batch > 65535) return TGEMM_ERR_UNSUPPORTED;
+
+  Bf16Args a;
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.sa = stride_a;
+  a.sb = stride_b;
+  a.sc = stride_c;
+  a.batch = static_cast<int>(batch);
+  // Vector paths need every problem's base aligned like the first one's.
+  const bool multi = batch > 1;
+  a.vec_a = (K == 0 || (aligned16(A) && lda % 8 == 0 && (!multi || stride_a % 8 == 0))) ? 1 : 0;
+  a.vec_b = (K == 0 || (aligned16(B) && ldb % 8 == 0 && (!multi || stride_b % 8 == 0))) ? 1 : 0;
+  const int64_t out_align = out_dtype == TGEMM_OUT_BF16 ? 8 : 4;
+  a.vec_c = (aligned16(C) && ldc % out_align == 0 && (!multi || stride_c % out_align == 0)) ? 1 : 0;
+
+  const int out_bf16 = out_dtype == TGEMM_OUT_BF16 ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (nk) {
+    if (use_thin(M, TGEMM_ALGO_AUTO) && tgemm::thin_nt_ok(a)) {
+      e = tgemm::launch_bf16_thin_nt(a, epilogue, out_bf16, s);
+    } else {
+      const int shape = pick_tiled_shape(M, N);
+      if (!tgemm::bf16_bt_direct_ok(a, shape)) return TGEMM_ERR_UNSUPPORTED;
+      e = tgemm::launch_bf16_tiled_bt(a, shape, epilogue, out_bf16, s);
+    }
+  } else if (use_thin(M, TGEMM_ALGO_AUTO)) {
+    e = tgemm::launch_bf16_thin(a, epilogue, out_bf16, s);
+  } else {
+    e = tgemm::launch_bf16_tiled(a, pick_tiled_shape(M, N), epilogue, out_bf16, s);
+  }
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
 int gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
               int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
               void* stream) {

@@ -77,6 +77,7 @@ __device__ __forceinline__ u32x4 transpose_col(const u32x4 (&r)[8], int j) {
 template <class T, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_general(Bf16Args p, int tiles_m,
                                                                 int tiles_n) {
+  apply_batch(p, OUT_BF16 ? 2 : 4);
   __shared__ u32x4 smem[T::LDS_SLOTS];
   u32x4* sA = smem;                   // [2][8 chunks][BM]
   u32x4* sB = smem + 2 * T::A_STAGE;  // [2][8 chunks][BN]
@@ -286,7 +287,7 @@ template <class T, int EPI, bool OUT_BF16>
 hipError_t launch_t(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + T::BM - 1) / T::BM;
   const int tiles_n = (a.N + T::BN - 1) / T::BN;
-  hipLaunchKernelGGL((tgemm_bf16_general<T, EPI, OUT_BF16>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((tgemm_bf16_general<T, EPI, OUT_BF16>), dim3(tiles_m * tiles_n, a.batch),
                      dim3(kThreads), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }

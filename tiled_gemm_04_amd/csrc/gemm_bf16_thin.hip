@@ -169,6 +169,7 @@ __device__ __forceinline__ void store4(const Bf16Args& p, int row, int col, cons
 
 template <int MB, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
+  apply_batch(p, OUT_BF16 ? 2 : 4);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
   f32x4 acc[MB][kFN];
   thin_accumulate<MB>(p, smem, acc);
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
 
 template <int MB, int EPI, bool OUT_BF16>
 hipError_t launch_m(const Bf16Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16>), dim3((a.N + kBN - 1) / kBN),
+  hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16>), dim3((a.N + kBN - 1) / kBN, a.batch),
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -262,6 +263,7 @@ __device__ __forceinline__ int swz(int r) {
 
 template <int MB, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_nt(Bf16Args p) {
+  apply_batch(p, OUT_BF16 ? 2 : 4);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[nt::kNS * nt::kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_nt(Bf16Args p) {
 
 template <int MB, int EPI, bool OUT_BF16>
 hipError_t launch_nt_m(const Bf16Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((tgemm_bf16_thin_nt<MB, EPI, OUT_BF16>), dim3((a.N + nt::kBN - 1) / nt::kBN),
+  hipLaunchKernelGGL((tgemm_bf16_thin_nt<MB, EPI, OUT_BF16>), dim3((a.N + nt::kBN - 1) / nt::kBN, a.batch),
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

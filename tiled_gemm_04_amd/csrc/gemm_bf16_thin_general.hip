@@ -67,6 +67,7 @@ struct Stage {
 
 template <int MB, int EPI, bool OUT_BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void tgemm_bf16_thin(Bf16Args p) {
+  apply_batch(p, OUT_BF16 ? 2 : 4);
   __shared__ float red[4 * 16 * kRedStride];
 
   const int tid = threadIdx.x;
@@ -201,11 +202,11 @@ hipError_t launch_m(const Bf16Args& a, hipStream_t s) {
   const bool vec = a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
                    a.lda * 2 * 64 < (int64_t{1} << 31) && a.ldb * 2 * kStepK < (int64_t{1} << 31);
   if (vec) {
-    hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16, true>), dim3(grid), dim3(kThreads), 0, s,
-                       a);
+    hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16, true>), dim3(grid, a.batch), dim3(kThreads),
+                       0, s, a);
   } else {
-    hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16, false>), dim3(grid), dim3(kThreads), 0,
-                       s, a);
+    hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16, false>), dim3(grid, a.batch), dim3(kThreads),
+                       0, s, a);
   }
   return hipGetLastError();
 }

@@ -178,6 +178,7 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], flo
 template <class C, bool BT, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
                                                                 int tiles_n) {
+  apply_batch(p, OUT_BF16 ? 2 : 4);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -413,7 +414,7 @@ template <class C, bool BT, int EPI, bool OUT_BF16>
 hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
   const int tiles_n = (a.N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16>), dim3(tiles_m * tiles_n, a.batch),
                      dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }

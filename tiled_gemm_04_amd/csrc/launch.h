@@ -18,7 +18,20 @@ struct Bf16Args {
   int vec_a;  // 1: A rows may be read with 16-byte loads (aligned base, lda % 8 == 0)
   int vec_b;  // 1: same for B
   int vec_c;  // 1: C rows may be written with 16-byte stores
+  // Strided batch: problem z (grid y) reads A + z*sa, B + z*sb and writes
+  // C + z*sc (elements); a single problem has batch 1.
+  int64_t sa = 0, sb = 0, sc = 0;
+  int batch = 1;
 };
+
+// Moves p to problem blockIdx.y of a strided batch (C elements of
+// out_bytes bytes).
+__device__ __forceinline__ void apply_batch(Bf16Args& p, int out_bytes) {
+  const int64_t z = blockIdx.y;
+  p.A += z * p.sa;
+  p.B += z * p.sb;
+  p.C = static_cast<char*>(p.C) + z * p.sc * out_bytes;
+}
 
 struct Fp8Args {
   const uint8_t* A;
