@@ -76,7 +76,12 @@ typedef enum {
 typedef enum {
     TGEMM_ALGO_AUTO = 0,   /* thin-M kernel for M <= 64, tiled kernel otherwise */
     TGEMM_ALGO_TILED = 1,  /* LDS-tiled MFMA kernel, any shape                  */
-    TGEMM_ALGO_THIN = 2    /* bandwidth-bound small-M kernel, requires M <= 64  */
+    TGEMM_ALGO_THIN = 2,   /* bandwidth-bound small-M kernel, requires M <= 64  */
+    /* The tiled kernel with a fixed tile shape (the offline autotune sweep
+     * times each against the automatic choice). */
+    TGEMM_ALGO_TILED_256x256 = 3,
+    TGEMM_ALGO_TILED_256x128 = 4,
+    TGEMM_ALGO_TILED_128x128 = 5
 } tgemm_algo_t;
 
 /*

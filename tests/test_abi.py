@@ -55,7 +55,7 @@ def _bf16(A=FAKE, B=FAKE, bias=FAKE, C=FAKE, M=64, N=64, K=64, lda=64, ldb=64, l
     (dict(epi=3), INV), (dict(epi=-1), INV), (dict(out=2), INV),
     (dict(epi=1, bias=NULL), INV), (dict(epi=2, bias=NULL), INV),
     (dict(lda=63), INV), (dict(ldb=10), INV), (dict(ldc=0), INV),
-    (dict(algo=3), INV), (dict(algo=2, M=65), UNS),
+    (dict(algo=6), INV), (dict(algo=2, M=65), UNS),
     (dict(M=0), OK), (dict(N=0, ldb=1, ldc=1), OK), (dict(M=0, A=NULL, C=NULL), OK),
 ])
 def test_bf16_validation(kw, status):
@@ -132,6 +132,9 @@ def test_kernel_selection_table():
     assert name(64, 64, 64, algo=binding.ALGO_TILED).startswith("tgemm_bf16_tiled")
     assert name(65, 64, 64, algo=binding.ALGO_THIN) is None
     assert name(-1, 64, 64) is None
+    assert name(4096, 4096, 4096, algo=binding.ALGO_TILED_128x128) == "tgemm_bf16_tiled_128x128x64"
+    assert name(4096, 4096, 4096, algo=binding.ALGO_TILED_256x128) == "tgemm_bf16_tiled_256x128x64"
+    assert name(64, 64, 64, algo=binding.ALGO_TILED_256x256) == "tgemm_bf16_tiled_256x256x32"
     assert binding.gemm_fp8_kernel_name(4096, 14336, 4096) == "tgemm_fp8_bs_256x256x128"
     assert binding.gemm_fp8_kernel_name(4097, 14335, 4096) == "tgemm_fp8_bs_256x256x128"
     assert binding.gemm_fp8_kernel_name(64, 64, 200).startswith("tgemm_fp8_bs_general")

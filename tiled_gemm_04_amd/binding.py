@@ -37,6 +37,9 @@ B_NK = 1  # B [N, K]
 ALGO_AUTO = 0
 ALGO_TILED = 1
 ALGO_THIN = 2
+ALGO_TILED_256x256 = 3
+ALGO_TILED_256x128 = 4
+ALGO_TILED_128x128 = 5
 
 _lib = None
 

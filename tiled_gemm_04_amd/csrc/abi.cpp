@@ -11,6 +11,10 @@
 #include "../../include/tgemm.h"
 #include "launch.h"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 using tgemm::Bf16Args;
 using tgemm::Fp8Args;
 
@@ -37,7 +41,7 @@ int validate_bf16(const void* A, const void* B, const void* bias, const void* C,
     return TGEMM_ERR_INVALID;
   if (epilogue < TGEMM_EPI_NONE || epilogue > TGEMM_EPI_BIAS_GELU_TANH) return TGEMM_ERR_INVALID;
   if (out_dtype != TGEMM_OUT_F32 && out_dtype != TGEMM_OUT_BF16) return TGEMM_ERR_INVALID;
-  if (algo < TGEMM_ALGO_AUTO || algo > TGEMM_ALGO_THIN) return TGEMM_ERR_INVALID;
+  if (algo < TGEMM_ALGO_AUTO || algo > TGEMM_ALGO_TILED_128x128) return TGEMM_ERR_INVALID;
   if (lda < K || ldb < N || ldc < N) return TGEMM_ERR_INVALID;
   if (lda < 1 || ldb < 1 || ldc < 1) return TGEMM_ERR_INVALID;
   if (!extent_ok(M, K, lda) || !extent_ok(K, N, ldb) || !extent_ok(M, N, ldc))
@@ -52,7 +56,11 @@ int validate_bf16(const void* A, const void* B, const void* bias, const void* C,
 
 // Shape-to-kernel table for the tiled family.  A launch wants at least one
 // full round of 256 workgroups (one per compute unit) and few idle units in
-// its last round; bigger tiles re-read less and run closer to the MFMA peak.
+// its last round; bigger tiles re-read less and run closer to the MFMA peak,
+// but only the part of a tile inside C is useful work (a 256-row tile at
+// M = 128 computes half padding).  Score = fill of the rounds x useful
+// fraction of the tiles' area x the shape's measured efficiency; checked by
+// the offline autotune sweep (tiled_gemm_04_amd/autotune.py).
 int pick_tiled_shape(int64_t M, int64_t N) {
   static const double kTileEfficiency[tgemm::kNumTiledShapes] = {1.0, 0.86, 0.62};
   constexpr int64_t kCUs = 256;
@@ -60,10 +68,13 @@ int pick_tiled_shape(int64_t M, int64_t N) {
   double best_score = -1.0;
   for (int s = 0; s < tgemm::kNumTiledShapes; ++s) {
     const tgemm::TiledShapeInfo info = tgemm::tiled_shape_info(s);
-    const int64_t tiles = ((M + info.bm - 1) / info.bm) * ((N + info.bn - 1) / info.bn);
+    const int64_t tm = (M + info.bm - 1) / info.bm, tn = (N + info.bn - 1) / info.bn;
+    const int64_t tiles = tm * tn;
     const int64_t rounds = (tiles + kCUs - 1) / kCUs;
     const double fill = static_cast<double>(tiles) / static_cast<double>(rounds * kCUs);
-    const double score = fill * kTileEfficiency[s];
+    const double useful = (static_cast<double>(M) / static_cast<double>(tm * info.bm)) *
+                          (static_cast<double>(N) / static_cast<double>(tn * info.bn));
+    const double score = fill * useful * kTileEfficiency[s];
     if (score > best_score + 1e-9) {
       best_score = score;
       best = s;
@@ -72,9 +83,19 @@ int pick_tiled_shape(int64_t M, int64_t N) {
   return best;
 }
 
+// Tile shape for the tiled family: fixed by the algo, else the table below.
+int tiled_shape_for(int64_t M, int64_t N, int algo) {
+  switch (algo) {
+    case TGEMM_ALGO_TILED_256x256: return tgemm::kTile256x256;
+    case TGEMM_ALGO_TILED_256x128: return tgemm::kTile256x128;
+    case TGEMM_ALGO_TILED_128x128: return tgemm::kTile128x128;
+    default: return pick_tiled_shape(M, N);
+  }
+}
+
 bool use_thin(int64_t M, int algo) {
   if (algo == TGEMM_ALGO_THIN) return true;
-  if (algo == TGEMM_ALGO_TILED) return false;
+  if (algo != TGEMM_ALGO_AUTO) return false;  // the tiled family, any tile shape
   return M <= kThinMaxM;
 }
 
@@ -138,6 +159,37 @@ int quantize_fp8(const void* X, void* Q, float* S, int64_t rows, int64_t cols, i
 
 }  // namespace
 
+namespace tgemm {
+
+void* device_scratch(size_t bytes, hipStream_t stream) {
+  struct Buf {
+    void* ptr = nullptr;
+    size_t cap = 0;
+  };
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, Buf> bufs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  Buf& b = bufs[{dev, stream}];
+  if (b.cap < bytes) {
+    // hipFree waits for the device, so no queued kernel still uses the old
+    // buffer.
+    if (b.ptr != nullptr && hipFree(b.ptr) != hipSuccess) return nullptr;
+    b.ptr = nullptr;
+    b.cap = 0;
+    const size_t want = bytes + bytes / 4;
+    if (hipMalloc(&b.ptr, want) != hipSuccess) {
+      b.ptr = nullptr;
+      return nullptr;
+    }
+    b.cap = want;
+  }
+  return b.ptr;
+}
+
+}  // namespace tgemm
+
 extern "C" {
 
 int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
@@ -169,7 +221,7 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C, int64_
   if (use_thin(M, algo)) {
     e = tgemm::launch_bf16_thin(a, epilogue, out_bf16, s);
   } else {
-    e = tgemm::launch_bf16_tiled(a, pick_tiled_shape(M, N), epilogue, out_bf16, s);
+    e = tgemm::launch_bf16_tiled(a, tiled_shape_for(M, N, algo), epilogue, out_bf16, s);
   }
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
@@ -413,7 +465,7 @@ const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue,
                     out_dtype, algo) != TGEMM_OK)
     return nullptr;
   if (use_thin(M, algo)) return tgemm::thin_kernel_name(static_cast<int>(M));
-  return tgemm::tiled_shape_info(pick_tiled_shape(M, N)).name;
+  return tgemm::tiled_shape_info(tiled_shape_for(M, N, algo)).name;
 }
 
 const char* gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K) {

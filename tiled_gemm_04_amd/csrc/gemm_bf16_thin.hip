@@ -54,10 +54,13 @@ __device__ __forceinline__ int x_swz(int r) { return (r >> 2) & 3; }
 // Streams the workgroup's 512-column stripe of W once and leaves the
 // products in acc[mb][j] (16 x 16 blocks, transposed by the operand swap:
 // element e of lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the
-// wave's 128).  Ends with every load landed; the caller synchronises the
-// workgroup before reusing smem.
+// wave's 128).  Slices [tb, te) of K (te < 0: through the last) are summed;
+// the end of the range acts as K, so nothing past it is loaded.  Ends with
+// every load landed; the caller synchronises the workgroup before reusing
+// smem.
 template <int MB>
-__device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem, f32x4 (&acc)[MB][kFN]) {
+__device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem, f32x4 (&acc)[MB][kFN],
+                                                int tb = 0, int te = -1) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -76,11 +79,14 @@ __device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem
   const int xr = lane >> 2;
   const int xc = (lane & 3) ^ x_swz(xr);
   const uint32_t x_off = static_cast<uint32_t>((16 * wave + xr) * lda2 + 16 * xc);
+  const int KT = (p.K + kBK - 1) / kBK;
+  if (te < 0) te = KT;
+  const int kend = p.K < te * kBK ? p.K : te * kBK;  // this range's end of K
   auto issue_slice = [&](int t) {
     const int stage = t % kNS;
     const int k0 = t * kBK;
     const i32x4 ww = make_window_words(p.B + static_cast<int64_t>(k0) * p.ldb + n0,
-                                       (static_cast<int64_t>(p.K - k0 - 1) * p.ldb + (p.N - n0)) * 2);
+                                       (static_cast<int64_t>(kend - k0 - 1) * p.ldb + (p.N - n0)) * 2);
 #pragma unroll
     for (int i = 0; i < kBK / 4; ++i) {
       const int k = 8 * wave + i;
@@ -88,9 +94,9 @@ __device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem
       buf_load16_lds(ww, smem_base + stage * kStage + k * kWRow,
                      static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange));
     }
-    const i32x4 wx = make_window_words(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (p.K - k0)) * 2);
+    const i32x4 wx = make_window_words(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (kend - k0)) * 2);
     buf_load16_lds(wx, smem_base + stage * kStage + kWStage + wave * 1024,
-                   x_off | (k0 + 8 * xc < p.K ? 0u : kOutOfRange));
+                   x_off | (k0 + 8 * xc < kend ? 0u : kOutOfRange));
   };
 
   // ---- LDS -> registers ----
@@ -109,12 +115,11 @@ __device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem
   const int xrow = lane & 15;
   const int x_rd = kWStage + xrow * 64 + (((lane >> 4) ^ x_swz(xrow)) * 16);
 
-  const int KT = (p.K + kBK - 1) / kBK;
-  if (KT > 0) {
-    for (int t = 0; t < kNS - 1; ++t) issue_slice(t);
+  if (te > tb) {
+    for (int t = tb; t < tb + kNS - 1; ++t) issue_slice(t);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kNS - 2) * kLoadsPerSlice) : "memory");
     lds_barrier();
-    for (int t = 0; t < KT; ++t) {
+    for (int t = tb; t < te; ++t) {
       issue_slice(t + kNS - 1);  // into the stage slice t-1 occupied
       const uint8_t* base = smem + (t % kNS) * kStage;
       bf16x8 fb[kFN], fx[MB];
@@ -216,6 +221,112 @@ hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s)
   if (epi == kEpiNone) return launch_m<MB, kEpiNone, false>(a, s);
   if (epi == kEpiBias) return launch_m<MB, kEpiBias, false>(a, s);
   return launch_m<MB, kEpiBiasGelu, false>(a, s);
+}
+
+// ---- Split-K for small M and few column stripes ----
+//
+// With N = 4096 the thin kernel has only 8 workgroups for 256 compute units,
+// and the weight stream stalls at a few percent of HBM bandwidth (any N
+// below 256 stripes leaves units idle).  The K
+// range is then cut into S chunks (grid z): workgroup (stripe, s) sums
+// slices [s*KTc, (s+1)*KTc) and writes its fp32 partial tile to
+// part[s][M][N]; a second kernel adds the S partials in order of s, then
+// the bias and the epilogue, and rounds once -- deterministic, no atomics.
+template <int MB>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_splitk(Bf16Args p, float* part, int ktc) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
+  f32x4 acc[MB][kFN];
+  const int KT = (p.K + kBK - 1) / kBK;
+  const int tb = blockIdx.z * ktc;
+  const int te = tb + ktc < KT ? tb + ktc : KT;
+  thin_accumulate<MB>(p, smem, acc, tb, te);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kBN;
+  Bf16Args pp = p;
+  pp.C = part + static_cast<int64_t>(blockIdx.z) * p.M * p.N;
+  pp.ldc = p.N;
+  pp.vec_c = (p.N % 4) == 0 ? 1 : 0;
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int col = n0 + kWTN * wave + 16 * j + 4 * (lane >> 4);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = 16 * mb + (lane & 15);
+      if (row >= p.M) continue;
+      const float v[4] = {acc[mb][j][0], acc[mb][j][1], acc[mb][j][2], acc[mb][j][3]};
+      store4<false>(pp, row, col, v);
+    }
+  }
+}
+
+// Thread t of workgroup x handles the 4 outputs 4 (256 x + t) .. +3 of the
+// row-major M x N result.
+template <int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(256) void tgemm_splitk_reduce(Bf16Args p, const float* part, int S) {
+  const int64_t i = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+  const int64_t MN = static_cast<int64_t>(p.M) * p.N;
+  if (i >= MN) return;
+  const int row = static_cast<int>(i / p.N);
+  const int col = static_cast<int>(i % p.N);
+  // A 4-group never straddles rows when N % 4 == 0; otherwise go element-wise.
+  const bool quad = (p.N % 4) == 0;
+  float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < S; ++s) {
+    const float* q = part + static_cast<int64_t>(s) * MN + i;
+    if (quad) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i + e < MN) sum[e] += q[e];
+    }
+  }
+  if (quad) {
+    float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (EPI != kEpiNone) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bias[e] = bf16_bits_to_f32(p.bias[col + e]);
+    }
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<EPI>(sum[e], bias[e]);
+    store4<OUT_BF16>(p, row, col, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i + e >= MN) break;
+      const int r = static_cast<int>((i + e) / p.N), c = static_cast<int>((i + e) % p.N);
+      const float b = EPI != kEpiNone ? bf16_bits_to_f32(p.bias[c]) : 0.0f;
+      const float v = apply_epilogue<EPI>(sum[e], b);
+      const int64_t off = static_cast<int64_t>(r) * p.ldc + c;
+      if constexpr (OUT_BF16) static_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
+      else static_cast<float*>(p.C)[off] = v;
+    }
+  }
+}
+
+template <int MB>
+hipError_t launch_splitk_m(const Bf16Args& a, float* part, int S, int ktc, int epi, int out_bf16,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((tgemm_bf16_thin_splitk<MB>), dim3((a.N + kBN - 1) / kBN, 1, S), dim3(kThreads), 0, s,
+                     a, part, ktc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t quads = (static_cast<int64_t>(a.M) * a.N + 3) / 4;
+  const dim3 grid(static_cast<unsigned>((quads + 255) / 256));
+  if (out_bf16) {
+    if (epi == kEpiNone) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiNone, true>), grid, dim3(256), 0, s, a, part, S);
+    else if (epi == kEpiBias) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBias, true>), grid, dim3(256), 0, s, a, part, S);
+    else hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBiasGelu, true>), grid, dim3(256), 0, s, a, part, S);
+  } else {
+    if (epi == kEpiNone) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiNone, false>), grid, dim3(256), 0, s, a, part, S);
+    else if (epi == kEpiBias) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBias, false>), grid, dim3(256), 0, s, a, part, S);
+    else hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBiasGelu, false>), grid, dim3(256), 0, s, a, part, S);
+  }
+  return hipGetLastError();
 }
 
 // ---- Small-M GEMM with K-contiguous weights, Wt [N, K] (the nn.Linear
@@ -602,6 +713,33 @@ hipError_t launch_bf16_thin_lsm(const Bf16Args& a, const LsmArgs& q, int out_bf1
   return hipGetLastError();
 }
 
+ThinSplit thin_split_plan(int64_t M, int64_t N, int64_t K) {
+  // Enough (stripe, chunk) workgroups to cover the compute units, chunks of
+  // at least 4 slices, and partial traffic (2 S M N fp32) at most half the
+  // weight's bytes (2 K N): S <= K / (8 M).
+  ThinSplit r{1, 0};
+  const int64_t stripes = (N + kBN - 1) / kBN;
+  const int64_t KT = (K + kBK - 1) / kBK;
+  if (M < 1 || stripes >= 256 || KT < 8) return r;
+  int64_t S = (256 + stripes - 1) / stripes;
+  S = S < KT / 4 ? S : KT / 4;
+  const int64_t cap = K / (8 * M);
+  S = S < cap ? S : cap;
+  if (S < 2) return r;
+  const int64_t ktc = (KT + S - 1) / S;
+  r.S = static_cast<int>((KT + ktc - 1) / ktc);
+  r.ktc = static_cast<int>(ktc);
+  return r;
+}
+
+hipError_t launch_bf16_thin_splitk(const Bf16Args& a, const ThinSplit& plan, float* part, int epi,
+                                   int out_bf16, hipStream_t s) {
+  if (a.M <= 16) return launch_splitk_m<1>(a, part, plan.S, plan.ktc, epi, out_bf16, s);
+  if (a.M <= 32) return launch_splitk_m<2>(a, part, plan.S, plan.ktc, epi, out_bf16, s);
+  if (a.M <= 48) return launch_splitk_m<3>(a, part, plan.S, plan.ktc, epi, out_bf16, s);
+  return launch_splitk_m<4>(a, part, plan.S, plan.ktc, epi, out_bf16, s);
+}
+
 bool thin_nt_ok(const Bf16Args& a) {
   return a.M <= 64 && a.vec_a && a.vec_b && a.K % 8 == 0 &&
          a.ldb * 2 * nt::kBN < (int64_t{1} << 31) && a.lda * 2 * 64 < (int64_t{1} << 31);
@@ -627,6 +765,14 @@ hipError_t launch_bf16_thin(const Bf16Args& a, int epi, int out_bf16, hipStream_
   const bool direct = a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
                       a.ldb * 2 * kBK < (int64_t{1} << 31) && a.lda * 2 * 64 < (int64_t{1} << 31);
   if (!direct) return launch_bf16_thin_general(a, epi, out_bf16, s);
+  if (a.batch == 1) {
+    const ThinSplit plan = thin_split_plan(a.M, a.N, a.K);
+    if (plan.S > 1) {
+      float* part = static_cast<float*>(
+          device_scratch(static_cast<size_t>(plan.S) * a.M * a.N * sizeof(float), s));
+      if (part != nullptr) return launch_bf16_thin_splitk(a, plan, part, epi, out_bf16, s);
+    }
+  }
   if (a.M <= 16) return dispatch_epi<1>(a, epi, out_bf16, s);
   if (a.M <= 32) return dispatch_epi<2>(a, epi, out_bf16, s);
   if (a.M <= 48) return dispatch_epi<3>(a, epi, out_bf16, s);

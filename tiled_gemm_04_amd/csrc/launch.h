@@ -98,6 +98,19 @@ bool thin_nt_ok(const Bf16Args& a);
 hipError_t launch_bf16_general(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                                hipStream_t stream);
 hipError_t launch_bf16_thin(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream);
+// Split-K for the thin kernel: S chunks of ktc slices (S == 1: no split).
+struct ThinSplit {
+  int S;
+  int ktc;
+};
+ThinSplit thin_split_plan(int64_t M, int64_t N, int64_t K);
+// part: S * M * N fp32 of device scratch.
+hipError_t launch_bf16_thin_splitk(const Bf16Args& a, const ThinSplit& plan, float* part, int epilogue,
+                                   int out_bf16, hipStream_t stream);
+// Library-owned device scratch of at least `bytes` for work on `stream` of
+// the current device (one buffer per device and stream, grown on demand,
+// kept until the process ends); nullptr if it cannot be allocated.
+void* device_scratch(size_t bytes, hipStream_t stream);
 // Register-transposing thin kernel for operands the direct-to-LDS one cannot take.
 hipError_t launch_bf16_thin_general(const Bf16Args& a, int epilogue, int out_bf16,
                                     hipStream_t stream);
