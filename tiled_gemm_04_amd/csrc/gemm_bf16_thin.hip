@@ -226,8 +226,8 @@ hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s)
 // ---- Split-K for small M and few column stripes ----
 //
 // With N = 4096 the thin kernel has only 8 workgroups for 256 compute units,
-// and the weight stream stalls at a few percent of HBM bandwidth (any N
-// below 256 stripes leaves units idle).  The K
+// and the weight stream stalls at a few percent of HBM bandwidth (up to
+// 128 stripes, half the units or more sit idle).  The K
 // range is then cut into S chunks (grid z): workgroup (stripe, s) sums
 // slices [s*KTc, (s+1)*KTc) and writes its fp32 partial tile to
 // part[s][M][N]; a second kernel adds the S partials in order of s, then
@@ -720,7 +720,7 @@ ThinSplit thin_split_plan(int64_t M, int64_t N, int64_t K) {
   ThinSplit r{1, 0};
   const int64_t stripes = (N + kBN - 1) / kBN;
   const int64_t KT = (K + kBK - 1) / kBK;
-  if (M < 1 || stripes >= 256 || KT < 8) return r;
+  if (M < 1 || stripes > 128 || KT < 8) return r;  // over half the units busy: no split
   int64_t S = (256 + stripes - 1) / stripes;
   S = S < KT / 4 ? S : KT / 4;
   const int64_t cap = K / (8 * M);
