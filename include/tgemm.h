@@ -21,9 +21,16 @@
  *           indexing of the DeepGEMM page, section 3.2).  The inner stride is
  *           always 1.
  * Memory.   All pointers are device pointers owned by the caller.  The
- *           library never allocates, frees or keeps them, and holds no
- *           mutable global state; calls from several host threads are safe.
- *           C must not overlap A, B, bias or the scale arrays (not checked).
+ *           library never allocates, frees or keeps them.  Two paths use
+ *           library-owned device scratch instead (split-K of the small-M
+ *           bf16 kernel; the split last round of gemm_fp8_blockscaled): one
+ *           buffer per device, stream and purpose, allocated on first use,
+ *           grown on demand and kept until the process ends, so the first
+ *           such call on a stream allocates (do not make it under graph
+ *           capture).  The scratch table is guarded by a lock; calls from
+ *           several host threads are safe, and calls on one stream
+ *           serialise on it.  C must not overlap A, B, bias or the scale
+ *           arrays (not checked).
  * Streams.  `stream` is a hipStream_t passed as void*; NULL is the default
  *           stream.  Calls only enqueue work on it and return; they never
  *           synchronise.  Results are visible to later work on that stream.
@@ -196,6 +203,47 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C,
  */
 int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
                          void* C, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * gemm_fp8_blockscaled_ex -- gemm_fp8_blockscaled with the tile scheduler's
+ * K split chosen by the caller (tests and tuning).
+ *
+ * The direct kernel gives each 256 x 256 output tile to one workgroup, one
+ * workgroup per compute unit at a time.  When the tiles would leave compute
+ * units idle (the DeepGEMM page, section 2.1: a grid too small for the
+ * machine leaves SMs unused), each tile of the last round is split along K
+ * into P ranges of whole scale groups, run by P workgroups; their fp32
+ * partial tiles go to library scratch and the workgroup that finishes last
+ * adds them in range order and writes C.
+ *
+ *   split_parts  0: automatic (only when the tiles would keep at most a
+ *                quarter of the compute units busy: P = compute units /
+ *                tiles, at most 8, at least eight scale groups per range;
+ *                measured on MI355X, a fuller grid runs faster unsplit);
+ *                1: never split; 2 .. 8:
+ *                split the last round's tiles into that many ranges (at
+ *                most one per scale group), whatever the grid
+ *
+ * The result differs from the unsplit one only by fp32 summation order;
+ * it does not depend on which workgroup finishes first.  If the scratch
+ * cannot be allocated the call runs unsplit.  Operands the direct kernel
+ * does not take run unsplit on the general kernel.  split_parts outside
+ * 0 .. 8 returns TGEMM_ERR_INVALID; otherwise as gemm_fp8_blockscaled.
+ */
+int gemm_fp8_blockscaled_ex(const void* A, const float* sA, const void* B, const float* sB,
+                            void* C, int64_t M, int64_t N, int64_t K, int split_parts,
+                            void* stream);
+
+/*
+ * gemm_fp8_split_plan -- the tile split gemm_fp8_blockscaled_ex would use
+ * (host only, no GPU call): for C [M, N] with K and `cus` compute units,
+ * *whole tiles run whole and the last *split_tiles tiles run in *parts K
+ * ranges each (*parts == 1: no split).  Returns TGEMM_OK, or
+ * TGEMM_ERR_INVALID for negative or oversized sizes, cus < 0, split_parts
+ * outside 0 .. 8 or a NULL output.
+ */
+int gemm_fp8_split_plan(int64_t M, int64_t N, int64_t K, int cus, int split_parts, int* whole,
+                        int* split_tiles, int* parts);
 
 /*
  * gemm_bf16_logsoftmax -- C[i,n] = y[i,n] - log sum_n' exp(y[i,n']),

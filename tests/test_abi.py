@@ -203,3 +203,75 @@ def test_strided_batched_validation():
     assert call(layout=1, K=60, lda=64, ldb=64) == UNS  # [N, K] weights need K % 8 == 0
     assert call(C=NULL) == INV
     assert call(sa=1 << 61, batch=8) == INV            # whole-batch extent overflows
+
+
+def test_fp8_ex_validation():
+    L = binding.lib()
+    for parts in (-1, 9):
+        assert L.gemm_fp8_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4, parts, NULL) == INV
+    assert L.gemm_fp8_blockscaled_ex(NULL, NULL, NULL, NULL, NULL, 0, 4, 4, 2, NULL) == OK
+    assert L.gemm_fp8_blockscaled_ex(FAKE, NULL, FAKE, FAKE, FAKE, 4, 4, 4, 2, NULL) == INV
+
+
+def _tiles(M, N):
+    return -(-M // 256) * -(-N // 256)
+
+
+@pytest.mark.parametrize("M,N,K,cus,want", [
+    # 896 tiles on 256 units: 3 full rounds + 128 tiles -> no split
+    (4096, 14336, 4096, 256, (896, 0, 1)),
+    (4097, 14335, 4096, 256, (952, 0, 1)),
+    (8192, 8192, 4096, 256, (1024, 0, 1)),
+    # one tile, 32 groups: four ranges of eight groups
+    (256, 256, 4096, 256, (0, 1, 4)),
+    # one tile, 128 groups: eight ranges (cap)
+    (256, 256, 16384, 256, (0, 1, 8)),
+    # fewer than 16 groups: no split
+    (256, 256, 1920, 256, (1, 0, 1)),
+    (256, 256, 256, 256, (1, 0, 1)),
+    # 9 tiles, 16 groups: two ranges
+    (600, 700, 2048, 256, (0, 9, 2)),
+    # 64 tiles = a quarter of the units: 256 / 64 = 4 ranges
+    (2048, 2048, 4096, 256, (0, 64, 4)),
+    # 65 or more tiles: no split
+    (16640, 256, 4096, 256, (65, 0, 1)),
+    (4096, 2048, 4096, 256, (128, 0, 1)),
+    (2560, 2560, 4096, 256, (100, 0, 1)),
+    # unknown compute-unit count -> no split
+    (256, 256, 4096, 0, (1, 0, 1)),
+    # the general kernel (K not a multiple of 16) never splits
+    (256, 256, 4100, 256, (1, 0, 1)),
+])
+def test_fp8_split_plan_automatic(M, N, K, cus, want):
+    got = binding.gemm_fp8_split_plan(M, N, K, cus)
+    assert got == want
+    whole, split, parts = got
+    assert whole + split == _tiles(M, N)
+    if parts > 1:
+        # the split tiles fit one round of workgroups, each range >= 8 groups
+        assert whole == 0 and split * parts <= cus and parts * 8 <= -(-K // 128)
+
+
+@pytest.mark.parametrize("forced,K,want_parts", [(1, 4096, 1), (2, 4096, 2), (8, 4096, 8),
+                                                 (5, 384, 3), (3, 384, 3), (2, 128, 1)])
+def test_fp8_split_plan_forced(forced, K, want_parts):
+    whole, split, parts = binding.gemm_fp8_split_plan(600, 700, K, 256, forced)
+    assert parts == want_parts
+    assert whole + split == _tiles(600, 700)
+    assert (split == 0) == (parts == 1)
+
+
+def test_fp8_split_plan_forced_multi_round():
+    # a forced split takes the last round of a longer grid
+    assert binding.gemm_fp8_split_plan(4096, 14336, 4096, 256, 2) == (768, 128, 2)
+    assert binding.gemm_fp8_split_plan(4097, 14335, 4096, 256, 3) == (768, 184, 3)
+
+
+def test_fp8_split_plan_validation():
+    L = binding.lib()
+    i = ctypes.c_int32()
+    p = ctypes.byref(i)
+    assert L.gemm_fp8_split_plan(-1, 4, 4, 256, 0, p, p, p) == INV
+    assert L.gemm_fp8_split_plan(4, 4, 4, -1, 0, p, p, p) == INV
+    assert L.gemm_fp8_split_plan(4, 4, 4, 256, 9, p, p, p) == INV
+    assert L.gemm_fp8_split_plan(4, 4, 4, 256, 0, None, p, p) == INV

@@ -68,6 +68,11 @@ def lib():
     L.gemm_bf16_ex.restype = i32
     L.gemm_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.gemm_fp8_blockscaled.restype = i32
+    L.gemm_fp8_blockscaled_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    L.gemm_fp8_blockscaled_ex.restype = i32
+    L.gemm_fp8_split_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(i32),
+                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.gemm_fp8_split_plan.restype = i32
     L.gemm_bf16_w8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
     L.gemm_bf16_w8.restype = i32
     L.gemm_w8_kernel_name.argtypes = [i64, i64, i64]
@@ -176,6 +181,12 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
     B: float8_e4m3fn [K, N] contiguous; sB: float32 [ceil(K/128), ceil(N/128)];
     C: bfloat16 [M, N] contiguous.
     """
+    return gemm_fp8_blockscaled_ex(A, sA, B, sB, C, 0, stream)
+
+
+def gemm_fp8_blockscaled_ex(A, sA, B, sB, C, split_parts=0, stream=None):
+    """gemm_fp8_blockscaled_ex of the C ABI: split_parts 0 automatic, 1 never,
+    2..8 K ranges per tile of the last round."""
     _check_cuda(A, sA, B, sB, C)
     if A.dtype != torch.float8_e4m3fn or B.dtype != torch.float8_e4m3fn:
         raise ValueError("A and B must be float8_e4m3fn")
@@ -189,11 +200,21 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
     G, H = (K + 127) // 128, (N + 127) // 128
     if K2 != K or tuple(C.shape) != (M, N) or tuple(sA.shape) != (M, G) or tuple(sB.shape) != (G, H):
         raise ValueError("shape mismatch")
-    st = lib().gemm_fp8_blockscaled(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
-                                    _stream_ptr(stream))
+    st = lib().gemm_fp8_blockscaled_ex(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
+                                       int(split_parts), _stream_ptr(stream))
     if st != TGEMM_OK:
-        raise TgemmError(st, "gemm_fp8_blockscaled")
+        raise TgemmError(st, "gemm_fp8_blockscaled_ex")
     return C
+
+
+def gemm_fp8_split_plan(M, N, K, cus, split_parts=0):
+    """(whole, split_tiles, parts) of the FP8 tile scheduler (host only)."""
+    w, t, p = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = lib().gemm_fp8_split_plan(M, N, K, cus, split_parts, ctypes.byref(w), ctypes.byref(t),
+                                   ctypes.byref(p))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_fp8_split_plan")
+    return w.value, t.value, p.value
 
 
 def _batch_stride(t):

@@ -12,6 +12,7 @@
 #include "launch.h"
 
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <utility>
 
@@ -161,17 +162,17 @@ int quantize_fp8(const void* X, void* Q, float* S, int64_t rows, int64_t cols, i
 
 namespace tgemm {
 
-void* device_scratch(size_t bytes, hipStream_t stream) {
+void* device_scratch(size_t bytes, hipStream_t stream, int slot, bool zeroed) {
   struct Buf {
     void* ptr = nullptr;
     size_t cap = 0;
   };
   static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, Buf> bufs;
+  static std::map<std::tuple<int, hipStream_t, int>, Buf> bufs;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
-  Buf& b = bufs[{dev, stream}];
+  Buf& b = bufs[{dev, stream, slot}];
   if (b.cap < bytes) {
     // hipFree waits for the device, so no queued kernel still uses the old
     // buffer.
@@ -183,9 +184,28 @@ void* device_scratch(size_t bytes, hipStream_t stream) {
       b.ptr = nullptr;
       return nullptr;
     }
+    if (zeroed && hipMemsetAsync(b.ptr, 0, want, stream) != hipSuccess) {
+      (void)hipFree(b.ptr);
+      b.ptr = nullptr;
+      return nullptr;
+    }
     b.cap = want;
   }
   return b.ptr;
+}
+
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cus.find(dev);
+  if (it != cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  cus[dev] = n;
+  return n;
 }
 
 }  // namespace tgemm
@@ -404,6 +424,12 @@ int gemm_bf16_logsoftmax(const void* X, const void* W, const void* bias, void* C
 
 int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB, void* C,
                          int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_fp8_blockscaled_ex(A, sA, B, sB, C, M, N, K, 0, stream);
+}
+
+int gemm_fp8_blockscaled_ex(const void* A, const float* sA, const void* B, const float* sB, void* C,
+                            int64_t M, int64_t N, int64_t K, int split_parts, void* stream) {
+  if (split_parts < 0 || split_parts > tgemm::kFp8MaxParts) return TGEMM_ERR_INVALID;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return TGEMM_ERR_INVALID;
   if (M == 0 || N == 0) return TGEMM_OK;
@@ -426,7 +452,18 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
   a.vec_a = (aligned16(A) && K % 16 == 0) ? 1 : 0;
   a.vec_b = (aligned8(B) && N % 8 == 0) ? 1 : 0;
   a.vec_c = (aligned16(C) && N % 8 == 0) ? 1 : 0;
-  const hipError_t e = tgemm::launch_fp8_blockscaled(a, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // Split the last, partly filled round of tiles along K (scratch for the
+  // partial tiles and their counters); without scratch the split is skipped.
+  const tgemm::Fp8Split plan = tgemm::fp8_split_plan(M, N, K, tgemm::device_cus(), split_parts);
+  void* part = nullptr;
+  uint32_t* count = nullptr;
+  if (plan.parts > 1 && plan.split_tiles <= tgemm::kFp8MaxSplitTiles) {
+    part = tgemm::device_scratch(tgemm::fp8_split_part_bytes(plan), s, tgemm::kScratchFp8Part);
+    count = static_cast<uint32_t*>(tgemm::device_scratch(
+        tgemm::kFp8MaxSplitTiles * sizeof(uint32_t), s, tgemm::kScratchFp8Count, true));
+  }
+  const hipError_t e = tgemm::launch_fp8_blockscaled(a, plan, part, count, s);
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
@@ -466,6 +503,19 @@ const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue,
     return nullptr;
   if (use_thin(M, algo)) return tgemm::thin_kernel_name(static_cast<int>(M));
   return tgemm::tiled_shape_info(tiled_shape_for(M, N, algo)).name;
+}
+
+int gemm_fp8_split_plan(int64_t M, int64_t N, int64_t K, int cus, int split_parts, int* whole,
+                        int* split_tiles, int* parts) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || cus < 0 ||
+      split_parts < 0 || split_parts > tgemm::kFp8MaxParts || whole == nullptr ||
+      split_tiles == nullptr || parts == nullptr)
+    return TGEMM_ERR_INVALID;
+  const tgemm::Fp8Split plan = tgemm::fp8_split_plan(M, N, K, cus, split_parts);
+  *whole = plan.whole;
+  *split_tiles = plan.split_tiles;
+  *parts = plan.parts;
+  return TGEMM_OK;
 }
 
 const char* gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K) {

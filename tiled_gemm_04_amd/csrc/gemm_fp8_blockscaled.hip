@@ -40,6 +40,16 @@
 //     loads of slice g+2 start right after that barrier (every wave is done
 //     with the stage) and finish early in slice g+1, one per slot.
 //
+// Tile scheduler: when the tiles would keep at most a quarter of the
+// compute units busy (one workgroup per unit), each tile is split along K
+// into P parts of whole scale groups, P = min(CUs / tiles, groups / 8, 8)
+// (DeepGEMM page, section 2.1: small grids leave compute units idle); a
+// caller may also force a split of the last round of a longer grid.  Every
+// part writes its fp32 partial tile to library scratch and bumps a per-tile
+// counter; the part that arrives last adds the partials in part order (the
+// same sum whatever the arrival order) and runs the epilogue.  No workgroup
+// ever waits for another.
+//
 // Requirements (checked by the launcher, otherwise the general kernel runs):
 // K a multiple of 16 (whole 16-byte chunks of A along K) and per-lane byte
 // offsets below 2^31.  Rows of A, B and C need no particular alignment: the
@@ -192,10 +202,23 @@ __device__ __forceinline__ void add_tail_products(f32x4 (&acc)[FM][kFN], const F
   }
 }
 
+// Work split of one launch: workgroups [0, whole) own whole tiles (logical
+// tiles 0 .. whole-1); the next split_tiles * parts workgroups own part q of
+// logical tile whole + t.  part: parts * split_tiles partial tiles of
+// kBM * kBN fp32; count: split_tiles counters, zero between calls.
+struct SplitTail {
+  int whole;
+  int split_tiles;
+  int parts;
+  f32x4* part;
+  uint32_t* count;
+};
+
 __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args p, int tiles_m,
-                                                                     int tiles_n) {
+                                                                     int tiles_n, SplitTail st) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
   __shared__ __attribute__((aligned(256))) float s_sa[2][kBM];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -203,8 +226,21 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   const int wm = wave >> 2;
   const int wn = wave & 3;
 
+  // Tile and K range (whole scale groups [g0, g1)) of this workgroup.
+  int logical, kpart = 0;
+  const int bid = blockIdx.x;
+  if (bid < st.whole) {
+    logical = xcd_remap(bid, st.whole);
+  } else {
+    const int r = xcd_remap(bid - st.whole, st.split_tiles * st.parts);
+    logical = st.whole + r / st.parts;
+    kpart = r % st.parts;
+  }
+  const int parts = bid < st.whole ? 1 : st.parts;
+  const int g0 = static_cast<int>(static_cast<int64_t>(p.G) * kpart / parts);
+  const int g1 = static_cast<int>(static_cast<int64_t>(p.G) * (kpart + 1) / parts);
   int tm, tn;
-  tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, kGroupM, tm, tn);
+  tile_coords(logical, tiles_m, tiles_n, kGroupM, tm, tn);
   const int m0 = tm * kBM;
   const int n0 = tn * kBN;
   const int hb = (n0 + wn * kWTN) / 128;  // this wave's B-scale column
@@ -327,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   };
 
   const int G = p.G;
-  if (G > 0) {
+  if (g1 > g0) {
     // B scales of this wave's column block, 64 groups per register: lane l
     // holds sB[g0 + l, hb] and each group's value is taken with readlane.
     auto sb_fetch = [&](int g0) {
@@ -341,19 +377,19 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
 #pragma unroll
     for (int j = 0; j < kFN; ++j) part[j] = f32x4{};
     srow[1] = 0.0f;
-    float sb_lanes = sb_fetch(0);
-    float sb_cur = sb_of(sb_lanes, 0);
-    // Prologue: slice 0, then the first kEarly blocks of slice 1.
+    float sb_lanes = sb_fetch(g0 & ~63);
+    float sb_cur = sb_of(sb_lanes, g0);
+    // Prologue: slice g0, then the first kEarly blocks of slice g0+1.
     {
-      const i32x4 w = window(0);
+      const i32x4 w = window(g0);
 #pragma unroll
-      for (int i = 0; i < kBlocksPerWave; ++i) issue(w, 0, i);
-      issue_scales(0);
+      for (int i = 0; i < kBlocksPerWave; ++i) issue(w, g0, i);
+      issue_scales(g0);
     }
-    if (G > 1) {
-      const i32x4 w = window(1);
+    if (g1 - g0 > 1) {
+      const i32x4 w = window(g0 + 1);
 #pragma unroll
-      for (int i = 0; i < kEarly; ++i) issue(w, 1, i);
+      for (int i = 0; i < kEarly; ++i) issue(w, g0 + 1, i);
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEarly) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -362,14 +398,14 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     // Same order as the reads of the next slice in the last row of the loop.
 #pragma unroll
     for (int j = 0; j < kFN; ++j) {
-      read_b(0, j);
-      if (j == 0) read_a(0, 0);
-      if (j == 1) read_scale(0, 0);
+      read_b(g0 & 1, j);
+      if (j == 0) read_a(g0 & 1, 0);
+      if (j == 1) read_scale(g0 & 1, 0);
     }
 
     float sb_prev = 0.0f;  // sB of the slice whose last row is pending
     float scale = 0.0f;    // sA * sB of the row being folded
-    for (int g = 0; g < G; ++g) {
+    for (int g = g0; g < g1; ++g) {
       const int stage = g & 1;
       if (((g + 1) & 63) == 0) {
         // Next 64 B scales; wait here (rarely) rather than at their use,
@@ -421,9 +457,57 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     scale = srow[1] * sb_prev;
 #pragma unroll
     for (int j = 0; j < kFN; ++j) fold(kFM - 1, j, scale);
-    if (tail_tile) add_tail_products(acc, p, m0 + wm * kWTM, n0, wn, lane, hb);
+    if (tail_tile && g1 == G) add_tail_products(acc, p, m0 + wm * kWTM, n0, wn, lane, hb);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (parts > 1) {
+    // Publish this part's fp32 partial tile (lane-contiguous 16-byte
+    // stores), then count the parts that are done; only the last one goes on.
+    const int t = logical - st.whole;
+    f32x4* const part0 = st.part + static_cast<int64_t>(t) * parts * (kFM * kFN * kThreads);
+    f32x4* const mine = part0 + static_cast<int64_t>(kpart) * (kFM * kFN * kThreads);
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) mine[(i * kFN + j) * kThreads + tid] = acc[i][j];
+    // Every wave's stores have reached L2 before the barrier; thread 0's
+    // release then writes them back for the other dies, once per workgroup
+    // (a device-scope fence in every wave would write back and invalidate
+    // the die's L2 eight times over).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t done =
+          __hip_atomic_fetch_add(st.count + t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = done + 1 == static_cast<uint32_t>(parts);
+      // The last part resets the counter for the next call.
+      if (last) __hip_atomic_store(st.count + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();  // thread 0's acquire (cache invalidation) precedes every wave's reads
+    if (!s_last) return;
+    // Sum in part order, ((P0 + P1) + P2) + ..., all read back from the
+    // scratch (this part's own as well), so the bits do not depend on which
+    // part came last.
+    // One part at a time, its 32 loads issued together.
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) acc[i][j] = part0[(i * kFN + j) * kThreads + tid];
+    for (int q = 1; q < parts; ++q) {
+      const f32x4* src = part0 + static_cast<int64_t>(q) * (kFM * kFN * kThreads) + tid;
+      f32x4 v[kFM][kFN];
+#pragma unroll
+      for (int i = 0; i < kFM; ++i)
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) v[i][j] = src[(i * kFN + j) * kThreads];
+#pragma unroll
+      for (int i = 0; i < kFM; ++i)
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) acc[i][j] += v[i][j];
+    }
+  }
   lds_barrier();  // every wave is done with the operand stages
 
   // ---- epilogue ----
@@ -446,12 +530,54 @@ const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K) {
   return fp8_direct_ok(M, N, K) ? "tgemm_fp8_bs_256x256x128" : "tgemm_fp8_bs_general_256x128x128";
 }
 
-hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t s) {
+Fp8Split fp8_split_plan(int64_t M, int64_t N, int64_t K, int cus, int forced_parts) {
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int64_t G = (K + 127) / 128;
+  Fp8Split plan{static_cast<int>(tiles), 0, 1};
+  if (cus <= 0 || tiles == 0 || forced_parts == 1 || !fp8_direct_ok(M, N, K)) return plan;
+  const int64_t left = tiles - (tiles - 1) / cus * cus;  // tiles of the last round
+  int64_t parts;
+  if (forced_parts >= 2) {
+    parts = forced_parts < G ? forced_parts : G;  // at least one scale group per part
+  } else {
+    // Measured on MI355X: splitting pays only when at most a quarter of the
+    // compute units would be busy (1 .. 32 tiles ran 1.2 - 3.5x faster; 128
+    // tiles, or the 128-tile last round of a 4096 x 14336 grid, ran 2 - 18 %
+    // slower, as a partly idle chip runs each tile faster), with at least
+    // eight scale groups per part (fewer leave the partial-tile traffic and
+    // the fixup exposed).
+    if (tiles > left || 4 * left > cus) return plan;
+    parts = cus / left;
+    if (parts > kFp8MaxParts) parts = kFp8MaxParts;
+    if (parts > G / 8) parts = G / 8;
+  }
+  if (parts < 2 || left > kFp8MaxSplitTiles) return plan;
+  plan.whole = static_cast<int>(tiles - left);
+  plan.split_tiles = static_cast<int>(left);
+  plan.parts = static_cast<int>(parts);
+  return plan;
+}
+
+size_t fp8_split_part_bytes(const Fp8Split& plan) {
+  return static_cast<size_t>(plan.split_tiles) * plan.parts * kBM * kBN * sizeof(float);
+}
+
+hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* part, uint32_t* count,
+                                  hipStream_t s) {
   if (!fp8_direct_ok(a.M, a.N, a.K)) return launch_fp8_general(a, s);
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.N + kBN - 1) / kBN;
-  hipLaunchKernelGGL(tgemm_fp8_bs_256x256x128, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
-                     tiles_m, tiles_n);
+  SplitTail st{tiles_m * tiles_n, 0, 1, nullptr, nullptr};
+  if (plan.parts > 1 && part != nullptr && count != nullptr &&
+      plan.whole + plan.split_tiles == tiles_m * tiles_n) {
+    st.whole = plan.whole;
+    st.split_tiles = plan.split_tiles;
+    st.parts = plan.parts;
+    st.part = static_cast<f32x4*>(part);
+    st.count = count;
+  }
+  hipLaunchKernelGGL(tgemm_fp8_bs_256x256x128, dim3(st.whole + st.split_tiles * st.parts),
+                     dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
   return hipGetLastError();
 }
 

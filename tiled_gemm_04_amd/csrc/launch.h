@@ -110,11 +110,35 @@ hipError_t launch_bf16_thin_splitk(const Bf16Args& a, const ThinSplit& plan, flo
 // Library-owned device scratch of at least `bytes` for work on `stream` of
 // the current device (one buffer per device and stream, grown on demand,
 // kept until the process ends); nullptr if it cannot be allocated.
-void* device_scratch(size_t bytes, hipStream_t stream);
+// Separate buffers per purpose (slot); a `zeroed` buffer is cleared on the
+// stream whenever it is (re)allocated.
+enum ScratchSlot { kScratchThinSplit = 0, kScratchFp8Part = 1, kScratchFp8Count = 2 };
+void* device_scratch(size_t bytes, hipStream_t stream, int slot = kScratchThinSplit,
+                     bool zeroed = false);
+// Compute units of the current device (0 if unknown).
+int device_cus();
 // Register-transposing thin kernel for operands the direct-to-LDS one cannot take.
 hipError_t launch_bf16_thin_general(const Bf16Args& a, int epilogue, int out_bf16,
                                     hipStream_t stream);
-hipError_t launch_fp8_blockscaled(const Fp8Args& a, hipStream_t stream);
+// Tile split of the direct FP8 kernel: `whole` tiles done whole, the last
+// round's `split_tiles` tiles in `parts` K ranges each (parts == 1: none).
+struct Fp8Split {
+  int whole;
+  int split_tiles;
+  int parts;
+};
+constexpr int kFp8MaxParts = 8;
+constexpr int kFp8MaxSplitTiles = 4096;  // counters held by the library scratch
+// forced_parts: 0 automatic (split only a grid that keeps at most a quarter
+// of the compute units busy, at least eight scale groups per part); 1 never;
+// 2 .. kFp8MaxParts split the last round's tiles into that many parts (at
+// most one per scale group).
+Fp8Split fp8_split_plan(int64_t M, int64_t N, int64_t K, int cus, int forced_parts);
+size_t fp8_split_part_bytes(const Fp8Split& plan);
+// part: fp8_split_part_bytes(plan) of scratch; count: plan.split_tiles
+// counters that are zero on entry (and again on exit).  Either NULL: no split.
+hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* part,
+                                  uint32_t* count, hipStream_t stream);
 // Register-staged kernel for FP8 operands the direct-to-LDS kernel cannot take.
 hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
@@ -140,5 +164,6 @@ hipError_t launch_quant_fp8_1x128(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quant_fp8_128x128(const QuantArgs& a, hipStream_t stream);
 const char* thin_kernel_name(int M);
 const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K);
+bool fp8_direct_ok(int64_t M, int64_t N, int64_t K);
 
 }  // namespace tgemm
