@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
                     help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
-                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt, thin_nt_m1..64)")
+                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt, thin_nt_m1..64, ffn_up_q8)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -89,6 +89,7 @@ KERNEL_SOURCES = {
     "w4": ["common.h", "launch.h", "gemm_wq_thin.hip"],
     "lsm": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
     "nt": ["common.h", "launch.h", "gemm_bf16_tiled.hip", "gemm_bf16_thin.hip"],
+    "q8": ["common.h", "launch.h", "gemm_bf16_tiled.hip"],
 }
 
 # Weight-only int8 LM head: the thin-M workloads' X [M, 4096] times int8
@@ -102,6 +103,9 @@ W8_CASES = {"w8_m1": 1, "w8_m8": 8, "w8_m32": 32, "w8_m64": 64,
 NT_CASES = {"square_nt": "square", "ffn_up_nt": "ffn_up", "ffn_down_nt": "ffn_down",
             "thin_nt_m1": "thin_m1", "thin_nt_m8": "thin_m8", "thin_nt_m32": "thin_m32",
             "thin_nt_m64": "thin_m64"}
+# The FFN up-projection with the FP8 1 x 128 activation quantiser in its
+# epilogue (codes + scales out, no bf16 output).
+Q8_CASES = {"ffn_up_q8": "ffn_up"}
 LSM_CASES = {"lsm_m1": 1, "lsm_m8": 8, "lsm_m32": 32, "lsm_m64": 64}
 QUANT_CASES = {"quant_a": ("a", "tgemm_quant_fp8_1x128"), "quant_b": ("b", "tgemm_quant_fp8_128x128")}
 
@@ -146,6 +150,9 @@ class Case:
         if name in NT_CASES:
             self._init_nt(name, dev)
             return
+        if name in Q8_CASES:
+            self._init_q8(name, dev)
+            return
         w = wl.WORKLOADS[name]
         self.w = w
         self.M, self.N, self.K = w.M, w.N, w.K
@@ -187,6 +194,9 @@ class Case:
         if self.family == "w8":
             return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
                     f"(Q[{self.K},{self.N}] int8 * S[{(self.K + 127) // 128},{self.N}])")
+        if self.family == "q8":
+            return (f"{self.name}: Q, S = quantize_fp8_1x128(gelu(A[{self.M},{self.K}] . "
+                    f"B[{self.K},{self.N}] + bias)) in one kernel")
         if self.family == "nt":
             return (f"{self.name}: C[{self.M},{self.N}] = A[{self.M},{self.K}] . Bt[{self.N},{self.K}]^T "
                     f"(weight K-contiguous)")
@@ -245,6 +255,30 @@ class Case:
         self.family = "nt"
         thin = w.name.startswith("thin")
         self.bound, self.peak = ("hbm", PEAK_HBM_GBS) if thin else ("mfma", PEAK_BF16_TFLOPS)
+        self.dtype = "bf16"
+        self.inputs_for_oracle = None
+
+    def _init_q8(self, name, dev):
+        import torch
+
+        import tiled_gemm_04_amd as tg
+        import workloads as wl
+
+        w = wl.WORKLOADS[Q8_CASES[name]]
+        a, b, bias = wl.bf16_inputs(w, device=dev)
+        G = (w.N + 127) // 128
+        q = torch.empty(w.M, w.N, dtype=torch.uint8, device=dev)
+        s = torch.empty(w.M, G, dtype=torch.float32, device=dev)
+        self.launch = lambda: tg.gemm_bf16_quant_fp8(a, b, bias, q, s, epilogue=w.epilogue)
+        self.w = None
+        self.M, self.N, self.K = w.M, w.N, w.K
+        self.flops = 2 * w.M * w.N * w.K
+        # A, B, bias read once; codes (1 byte each) and scales written once.
+        self.bytes = 2 * (w.M * w.K + w.K * w.N) + 2 * w.N + w.M * w.N + 4 * w.M * G
+        self.kernel = tg.gemm_bf16_kernel_name(w.M, w.N, w.K, w.epilogue, tg.OUT_BF16).replace(
+            "tgemm_bf16_tiled_", "tgemm_bf16_tiled_q8_")
+        self.family = "q8"
+        self.bound, self.peak = "mfma", PEAK_BF16_TFLOPS
         self.dtype = "bf16"
         self.inputs_for_oracle = None
 
@@ -423,7 +457,7 @@ def main():
                      "fp8_ragged", "tiny", "quant_a", "quant_b", "w8_m1", "w8_m8", "w8_m32",
                      "w8_m64", "w4_m1", "w4_m8", "w4_m32", "w4_m64", "lsm_m1", "lsm_m8", "lsm_m32",
                      "lsm_m64", "square_nt", "ffn_up_nt", "ffn_down_nt", "thin_nt_m1",
-                     "thin_nt_m8", "thin_nt_m32", "thin_nt_m64"):
+                     "thin_nt_m8", "thin_nt_m32", "thin_nt_m64", "ffn_up_q8"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

@@ -376,6 +376,38 @@ int quantize_fp8_1x128(const void* X, void* Q, float* S, int64_t M, int64_t K, i
                        void* stream);
 
 /*
+ * gemm_bf16_quant_fp8 -- Q, S = quantize_1x128( bf16( epilogue(A B + bias) ) )
+ *
+ * The bf16 GEMM with the activation quantiser welded into its epilogue (the
+ * DeepGEMM page, section 1.2: activation, quantisation and scaling in one
+ * kernel; section 2.4 for the 1 x 128 groups): each output is computed and
+ * rounded to bf16 exactly as gemm_bf16 with bf16 output computes it, and
+ * instead of being stored it is quantised as quantize_fp8_1x128 quantises
+ * X -- per row, groups of 128 consecutive columns, scale = amax / 448 (1
+ * for an all-zero group), code = e4m3fn(clamp(value / scale, -448, 448)).
+ * The bf16 output is never written.  Q and S are the A operand and sA of a
+ * following gemm_fp8_blockscaled (an FFN up-projection feeding an FP8
+ * down-projection).  Codes and scales equal, bit for bit, gemm_bf16_ex on
+ * the same tiled kernel followed by quantize_fp8_1x128 on its output.
+ *
+ *   A, B, bias, M, N, K, lda, ldb, epilogue   as gemm_bf16 (B is [K, N])
+ *   Q     e4m3fn bytes [M, N], packed row-major (row stride N)
+ *   S     fp32 [M, ceil(N/128)], packed row-major
+ *   algo  TGEMM_ALGO_AUTO / TGEMM_ALGO_TILED (the tiled kernel's shape table)
+ *         or TGEMM_ALGO_TILED_256x256 / _256x128 / _128x128
+ *
+ * Supported: the direct tiled kernel's operands -- A and B 16-byte aligned,
+ * lda and ldb multiples of 8, K and N multiples of 8.  Others, and
+ * TGEMM_ALGO_THIN, return TGEMM_ERR_UNSUPPORTED.  NULL Q or S (with M, N >
+ * 0) and the gemm_bf16 argument errors return TGEMM_ERR_INVALID.  Q and S
+ * must not overlap the inputs.  Returns TGEMM_OK, TGEMM_ERR_INVALID,
+ * TGEMM_ERR_UNSUPPORTED or TGEMM_ERR_LAUNCH.
+ */
+int gemm_bf16_quant_fp8(const void* A, const void* B, const void* bias, void* Q, float* S,
+                        int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int epilogue,
+                        int algo, void* stream);
+
+/*
  * quantize_fp8_128x128 -- FP8 codes and scales for the B operand of
  * gemm_fp8_blockscaled: one scale per 128 x 128 block.
  *

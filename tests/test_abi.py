@@ -275,3 +275,21 @@ def test_fp8_split_plan_validation():
     assert L.gemm_fp8_split_plan(4, 4, 4, -1, 0, p, p, p) == INV
     assert L.gemm_fp8_split_plan(4, 4, 4, 256, 9, p, p, p) == INV
     assert L.gemm_fp8_split_plan(4, 4, 4, 256, 0, None, p, p) == INV
+
+
+def test_bf16_quant_fp8_validation():
+    L = binding.lib()
+    S = ctypes.c_void_p(0x2000)
+    # M, N, K, lda, ldb, epilogue, algo
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, -1, 8, 8, 8, 8, 0, 0, NULL) == INV
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, 8, 8, 8, 4, 8, 0, 0, NULL) == INV   # lda < K
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, 8, 8, 8, 8, 8, 1, 0, NULL) == INV   # bias missing
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, 8, 8, 8, 8, 8, 3, 0, NULL) == INV   # epilogue
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, NULL, S, 8, 8, 8, 8, 8, 0, 0, NULL) == INV   # Q
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, NULL, 8, 8, 8, 8, 8, 0, 0, NULL) == INV  # S
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, 8, 8, 8, 8, 8, 0, 9, NULL) == INV   # algo
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, 8, 8, 8, 8, 8, 0, 2, NULL) == UNS   # thin
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, 8, 12, 8, 8, 12, 0, 0, NULL) == UNS  # N % 8
+    assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, 8, 8, 12, 12, 8, 0, 0, NULL) == UNS  # K % 8
+    assert L.gemm_bf16_quant_fp8(ctypes.c_void_p(0x1002), FAKE, NULL, FAKE, S, 8, 8, 8, 8, 8, 0, 0, NULL) == UNS
+    assert L.gemm_bf16_quant_fp8(NULL, NULL, NULL, NULL, NULL, 0, 8, 8, 8, 8, 0, 0, NULL) == OK

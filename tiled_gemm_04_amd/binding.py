@@ -73,6 +73,8 @@ def lib():
     L.gemm_fp8_split_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(i32),
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.gemm_fp8_split_plan.restype = i32
+    L.gemm_bf16_quant_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.gemm_bf16_quant_fp8.restype = i32
     L.gemm_bf16_w8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
     L.gemm_bf16_w8.restype = i32
     L.gemm_w8_kernel_name.argtypes = [i64, i64, i64]
@@ -205,6 +207,34 @@ def gemm_fp8_blockscaled_ex(A, sA, B, sB, C, split_parts=0, stream=None):
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_fp8_blockscaled_ex")
     return C
+
+
+def gemm_bf16_quant_fp8(A, B, bias, Q, S, epilogue=EPI_NONE, algo=ALGO_AUTO, stream=None):
+    """Q, S = 1x128 FP8 quantisation of bf16(epilogue(A @ B + bias)), one kernel.
+
+    A: bf16 [M, K] (row stride free); B: bf16 [K, N] (row stride free);
+    bias: bf16 [N] or None; Q: float8_e4m3fn or uint8 [M, N] contiguous;
+    S: float32 [M, ceil(N/128)] contiguous.
+    """
+    _check_cuda(A, B, Q, S, *([bias] if bias is not None else []))
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("A and B must be bfloat16")
+    if Q.dtype not in (torch.float8_e4m3fn, torch.uint8) or S.dtype != torch.float32:
+        raise ValueError("Q must be float8_e4m3fn (or uint8) and S float32")
+    if not Q.is_contiguous() or not S.is_contiguous():
+        raise ValueError("Q and S must be contiguous (packed row-major)")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(Q.shape) != (M, N) or tuple(S.shape) != (M, (N + 127) // 128):
+        raise ValueError("shape mismatch")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
+        raise ValueError("bias must be bfloat16 [N]")
+    st = lib().gemm_bf16_quant_fp8(_ptr(A), _ptr(B), _ptr(bias) if bias is not None else None,
+                                   _ptr(Q), _ptr(S), M, N, K, _row_major(A, "A"), _row_major(B, "B"),
+                                   int(epilogue), int(algo), _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_bf16_quant_fp8")
+    return Q, S
 
 
 def gemm_fp8_split_plan(M, N, K, cus, split_parts=0):

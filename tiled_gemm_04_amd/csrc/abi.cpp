@@ -246,6 +246,37 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C, int64_
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
+int gemm_bf16_quant_fp8(const void* A, const void* B, const void* bias, void* Q, float* S,
+                        int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int epilogue,
+                        int algo, void* stream) {
+  // Q is [M, N] bytes, packed: checked as C with ldc = N.
+  const int st = validate_bf16(A, B, bias, Q, M, N, K, lda, ldb, N > 0 ? N : 1, epilogue,
+                               TGEMM_OUT_BF16, algo);
+  if (st != TGEMM_OK) return st;
+  if (algo == TGEMM_ALGO_THIN) return TGEMM_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return TGEMM_OK;
+  if (S == nullptr) return TGEMM_ERR_INVALID;
+  Bf16Args a;
+  a.A = static_cast<const uint16_t*>(A);
+  a.B = static_cast<const uint16_t*>(B);
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.C = Q;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = N;
+  a.vec_a = (K == 0 || (aligned16(A) && lda % 8 == 0)) ? 1 : 0;
+  a.vec_b = (K == 0 || (aligned16(B) && ldb % 8 == 0)) ? 1 : 0;
+  a.vec_c = (aligned8(Q) && N % 8 == 0) ? 1 : 0;
+  a.qscale = S;
+  const int shape = tiled_shape_for(M, N, algo);
+  if (!tgemm::bf16_direct_ok(a, shape)) return TGEMM_ERR_UNSUPPORTED;
+  const hipError_t e = tgemm::launch_bf16_tiled_q8(a, shape, epilogue, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
 int gemm_bf16_nt(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
                  int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
                  void* stream) {

@@ -175,7 +175,114 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], flo
   }
 }
 
-template <class C, bool BT, int EPI, bool OUT_BF16>
+// Quantising epilogue of one wave (DeepGEMM page, section 1.2: activation,
+// quantisation and scaling welded into the producing kernel).  Each output
+// is epilogue(acc + bias) rounded to bf16, exactly what the plain epilogue
+// stores; the values are then quantised in groups of 128 consecutive
+// columns of a row, as the standalone 1 x 128 quantiser does (same scale,
+// quotient and rounding code), so codes and scales equal that quantiser's on
+// the bf16 output, bit for bit.  A 128-column group spans two waves (wave
+// tiles are 64 columns wide), so the group maximum goes through LDS:
+// phase 1 forms each row's maximum over the wave's 64 columns (8 lanes hold
+// a row after the LDS strip transpose) into amax_tab[row][wn], keeping the
+// rounded values in registers; after a barrier, phase 2 combines the two
+// halves, writes 8 codes (8 bytes) per lane and, from the even wave of the
+// pair, the group's scale.  Rows >= M and columns >= N are not stored.
+template <int EPI, int FM, int FN, int WN>
+__device__ __forceinline__ void store_wave_tile_q8(const f32x16 (&acc)[FM][FN], float* strip,
+                                                   float* amax_tab, int lane, int wn, int trow0,
+                                                   int row0, int col0, const Bf16Args& p) {
+  constexpr int WTN = 32 * FN;
+  static_assert(WTN == 64, "a 128-column group must span a wave pair");
+  constexpr int PITCH = WTN + 4;
+  constexpr int LANES_PER_ROW = WTN / 8;
+  constexpr int ROWS_PER_PASS = kWave / LANES_PER_ROW;
+  constexpr int PASSES = 32 / ROWS_PER_PASS;
+  const int lrow = lane & 31;
+  const int lhalf = lane >> 5;
+  const int erow = lane / LANES_PER_ROW;
+  const int ecol = 8 * (lane % LANES_PER_ROW);
+  const int gcol = col0 + ecol;
+  float bias[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bias[e] = 0.0f;
+    if constexpr (EPI != kEpiNone) {
+      if (gcol + e < p.N) bias[e] = bf16_bits_to_f32(p.bias[gcol + e]);
+    }
+  }
+  // Phase 1: rounded outputs (packed bf16 pairs) and per-row partial maxima.
+  u32x4 hv[FM][PASSES];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(strip + lrow * PITCH + 32 * j + 8 * g + 4 * lhalf) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                  acc[i][j][4 * g + 3]};
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int rr = erow + ROWS_PER_PASS * pass;
+      const float* src = strip + rr * PITCH + ecol;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = gcol + e < p.N ? apply_epilogue<EPI>(v[e], bias[e]) : 0.0f;
+      const u32x4 h = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7])};
+      hv[i][pass] = h;
+      float m = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(h[d] << 16)));
+        m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(h[d] & 0xffff0000u)));
+      }
+#pragma unroll
+      for (int d = 1; d < LANES_PER_ROW; d <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d, kWave));
+      if (lane % LANES_PER_ROW == 0) amax_tab[(trow0 + 32 * i + rr) * WN + wn] = m;
+    }
+  }
+  __syncthreads();
+  // Phase 2: the pair's maximum, scale, codes.
+  const int G = (p.N + 127) / 128;
+  uint8_t* const q = static_cast<uint8_t*>(p.C);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int rr = erow + ROWS_PER_PASS * pass;
+      const float* t = amax_tab + (trow0 + 32 * i + rr) * WN;
+      const float amax = __builtin_fmaxf(t[wn], t[wn ^ 1]);
+      const float scale = fp8q::group_scale(amax);
+      const u32x4 h = hv[i][pass];
+      float x[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        x[2 * d] = __uint_as_float(h[d] << 16);
+        x[2 * d + 1] = __uint_as_float(h[d] & 0xffff0000u);
+      }
+      const u32x2 codes = fp8q::codes8(x, scale);
+      const int row = row0 + 32 * i + rr;
+      if (row < p.M) {
+        uint8_t* out = q + static_cast<int64_t>(row) * p.ldc + gcol;
+        if (p.vec_c && gcol + 8 <= p.N) {
+          *reinterpret_cast<u32x2*>(out) = codes;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gcol + e < p.N) out[e] = static_cast<uint8_t>(codes[e / 4] >> (8 * (e % 4)));
+        }
+        if ((wn & 1) == 0 && ecol == 0 && col0 < p.N)
+          p.qscale[static_cast<int64_t>(row) * G + col0 / 128] = scale;
+      }
+    }
+  }
+}
+
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
                                                                 int tiles_n) {
   apply_batch(p, OUT_BF16 ? 2 : 4);
@@ -404,19 +511,35 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
   lds_barrier();  // every wave is done with the operand stages
 
   // ---- epilogue ----
-  store_wave_tile<EPI, OUT_BF16, C::FM, C::FN>(
-      acc, reinterpret_cast<float*>(smem) + wave * 32 * C::EPI_PITCH, lane, m0 + wm * C::WTM,
-      n0 + wn * C::WTN, p);
+  if constexpr (QUANT) {
+    static_assert((C::WAVES * 32 * C::EPI_PITCH + C::BM * C::WN) * 4 <= C::LDS_BYTES,
+                  "strips and the row-maximum table must fit in LDS");
+    store_wave_tile_q8<EPI, C::FM, C::FN, C::WN>(
+        acc, reinterpret_cast<float*>(smem) + wave * 32 * C::EPI_PITCH,
+        reinterpret_cast<float*>(smem) + C::WAVES * 32 * C::EPI_PITCH, lane, wn, wm * C::WTM,
+        m0 + wm * C::WTM, n0 + wn * C::WTN, p);
+  } else {
+    store_wave_tile<EPI, OUT_BF16, C::FM, C::FN>(
+        acc, reinterpret_cast<float*>(smem) + wave * 32 * C::EPI_PITCH, lane, m0 + wm * C::WTM,
+        n0 + wn * C::WTN, p);
+  }
 }
 
 
-template <class C, bool BT, int EPI, bool OUT_BF16>
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
 hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
   const int tiles_n = (a.N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16>), dim3(tiles_m * tiles_n, a.batch),
+  hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16, QUANT>), dim3(tiles_m * tiles_n, a.batch),
                      dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+template <class C>
+hipError_t dispatch_q8(const Bf16Args& a, int epi, hipStream_t s) {
+  if (epi == kEpiNone) return launch_c<C, false, kEpiNone, true, true>(a, s);
+  if (epi == kEpiBias) return launch_c<C, false, kEpiBias, true, true>(a, s);
+  return launch_c<C, false, kEpiBiasGelu, true, true>(a, s);
 }
 
 template <class C, bool BT>
@@ -470,6 +593,15 @@ hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epi, int out_bf16
     case kTile256x256: return dispatch_epi<Cfg256x256, false>(a, epi, out_bf16, s);
     case kTile256x128: return dispatch_epi<Cfg256x128, false>(a, epi, out_bf16, s);
     default: return dispatch_epi<Cfg128x128, false>(a, epi, out_bf16, s);
+  }
+}
+
+hipError_t launch_bf16_tiled_q8(const Bf16Args& a, int shape, int epi, hipStream_t s) {
+  if (!bf16_direct_ok(a, shape) || a.batch != 1 || a.qscale == nullptr) return hipErrorInvalidValue;
+  switch (shape) {
+    case kTile256x256: return dispatch_q8<Cfg256x256>(a, epi, s);
+    case kTile256x128: return dispatch_q8<Cfg256x128>(a, epi, s);
+    default: return dispatch_q8<Cfg128x128>(a, epi, s);
   }
 }
 

@@ -22,6 +22,9 @@ struct Bf16Args {
   // C + z*sc (elements); a single problem has batch 1.
   int64_t sa = 0, sb = 0, sc = 0;
   int batch = 1;
+  // Quantising epilogue only: C holds e4m3fn codes (row stride ldc bytes)
+  // and qscale the fp32 scales [M, ceil(N/128)], packed.
+  float* qscale = nullptr;
 };
 
 // Moves p to problem blockIdx.y of a strided batch (C elements of
@@ -91,6 +94,11 @@ hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epilogue, int out
 hipError_t launch_bf16_tiled_bt(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                                 hipStream_t stream);
 bool bf16_bt_direct_ok(const Bf16Args& a, int shape);
+bool bf16_direct_ok(const Bf16Args& a, int shape);
+// The tiled kernel with a quantising epilogue: epilogue(A.B + bias) rounded
+// to bf16, then 1 x 128 FP8 codes into C (bytes) and scales into qscale.
+// hipErrorInvalidValue when the operands do not meet bf16_direct_ok.
+hipError_t launch_bf16_tiled_q8(const Bf16Args& a, int shape, int epilogue, hipStream_t stream);
 // Small-M kernel for B given as [N, K] (M <= 64, aligned operands).
 hipError_t launch_bf16_thin_nt(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream);
 bool thin_nt_ok(const Bf16Args& a);

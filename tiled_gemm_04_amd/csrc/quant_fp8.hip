@@ -35,44 +35,8 @@ namespace tgemm {
 namespace {
 
 constexpr int kGroup = 128;
-constexpr float kE4m3Max = 448.0f;
-
-__device__ __forceinline__ float group_scale(float amax) {
-  return amax == 0.0f ? 1.0f : amax / kE4m3Max;
-}
-
-// x / scale rounded to nearest in fp32, from inv = 1/scale rounded to
-// nearest (one correctly rounded division per group): q0 = x * inv, then
-// one correction with the exact remainder x - scale * q0 (an FMA).  With inv
-// correctly rounded and q0 within one ulp, q0 + remainder * inv rounded is
-// the correctly rounded quotient (Markstein's division step); checked equal
-// to the IEEE division on 4 million random operand pairs of this form on
-// MI355X.  A zero quotient takes x's sign, as the division gives -0 for -0.
-__device__ __forceinline__ float quotient(float x, float scale, float inv) {
-  const float q0 = x * inv;
-  const float q = __builtin_fmaf(__builtin_fmaf(-scale, q0, x), inv, q0);
-  return __builtin_copysignf(q, x);
-}
-
-// e4m3fn codes of two values already clamped to [-448, 448], to nearest
-// with ties to even (v_cvt_pk_fp8_f32; its codes for every bf16 value, every
-// rounding tie and 8 million random fp32 values in that range equal a
-// bit-level rounding of the 23-bit mantissa to 3 bits, subnormals included),
-// in the low 16 bits of the result.
-__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
-}
-
-// Eight codes of x[0..7] under one group scale, packed little-endian.
-__device__ __forceinline__ u32x2 codes8(const float (&x)[8], float scale) {
-  const float inv = 1.0f / scale;
-  float c[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    c[e] = __builtin_amdgcn_fmed3f(quotient(x[e], scale, inv), -kE4m3Max, kE4m3Max);
-  return u32x2{e4m3_pair(c[0], c[1]) | (e4m3_pair(c[2], c[3]) << 16),
-               e4m3_pair(c[4], c[5]) | (e4m3_pair(c[6], c[7]) << 16)};
-}
+using fp8q::codes8;
+using fp8q::group_scale;
 
 // Eight bf16 values of one row starting at column c (columns >= ncols read
 // as 0; a zero never changes a group maximum).
