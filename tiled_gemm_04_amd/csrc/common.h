@@ -21,6 +21,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// 16-byte vectors at 2- or 4-byte alignment: stored with one 16-byte global
+// store (the memory path on gfx950 takes any byte address), for output rows
+// that are not 16-byte aligned.
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies, 32 CUs each
 

@@ -154,6 +154,11 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], flo
             *reinterpret_cast<u32x4*>(out) =
                 u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                       pack_bf16x2(v[6], v[7])};
+          } else if (gcol + 8 <= p.N) {
+            // Row not 16-byte aligned: one unaligned 16-byte store.
+            *reinterpret_cast<u32x4_a2*>(out) =
+                u32x4_a2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7])};
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -164,6 +169,9 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], flo
           if (full_cols) {
             *reinterpret_cast<f32x4*>(out) = f32x4{v[0], v[1], v[2], v[3]};
             *reinterpret_cast<f32x4*>(out + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          } else if (gcol + 8 <= p.N) {
+            *reinterpret_cast<f32x4_a4*>(out) = f32x4_a4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4_a4*>(out + 4) = f32x4_a4{v[4], v[5], v[6], v[7]};
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)

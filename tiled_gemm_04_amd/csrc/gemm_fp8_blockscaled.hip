@@ -55,8 +55,8 @@
 // offsets below 2^31.  Rows of A, B and C need no particular alignment: the
 // 16-byte buffer loads are byte-addressed (gfx9 unaligned access mode; on
 // MI355X they return the exact bytes at any offset), B columns past N only
-// reach accumulators of columns that are never stored, and the stores fall
-// back to 2-byte writes when C rows are not 16-byte aligned.
+// reach accumulators of columns that are never stored, and the stores use
+// unaligned 16-byte writes when C rows are not 16-byte aligned.
 #include "common.h"
 #include "launch.h"
 
@@ -158,6 +158,10 @@ __device__ __forceinline__ void store_wave(const f32x4 (&acc)[FM][kFN], float* s
         if (full_cols) {
           *reinterpret_cast<u32x4*>(out) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
                                                  pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+        } else if (gcol + 8 <= p.N) {
+          // Row not 16-byte aligned (N % 8 != 0): one unaligned 16-byte store.
+          *reinterpret_cast<u32x4_a2*>(out) = u32x4_a2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                       pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
         } else {
           const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
