@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
     TGEMM_OK = 0,
     TGEMM_ERR_INVALID = 1,      /* bad pointer, size, stride or enum value      */
-    TGEMM_ERR_UNSUPPORTED = 2,  /* valid request this build cannot run          */
+    TGEMM_ERR_UNSUPPORTED = 2,  /* valid request the kernels do not support      */
     TGEMM_ERR_LAUNCH = 3        /* the HIP runtime refused the kernel launch    */
 } tgemm_status_t;
 

@@ -4,7 +4,7 @@ one MI355X measured, so box-to-box spread does not trip it).
 
 Opt-in: marked ``perf`` (run with ``pytest -m perf`` on a GPU); skipped
 without one.  The timing is the benchmark's own (bench.Case: warm-up, then
-HIP events around back-to-back launches); HBM-bound workloads are judged in
+HIP events around back-to-back launches); HBM-bound workloads are measured in
 GB/s of algorithmic bytes, MFMA-bound ones in TFLOP/s.
 """
 
