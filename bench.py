@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
                     help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
-                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt, thin_nt_m1..64, ffn_up_q8)")
+                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt, thin_nt_m1..64, ffn_up_q8, fp8_nt, fp8_ragged_nt)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -106,6 +106,8 @@ NT_CASES = {"square_nt": "square", "ffn_up_nt": "ffn_up", "ffn_down_nt": "ffn_do
 # The FFN up-projection with the FP8 1 x 128 activation quantiser in its
 # epilogue (codes + scales out, no bf16 output).
 Q8_CASES = {"ffn_up_q8": "ffn_up"}
+# The FP8 workloads with the weight stored [N, K] (K-contiguous).
+FP8_NT_CASES = {"fp8_nt": "fp8", "fp8_ragged_nt": "fp8_ragged"}
 LSM_CASES = {"lsm_m1": 1, "lsm_m8": 8, "lsm_m32": 32, "lsm_m64": 64}
 QUANT_CASES = {"quant_a": ("a", "tgemm_quant_fp8_1x128"), "quant_b": ("b", "tgemm_quant_fp8_128x128")}
 
@@ -153,6 +155,9 @@ class Case:
         if name in Q8_CASES:
             self._init_q8(name, dev)
             return
+        if name in FP8_NT_CASES:
+            self._init_fp8_nt(name, dev)
+            return
         w = wl.WORKLOADS[name]
         self.w = w
         self.M, self.N, self.K = w.M, w.N, w.K
@@ -194,6 +199,9 @@ class Case:
         if self.family == "w8":
             return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
                     f"(Q[{self.K},{self.N}] int8 * S[{(self.K + 127) // 128},{self.N}])")
+        if self.name in FP8_NT_CASES:
+            return (f"{self.name}: C[{self.M},{self.N}] = A[{self.M},{self.K}] . Bt[{self.N},{self.K}]^T "
+                    f"(FP8 e4m3, 1x128 / 128x128 scales, weight K-contiguous)")
         if self.family == "q8":
             return (f"{self.name}: Q, S = quantize_fp8_1x128(gelu(A[{self.M},{self.K}] . "
                     f"B[{self.K},{self.N}] + bias)) in one kernel")
@@ -256,6 +264,28 @@ class Case:
         thin = w.name.startswith("thin")
         self.bound, self.peak = ("hbm", PEAK_HBM_GBS) if thin else ("mfma", PEAK_BF16_TFLOPS)
         self.dtype = "bf16"
+        self.inputs_for_oracle = None
+
+    def _init_fp8_nt(self, name, dev):
+        import torch
+
+        import tiled_gemm_04_amd as tg
+        import workloads as wl
+
+        w = wl.WORKLOADS[FP8_NT_CASES[name]]
+        qa, sa, qb, sb = wl.fp8_inputs(w, device=dev)
+        bt = qb.t().contiguous()
+        del qb
+        c = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev)
+        self.launch = lambda: tg.gemm_fp8_blockscaled_nt(qa, sa, bt, sb, c)
+        self.w = None
+        self.M, self.N, self.K = w.M, w.N, w.K
+        self.flops = 2 * w.M * w.N * w.K
+        self.bytes = w.M * w.K + w.K * w.N + 2 * w.M * w.N + 4 * (sa.numel() + sb.numel())
+        self.kernel = "tgemm_fp8_bs_nt_256x256x128"
+        self.family = "fp8"
+        self.bound, self.peak = "mfma", PEAK_FP8_TFLOPS
+        self.dtype = "fp8_e4m3"
         self.inputs_for_oracle = None
 
     def _init_q8(self, name, dev):
@@ -457,7 +487,8 @@ def main():
                      "fp8_ragged", "tiny", "quant_a", "quant_b", "w8_m1", "w8_m8", "w8_m32",
                      "w8_m64", "w4_m1", "w4_m8", "w4_m32", "w4_m64", "lsm_m1", "lsm_m8", "lsm_m32",
                      "lsm_m64", "square_nt", "ffn_up_nt", "ffn_down_nt", "thin_nt_m1",
-                     "thin_nt_m8", "thin_nt_m32", "thin_nt_m64", "ffn_up_q8"):
+                     "thin_nt_m8", "thin_nt_m32", "thin_nt_m64", "ffn_up_q8", "fp8_nt",
+                     "fp8_ragged_nt"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

@@ -235,6 +235,31 @@ int gemm_fp8_blockscaled_ex(const void* A, const float* sA, const void* B, const
                             void* stream);
 
 /*
+ * gemm_fp8_blockscaled_nt -- gemm_fp8_blockscaled with the weight stored
+ * K-contiguous: C[i,j] = sum_g sA[i,g] * sB[g, j/128] * sum_{k in g} A[i,k] * Bt[j,k]
+ *
+ * The layout nn.Linear keeps its weight in ([out, in] = [N, K]), in which
+ * FP8 checkpoints are usually stored; the GEMM compute-cost page (section
+ * 5.2) asks for operands in the layout the kernel reads, so no transpose
+ * pass is needed.  Same scales and rounding as gemm_fp8_blockscaled:
+ *
+ *   A    e4m3fn bytes [M, K], packed row-major
+ *   sA   fp32 [M, ceil(K/128)]
+ *   Bt   e4m3fn bytes [N, K], packed row-major (row j = column j of B)
+ *   sB   fp32 [ceil(K/128), ceil(N/128)] (block (g, h) covers K rows
+ *        [128g, 128g+128) and columns [128h, 128h+128) of B), as before
+ *   C    bf16 [M, N], packed row-major
+ *
+ * The Bt tile is read like A's, so every MFMA operand holds the same bytes
+ * as in gemm_fp8_blockscaled on the transposed weight, and the results are
+ * equal bit for bit (same kernel schedule and tile split).  Supported:
+ * K % 16 == 0 (else TGEMM_ERR_UNSUPPORTED); any M, N, alignment.  Other
+ * errors as gemm_fp8_blockscaled.
+ */
+int gemm_fp8_blockscaled_nt(const void* A, const float* sA, const void* Bt, const float* sB,
+                            void* C, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * gemm_fp8_split_plan -- the tile split gemm_fp8_blockscaled_ex would use
  * (host only, no GPU call): for C [M, N] with K and `cus` compute units,
  * *whole tiles run whole and the last *split_tiles tiles run in *parts K

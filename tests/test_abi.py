@@ -293,3 +293,12 @@ def test_bf16_quant_fp8_validation():
     assert L.gemm_bf16_quant_fp8(FAKE, FAKE, NULL, FAKE, S, 8, 8, 12, 12, 8, 0, 0, NULL) == UNS  # K % 8
     assert L.gemm_bf16_quant_fp8(ctypes.c_void_p(0x1002), FAKE, NULL, FAKE, S, 8, 8, 8, 8, 8, 0, 0, NULL) == UNS
     assert L.gemm_bf16_quant_fp8(NULL, NULL, NULL, NULL, NULL, 0, 8, 8, 8, 8, 0, 0, NULL) == OK
+
+
+def test_fp8_nt_validation():
+    L = binding.lib()
+    assert L.gemm_fp8_blockscaled_nt(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 16, NULL) == INV
+    assert L.gemm_fp8_blockscaled_nt(FAKE, NULL, FAKE, FAKE, FAKE, 4, 4, 16, NULL) == INV
+    assert L.gemm_fp8_blockscaled_nt(FAKE, FAKE, FAKE, FAKE, NULL, 4, 4, 16, NULL) == INV
+    assert L.gemm_fp8_blockscaled_nt(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 24, NULL) == UNS  # K % 16
+    assert L.gemm_fp8_blockscaled_nt(NULL, NULL, NULL, NULL, NULL, 0, 4, 16, NULL) == OK

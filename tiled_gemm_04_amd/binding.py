@@ -73,6 +73,8 @@ def lib():
     L.gemm_fp8_split_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(i32),
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.gemm_fp8_split_plan.restype = i32
+    L.gemm_fp8_blockscaled_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    L.gemm_fp8_blockscaled_nt.restype = i32
     L.gemm_bf16_quant_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
     L.gemm_bf16_quant_fp8.restype = i32
     L.gemm_bf16_w8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
@@ -235,6 +237,32 @@ def gemm_bf16_quant_fp8(A, B, bias, Q, S, epilogue=EPI_NONE, algo=ALGO_AUTO, str
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_bf16_quant_fp8")
     return Q, S
+
+
+def gemm_fp8_blockscaled_nt(A, sA, Bt, sB, C, stream=None):
+    """gemm_fp8_blockscaled with the weight K-contiguous: Bt float8_e4m3fn [N, K].
+
+    A: float8_e4m3fn [M, K]; sA: float32 [M, ceil(K/128)]; sB: float32
+    [ceil(K/128), ceil(N/128)]; C: bfloat16 [M, N]; all contiguous.
+    """
+    _check_cuda(A, sA, Bt, sB, C)
+    if A.dtype != torch.float8_e4m3fn or Bt.dtype != torch.float8_e4m3fn:
+        raise ValueError("A and Bt must be float8_e4m3fn")
+    if sA.dtype != torch.float32 or sB.dtype != torch.float32 or C.dtype != torch.bfloat16:
+        raise ValueError("scales must be float32 and C bfloat16")
+    for t, n in ((A, "A"), (Bt, "Bt"), (sA, "sA"), (sB, "sB"), (C, "C")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous (packed row-major)")
+    M, K = A.shape
+    N, K2 = Bt.shape
+    G, H = (K + 127) // 128, (N + 127) // 128
+    if K2 != K or tuple(C.shape) != (M, N) or tuple(sA.shape) != (M, G) or tuple(sB.shape) != (G, H):
+        raise ValueError("shape mismatch")
+    st = lib().gemm_fp8_blockscaled_nt(_ptr(A), _ptr(sA), _ptr(Bt), _ptr(sB), _ptr(C), M, N, K,
+                                       _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_fp8_blockscaled_nt")
+    return C
 
 
 def gemm_fp8_split_plan(M, N, K, cus, split_parts=0):

@@ -158,6 +158,52 @@ int quantize_fp8(const void* X, void* Q, float* S, int64_t rows, int64_t cols, i
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
+// FP8 block-scaled GEMM with B given as [K, N] (bt false) or [N, K] (bt
+// true); the split plan and its scratch as gemm_fp8_blockscaled_ex documents.
+int fp8_call(const void* A, const float* sA, const void* B, const float* sB, void* C, int64_t M,
+             int64_t N, int64_t K, int split_parts, bool bt, void* stream) {
+  if (split_parts < 0 || split_parts > tgemm::kFp8MaxParts) return TGEMM_ERR_INVALID;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return TGEMM_ERR_INVALID;
+  if (M == 0 || N == 0) return TGEMM_OK;
+  if (C == nullptr) return TGEMM_ERR_INVALID;
+  if (K > 0 && (A == nullptr || B == nullptr || sA == nullptr || sB == nullptr))
+    return TGEMM_ERR_INVALID;
+  if (!extent_ok(M, K, K) || !extent_ok(M, N, N)) return TGEMM_ERR_INVALID;
+  if (bt ? !extent_ok(N, K, K) : !extent_ok(K, N, N)) return TGEMM_ERR_INVALID;
+  if (bt && !tgemm::fp8_nt_ok(M, N, K)) return TGEMM_ERR_UNSUPPORTED;
+
+  Fp8Args a;
+  a.A = static_cast<const uint8_t*>(A);
+  a.sA = sA;
+  a.B = static_cast<const uint8_t*>(B);
+  a.sB = sB;
+  a.C = static_cast<uint16_t*>(C);
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.G = static_cast<int>((K + 127) / 128);
+  a.H = static_cast<int>((N + 127) / 128);
+  a.vec_a = (aligned16(A) && K % 16 == 0) ? 1 : 0;
+  a.vec_b = bt ? a.vec_a : ((aligned8(B) && N % 8 == 0) ? 1 : 0);
+  a.vec_c = (aligned16(C) && N % 8 == 0) ? 1 : 0;
+  a.bt = bt ? 1 : 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // Split the tiles along K when they leave most compute units idle (scratch
+  // for the partial tiles and their counters); without scratch the split is
+  // skipped.
+  const tgemm::Fp8Split plan = tgemm::fp8_split_plan(M, N, K, tgemm::device_cus(), split_parts);
+  void* part = nullptr;
+  uint32_t* count = nullptr;
+  if (plan.parts > 1 && plan.split_tiles <= tgemm::kFp8MaxSplitTiles) {
+    part = tgemm::device_scratch(tgemm::fp8_split_part_bytes(plan), s, tgemm::kScratchFp8Part);
+    count = static_cast<uint32_t*>(tgemm::device_scratch(
+        tgemm::kFp8MaxSplitTiles * sizeof(uint32_t), s, tgemm::kScratchFp8Count, true));
+  }
+  const hipError_t e = tgemm::launch_fp8_blockscaled(a, plan, part, count, s);
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 namespace tgemm {
@@ -460,42 +506,12 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
 
 int gemm_fp8_blockscaled_ex(const void* A, const float* sA, const void* B, const float* sB, void* C,
                             int64_t M, int64_t N, int64_t K, int split_parts, void* stream) {
-  if (split_parts < 0 || split_parts > tgemm::kFp8MaxParts) return TGEMM_ERR_INVALID;
-  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
-    return TGEMM_ERR_INVALID;
-  if (M == 0 || N == 0) return TGEMM_OK;
-  if (C == nullptr) return TGEMM_ERR_INVALID;
-  if (K > 0 && (A == nullptr || B == nullptr || sA == nullptr || sB == nullptr))
-    return TGEMM_ERR_INVALID;
-  if (!extent_ok(M, K, K) || !extent_ok(K, N, N) || !extent_ok(M, N, N)) return TGEMM_ERR_INVALID;
+  return fp8_call(A, sA, B, sB, C, M, N, K, split_parts, false, stream);
+}
 
-  Fp8Args a;
-  a.A = static_cast<const uint8_t*>(A);
-  a.sA = sA;
-  a.B = static_cast<const uint8_t*>(B);
-  a.sB = sB;
-  a.C = static_cast<uint16_t*>(C);
-  a.M = static_cast<int>(M);
-  a.N = static_cast<int>(N);
-  a.K = static_cast<int>(K);
-  a.G = static_cast<int>((K + 127) / 128);
-  a.H = static_cast<int>((N + 127) / 128);
-  a.vec_a = (aligned16(A) && K % 16 == 0) ? 1 : 0;
-  a.vec_b = (aligned8(B) && N % 8 == 0) ? 1 : 0;
-  a.vec_c = (aligned16(C) && N % 8 == 0) ? 1 : 0;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  // Split the last, partly filled round of tiles along K (scratch for the
-  // partial tiles and their counters); without scratch the split is skipped.
-  const tgemm::Fp8Split plan = tgemm::fp8_split_plan(M, N, K, tgemm::device_cus(), split_parts);
-  void* part = nullptr;
-  uint32_t* count = nullptr;
-  if (plan.parts > 1 && plan.split_tiles <= tgemm::kFp8MaxSplitTiles) {
-    part = tgemm::device_scratch(tgemm::fp8_split_part_bytes(plan), s, tgemm::kScratchFp8Part);
-    count = static_cast<uint32_t*>(tgemm::device_scratch(
-        tgemm::kFp8MaxSplitTiles * sizeof(uint32_t), s, tgemm::kScratchFp8Count, true));
-  }
-  const hipError_t e = tgemm::launch_fp8_blockscaled(a, plan, part, count, s);
-  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+int gemm_fp8_blockscaled_nt(const void* A, const float* sA, const void* Bt, const float* sB, void* C,
+                            int64_t M, int64_t N, int64_t K, void* stream) {
+  return fp8_call(A, sA, Bt, sB, C, M, N, K, 0, true, stream);
 }
 
 int gemm_bf16_w8(const void* X, const void* Q, const float* S, const void* bias, void* C,

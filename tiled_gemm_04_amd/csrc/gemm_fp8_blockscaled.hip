@@ -218,6 +218,10 @@ struct SplitTail {
   uint32_t* count;
 };
 
+// BT: B given as [N, K] (K-contiguous rows, the nn.Linear weight layout);
+// its tile is then loaded, stored and read exactly like A's, and its MFMA
+// operands carry the same bytes as the [K, N] path's transposed reads.
+template <bool BT>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args p, int tiles_m,
                                                                      int tiles_n, SplitTail st) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
@@ -261,6 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   // 32 + b holds B rows 4b .. 4b+3; slot 64b + lane holds chunk
   // (slot % chunks-per-row) ^ swizzle(row) of its row. ----
   const bool loads_a = wave < 4;
+  const bool a_like = loads_a || BT;  // rows are K-contiguous, 8 per block
   const int blk0 = (wave & 3) * kBlocksPerWave;
   // A block blk (rows 8 blk .. +7): slot 64 blk + lane is row 8 blk + lane/8,
   // physical chunk lane % 8, logical chunk (lane % 8) ^ a_swz(row), and
@@ -269,12 +274,12 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   // lane % 16, and b_swz(row) likewise has two forms by the parity of blk
   // (bit 3 of it is (wave & 3) & 1 for every block of this wave).  The row
   // offset of the block is a wave-uniform addend, so a lane keeps only its
-  // two in-block offsets.
+  // two in-block offsets.  With BT, B blocks hold 8 rows of [N, K] like A's.
   int lc[2];       // logical chunk for even / odd blocks
   uint32_t vo[2];  // in-block byte offset for even / odd blocks
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
-    if (loads_a) {
+    if (a_like) {
       lc[par] = (lane & 7) ^ a_swz(8 * par + (lane >> 3));
       vo[par] = static_cast<uint32_t>((lane >> 3) * p.K + 16 * lc[par]);
     } else {
@@ -289,11 +294,13 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   // starts at win0 + g * wstep and spans wsize0 - g * wstep bytes (A rows
   // m0 .. M-1 from column 128 g; B rows 128 g .. K-1 from column n0), so
   // bytes past M or K read as zeros.
-  const uint8_t* win0 = loads_a ? p.A + static_cast<int64_t>(m0) * p.K : p.B + n0;
+  const uint8_t* win0 = loads_a ? p.A + static_cast<int64_t>(m0) * p.K
+                                : (BT ? p.B + static_cast<int64_t>(n0) * p.K : p.B + n0);
   const int64_t wsize0 = loads_a ? static_cast<int64_t>(p.M - m0 - 1) * p.K + p.K
-                                 : static_cast<int64_t>(p.K - 1) * p.N + (p.N - n0);
-  const int64_t wstep = loads_a ? int64_t{kBK} : int64_t{kBK} * p.N;
-  const uint32_t blk_stride = loads_a ? 8u * p.K : 4u * p.N;  // bytes per block of rows
+                                 : (BT ? static_cast<int64_t>(p.N - n0 - 1) * p.K + p.K
+                                       : static_cast<int64_t>(p.K - 1) * p.N + (p.N - n0));
+  const int64_t wstep = a_like ? int64_t{kBK} : int64_t{kBK} * p.N;
+  const uint32_t blk_stride = a_like ? 8u * p.K : 4u * p.N;  // bytes per block of rows
   auto window = [&](int g) {
     return make_window_words(win0 + g * wstep, wsize0 - g * wstep);
   };
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   // and a large negative number for B waves (no column check).
   int kc[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) kc[par] = loads_a ? 16 * lc[par] : -(1 << 30);
+  for (int par = 0; par < 2; ++par) kc[par] = a_like ? 16 * lc[par] : -(1 << 30);
   const uint32_t dst0 = smem_base + (loads_a ? 0u : static_cast<uint32_t>(kAStage)) +
                         static_cast<uint32_t>(blk0) * 1024u;
   const uint32_t off0 = static_cast<uint32_t>(blk0) * blk_stride;
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   };
   // The tile holding column N-1 adds the products that the range check
   // drops from B's last row (add_tail_products).
-  const bool tail_tile = (p.N & 3) != 0 && n0 + kBN >= p.N;
+  const bool tail_tile = !BT && (p.N & 3) != 0 && n0 + kBN >= p.N;
 
   // ---- LDS -> registers ----
   const int l16 = lane & 15;
@@ -335,23 +342,40 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   const int a_off1 = a_row * kBK + (((2 * lq + 1) ^ a_swz(l16)) * 16);
   // B operand of column block j: column chunk cj = 4 wn + j; transposed read
   // s covers K rows 32 lq + 8 s + e for lane 16 lq + 2 e + h, columns 8 h .. +7.
+  // BT: column block j is row block 4 wn + j of the [N, K] tile, read like
+  // an A operand (b_off[0], b_off[1]: its two chunks in block 0).
   const int be = l16 >> 1, bh = l16 & 1;
   int b_off[kFN];
+  if constexpr (BT) {
+    const int b_row = wn * kWTN + l16;
+    b_off[0] = kAStage + b_row * kBK + (((2 * lq) ^ a_swz(l16)) * 16);
+    b_off[1] = kAStage + b_row * kBK + (((2 * lq + 1) ^ a_swz(l16)) * 16);
+    b_off[2] = b_off[3] = 0;
+  } else {
 #pragma unroll
-  for (int j = 0; j < kFN; ++j) {
-    const int k = 32 * lq + be;
-    b_off[j] = kAStage + k * kBN + (((4 * wn + j) ^ b_swz(k)) * 16) + 8 * bh;
+    for (int j = 0; j < kFN; ++j) {
+      const int k = 32 * lq + be;
+      b_off[j] = kAStage + k * kBN + (((4 * wn + j) ^ b_swz(k)) * 16) + 8 * bh;
+    }
   }
   i32x8 fb[kFN];
   i32x8 fa[2];
   float srow[2];  // sA of the row block whose FMAs are pending / next (times sB at fold)
   f32x4 part[kFN];
   auto read_b = [&](int stage, int j) {
-    const uint8_t* base = smem + stage * kStage + b_off[j];
-    i32x2 q[4];
+    if constexpr (BT) {
+      const uint8_t* base = smem + stage * kStage + 16 * j * kBK;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(base + b_off[0]);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(base + b_off[1]);
+      fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
+      const uint8_t* base = smem + stage * kStage + b_off[j];
+      i32x2 q[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) q[s] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + s * 8 * kBN));
-    fb[j] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+      for (int s = 0; s < 4; ++s)
+        q[s] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + s * 8 * kBN));
+      fb[j] = i32x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+    }
   };
   auto read_a = [&](int stage, int i) {
     const uint8_t* base = smem + stage * kStage + 16 * i * kBK;
@@ -530,6 +554,13 @@ bool fp8_direct_ok(int64_t M, int64_t N, int64_t K) {
          static_cast<int64_t>(kBM) * ((K + 127) / 128) * 4 < (int64_t{1} << 31);
 }
 
+bool fp8_nt_ok(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  // Per-lane offsets: a tile's 256 rows of A and of Bt.
+  return K % 16 == 0 && K * kBM < (int64_t{1} << 31) && K * kBN < (int64_t{1} << 31) &&
+         static_cast<int64_t>(kBM) * ((K + 127) / 128) * 4 < (int64_t{1} << 31);
+}
+
 const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K) {
   return fp8_direct_ok(M, N, K) ? "tgemm_fp8_bs_256x256x128" : "tgemm_fp8_bs_general_256x128x128";
 }
@@ -568,7 +599,8 @@ size_t fp8_split_part_bytes(const Fp8Split& plan) {
 
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* part, uint32_t* count,
                                   hipStream_t s) {
-  if (!fp8_direct_ok(a.M, a.N, a.K)) return launch_fp8_general(a, s);
+  if (a.bt && !fp8_nt_ok(a.M, a.N, a.K)) return hipErrorInvalidValue;
+  if (!a.bt && !fp8_direct_ok(a.M, a.N, a.K)) return launch_fp8_general(a, s);
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.N + kBN - 1) / kBN;
   SplitTail st{tiles_m * tiles_n, 0, 1, nullptr, nullptr};
@@ -580,8 +612,13 @@ hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* 
     st.part = static_cast<f32x4*>(part);
     st.count = count;
   }
-  hipLaunchKernelGGL(tgemm_fp8_bs_256x256x128, dim3(st.whole + st.split_tiles * st.parts),
-                     dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
+  if (a.bt) {
+    hipLaunchKernelGGL(tgemm_fp8_bs_256x256x128<true>, dim3(st.whole + st.split_tiles * st.parts),
+                       dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
+  } else {
+    hipLaunchKernelGGL(tgemm_fp8_bs_256x256x128<false>, dim3(st.whole + st.split_tiles * st.parts),
+                       dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
+  }
   return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ struct Fp8Args {
   int vec_a;  // 1: A rows are 16-byte aligned (K % 16 == 0 and aligned base)
   int vec_b;  // 1: B rows are 8-byte aligned (N % 8 == 0 and aligned base)
   int vec_c;  // 1: C rows may be written with 16-byte stores (N % 8 == 0, aligned base)
+  int bt = 0;  // 1: B is given as [N, K] (K-contiguous rows, packed)
 };
 
 // FP8 quantiser problem: bf16 X [rows, cols] (row stride ldx) -> e4m3fn
@@ -173,5 +174,7 @@ hipError_t launch_quant_fp8_128x128(const QuantArgs& a, hipStream_t stream);
 const char* thin_kernel_name(int M);
 const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K);
 bool fp8_direct_ok(int64_t M, int64_t N, int64_t K);
+// The direct kernel with B as [N, K]: K % 16 == 0 and offsets below 2^31.
+bool fp8_nt_ok(int64_t M, int64_t N, int64_t K);
 
 }  // namespace tgemm
