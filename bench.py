@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square",
                     help="headline workload (square, ffn_up, ffn_down, thin_m1..64, fp8, fp8_ragged, "
-                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt, thin_nt_m1..64, ffn_up_q8, fp8_nt, fp8_ragged_nt)")
+                         "tiny, quant_a, quant_b, w8_m1..64, w4_m1..64, lsm_m1..64, square_nt, ffn_up_nt, ffn_down_nt, thin_nt_m1..64, ffn_up_q8, fp8_nt, fp8_ragged_nt, w8_lsm_m1/m64, w4_lsm_m1/m64)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
@@ -90,12 +90,15 @@ KERNEL_SOURCES = {
     "lsm": ["common.h", "launch.h", "gemm_bf16_thin.hip"],
     "nt": ["common.h", "launch.h", "gemm_bf16_tiled.hip", "gemm_bf16_thin.hip"],
     "q8": ["common.h", "launch.h", "gemm_bf16_tiled.hip"],
+    "wq_lsm": ["common.h", "launch.h", "gemm_wq_thin.hip", "gemm_bf16_thin.hip"],
 }
 
 # Weight-only int8 LM head: the thin-M workloads' X [M, 4096] times int8
 # codes Q [4096, 128256] with fp32 scales per (128 rows, column).
 W8_CASES = {"w8_m1": 1, "w8_m8": 8, "w8_m32": 32, "w8_m64": 64,
-            "w4_m1": 1, "w4_m8": 8, "w4_m32": 32, "w4_m64": 64}
+            "w4_m1": 1, "w4_m8": 8, "w4_m32": 32, "w4_m64": 64,
+            # the same heads with bias and log-softmax fused (two kernels per call)
+            "w8_lsm_m1": 1, "w8_lsm_m64": 64, "w4_lsm_m1": 1, "w4_lsm_m64": 64}
 
 # FP8 quantisers, timed on the FP8 workload's unquantised operands (bf16):
 # activations A [4096, 4096] in 1 x 128 groups, weights B [4096, 14336] in
@@ -196,6 +199,10 @@ class Case:
         if self.family == "quant":
             grouping = "1x128" if self.name == "quant_a" else "128x128"
             return f"{self.name}: Q, S = quantize_fp8_{grouping}(X[{self.M},{self.N}] bf16)"
+        if self.family == "wq_lsm":
+            code = "int8" if self.name.startswith("w8") else "int4, two per byte"
+            return (f"{self.name}: C[{self.M},{self.N}] = log_softmax(X[{self.M},{self.K}] . "
+                    f"(Q[{self.K},{self.N}] {code} * S) + bias[{self.N}]) over each row")
         if self.family == "w8":
             return (f"{self.name}: C[{self.M},{self.N}] = X[{self.M},{self.K}] . "
                     f"(Q[{self.K},{self.N}] int8 * S[{(self.K + 127) // 128},{self.N}])")
@@ -228,8 +235,6 @@ class Case:
         bits = 8 if name.startswith("w8") else 4
         q, s = (wl.w8_weights if bits == 8 else wl.w4_weights)(K, N, w.seed, dev)
         c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        fn = tg.gemm_bf16_w8 if bits == 8 else tg.gemm_bf16_w4
-        self.launch = lambda: fn(x, q, s, None, c)
         self.w = None
         self.M, self.N, self.K = M, N, K
         self.flops = 2 * M * N * K
@@ -237,6 +242,18 @@ class Case:
         self.bytes = 2 * M * K + q.numel() + 4 * s.numel() + 2 * M * N
         self.kernel = (tg.gemm_w8_kernel_name if bits == 8 else tg.gemm_w4_kernel_name)(M, N, K)
         self.family = "w8" if bits == 8 else "w4"
+        if "_lsm_" in name:
+            b = wl.bf16((N,), "normal", 0.02, w.seed, wl.T_BIAS, dev)
+            ws = torch.empty(tg.gemm_logsoftmax_workspace_size(M, N, tg.OUT_BF16), dtype=torch.uint8,
+                             device=dev)
+            fn = tg.gemm_bf16_w8_logsoftmax if bits == 8 else tg.gemm_bf16_w4_logsoftmax
+            self.launch = lambda: fn(x, q, s, b, c, workspace=ws)
+            self.bytes += 2 * N  # the bias
+            self.kernel = self.kernel.replace("_thin_", "_thin_lsm_")
+            self.family = "wq_lsm"
+        else:
+            fn = tg.gemm_bf16_w8 if bits == 8 else tg.gemm_bf16_w4
+            self.launch = lambda: fn(x, q, s, None, c)
         self.bound, self.peak = "hbm", PEAK_HBM_GBS
         self.dtype = "bf16 x int8" if bits == 8 else "bf16 x int4"
         self.inputs_for_oracle = None
@@ -488,7 +505,7 @@ def main():
                      "w8_m64", "w4_m1", "w4_m8", "w4_m32", "w4_m64", "lsm_m1", "lsm_m8", "lsm_m32",
                      "lsm_m64", "square_nt", "ffn_up_nt", "ffn_down_nt", "thin_nt_m1",
                      "thin_nt_m8", "thin_nt_m32", "thin_nt_m64", "ffn_up_q8", "fp8_nt",
-                     "fp8_ragged_nt"):
+                     "fp8_ragged_nt", "w8_lsm_m1", "w8_lsm_m64", "w4_lsm_m1", "w4_lsm_m64"):
             if name == args.workload:
                 continue
             c = Case(name, dev)

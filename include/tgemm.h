@@ -305,6 +305,30 @@ int gemm_bf16_logsoftmax(const void* X, const void* W, const void* bias, void* C
                          int64_t ldx, int64_t ldw, int64_t ldc, int out_dtype,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * gemm_bf16_w8_logsoftmax, gemm_bf16_w4_logsoftmax -- the weight-only int8 /
+ * int4 LM head with bias and log-softmax over each row:
+ *   C[i,n] = y[i,n] - log sum_n' exp(y[i,n']),  y = X (q s) + bias
+ *
+ * The GEMM compute-cost page's two remedies for the LM head (section 7.2)
+ * together: the integer weight of gemm_bf16_w8 / gemm_bf16_w4 (plan A) and
+ * the fused bias + LogSoftmax of gemm_bf16_logsoftmax (plan B).  Weight
+ * codes, scales and their layouts as gemm_bf16_w8 / gemm_bf16_w4; bias,
+ * output, workspace (gemm_logsoftmax_workspace_size(M, N, out_dtype) bytes)
+ * and the two-pass scheme as gemm_bf16_logsoftmax.  Supported: the integer
+ * heads' shapes (M <= 64, K % 8 == 0, N % 4 == 0, ldq % 4 == 0); others
+ * return TGEMM_ERR_UNSUPPORTED.  N == 0 with M > 0, a NULL or short
+ * workspace and the gemm_bf16_w8 argument errors return TGEMM_ERR_INVALID.
+ * Returns TGEMM_OK, TGEMM_ERR_INVALID, TGEMM_ERR_UNSUPPORTED or
+ * TGEMM_ERR_LAUNCH.
+ */
+int gemm_bf16_w8_logsoftmax(const void* X, const void* Q, const float* S, const void* bias, void* C,
+                            int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                            int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+int gemm_bf16_w4_logsoftmax(const void* X, const void* Q, const float* S, const void* bias, void* C,
+                            int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                            int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Bytes of workspace gemm_bf16_logsoftmax needs: M * ceil(N/512) * 8
  * rounded up to a multiple of 256, plus M * N * 4 when out_dtype is
  * TGEMM_OUT_BF16; -1 for negative or oversized sizes or an unknown

@@ -202,6 +202,26 @@ def gemm_bf16_logsoftmax_bits(x_bits, w_bits, bias_bits=None):
     return out, 2.0 * np.max(d, axis=1, keepdims=True) + np.abs(out)
 
 
+def _logsoftmax_with_denominators(y, d):
+    out = log_softmax_rows(y)
+    return out, 2.0 * np.max(d, axis=1, keepdims=True) + np.abs(out)
+
+
+def gemm_bf16_w8_logsoftmax_bits(x_bits, q, s, bias_bits=None):
+    """Oracle for the int8-weight LM head with bias and log-softmax (the GEMM
+    compute-cost page, section 7.2, plans A and B together): the row-wise
+    log-softmax of ``x (q s) + b`` and the denominators of
+    gemm_bf16_logsoftmax_bits."""
+    y, d = gemm_bf16_w8_bits(x_bits, q, s, bias_bits, EPI_BIAS if bias_bits is not None else EPI_NONE)
+    return _logsoftmax_with_denominators(y, d)
+
+
+def gemm_bf16_w4_logsoftmax_bits(x_bits, packed, s, bias_bits=None):
+    """As gemm_bf16_w8_logsoftmax_bits for packed int4 codes."""
+    y, d = gemm_bf16_w4_bits(x_bits, packed, s, bias_bits, EPI_BIAS if bias_bits is not None else EPI_NONE)
+    return _logsoftmax_with_denominators(y, d)
+
+
 def gemm_fp8_blockscaled_bits(qa_bits, sa, qb_bits, sb):
     """Oracle for the FP8 block-scaled path: dequantise, then contract."""
     return gemm_f64(dequant_fp8_a(qa_bits, sa), dequant_fp8_b(qb_bits, sb))

@@ -302,3 +302,17 @@ def test_fp8_nt_validation():
     assert L.gemm_fp8_blockscaled_nt(FAKE, FAKE, FAKE, FAKE, NULL, 4, 4, 16, NULL) == INV
     assert L.gemm_fp8_blockscaled_nt(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 24, NULL) == UNS  # K % 16
     assert L.gemm_fp8_blockscaled_nt(NULL, NULL, NULL, NULL, NULL, 0, 4, 16, NULL) == OK
+
+
+def test_wq_logsoftmax_validation():
+    L = binding.lib()
+    WS = ctypes.c_void_p(0x3000)
+    for f in (L.gemm_bf16_w8_logsoftmax, L.gemm_bf16_w4_logsoftmax):
+        # X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, out, ws, ws_bytes
+        assert f(FAKE, FAKE, FAKE, NULL, FAKE, 2, 0, 64, 64, 0, 0, 1, WS, 1 << 20, NULL) == INV  # N == 0
+        assert f(FAKE, FAKE, FAKE, NULL, FAKE, 2, 512, 64, 64, 512, 512, 1, NULL, 1 << 20, NULL) == INV
+        assert f(FAKE, FAKE, FAKE, NULL, FAKE, 2, 512, 64, 64, 512, 512, 1, WS, 16, NULL) == INV  # short
+        assert f(FAKE, FAKE, NULL, NULL, FAKE, 2, 512, 64, 64, 512, 512, 1, WS, 1 << 20, NULL) == INV  # S
+        assert f(FAKE, FAKE, FAKE, NULL, FAKE, 65, 512, 64, 64, 512, 512, 1, WS, 1 << 24, NULL) == UNS  # M
+        assert f(FAKE, FAKE, FAKE, NULL, FAKE, 2, 510, 64, 64, 512, 512, 1, WS, 1 << 20, NULL) == UNS  # N % 4
+        assert f(NULL, NULL, NULL, NULL, NULL, 0, 512, 64, 64, 512, 512, 1, NULL, 0, NULL) == OK

@@ -623,3 +623,41 @@ def test_nt_oracle_brute_force_and_transpose_relation():
     y1, d1 = gemm.gemm_bf16_nt_bits(ab, btb, bias, gemm.EPI_BIAS_GELU_TANH)
     y2, d2 = gemm.gemm_bf16_bits(ab, np.ascontiguousarray(btb.T), bias, gemm.EPI_BIAS_GELU_TANH)
     assert np.array_equal(y1, y2) and np.array_equal(d1, d2)
+
+
+def test_w8_logsoftmax_equals_bf16_head_on_bf16_exact_weights():
+    """With power-of-two scales the int8 weights are exact in bf16: the int8
+    log-softmax oracle must equal the bf16 one (values and denominators), with
+    and without bias; the int4 oracle on the same codes packed must equal the
+    int8 one; every row sums to 1 in probability."""
+    rng = np.random.default_rng(61)
+    M, K, N = 4, 256, 300
+    xb = formats.bf16_encode_rne(rng.standard_normal((M, K)).astype(np.float32))
+    q = rng.integers(-7, 8, (K, N)).astype(np.int8)
+    s = np.ldexp(1.0, rng.integers(-8, -3, (2, N))).astype(np.float32)
+    wb = formats.bf16_encode_rne(gemm.dequant_w8(q, s).astype(np.float32))
+    bb = formats.bf16_encode_rne((0.3 * rng.standard_normal(N)).astype(np.float32))
+    for bias in (None, bb):
+        o8, d8 = gemm.gemm_bf16_w8_logsoftmax_bits(xb, q, s, bias)
+        ob, db = gemm.gemm_bf16_logsoftmax_bits(xb, wb, bias)
+        assert np.array_equal(o8, ob) and np.array_equal(d8, db)
+        o4, d4 = gemm.gemm_bf16_w4_logsoftmax_bits(xb, quant.pack_int4(q), s, bias)
+        assert np.array_equal(o4, o8) and np.array_equal(d4, d8)
+        assert np.allclose(np.exp(o8).sum(axis=1), 1.0, rtol=1e-12)
+
+
+def test_w8_logsoftmax_brute_force_small():
+    """A 2 x 3 case by hand: logits from explicit loops over the dequantised
+    weights, then log-softmax by its definition."""
+    xb = formats.bf16_encode_rne(np.array([[1.0, -2.0], [0.5, 0.25]], dtype=np.float32))
+    q = np.array([[3, -1, 0], [2, 5, -7]], dtype=np.int8)
+    s = np.array([[0.5, 0.25, 2.0]], dtype=np.float32)
+    bias = formats.bf16_encode_rne(np.array([0.125, -1.0, 0.0], dtype=np.float32))
+    x = formats.bf16_decode(xb)
+    b = formats.bf16_decode(bias)
+    out, _ = gemm.gemm_bf16_w8_logsoftmax_bits(xb, q, s, bias)
+    for i in range(2):
+        y = [sum(x[i, k] * q[k, n] * float(s[0, n]) for k in range(2)) + b[n] for n in range(3)]
+        lse = math.log(sum(math.exp(v) for v in y))
+        for n in range(3):
+            assert abs(out[i, n] - (y[n] - lse)) <= 1e-14 * max(1.0, abs(y[n] - lse))

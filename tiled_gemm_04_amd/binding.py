@@ -73,6 +73,9 @@ def lib():
     L.gemm_fp8_split_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(i32),
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.gemm_fp8_split_plan.restype = i32
+    for f in ("gemm_bf16_w8_logsoftmax", "gemm_bf16_w4_logsoftmax"):
+        getattr(L, f).argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, i64, vp]
+        getattr(L, f).restype = i32
     L.gemm_fp8_blockscaled_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.gemm_fp8_blockscaled_nt.restype = i32
     L.gemm_bf16_quant_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
@@ -422,6 +425,49 @@ def gemm_bf16_w4(X, Q, S, bias, C, epilogue=EPI_NONE, stream=None):
     code (2r, n) in its low nibble and (2r+1, n) in its high nibble, each a
     4-bit two's-complement value."""
     return _weight_only("gemm_bf16_w4", 4, X, Q, S, bias, C, epilogue, stream)
+
+
+def _weight_only_logsoftmax(name, bits, X, Q, S, bias, C, workspace, stream):
+    _check_cuda(X, Q, S, bias, C)
+    qdt = torch.int8 if bits == 8 else torch.uint8
+    if X.dtype != torch.bfloat16 or Q.dtype != qdt or S.dtype != torch.float32:
+        raise ValueError(f"X must be bfloat16, Q {qdt} and S float32")
+    if C.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("C must be bfloat16 or float32")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    ldx, ldq, ldc = _row_major(X, "X"), _row_major(Q, "Q"), _row_major(C, "C")
+    M, K = X.shape
+    Kq, N = Q.shape
+    if bits == 4 and K % 2:
+        raise ValueError("int4 codes pair up along K: K must be even")
+    if Kq != (K if bits == 8 else K // 2) or tuple(C.shape) != (M, N) \
+            or tuple(S.shape) != ((K + 127) // 128, N) or (bias is not None and bias.numel() != N):
+        raise ValueError("shape mismatch")
+    if not S.is_contiguous():
+        raise ValueError("S must be contiguous")
+    out = OUT_BF16 if C.dtype == torch.bfloat16 else OUT_F32
+    need = gemm_logsoftmax_workspace_size(M, N, out)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    _check_cuda(workspace)
+    st = getattr(lib(), name)(_ptr(X), _ptr(Q), _ptr(S), _ptr(bias), _ptr(C), M, N, K, ldx, ldq, ldc,
+                              out, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, name)
+    return C
+
+
+def gemm_bf16_w8_logsoftmax(X, Q, S, bias, C, workspace=None, stream=None):
+    """C[M,N] = log_softmax(X @ (Q * S[k/128, n]) + bias, over N): the int8 LM head
+    of gemm_bf16_w8 with the fused log-softmax of gemm_bf16_logsoftmax."""
+    return _weight_only_logsoftmax("gemm_bf16_w8_logsoftmax", 8, X, Q, S, bias, C, workspace, stream)
+
+
+def gemm_bf16_w4_logsoftmax(X, Q, S, bias, C, workspace=None, stream=None):
+    """gemm_bf16_w8_logsoftmax with int4 codes packed two per byte along K."""
+    return _weight_only_logsoftmax("gemm_bf16_w4_logsoftmax", 4, X, Q, S, bias, C, workspace, stream)
 
 
 def gemm_w8_kernel_name(M, N, K):

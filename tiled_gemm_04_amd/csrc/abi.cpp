@@ -130,6 +130,62 @@ int gemm_weight_only(int bits, const void* X, const void* Q, const float* S, con
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
+// Workspace split of the log-softmax heads: (max, sum exp) pairs first,
+// rounded up to 256 bytes, then the fp32 logits when the output is bf16
+// (fp32 output holds them in C itself).
+tgemm::LsmArgs lsm_args(void* workspace, int64_t M, int64_t N, int out_dtype, void* C, int64_t ldc,
+                        int vec_c) {
+  tgemm::LsmArgs q;
+  q.part = static_cast<float2*>(workspace);
+  q.G = static_cast<int>(tgemm::lsm_workgroups(N));
+  if (out_dtype == TGEMM_OUT_F32) {
+    q.logits = static_cast<float*>(C);
+    q.ldl = ldc;
+    q.vec_l = vec_c;
+  } else {
+    q.logits = reinterpret_cast<float*>(static_cast<char*>(workspace) + (M * q.G * 8 + 255) / 256 * 256);
+    q.ldl = N;
+    q.vec_l = aligned16(q.logits) ? 1 : 0;
+  }
+  return q;
+}
+
+int64_t lsm_workspace_bytes(int64_t M, int64_t N, int out_dtype) {
+  const int64_t pairs = (M * tgemm::lsm_workgroups(N) * 8 + 255) / 256 * 256;
+  return pairs + (out_dtype == TGEMM_OUT_BF16 ? M * N * 4 : 0);
+}
+
+int gemm_wq_logsoftmax(int bits, const void* X, const void* Q, const float* S, const void* bias,
+                       void* C, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                       int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (M > 0 && N == 0) return TGEMM_ERR_INVALID;  // no distribution over zero columns
+  const int v = validate_bf16(X, Q, bias, C, M, N, K, ldx, ldq, ldc, TGEMM_EPI_NONE, out_dtype,
+                              TGEMM_ALGO_AUTO);
+  if (v != TGEMM_OK || M == 0) return v;
+  if (K > 0 && S == nullptr) return TGEMM_ERR_INVALID;
+  if (workspace == nullptr || workspace_bytes < lsm_workspace_bytes(M, N, out_dtype))
+    return TGEMM_ERR_INVALID;
+  if (!tgemm::wq_supported(bits, M, N, K, ldx, ldq)) return TGEMM_ERR_UNSUPPORTED;
+  tgemm::W8Args a;
+  a.X = static_cast<const uint16_t*>(X);
+  a.Q = static_cast<const uint8_t*>(Q);
+  a.S = S;
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.C = C;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.ldx = ldx;
+  a.ldq = ldq;
+  a.ldc = ldc;
+  const int64_t out_align = out_dtype == TGEMM_OUT_BF16 ? 8 : 4;
+  a.vec_c = (aligned16(C) && ldc % out_align == 0) ? 1 : 0;
+  const tgemm::LsmArgs q = lsm_args(workspace, M, N, out_dtype, C, ldc, a.vec_c);
+  const hipError_t e = tgemm::launch_wq_thin_lsm(bits, a, q, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
 const char* weight_only_name(int bits, int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return nullptr;
   if (!tgemm::wq_supported(bits, M, N, K, K, N)) return nullptr;
@@ -450,10 +506,21 @@ int gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M
 int64_t gemm_logsoftmax_workspace_size(int64_t M, int64_t N, int out_dtype) {
   if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return -1;
   if (out_dtype != TGEMM_OUT_F32 && out_dtype != TGEMM_OUT_BF16) return -1;
-  // Per-stripe pairs, rounded up to 256 bytes, then fp32 logits when the
-  // output is bf16.
-  const int64_t pairs = (M * tgemm::lsm_workgroups(N) * 8 + 255) / 256 * 256;
-  return pairs + (out_dtype == TGEMM_OUT_BF16 ? M * N * 4 : 0);
+  return lsm_workspace_bytes(M, N, out_dtype);
+}
+
+int gemm_bf16_w8_logsoftmax(const void* X, const void* Q, const float* S, const void* bias, void* C,
+                            int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                            int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm_wq_logsoftmax(8, X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, out_dtype, workspace,
+                            workspace_bytes, stream);
+}
+
+int gemm_bf16_w4_logsoftmax(const void* X, const void* Q, const float* S, const void* bias, void* C,
+                            int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
+                            int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm_wq_logsoftmax(4, X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, out_dtype, workspace,
+                            workspace_bytes, stream);
 }
 
 int gemm_bf16_logsoftmax(const void* X, const void* W, const void* bias, void* C, int64_t M,
@@ -481,19 +548,7 @@ int gemm_bf16_logsoftmax(const void* X, const void* W, const void* bias, void* C
   const int64_t out_align = out_dtype == TGEMM_OUT_BF16 ? 8 : 4;
   a.vec_c = (aligned16(C) && ldc % out_align == 0) ? 1 : 0;
   if (!tgemm::lsm_direct_ok(a)) return TGEMM_ERR_UNSUPPORTED;
-  tgemm::LsmArgs q;
-  q.part = static_cast<float2*>(workspace);
-  q.G = static_cast<int>(tgemm::lsm_workgroups(N));
-  if (out_dtype == TGEMM_OUT_F32) {
-    q.logits = static_cast<float*>(C);
-    q.ldl = ldc;
-    q.vec_l = a.vec_c;
-  } else {
-    q.logits = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        (M * q.G * 8 + 255) / 256 * 256);
-    q.ldl = N;
-    q.vec_l = aligned16(q.logits) ? 1 : 0;
-  }
+  const tgemm::LsmArgs q = lsm_args(workspace, M, N, out_dtype, C, ldc, a.vec_c);
   const hipError_t e = tgemm::launch_bf16_thin_lsm(a, q, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
                                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;

@@ -698,6 +698,16 @@ bool lsm_direct_ok(const Bf16Args& a) {
          a.ldb * 2 * kBK < (int64_t{1} << 31) && a.lda * 2 * 64 < (int64_t{1} << 31);
 }
 
+hipError_t launch_lsm_normalize(const LsmArgs& q, void* C, int64_t ldc, int M, int N, int vec_c,
+                                int out_bf16, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((N + kChunk - 1) / kChunk), static_cast<unsigned>(M));
+  if (out_bf16)
+    hipLaunchKernelGGL((tgemm_lsm_normalize<true>), grid, dim3(256), 0, s, q, C, ldc, N, vec_c);
+  else
+    hipLaunchKernelGGL((tgemm_lsm_normalize<false>), grid, dim3(256), 0, s, q, C, ldc, N, vec_c);
+  return hipGetLastError();
+}
+
 hipError_t launch_bf16_thin_lsm(const Bf16Args& a, const LsmArgs& q, int out_bf16, hipStream_t s) {
   hipError_t e;
   if (a.M <= 16) e = launch_lsm_m<1>(a, q, s);
@@ -705,12 +715,7 @@ hipError_t launch_bf16_thin_lsm(const Bf16Args& a, const LsmArgs& q, int out_bf1
   else if (a.M <= 48) e = launch_lsm_m<3>(a, q, s);
   else e = launch_lsm_m<4>(a, q, s);
   if (e != hipSuccess) return e;
-  const dim3 grid(static_cast<unsigned>((a.N + kChunk - 1) / kChunk), static_cast<unsigned>(a.M));
-  if (out_bf16)
-    hipLaunchKernelGGL((tgemm_lsm_normalize<true>), grid, dim3(256), 0, s, q, a.C, a.ldc, a.N, a.vec_c);
-  else
-    hipLaunchKernelGGL((tgemm_lsm_normalize<false>), grid, dim3(256), 0, s, q, a.C, a.ldc, a.N, a.vec_c);
-  return hipGetLastError();
+  return launch_lsm_normalize(q, a.C, a.ldc, a.M, a.N, a.vec_c, out_bf16, s);
 }
 
 ThinSplit thin_split_plan(int64_t M, int64_t N, int64_t K) {

@@ -136,8 +136,13 @@ __device__ __forceinline__ bf16x8 nibbles_to_bf16(uint32_t codes) {
   return __builtin_bit_cast(bf16x8, u32x4{hi2(f[0], f[1]), hi2(f[2], f[3]), hi2(f[4], f[5]), hi2(f[6], f[7])});
 }
 
-template <int BITS, int MB, int EPI, bool OUT_BF16>
-__device__ __forceinline__ void wq_thin_body(const W8Args& p, uint8_t* smem) {
+// Streams the workgroup's 512-column stripe of Q once and leaves the scaled
+// products in acc[mb][j] (16 x 16 blocks, transposed by the operand swap:
+// element e of lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the
+// wave's 64).  Ends with every load landed; the caller synchronises the
+// workgroup before reusing smem.
+template <int BITS, int MB>
+__device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f32x4 (&acc)[MB][kFN]) {
   using Sh = WqShape<BITS>;
   constexpr int kBK = Sh::kBK;
   constexpr int kStage = Sh::kStage;
@@ -148,9 +153,6 @@ __device__ __forceinline__ void wq_thin_body(const W8Args& p, uint8_t* smem) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * kBN;
 
-  // acc[mb][j]: 16 x 16 block, transposed by the operand swap: element e of
-  // lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the wave's 64.
-  f32x4 acc[MB][kFN];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -288,8 +290,14 @@ __device__ __forceinline__ void wq_thin_body(const W8Args& p, uint8_t* smem) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
   }
+}
 
-  // ---- epilogue: lane holds 4 consecutive columns of one row per block ----
+// Epilogue: each lane holds 4 consecutive columns of one row per block.
+template <int MB, int EPI, bool OUT_BF16>
+__device__ __forceinline__ void wq_store(const W8Args& p, const f32x4 (&acc)[MB][kFN]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kBN;
 #pragma unroll
   for (int j = 0; j < kFN; ++j) {
     const int col = n0 + kWTN * wave + 16 * j + 4 * (lane >> 4);
@@ -334,13 +342,104 @@ __device__ __forceinline__ void wq_thin_body(const W8Args& p, uint8_t* smem) {
 template <int MB, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_w8_thin(W8Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * WqShape<8>::kStage];
-  wq_thin_body<8, MB, EPI, OUT_BF16>(p, smem);
+  f32x4 acc[MB][kFN];
+  wq_accumulate<8, MB>(p, smem, acc);
+  wq_store<MB, EPI, OUT_BF16>(p, acc);
 }
 
 template <int MB, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_w4_thin(W8Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * WqShape<4>::kStage];
-  wq_thin_body<4, MB, EPI, OUT_BF16>(p, smem);
+  f32x4 acc[MB][kFN];
+  wq_accumulate<4, MB>(p, smem, acc);
+  wq_store<MB, EPI, OUT_BF16>(p, acc);
+}
+
+// ---- The low-precision LM head with bias and LogSoftmax (the GEMM
+// compute-cost page, section 7.2: its plan A, the integer weight, and plan
+// B, the output projection, bias and LogSoftmax fused), pass 1: the stripe's
+// logits with bias, their safe-softmax pair (row maximum m_w and
+// s_w = sum exp(y - m_w) over the stripe) into part[row * G + w], and the
+// fp32 logits into their buffer; pass 2 is the bf16 head's normalisation.
+template <int BITS, int MB>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_wq_thin_lsm(W8Args p, LsmArgs q) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * WqShape<BITS>::kStage];
+  f32x4 acc[MB][kFN];
+  wq_accumulate<BITS, MB>(p, smem, acc);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kBN;
+  constexpr int kWaves = kThreads / 64;
+  constexpr float kNegInf = -__builtin_inff();
+
+  // Logits with bias; columns past N take -inf, which no maximum or sum sees.
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int col = n0 + kWTN * wave + 16 * j + 4 * (lane >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = col + e < p.N;
+      const float b = (in && p.bias != nullptr) ? bf16_bits_to_f32(p.bias[col + e]) : 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][j][e] = in ? acc[mb][j][e] + b : kNegInf;
+    }
+  }
+
+  // Row 16 mb + l%16 of the stripe: lanes l, l^16, l^32, l^48 of each wave
+  // hold its columns; the eight waves meet in LDS.
+  float* red = reinterpret_cast<float*>(smem);  // [8 waves][64 rows]
+  __syncthreads();  // every wave's loads have landed: smem is free
+  float mrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float m = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = __builtin_fmaxf(m, acc[mb][j][e]);
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16, 64));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
+    if (lane < 16) red[wave * 64 + 16 * mb + lane] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = 16 * mb + (lane & 15);
+    float m = red[r];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = __builtin_fmaxf(m, red[64 * w + r]);
+    mrow[mb] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t += __expf(acc[mb][j][e] - mrow[mb]);
+    t += __shfl_xor(t, 16, 64);
+    t += __shfl_xor(t, 32, 64);
+    if (lane < 16) red[wave * 64 + 16 * mb + lane] = t;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < 16) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = 16 * mb + lane;
+      float srow = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) srow += red[64 * w + r];
+      if (r < p.M) q.part[static_cast<int64_t>(r) * gridDim.x + blockIdx.x] = float2{mrow[mb], srow};
+    }
+  }
+
+  // fp32 logits (bias already added) to their buffer.
+  W8Args pl = p;
+  pl.C = q.logits;
+  pl.ldc = q.ldl;
+  pl.vec_c = q.vec_l;
+  wq_store<MB, kEpiNone, false>(pl, acc);
 }
 
 template <int BITS, int MB, int EPI, bool OUT_BF16>
@@ -390,6 +489,28 @@ const char* wq_kernel_name(int bits, int M) {
       {"tgemm_w4_thin_m16", "tgemm_w4_thin_m32", "tgemm_w4_thin_m48", "tgemm_w4_thin_m64"}};
   const int m = M <= 16 ? 0 : M <= 32 ? 1 : M <= 48 ? 2 : 3;
   return kNames[bits == 8 ? 0 : 1][m];
+}
+
+hipError_t launch_wq_thin_lsm(int bits, const W8Args& a, const LsmArgs& q, int out_bf16,
+                              hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(q.G));
+  const int m = a.M <= 16 ? 1 : a.M <= 32 ? 2 : a.M <= 48 ? 3 : 4;
+#define TGEMM_WQ_LSM(B, MBV) hipLaunchKernelGGL((tgemm_wq_thin_lsm<B, MBV>), grid, dim3(kThreads), 0, s, a, q)
+  if (bits == 8) {
+    if (m == 1) TGEMM_WQ_LSM(8, 1);
+    else if (m == 2) TGEMM_WQ_LSM(8, 2);
+    else if (m == 3) TGEMM_WQ_LSM(8, 3);
+    else TGEMM_WQ_LSM(8, 4);
+  } else {
+    if (m == 1) TGEMM_WQ_LSM(4, 1);
+    else if (m == 2) TGEMM_WQ_LSM(4, 2);
+    else if (m == 3) TGEMM_WQ_LSM(4, 3);
+    else TGEMM_WQ_LSM(4, 4);
+  }
+#undef TGEMM_WQ_LSM
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_lsm_normalize(q, a.C, a.ldc, a.M, a.N, a.vec_c, out_bf16, s);
 }
 
 hipError_t launch_wq_thin(int bits, const W8Args& a, int epi, int out_bf16, hipStream_t s) {

@@ -167,6 +167,13 @@ struct LsmArgs {
   int vec_l;  // 1: logit rows may be read and written with 16-byte accesses
 };
 hipError_t launch_bf16_thin_lsm(const Bf16Args& a, const LsmArgs& q, int out_bf16, hipStream_t stream);
+// Pass 2 of the log-softmax heads: merge each row's G pairs, write y - lse.
+hipError_t launch_lsm_normalize(const LsmArgs& q, void* C, int64_t ldc, int M, int N, int vec_c,
+                                int out_bf16, hipStream_t stream);
+// The int8 / int4 weight-only head (bits 8 or 4) with bias and log-softmax;
+// same stripes (q.G = lsm_workgroups(N)) and workspace as the bf16 head.
+hipError_t launch_wq_thin_lsm(int bits, const W8Args& a, const LsmArgs& q, int out_bf16,
+                              hipStream_t stream);
 int64_t lsm_workgroups(int64_t N);
 bool lsm_direct_ok(const Bf16Args& a);
 hipError_t launch_quant_fp8_1x128(const QuantArgs& a, hipStream_t stream);
