@@ -198,7 +198,9 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C,
  *   C    bf16 [M, N], packed row-major
  *
  * Dequantised value = decode(code) * scale.  Scales must be finite; NaN
- * codes (0x7F, 0xFF) propagate to the outputs they touch.
+ * codes (0x7F, 0xFF) propagate to the outputs they touch.  Grids that would
+ * keep few compute units busy are split along K (automatic plan of
+ * gemm_fp8_blockscaled_ex; the split uses library scratch, see Memory).
  * Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
  */
 int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
