@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the attainable-ceiling probes (MFMA loops, HBM stream read)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (the reference kernel for "
                          "scaling HBM byte counters) and exit")
@@ -457,6 +459,56 @@ def cpu_baseline(case, budget_s=12.0):
                       f"GEMM (fp64 decode + contraction + |a||b| denominators)"}
 
 
+def measure_ceilings(dev):
+    """Attainable ceilings on this machine (informational): the library's MFMA-only
+    loops on random register operands and its streaming read of a 1 GiB buffer
+    (beyond the 256 MB last-level cache), each the best of three timed calls
+    after one warm-up, HIP events on the launch stream."""
+    import torch
+
+    import tiled_gemm_04_amd as tg
+
+    def best(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) / 1e3)
+        return min(t)
+
+    out = {}
+    iters = 2000
+    buf = torch.empty(tg.gemm_probe_out_elems(tg.PROBE_MFMA_BF16), dtype=torch.float32, device=dev)
+    for key, probe in (("mfma_bf16_tflops", tg.PROBE_MFMA_BF16), ("mfma_fp8_tflops", tg.PROBE_MFMA_FP8)):
+        sec = best(lambda: tg.gemm_probe_mfma(probe, iters, buf))
+        out[key] = round(tg.gemm_probe_mfma_flop(probe, iters) / sec / 1e12, 1)
+    src = torch.ones(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    xo = torch.empty(tg.gemm_probe_out_elems(tg.PROBE_STREAM_READ), dtype=torch.int32, device=dev)
+    sec = best(lambda: tg.gemm_probe_stream_read(src, xo))
+    out["hbm_read_gbs"] = round((1 << 30) / sec / 1e9, 1)
+    out["note"] = ("measured on this box: MFMA-only loops on random register operands and a 1 GiB "
+                   "streaming read; frac_of_ceiling entries are achieved / these, informational")
+    del buf, src, xo
+    torch.cuda.empty_cache()
+    return out
+
+
+def ceiling_frac(roof, ceilings, fp8):
+    """achieved / the measured ceiling of the kernel's bound (roof: a roofline
+    dict, or a secondary entry with tflops / gbs)."""
+    if not ceilings:
+        return None
+    hbm = roof["bound"] == "hbm"
+    c = ceilings["hbm_read_gbs"] if hbm else ceilings["mfma_fp8_tflops" if fp8 else "mfma_bf16_tflops"]
+    achieved = roof["achieved"] if "achieved" in roof else roof["gbs" if hbm else "tflops"]
+    return round(achieved / c, 4) if c > 0 else None
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -495,6 +547,7 @@ def main():
         "roofline": head.roofline(kern_ms),
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
     }
+    head_fp8 = head.family == "fp8"
     del head.launch
     torch.cuda.empty_cache()
 
@@ -516,9 +569,21 @@ def main():
                          "gbs": round(c.bytes / (km * 1e-3) / 1e9, 1),
                          "bound": r["bound"], "frac": r["frac"], "kernel": c.kernel,
                          "traffic": r["traffic"]}
+            sec[name]["_fp8"] = c.family == "fp8"
             del c
             torch.cuda.empty_cache()
         line["secondary"] = sec
+
+    # The probes run last, so their heat and power draw do not colour the
+    # measurements above.
+    ceilings = None if args.no_ceilings else measure_ceilings(dev)
+    if ceilings:
+        line["ceilings"] = ceilings
+        line["roofline"]["frac_of_ceiling"] = ceiling_frac(line["roofline"], ceilings, head_fp8)
+    for v in line.get("secondary", {}).values():
+        fp8 = v.pop("_fp8")
+        if ceilings:
+            v["frac_of_ceiling"] = ceiling_frac(v, ceilings, fp8)
 
     if not args.no_cpu_baseline and head.inputs_for_oracle is not None:
         line["cpu_baseline"] = cpu_baseline(head)

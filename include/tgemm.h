@@ -495,6 +495,49 @@ const char* gemm_status_string(int status);
 /* TGEMM_ABI_VERSION of the built library. */
 int gemm_abi_version(void);
 
+/*
+ * Attainable-ceiling probes -- measurement kernels, not part of any GEMM.
+ *
+ * The published peaks (2.5 PFLOP/s dense bf16, 5 PFLOP/s fp8, 8 TB/s HBM)
+ * are not what this part sustains under load: the matrix-heavy kernels run
+ * power-bound below the peak clock, and a plain streaming read does not
+ * reach the HBM spec.  These probes measure what the hardware delivers with
+ * nothing else in the way, so a kernel's fraction of them can be reported
+ * next to its fraction of the published peak (the DeepGEMM page, section
+ * 3.4: time, fraction of peak, bandwidth).
+ *
+ *   TGEMM_PROBE_MFMA_BF16 / _FP8: one 512-thread workgroup per compute unit;
+ *       every wave issues 32 MFMAs per iteration (v_mfma_f32_32x32x16_bf16,
+ *       or v_mfma_scale_f32_16x16x128_f8f6f4 on e4m3 operands) on seeded
+ *       pseudo-random operands held in registers and rotated between
+ *       instructions, into four independent accumulators; each thread
+ *       writes one float (the sum of its accumulators) to out.  FLOP per
+ *       call: gemm_probe_mfma_flop(probe, iters).
+ *   TGEMM_PROBE_STREAM_READ: a streaming read of src (bytes, a multiple of
+ *       16, src 16-byte aligned) taken as rows of (compute units) KiB, one
+ *       workgroup per compute unit reading its KiB of every row with
+ *       non-temporal 16-byte loads (the fastest read pattern measured on this
+ *       part), plus a grid-stride tail; each thread writes the XOR of the
+ *       32-bit words it read, so the XOR of all of out equals the XOR of all
+ *       words of src.
+ *
+ * gemm_probe_out_elems(probe): the number of 32-bit outputs the probe
+ * writes on the current device (-1 for an unknown probe or device).
+ * Returns TGEMM_OK, TGEMM_ERR_INVALID (unknown probe, negative or oversized
+ * iters, NULL or short out, bytes not a multiple of 16, unaligned src),
+ * TGEMM_ERR_UNSUPPORTED (device properties unavailable) or TGEMM_ERR_LAUNCH.
+ */
+typedef enum {
+    TGEMM_PROBE_MFMA_BF16 = 0,
+    TGEMM_PROBE_MFMA_FP8 = 1,
+    TGEMM_PROBE_STREAM_READ = 2
+} tgemm_probe_t;
+
+int64_t gemm_probe_out_elems(int probe);
+double gemm_probe_mfma_flop(int probe, int64_t iters);
+int gemm_probe_mfma(int probe, int64_t iters, float* out, int64_t out_elems, uint64_t seed, void* stream);
+int gemm_probe_stream_read(const void* src, int64_t bytes, uint32_t* out, int64_t out_elems, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -316,3 +316,17 @@ def test_wq_logsoftmax_validation():
         assert f(FAKE, FAKE, FAKE, NULL, FAKE, 65, 512, 64, 64, 512, 512, 1, WS, 1 << 24, NULL) == UNS  # M
         assert f(FAKE, FAKE, FAKE, NULL, FAKE, 2, 510, 64, 64, 512, 512, 1, WS, 1 << 20, NULL) == UNS  # N % 4
         assert f(NULL, NULL, NULL, NULL, NULL, 0, 512, 64, 64, 512, 512, 1, NULL, 0, NULL) == OK
+
+
+def test_probe_validation():
+    L = binding.lib()
+    out = ctypes.c_void_p(0x4000)
+    assert L.gemm_probe_mfma(5, 10, out, 1 << 20, 1, NULL) == INV      # unknown probe
+    assert L.gemm_probe_mfma(0, -1, out, 1 << 20, 1, NULL) == INV      # negative iters
+    assert L.gemm_probe_mfma(0, 1 << 40, out, 1 << 20, 1, NULL) == INV  # oversized iters
+    assert L.gemm_probe_mfma(1, 10, NULL, 1 << 20, 1, NULL) == INV     # no output
+    assert L.gemm_probe_stream_read(FAKE, 24, out, 1 << 20, NULL) == INV             # bytes % 16
+    assert L.gemm_probe_stream_read(ctypes.c_void_p(0x1008), 32, out, 1 << 20, NULL) == INV  # unaligned
+    assert L.gemm_probe_stream_read(NULL, 32, out, 1 << 20, NULL) == INV
+    assert L.gemm_probe_out_elems(7) == -1
+    assert L.gemm_probe_mfma_flop(7, 10) < 0

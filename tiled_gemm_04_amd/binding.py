@@ -76,6 +76,14 @@ def lib():
     for f in ("gemm_bf16_w8_logsoftmax", "gemm_bf16_w4_logsoftmax"):
         getattr(L, f).argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, vp, i64, vp]
         getattr(L, f).restype = i32
+    L.gemm_probe_out_elems.argtypes = [i32]
+    L.gemm_probe_out_elems.restype = i64
+    L.gemm_probe_mfma_flop.argtypes = [i32, i64]
+    L.gemm_probe_mfma_flop.restype = ctypes.c_double
+    L.gemm_probe_mfma.argtypes = [i32, i64, vp, i64, ctypes.c_uint64, vp]
+    L.gemm_probe_mfma.restype = i32
+    L.gemm_probe_stream_read.argtypes = [vp, i64, vp, i64, vp]
+    L.gemm_probe_stream_read.restype = i32
     L.gemm_fp8_blockscaled_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.gemm_fp8_blockscaled_nt.restype = i32
     L.gemm_bf16_quant_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
@@ -266,6 +274,44 @@ def gemm_fp8_blockscaled_nt(A, sA, Bt, sB, C, stream=None):
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_fp8_blockscaled_nt")
     return C
+
+
+PROBE_MFMA_BF16, PROBE_MFMA_FP8, PROBE_STREAM_READ = 0, 1, 2
+
+
+def gemm_probe_out_elems(probe):
+    """Number of 32-bit outputs the probe writes on the current device."""
+    return int(lib().gemm_probe_out_elems(int(probe)))
+
+
+def gemm_probe_mfma_flop(probe, iters):
+    return float(lib().gemm_probe_mfma_flop(int(probe), int(iters)))
+
+
+def gemm_probe_mfma(probe, iters, out, seed=1, stream=None):
+    """MFMA-only loop on seeded random register operands (probe PROBE_MFMA_BF16
+    or PROBE_MFMA_FP8); out: float32 tensor of at least gemm_probe_out_elems()."""
+    _check_cuda(out)
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor")
+    st = lib().gemm_probe_mfma(int(probe), int(iters), _ptr(out), out.numel(), int(seed), _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_probe_mfma")
+    return out
+
+
+def gemm_probe_stream_read(src, out, stream=None):
+    """Streaming read of src (16-byte aligned, size a multiple of 16 bytes);
+    out: int32 tensor of at least gemm_probe_out_elems(PROBE_STREAM_READ)
+    holding per-thread XORs of the 32-bit words read."""
+    _check_cuda(src, out)
+    if out.dtype != torch.int32 or not out.is_contiguous() or not src.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor and src contiguous")
+    nbytes = src.numel() * src.element_size()
+    st = lib().gemm_probe_stream_read(_ptr(src), nbytes, _ptr(out), out.numel(), _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_probe_stream_read")
+    return out
 
 
 def gemm_fp8_split_plan(M, N, K, cus, split_parts=0):

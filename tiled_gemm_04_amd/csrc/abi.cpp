@@ -620,6 +620,46 @@ int gemm_fp8_split_plan(int64_t M, int64_t N, int64_t K, int cus, int split_part
   return TGEMM_OK;
 }
 
+int64_t gemm_probe_out_elems(int probe) {
+  const int cus = tgemm::device_cus();
+  if (cus <= 0) return -1;
+  if (probe == TGEMM_PROBE_MFMA_BF16 || probe == TGEMM_PROBE_MFMA_FP8) return tgemm::probe_mfma_threads(cus);
+  if (probe == TGEMM_PROBE_STREAM_READ) return tgemm::probe_stream_threads(cus);
+  return -1;
+}
+
+double gemm_probe_mfma_flop(int probe, int64_t iters) {
+  const int cus = tgemm::device_cus();
+  if (cus <= 0 || iters < 0) return -1.0;
+  // 32 MFMAs per wave and iteration: 32x32x16 bf16 = 32768 FLOP, 16x16x128 fp8 = 65536.
+  const double per = probe == TGEMM_PROBE_MFMA_BF16 ? 32768.0 : probe == TGEMM_PROBE_MFMA_FP8 ? 65536.0 : -1.0;
+  if (per < 0) return -1.0;
+  return static_cast<double>(tgemm::probe_mfma_threads(cus) / 64) * 32.0 * per * static_cast<double>(iters);
+}
+
+int gemm_probe_mfma(int probe, int64_t iters, float* out, int64_t out_elems, uint64_t seed, void* stream) {
+  if (probe != TGEMM_PROBE_MFMA_BF16 && probe != TGEMM_PROBE_MFMA_FP8) return TGEMM_ERR_INVALID;
+  if (iters < 0 || iters > 0x7fffffff || out == nullptr) return TGEMM_ERR_INVALID;
+  const int64_t need = gemm_probe_out_elems(probe);
+  if (need < 0) return TGEMM_ERR_UNSUPPORTED;
+  if (out_elems < need) return TGEMM_ERR_INVALID;
+  const hipError_t e = tgemm::launch_probe_mfma(probe == TGEMM_PROBE_MFMA_BF16 ? 0 : 1, tgemm::device_cus(),
+                                                static_cast<int>(iters), seed, out,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+int gemm_probe_stream_read(const void* src, int64_t bytes, uint32_t* out, int64_t out_elems, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || out == nullptr) return TGEMM_ERR_INVALID;
+  if (bytes > 0 && (src == nullptr || !aligned16(src))) return TGEMM_ERR_INVALID;
+  const int64_t need = gemm_probe_out_elems(TGEMM_PROBE_STREAM_READ);
+  if (need < 0) return TGEMM_ERR_UNSUPPORTED;
+  if (out_elems < need) return TGEMM_ERR_INVALID;
+  const hipError_t e = tgemm::launch_probe_stream_read(src, bytes / 16, tgemm::device_cus(), out,
+                                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
 const char* gemm_fp8_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return nullptr;
   return tgemm::fp8_kernel_name(M, N, K);

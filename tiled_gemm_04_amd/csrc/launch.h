@@ -178,6 +178,13 @@ int64_t lsm_workgroups(int64_t N);
 bool lsm_direct_ok(const Bf16Args& a);
 hipError_t launch_quant_fp8_1x128(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quant_fp8_128x128(const QuantArgs& a, hipStream_t stream);
+// Attainable-ceiling probes (measurement kernels, not part of any GEMM).
+// kind 0: bf16 MFMA loop, 1: fp8 MFMA loop; one output float per thread.
+int64_t probe_mfma_threads(int cus);
+int64_t probe_stream_threads(int cus);
+hipError_t launch_probe_mfma(int kind, int cus, int iters, uint64_t seed, float* out, hipStream_t stream);
+hipError_t launch_probe_stream_read(const void* src, int64_t n16, int cus, uint32_t* out,
+                                    hipStream_t stream);
 const char* thin_kernel_name(int M);
 const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K);
 bool fp8_direct_ok(int64_t M, int64_t N, int64_t K);
