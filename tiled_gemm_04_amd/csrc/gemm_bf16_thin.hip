@@ -12,10 +12,19 @@
 //   * a workgroup owns 512 consecutive columns, so every row of its W stripe
 //     is one contiguous KiB; measured on MI355X, KiB-wide row stripes read
 //     at about 6.4 TB/s against about 6.0 TB/s for 256-byte stripes;
-//   * the stripe is walked in slices of 32 rows that go global -> LDS with
-//     direct buffer loads (one load instruction = one row), four LDS stages
-//     deep (three slices, 96 KiB, in flight per compute unit); the matching
-//     16-row blocks of X come the same way;
+//   * the stripe is walked in slices of 32 rows (one 16-byte load
+//     instruction per wave = one KiB row), with the matching 16-row blocks of
+//     X, in one of two pipelines:
+//       - register-staged (the full-width kernels): each wave keeps two
+//         slices in flight in registers, loaded with the non-temporal hint,
+//         and writes each to one of two LDS stages before it is used.  At
+//         any moment every compute unit reads neighbouring KiBs of the same
+//         few W rows, the pattern that streams fastest on MI355X (about
+//         7.0 TB/s, against about 6.3 TB/s for the same rows through direct
+//         loads into LDS, which take no cache hint);
+//       - direct-to-LDS (the split-K kernel, whose short K chunks gain more
+//         from depth): buffer loads write LDS themselves, four stages deep
+//         (three slices, 96 KiB, in flight per compute unit);
 //   * each wave owns 128 columns over the whole of K (no cross-wave
 //     reduction); its MFMA B operands are read from the N-contiguous rows
 //     with ds_read_b64_tr_b16, exactly as in the tiled kernel, and the
@@ -33,13 +42,16 @@ constexpr int kBN = 512;        // columns per workgroup
 constexpr int kWTN = 128;       // columns per wave
 constexpr int kFN = kWTN / 16;  // 16-column MFMA blocks per wave
 constexpr int kBK = 32;         // K rows per slice
-constexpr int kNS = 4;          // LDS stages
+constexpr int kNSReg = 2;       // LDS stages, register-staged pipeline
+constexpr int kNSLds = 4;       // LDS stages, direct-to-LDS pipeline
 constexpr int kWRow = kBN * 2;  // bytes per W row of the stripe (1 KiB)
 constexpr int kWStage = kBK * kWRow;
 constexpr int kXStage = 4 * 1024;  // four 16-row blocks of X, 64 bytes per row
 constexpr int kStage = kWStage + kXStage;
-constexpr int kLoadsPerSlice = kBK / 4 + 1;  // per wave: 8 W rows and one X block
-static_assert(kNS * kStage <= 160 * 1024, "LDS capacity");
+constexpr int kWRows = kBK / 4;  // W rows per wave and slice
+constexpr int kLoadsPerSlice = kWRows + 1;  // direct-to-LDS loads per wave and slice
+constexpr uint32_t kCacheNT = 2;  // buffer-load cache policy: non-temporal
+static_assert(kNSLds * kStage <= 160 * 1024, "LDS capacity");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -51,16 +63,36 @@ __device__ __forceinline__ int w_swz(int k) { return 2 * ((k & 3) | (((k >> 3) &
 // XOR on the chunk index of row r of an X block (4 chunks of 16 bytes).
 __device__ __forceinline__ int x_swz(int r) { return (r >> 2) & 3; }
 
+// One slice of one wave in flight: its 8 W rows and its X block, 16 bytes
+// per lane each.
+struct SliceRegs {
+  u32x4 w[kWRows];
+  u32x4 x;
+};
+
+// Buffer descriptor over [base, base + bytes), bytes clamped to [0, 2^31 - 1]
+// with 32-bit compares so the descriptor stays in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window32(const void* base, int64_t bytes) {
+  const uint64_t u = static_cast<uint64_t>(bytes);
+  const int32_t hi = static_cast<int32_t>(u >> 32);
+  const uint32_t lo = static_cast<uint32_t>(u);
+  const int32_t n = hi < 0 ? 0 : ((hi > 0 || lo > 0x7fffffffu) ? 0x7fffffff : static_cast<int32_t>(lo));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           static_cast<int>(kBufferFlags));
+}
+
 // Streams the workgroup's 512-column stripe of W once and leaves the
 // products in acc[mb][j] (16 x 16 blocks, transposed by the operand swap:
 // element e of lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the
 // wave's 128).  Slices [tb, te) of K (te < 0: through the last) are summed;
-// the end of the range acts as K, so nothing past it is loaded.  Ends with
-// every load landed; the caller synchronises the workgroup before reusing
-// smem.
-template <int MB>
+// the end of the range acts as K, so nothing past it is loaded.  REG picks
+// the register-staged pipeline (two LDS stages) over the direct-to-LDS one
+// (four stages); smem must hold that many.  Ends with no load still writing
+// LDS; the caller synchronises the workgroup before reusing smem.
+template <int MB, bool REG>
 __device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem, f32x4 (&acc)[MB][kFN],
                                                 int tb = 0, int te = -1) {
+  constexpr int NS = REG ? kNSReg : kNSLds;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,32 +103,48 @@ __device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem
 #pragma unroll
     for (int j = 0; j < kFN; ++j) acc[mb][j] = f32x4{};
 
-  // ---- global -> LDS: wave w loads W rows 8w .. 8w+7 of a slice (lane l ->
-  // physical chunk l, logical chunk l ^ w_swz(row)) and X block w (rows
-  // 16w .. 16w+15, lane l -> row l/4, physical chunk l%4). ----
+  // ---- global -> LDS (through registers or directly): wave w loads W
+  // rows 8w .. 8w+7 of a slice (lane l reads logical chunk l ^ w_swz(row)
+  // and stores it as physical chunk l) and X block w (rows 16w .. 16w+15,
+  // lane l -> row l/4, physical chunk l%4).  Each lane's offsets within a
+  // slice do not depend on the slice; columns past N are flagged out of
+  // range (read as zero). ----
   const int64_t lda2 = p.lda * 2, ldb2 = p.ldb * 2;
-  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+  uint32_t w_off[kWRows];
+#pragma unroll
+  for (int i = 0; i < kWRows; ++i) {
+    const int k = kWRows * wave + i;
+    const int c = lane ^ w_swz(k);
+    w_off[i] = static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange);
+  }
   const int xr = lane >> 2;
   const int xc = (lane & 3) ^ x_swz(xr);
   const uint32_t x_off = static_cast<uint32_t>((16 * wave + xr) * lda2 + 16 * xc);
   const int KT = (p.K + kBK - 1) / kBK;
   if (te < 0) te = KT;
   const int kend = p.K < te * kBK ? p.K : te * kBK;  // this range's end of K
-  auto issue_slice = [&](int t) {
-    const int stage = t % kNS;
+  // Slice t into registers.  W rows are read once by the whole grid and go
+  // with the non-temporal hint; the X block is re-read by every workgroup
+  // and stays cacheable.  Slices at or past the range's end get empty
+  // windows: their loads read nothing and return zeros.
+  auto load_slice = [&](int t, SliceRegs& r) {
     const int k0 = t * kBK;
-    const i32x4 ww = make_window_words(p.B + static_cast<int64_t>(k0) * p.ldb + n0,
-                                       (static_cast<int64_t>(kend - k0 - 1) * p.ldb + (p.N - n0)) * 2);
+    const __amdgpu_buffer_rsrc_t ww = window32(p.B + static_cast<int64_t>(k0) * p.ldb + n0,
+                                               (static_cast<int64_t>(kend - k0 - 1) * p.ldb + (p.N - n0)) * 2);
 #pragma unroll
-    for (int i = 0; i < kBK / 4; ++i) {
-      const int k = 8 * wave + i;
-      const int c = lane ^ w_swz(k);
-      buf_load16_lds(ww, smem_base + stage * kStage + k * kWRow,
-                     static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange));
-    }
-    const i32x4 wx = make_window_words(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (kend - k0)) * 2);
-    buf_load16_lds(wx, smem_base + stage * kStage + kWStage + wave * 1024,
-                   x_off | (k0 + 8 * xc < kend ? 0u : kOutOfRange));
+    for (int i = 0; i < kWRows; ++i)
+      r.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ww, w_off[i], 0, kCacheNT));
+    const __amdgpu_buffer_rsrc_t wx =
+        window32(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (kend - k0)) * 2);
+    r.x = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wx, x_off | (k0 + 8 * xc < kend ? 0u : kOutOfRange), 0, 0));
+  };
+  auto store_slice = [&](int t, const SliceRegs& r) {
+    uint8_t* st = smem + (t % NS) * kStage;
+#pragma unroll
+    for (int i = 0; i < kWRows; ++i)
+      *reinterpret_cast<u32x4*>(st + (kWRows * wave + i) * kWRow + 16 * lane) = r.w[i];
+    *reinterpret_cast<u32x4*>(st + kWStage + wave * 1024 + 16 * lane) = r.x;
   };
 
   // ---- LDS -> registers ----
@@ -115,33 +163,72 @@ __device__ __forceinline__ void thin_accumulate(const Bf16Args& p, uint8_t* smem
   const int xrow = lane & 15;
   const int x_rd = kWStage + xrow * 64 + (((lane >> 4) ^ x_swz(xrow)) * 16);
 
-  if (te > tb) {
-    for (int t = tb; t < tb + kNS - 1; ++t) issue_slice(t);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kNS - 2) * kLoadsPerSlice) : "memory");
-    lds_barrier();
-    for (int t = tb; t < te; ++t) {
-      issue_slice(t + kNS - 1);  // into the stage slice t-1 occupied
-      const uint8_t* base = smem + (t % kNS) * kStage;
-      bf16x8 fb[kFN], fx[MB];
+  auto compute_slice = [&](int t) {
+    const uint8_t* base = smem + (t % NS) * kStage;
+    bf16x8 fb[kFN], fx[MB];
 #pragma unroll
-      for (int j = 0; j < kFN; ++j) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, base + b_off[j]));
-        const i16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, base + b_off[j] + 4 * kWRow));
-        fb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        fx[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd + mb * 1024));
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < kFN; ++j)
-          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fx[mb], acc[mb][j], 0, 0, 0);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kNS - 2) * kLoadsPerSlice) : "memory");
-      lds_barrier();  // slice t+1 landed everywhere; slice t no longer read
+    for (int j = 0; j < kFN; ++j) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, base + b_off[j]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, base + b_off[j] + 4 * kWRow));
+      fb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      fx[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd + mb * 1024));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+        acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fx[mb], acc[mb][j], 0, 0, 0);
+  };
+  if constexpr (REG) {
+    // One slice: its registers go to LDS stage t % NS, the same registers
+    // are refilled with slice t + 2, and after the barrier (stage t complete
+    // in every wave; stage t - 1 no longer read) the slice is multiplied.
+    // Two slices stay in flight per wave while the MFMAs run.
+    auto step = [&](int t, SliceRegs& r) {
+      store_slice(t, r);
+      load_slice(t + 2, r);
+      lds_barrier();
+      compute_slice(t);
+    };
+    if (te > tb) {
+      SliceRegs r0, r1;
+      load_slice(tb, r0);
+      load_slice(tb + 1, r1);
+      int t = tb;
+      for (; t + 1 < te; t += 2) {
+        step(t, r0);
+        step(t + 1, r1);
+      }
+      if (t < te) step(t, r0);
+    }
+  } else {
+    // Direct buffer loads into LDS stage t % NS, NS - 1 slices in flight;
+    // the same lane -> LDS placement as above.
+    const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+    auto issue_slice = [&](int t) {
+      const uint32_t stage = smem_base + static_cast<uint32_t>((t % NS) * kStage);
+      const int k0 = t * kBK;
+      const i32x4 ww = make_window_words(p.B + static_cast<int64_t>(k0) * p.ldb + n0,
+                                         (static_cast<int64_t>(kend - k0 - 1) * p.ldb + (p.N - n0)) * 2);
+#pragma unroll
+      for (int i = 0; i < kWRows; ++i) buf_load16_lds(ww, stage + (kWRows * wave + i) * kWRow, w_off[i]);
+      const i32x4 wx = make_window_words(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (kend - k0)) * 2);
+      buf_load16_lds(wx, stage + kWStage + wave * 1024, x_off | (k0 + 8 * xc < kend ? 0u : kOutOfRange));
+    };
+    if (te > tb) {
+      for (int t = tb; t < tb + NS - 1; ++t) issue_slice(t);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoadsPerSlice) : "memory");
+      lds_barrier();
+      for (int t = tb; t < te; ++t) {
+        issue_slice(t + NS - 1);  // into the stage slice t-1 occupied
+        compute_slice(t);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoadsPerSlice) : "memory");
+        lds_barrier();  // slice t+1 landed everywhere; slice t no longer read
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
+    }
   }
 }
 
@@ -175,9 +262,9 @@ __device__ __forceinline__ void store4(const Bf16Args& p, int row, int col, cons
 template <int MB, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
   apply_batch(p, OUT_BF16 ? 2 : 4);
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNSReg * kStage];
   f32x4 acc[MB][kFN];
-  thin_accumulate<MB>(p, smem, acc);
+  thin_accumulate<MB, true>(p, smem, acc);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * kBN;
@@ -230,16 +317,17 @@ hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s)
 // 128 stripes, half the units or more sit idle).  The K
 // range is then cut into S chunks (grid z): workgroup (stripe, s) sums
 // slices [s*KTc, (s+1)*KTc) and writes its fp32 partial tile to
-// part[s][M][N]; a second kernel adds the S partials in order of s, then
-// the bias and the epilogue, and rounds once -- deterministic, no atomics.
+// part[s][M][N] (through the direct-to-LDS pipeline); a second kernel adds
+// the S partials in order of s, then the bias and the epilogue, and rounds
+// once -- deterministic, no atomics.
 template <int MB>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_splitk(Bf16Args p, float* part, int ktc) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNSLds * kStage];
   f32x4 acc[MB][kFN];
   const int KT = (p.K + kBK - 1) / kBK;
   const int tb = blockIdx.z * ktc;
   const int te = tb + ktc < KT ? tb + ktc : KT;
-  thin_accumulate<MB>(p, smem, acc, tb, te);
+  thin_accumulate<MB, false>(p, smem, acc, tb, te);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * kBN;
@@ -542,9 +630,9 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 
 template <int MB>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_lsm(Bf16Args p, LsmArgs q) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNSReg * kStage];
   f32x4 acc[MB][kFN];
-  thin_accumulate<MB>(p, smem, acc);
+  thin_accumulate<MB, true>(p, smem, acc);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * kBN;
