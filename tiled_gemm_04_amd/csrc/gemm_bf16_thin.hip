@@ -15,16 +15,18 @@
 //   * the stripe is walked in slices of 32 rows (one 16-byte load
 //     instruction per wave = one KiB row), with the matching 16-row blocks of
 //     X, in one of two pipelines:
-//       - register-staged (the full-width kernels): each wave keeps two
-//         slices in flight in registers, loaded with the non-temporal hint,
-//         and writes each to one of two LDS stages before it is used.  At
-//         any moment every compute unit reads neighbouring KiBs of the same
-//         few W rows, the pattern that streams fastest on MI355X (about
-//         7.0 TB/s, against about 6.3 TB/s for the same rows through direct
-//         loads into LDS, which take no cache hint);
-//       - direct-to-LDS (the split-K kernel, whose short K chunks gain more
-//         from depth): buffer loads write LDS themselves, four stages deep
-//         (three slices, 96 KiB, in flight per compute unit);
+//       - register-staged (grids of at least three quarters of the
+//         compute units): each wave keeps two slices in flight in
+//         registers, loaded with the non-temporal hint, and writes each to
+//         one of two LDS stages before it is used.  At any moment every
+//         compute unit reads neighbouring KiBs of the same few W rows, the
+//         pattern that streams fastest on MI355X (about 7.0 TB/s, against
+//         about 6.3 TB/s for the same rows through direct loads into LDS,
+//         which take no cache hint);
+//       - direct-to-LDS (smaller grids and the split-K kernel, where each
+//         unit's rate is bounded by the bytes it keeps in flight): buffer
+//         loads write LDS themselves, four stages deep (three slices,
+//         96 KiB, in flight per compute unit);
 //   * each wave owns 128 columns over the whole of K (no cross-wave
 //     reduction); its MFMA B operands are read from the N-contiguous rows
 //     with ds_read_b64_tr_b16, exactly as in the tiled kernel, and the
@@ -80,6 +82,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window32(const void* base, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
                                            static_cast<int>(kBufferFlags));
 }
+
+// The register-staged pipeline streams fastest when the grid covers the
+// chip; with fewer workgroups each compute unit's share of the stream is
+// bounded by the bytes it keeps in flight, and the deeper direct-to-LDS
+// pipeline wins.  Register staging from three quarters of the compute units.
+bool use_reg_pipeline(int64_t workgroups) { return 4 * workgroups >= 3 * static_cast<int64_t>(device_cus()); }
 
 // Streams the workgroup's 512-column stripe of W once and leaves the
 // products in acc[mb][j] (16 x 16 blocks, transposed by the operand swap:
@@ -259,12 +267,12 @@ __device__ __forceinline__ void store4(const Bf16Args& p, int row, int col, cons
   }
 }
 
-template <int MB, int EPI, bool OUT_BF16>
+template <int MB, int EPI, bool OUT_BF16, bool REG>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
   apply_batch(p, OUT_BF16 ? 2 : 4);
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNSReg * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[(REG ? kNSReg : kNSLds) * kStage];
   f32x4 acc[MB][kFN];
-  thin_accumulate<MB, true>(p, smem, acc);
+  thin_accumulate<MB, REG>(p, smem, acc);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * kBN;
@@ -293,8 +301,11 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin(Bf16Args p) {
 
 template <int MB, int EPI, bool OUT_BF16>
 hipError_t launch_m(const Bf16Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16>), dim3((a.N + kBN - 1) / kBN, a.batch),
-                     dim3(kThreads), 0, s, a);
+  const dim3 grid((a.N + kBN - 1) / kBN, a.batch);
+  if (use_reg_pipeline(static_cast<int64_t>(grid.x) * grid.y))
+    hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((tgemm_bf16_thin<MB, EPI, OUT_BF16, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -423,8 +434,10 @@ hipError_t launch_splitk_m(const Bf16Args& a, float* part, int S, int ktc, int e
 // Each output column is one contiguous weight row, so a workgroup owns 256
 // rows of Wt (256 columns of C) and walks K in slices of 64: a slice of a
 // row is one 128-byte cache line.  A load instruction brings 8 rows' lines
-// (1 KiB) straight into LDS, four stages deep (three slices, 120 KiB, in
-// flight).  Both MFMA operands are K-contiguous rows in LDS, read with one
+// (1 KiB); the same two pipelines as the [K, N] kernel, chosen the same way,
+// take them to LDS (register-staged: two slices in flight per wave, two
+// LDS stages, non-temporal weight loads; direct-to-LDS: four stages, three
+// slices, 120 KiB, in flight).  Both MFMA operands are K-contiguous rows in LDS, read with one
 // 16-byte read per lane (8 consecutive k); the 16-byte chunks of each
 // 128-byte row are XOR-permuted by (row / 2) % 8 so the 16 rows one read
 // covers land in 16 distinct bank slots.  Four waves each own 64 columns
@@ -433,14 +446,15 @@ hipError_t launch_splitk_m(const Bf16Args& a, float* part, int S, int ktc, int e
 // Workgroup b walks its slices starting at slice 3b (mod the slice count).
 // Weight rows (2K bytes apart, 8 KiB at K = 4096) read at one K offset by
 // every workgroup at once concentrate on a few HBM channels; measured on
-// the 4096 x 128256 head, the staggered start takes the stream from 4.3 to
-// 6.0 TB/s (the sum is the same, in a rotated order).
+// the 4096 x 128256 head with direct-to-LDS loads, the staggered start takes
+// the stream from 4.3 to 6.0 TB/s (the sum is the same, in a rotated order).
 namespace nt {
 constexpr int kBN = 256;        // weight rows (output columns) per workgroup
 constexpr int kWTN = kBN / 4;   // per wave
 constexpr int kFN = kWTN / 16;  // 16-column MFMA blocks per wave
 constexpr int kBK = 64;         // K per slice
-constexpr int kNS = 4;          // LDS stages
+constexpr int kNSReg = 2;       // LDS stages, register-staged pipeline
+constexpr int kNSLds = 4;       // LDS stages, direct-to-LDS pipeline
 constexpr int kStagger = 3;     // first slice of workgroup b: kStagger * b (mod slices)
 constexpr int kRow = kBK * 2;   // bytes per LDS row (weight or X)
 constexpr int kChunks = kRow / 16;         // 16-byte chunks per row
@@ -451,7 +465,12 @@ constexpr int kStage = kWStage + kXStage;
 constexpr int kWLoads = kWStage / 1024 / 4;  // per wave and slice
 constexpr int kXLoads = kXStage / 1024 / 4;
 constexpr int kLoadsPerSlice = kWLoads + kXLoads;
-static_assert(kNS * kStage <= 160 * 1024, "LDS capacity");
+static_assert(kNSLds * kStage <= 160 * 1024, "LDS capacity");
+// One slice of one wave in flight, 16 bytes per lane per load.
+struct SliceRegs {
+  u32x4 w[kWLoads];
+  u32x4 x[kXLoads];
+};
 // 16 consecutive rows read at one logical chunk land in 16 distinct 16-byte
 // bank slots.
 __device__ __forceinline__ int swz(int r) {
@@ -460,10 +479,11 @@ __device__ __forceinline__ int swz(int r) {
 }
 }  // namespace nt
 
-template <int MB, int EPI, bool OUT_BF16>
+template <int MB, int EPI, bool OUT_BF16, bool REG>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_nt(Bf16Args p) {
+  constexpr int NS = REG ? nt::kNSReg : nt::kNSLds;
   apply_batch(p, OUT_BF16 ? 2 : 4);
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[nt::kNS * nt::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * nt::kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -479,7 +499,6 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_nt(Bf16Args p) {
   // +7 of the stripe (lane l -> row l/8, physical chunk l%8, logical chunk
   // (l%8) ^ swz(row)); X loads cover rows 16w + 8i .. +7 the same way. ----
   const int64_t lda2 = p.lda * 2, ldb2 = p.ldb * 2;
-  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
   const int lr = lane / nt::kChunks, lc = lane % nt::kChunks;
   uint32_t w_off[nt::kWLoads];
   int w_kc[nt::kWLoads];
@@ -501,24 +520,37 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_nt(Bf16Args p) {
   }
   const int KT = (p.K + nt::kBK - 1) / nt::kBK;
   const int t0 = KT > 0 ? static_cast<int>((static_cast<int64_t>(blockIdx.x) * nt::kStagger) % KT) : 0;
-  auto issue_slice = [&](int t) {
-    const uint32_t stage = smem_base + static_cast<uint32_t>((t % nt::kNS) * nt::kStage);
-    // The t-th slice walked is slice (t0 + t) mod KT; t >= KT loads nothing
-    // (k0 = K: empty windows).
+  // The t-th slice walked is slice (t0 + t) mod KT; t >= KT loads nothing
+  // (k0 = K: every offset flagged out of range).  Weight rows n0 .. N-1 and
+  // X rows 0 .. M-1 from column k0; rows past the ends and columns past K
+  // read zeros.  Weight lines are read once by the whole grid and carry the
+  // non-temporal hint; X is re-read by every workgroup and stays cacheable.
+  auto load_slice = [&](int t, nt::SliceRegs& r) {
     const int k0 = t < KT ? (t0 + t < KT ? t0 + t : t0 + t - KT) * nt::kBK : p.K;
-    // Weight rows n0 .. N-1 and X rows 0 .. M-1 from column k0; rows past
-    // the ends and columns past K read zeros.
-    const i32x4 ww = make_window_words(p.B + static_cast<int64_t>(n0) * p.ldb + k0,
-                                       (static_cast<int64_t>(p.N - n0 - 1) * p.ldb + (p.K - k0)) * 2);
+    const __amdgpu_buffer_rsrc_t ww = window32(p.B + static_cast<int64_t>(n0) * p.ldb + k0,
+                                               (static_cast<int64_t>(p.N - n0 - 1) * p.ldb + (p.K - k0)) * 2);
 #pragma unroll
     for (int i = 0; i < nt::kWLoads; ++i)
-      buf_load16_lds(ww, stage + (nt::kWTN * wave + nt::kRowsPerLoad * i) * nt::kRow,
-                     w_off[i] | (k0 + w_kc[i] < p.K ? 0u : kOutOfRange));
-    const i32x4 wx = make_window_words(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (p.K - k0)) * 2);
+      r.w[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ww, w_off[i] | (k0 + w_kc[i] < p.K ? 0u : kOutOfRange), 0,
+                                                       kCacheNT));
+    const __amdgpu_buffer_rsrc_t wx =
+        window32(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (p.K - k0)) * 2);
 #pragma unroll
     for (int i = 0; i < nt::kXLoads; ++i)
-      buf_load16_lds(wx, stage + nt::kWStage + (16 * wave + nt::kRowsPerLoad * i) * nt::kRow,
-                     x_off[i] | (k0 + x_kc[i] < p.K ? 0u : kOutOfRange));
+      r.x[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wx, x_off[i] | (k0 + x_kc[i] < p.K ? 0u : kOutOfRange), 0, 0));
+  };
+  // Lane l's 16 bytes of load i go to LDS at the load's first row + 16 l.
+  auto store_slice = [&](int t, const nt::SliceRegs& r) {
+    uint8_t* st = smem + (t % NS) * nt::kStage;
+#pragma unroll
+    for (int i = 0; i < nt::kWLoads; ++i)
+      *reinterpret_cast<u32x4*>(st + (nt::kWTN * wave + nt::kRowsPerLoad * i) * nt::kRow + 16 * lane) = r.w[i];
+#pragma unroll
+    for (int i = 0; i < nt::kXLoads; ++i)
+      *reinterpret_cast<u32x4*>(st + nt::kWStage + (16 * wave + nt::kRowsPerLoad * i) * nt::kRow + 16 * lane) =
+          r.x[i];
   };
 
   // ---- LDS -> registers: operand of MFMA step u (K 32u .. 32u+31 of the
@@ -527,34 +559,77 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_nt(Bf16Args p) {
   const int w_rd = (nt::kWTN * wave + l16) * nt::kRow;  // + 16 j rows; swz(row) = swz(l16)
   const int x_rd = nt::kWStage + l16 * nt::kRow;  // + 16 mb rows
   const int sw = nt::swz(l16);
-
-  if (KT > 0) {
-    for (int t = 0; t < nt::kNS - 1; ++t) issue_slice(t);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((nt::kNS - 2) * nt::kLoadsPerSlice) : "memory");
-    lds_barrier();
-    for (int t = 0; t < KT; ++t) {
-      issue_slice(t + nt::kNS - 1);  // into the stage slice t-1 occupied
-      const uint8_t* base = smem + (t % nt::kNS) * nt::kStage;
+  auto compute_slice = [&](int t) {
+    const uint8_t* base = smem + (t % NS) * nt::kStage;
 #pragma unroll
-      for (int u = 0; u < nt::kBK / 32; ++u) {
-        const int ch = ((4 * u + lq) ^ sw) * 16;
-        bf16x8 fw[nt::kFN], fx[MB];
+    for (int u = 0; u < nt::kBK / 32; ++u) {
+      const int ch = ((4 * u + lq) ^ sw) * 16;
+      bf16x8 fw[nt::kFN], fx[MB];
+#pragma unroll
+      for (int j = 0; j < nt::kFN; ++j)
+        fw[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + w_rd + 16 * j * nt::kRow + ch));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        fx[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd + 16 * mb * nt::kRow + ch));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < nt::kFN; ++j)
-          fw[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + w_rd + 16 * j * nt::kRow + ch));
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          fx[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd + 16 * mb * nt::kRow + ch));
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int j = 0; j < nt::kFN; ++j)
-            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx[mb], acc[mb][j], 0, 0, 0);
-      }
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((nt::kNS - 2) * nt::kLoadsPerSlice) : "memory");
-      lds_barrier();  // slice t+1 landed everywhere; slice t no longer read
+          acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[j], fx[mb], acc[mb][j], 0, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
+  };
+  if constexpr (REG) {
+    // As in the [K, N] kernel: slice t's registers go to LDS stage t % NS
+    // and are refilled with slice t + 2; after the barrier slice t is
+    // multiplied.
+    auto step = [&](int t, nt::SliceRegs& r) {
+      store_slice(t, r);
+      load_slice(t + 2, r);
+      lds_barrier();
+      compute_slice(t);
+    };
+    if (KT > 0) {
+      nt::SliceRegs r0, r1;
+      load_slice(0, r0);
+      load_slice(1, r1);
+      int t = 0;
+      for (; t + 1 < KT; t += 2) {
+        step(t, r0);
+        step(t + 1, r1);
+      }
+      if (t < KT) step(t, r0);
+    }
+  } else {
+    // Direct buffer loads into LDS stage t % NS, NS - 1 slices in flight,
+    // with the same lane -> LDS placement as store_slice.
+    const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+    auto issue_slice = [&](int t) {
+      const uint32_t stage = smem_base + static_cast<uint32_t>((t % NS) * nt::kStage);
+      const int k0 = t < KT ? (t0 + t < KT ? t0 + t : t0 + t - KT) * nt::kBK : p.K;
+      const i32x4 ww = make_window_words(p.B + static_cast<int64_t>(n0) * p.ldb + k0,
+                                         (static_cast<int64_t>(p.N - n0 - 1) * p.ldb + (p.K - k0)) * 2);
+#pragma unroll
+      for (int i = 0; i < nt::kWLoads; ++i)
+        buf_load16_lds(ww, stage + (nt::kWTN * wave + nt::kRowsPerLoad * i) * nt::kRow,
+                       w_off[i] | (k0 + w_kc[i] < p.K ? 0u : kOutOfRange));
+      const i32x4 wx = make_window_words(p.A + k0, (static_cast<int64_t>(p.M - 1) * p.lda + (p.K - k0)) * 2);
+#pragma unroll
+      for (int i = 0; i < nt::kXLoads; ++i)
+        buf_load16_lds(wx, stage + nt::kWStage + (16 * wave + nt::kRowsPerLoad * i) * nt::kRow,
+                       x_off[i] | (k0 + x_kc[i] < p.K ? 0u : kOutOfRange));
+    };
+    if (KT > 0) {
+      for (int t = 0; t < NS - 1; ++t) issue_slice(t);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * nt::kLoadsPerSlice) : "memory");
+      lds_barrier();
+      for (int t = 0; t < KT; ++t) {
+        issue_slice(t + NS - 1);  // into the stage slice t-1 occupied
+        compute_slice(t);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * nt::kLoadsPerSlice) : "memory");
+        lds_barrier();  // slice t+1 landed everywhere; slice t no longer read
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
+    }
   }
 
   // ---- epilogue: element e of lane l in block (mb, j) is row 16 mb + l%16,
@@ -582,8 +657,11 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_nt(Bf16Args p) {
 
 template <int MB, int EPI, bool OUT_BF16>
 hipError_t launch_nt_m(const Bf16Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((tgemm_bf16_thin_nt<MB, EPI, OUT_BF16>), dim3((a.N + nt::kBN - 1) / nt::kBN, a.batch),
-                     dim3(kThreads), 0, s, a);
+  const dim3 grid((a.N + nt::kBN - 1) / nt::kBN, a.batch);
+  if (use_reg_pipeline(static_cast<int64_t>(grid.x) * grid.y))
+    hipLaunchKernelGGL((tgemm_bf16_thin_nt<MB, EPI, OUT_BF16, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((tgemm_bf16_thin_nt<MB, EPI, OUT_BF16, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -628,11 +706,11 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mn;
 }
 
-template <int MB>
+template <int MB, bool REG>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_bf16_thin_lsm(Bf16Args p, LsmArgs q) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNSReg * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[(REG ? kNSReg : kNSLds) * kStage];
   f32x4 acc[MB][kFN];
-  thin_accumulate<MB, true>(p, smem, acc);
+  thin_accumulate<MB, REG>(p, smem, acc);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * kBN;
@@ -773,7 +851,10 @@ __global__ __launch_bounds__(256) void tgemm_lsm_normalize(LsmArgs q, void* C, i
 
 template <int MB>
 hipError_t launch_lsm_m(const Bf16Args& a, const LsmArgs& q, hipStream_t s) {
-  hipLaunchKernelGGL((tgemm_bf16_thin_lsm<MB>), dim3(q.G), dim3(kThreads), 0, s, a, q);
+  if (use_reg_pipeline(q.G))
+    hipLaunchKernelGGL((tgemm_bf16_thin_lsm<MB, true>), dim3(q.G), dim3(kThreads), 0, s, a, q);
+  else
+    hipLaunchKernelGGL((tgemm_bf16_thin_lsm<MB, false>), dim3(q.G), dim3(kThreads), 0, s, a, q);
   return hipGetLastError();
 }
 
