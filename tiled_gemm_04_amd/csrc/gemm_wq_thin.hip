@@ -19,10 +19,12 @@
 // Layout of the work (the bf16 thin-M kernel's, with byte rows):
 //   * a workgroup owns 512 consecutive columns: a byte row of its stripe is
 //     512 contiguous bytes; the stripe is walked in slices of 32 byte rows
-//     (32 K rows of int8, 64 of int4) that go global -> LDS with direct
-//     buffer loads (one load = two byte rows), six LDS stages deep, together
-//     with the matching 16-row blocks of X and the 512 scales of the slice's
-//     group;
+//     (32 K rows of int8, 64 of int4), each with the matching 16-row blocks
+//     of X and the 512 scales of the slice's group, one load instruction
+//     per two byte rows.  int8 slices for up to 48 rows of X go through
+//     registers (four slices in flight per wave, codes with the
+//     non-temporal hint) into two LDS stages; int4 slices and int8 at 49-64
+//     rows go global -> LDS with direct buffer loads, six LDS stages deep;
 //   * eight waves (two per SIMD, so one wave's conversions overlap the
 //     other's MFMAs and loads) each own 64 columns over the whole of K.  A
 //     wave's MFMA operand for 16 columns comes from one ds_read_b64_tr_b8
@@ -73,6 +75,17 @@ struct WqShape {
   static_assert(kNS * kStage <= 160 * 1024, "LDS capacity");
 };
 
+// Load pipeline: int8 slices for up to 48 rows of X stream through
+// registers into two LDS stages.  int4 slices (twice the conversion work per
+// byte, two per barrier) and int8 at 49-64 rows (whose four register slices
+// would not fit beside the group partials and accumulators in a wave's 256
+// registers) go straight into LDS, kNS stages deep.
+template <int BITS, int MB>
+struct WqStages {
+  static constexpr bool kRegisters = BITS == 8 && MB <= 3;
+  static constexpr int kCount = kRegisters ? 2 : kNS;
+};
+
 #define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
@@ -101,6 +114,27 @@ __device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, u
                :
                : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_words(window))
                : "memory", "m0");
+}
+
+// int8 codes stream through registers (see wq_accumulate): one slice of
+// one wave in flight is its two 16-byte Q loads, its X load and its scale.
+constexpr int kRegSlices = 4;     // slices in flight per wave
+constexpr uint32_t kCacheNT = 2;   // buffer-load cache policy: non-temporal
+struct WqRegs {
+  u32x4 q[2];
+  u32x4 x;
+  uint32_t s;
+};
+
+// Buffer descriptor over [base, base + bytes), bytes clamped to [0, 2^31 - 1]
+// with 32-bit compares so the descriptor stays in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wq_window(const void* base, int64_t bytes) {
+  const uint64_t u = static_cast<uint64_t>(bytes);
+  const int32_t hi = static_cast<int32_t>(u >> 32);
+  const uint32_t lo = static_cast<uint32_t>(u);
+  const int32_t n = hi < 0 ? 0 : ((hi > 0 || lo > 0x7fffffffu) ? 0x7fffffff : static_cast<int32_t>(lo));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           static_cast<int>(kBufferFlags));
 }
 
 // Eight int8 codes (two dwords, K order) as 8 bf16, exactly.
@@ -147,6 +181,7 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
   constexpr int kBK = Sh::kBK;
   constexpr int kStage = Sh::kStage;
   constexpr int kXStage = Sh::kXStage;
+  constexpr int NS = WqStages<BITS, MB>::kCount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -183,7 +218,7 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
   const int G = (p.K + kGroupK - 1) / kGroupK;
   const int64_t q_rows = BITS == 8 ? p.K : p.K / 2;  // byte rows of Q
   auto issue_slice = [&](int t) {
-    const uint32_t stage = smem_base + static_cast<uint32_t>((t % kNS) * kStage);
+    const uint32_t stage = smem_base + static_cast<uint32_t>((t % NS) * kStage);
     const int k0 = t * kBK;
     const int64_t r0 = static_cast<int64_t>(t) * kRows;
     const i32x4 ww = make_window_words(p.Q + r0 * p.ldq + n0, (q_rows - r0 - 1) * p.ldq + (p.N - n0));
@@ -195,6 +230,32 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     const i32x4 ws = make_window_words(p.S + static_cast<int64_t>(g) * p.N + n0,
                                        g < G ? static_cast<int64_t>(p.N - n0) * 4 : 0);
     buf_load4_lds(ws, stage + kWStage + kXStage + 64 * wave * 4, static_cast<uint32_t>((64 * wave + lane) * 4));
+  };
+  // The same slice through registers: Q with the non-temporal hint (read
+  // once by the whole grid), X and the scales cacheable; each lane's bytes
+  // land in LDS where the direct loads above put them.
+  auto load_regs = [&](int t, WqRegs& r) {
+    const int k0 = t * kBK;
+    const int64_t r0 = static_cast<int64_t>(t) * kRows;
+    const __amdgpu_buffer_rsrc_t ww = wq_window(p.Q + r0 * p.ldq + n0, (q_rows - r0 - 1) * p.ldq + (p.N - n0));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      r.q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ww, w_off[i], 0, kCacheNT));
+    const __amdgpu_buffer_rsrc_t wx =
+        wq_window(p.X + k0, (static_cast<int64_t>(p.M - 1) * p.ldx + (p.K - k0)) * 2);
+    r.x = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wx, x_off | (k0 + 8 * xc < p.K ? 0u : kOutOfRange), 0, 0));
+    const int g = k0 / kGroupK;
+    const __amdgpu_buffer_rsrc_t ws = wq_window(p.S + static_cast<int64_t>(g) * p.N + n0,
+                                                g < G ? static_cast<int64_t>(p.N - n0) * 4 : 0);
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(ws, static_cast<uint32_t>((64 * wave + lane) * 4), 0, 0);
+  };
+  auto store_regs = [&](int t, const WqRegs& r) {
+    uint8_t* st = smem + (t % NS) * kStage;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(st + (4 * wave + 2 * i) * kWRow + 16 * lane) = r.q[i];
+    *reinterpret_cast<u32x4*>(st + x_dst + 16 * lane) = r.x;
+    *reinterpret_cast<uint32_t*>(st + kWStage + kXStage + 64 * wave * 4 + 4 * lane) = r.s;
   };
 
   // ---- LDS -> registers ----
@@ -233,7 +294,7 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     // when it ends a 128-row group.  A slice at or past KT (the partner of
     // an odd last slice of a pair) reads zeros and adds nothing.
     auto process = [&](int t) {
-      const uint8_t* base = smem + (t % kNS) * kStage;
+      const uint8_t* base = smem + (t % NS) * kStage;
       constexpr int kSteps = kBK / 32;  // 16 x 16 x 32 MFMA steps per slice
       bf16x8 fb[kSteps][kFN], fx[kSteps][MB];
 #pragma unroll
@@ -273,22 +334,47 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
         }
       }
     };
-    // kPerBar slices per barrier; their loads go kAhead slices ahead, into
-    // the stages the previous group of slices occupied.
-    constexpr int kPerBar = Sh::kPerBar;
-    constexpr int kAhead = kNS - kPerBar;
-    for (int t = 0; t < kAhead; ++t) issue_slice(t);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
-    lds_barrier();
-    for (int t = 0; t < KT; t += kPerBar) {
+    if constexpr (WqStages<BITS, MB>::kRegisters) {
+      // R slices in flight per wave in registers; slice t goes to LDS
+      // stage t % 2, its registers are refilled with slice t + R, and after
+      // the barrier (stage t complete in every wave, stage t - 1 no longer
+      // read) it is processed.
+      constexpr int R = kRegSlices;
+      auto step = [&](int t, WqRegs& r) {
+        store_regs(t, r);
+        load_regs(t + R, r);
+        lds_barrier();
+        process(t);
+      };
+      WqRegs r[R];
 #pragma unroll
-      for (int h = 0; h < kPerBar; ++h) issue_slice(t + kAhead + h);
+      for (int h = 0; h < R; ++h) load_regs(h, r[h]);
+      int t = 0;
+      for (; t + R <= KT; t += R) {
 #pragma unroll
-      for (int h = 0; h < kPerBar; ++h) process(t + h);
+        for (int h = 0; h < R; ++h) step(t + h, r[h]);
+      }
+#pragma unroll
+      for (int h = 0; h < R - 1; ++h)
+        if (t + h < KT) step(t + h, r[h]);
+    } else {
+      // kPerBar slices per barrier; their loads go kAhead slices ahead,
+      // into the stages the previous group of slices occupied.
+      constexpr int kPerBar = Sh::kPerBar;
+      constexpr int kAhead = NS - kPerBar;
+      for (int t = 0; t < kAhead; ++t) issue_slice(t);
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
-      lds_barrier();  // the next slices landed everywhere; these are no longer read
+      lds_barrier();
+      for (int t = 0; t < KT; t += kPerBar) {
+#pragma unroll
+        for (int h = 0; h < kPerBar; ++h) issue_slice(t + kAhead + h);
+#pragma unroll
+        for (int h = 0; h < kPerBar; ++h) process(t + h);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
+        lds_barrier();  // the next slices landed everywhere; these are no longer read
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
   }
 }
 
@@ -341,7 +427,7 @@ __device__ __forceinline__ void wq_store(const W8Args& p, const f32x4 (&acc)[MB]
 
 template <int MB, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_w8_thin(W8Args p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * WqShape<8>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WqStages<8, MB>::kCount * WqShape<8>::kStage];
   f32x4 acc[MB][kFN];
   wq_accumulate<8, MB>(p, smem, acc);
   wq_store<MB, EPI, OUT_BF16>(p, acc);
@@ -349,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_w8_thin(W8Args p) {
 
 template <int MB, int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_w4_thin(W8Args p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * WqShape<4>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WqStages<4, MB>::kCount * WqShape<4>::kStage];
   f32x4 acc[MB][kFN];
   wq_accumulate<4, MB>(p, smem, acc);
   wq_store<MB, EPI, OUT_BF16>(p, acc);
@@ -363,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_w4_thin(W8Args p) {
 // fp32 logits into their buffer; pass 2 is the bf16 head's normalisation.
 template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_wq_thin_lsm(W8Args p, LsmArgs q) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * WqShape<BITS>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WqStages<BITS, MB>::kCount * WqShape<BITS>::kStage];
   f32x4 acc[MB][kFN];
   wq_accumulate<BITS, MB>(p, smem, acc);
   const int lane = threadIdx.x & 63;
