@@ -78,6 +78,18 @@ def test_w8_shapes(shape):
     _check(x, q, s, None, tg.EPI_NONE, torch.bfloat16, "shape")
 
 
+@pytest.mark.parametrize("shape", [(1, 4096, 4096), (8, 14336, 4096), (33, 2048, 4096), (64, 4096, 4096),
+                                   (5, 1000, 1992), (16, 516, 2056)])
+@pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
+def test_w8_split_k(shape, out):
+    """Narrow weights (at most 128 stripes of 512 columns) are cut along K
+    into chunks of whole 128-row scale groups; the fp32 partials are summed
+    in chunk order with the bias and tanh-GeLU.  Checked against the oracle."""
+    M, N, K = shape
+    x, q, s, b = _inputs(M, N, K, 4700 + M + K, _dev(), bias=True)
+    _check(x, q, s, b, tg.EPI_BIAS_GELU_TANH, out, "split-k")
+
+
 @pytest.mark.parametrize("epi", [tg.EPI_NONE, tg.EPI_BIAS, tg.EPI_BIAS_GELU_TANH])
 @pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
 def test_w8_epilogues_and_outputs(epi, out):

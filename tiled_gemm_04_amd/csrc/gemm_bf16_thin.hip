@@ -414,18 +414,7 @@ hipError_t launch_splitk_m(const Bf16Args& a, float* part, int S, int ktc, int e
                      a, part, ktc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t quads = (static_cast<int64_t>(a.M) * a.N + 3) / 4;
-  const dim3 grid(static_cast<unsigned>((quads + 255) / 256));
-  if (out_bf16) {
-    if (epi == kEpiNone) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiNone, true>), grid, dim3(256), 0, s, a, part, S);
-    else if (epi == kEpiBias) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBias, true>), grid, dim3(256), 0, s, a, part, S);
-    else hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBiasGelu, true>), grid, dim3(256), 0, s, a, part, S);
-  } else {
-    if (epi == kEpiNone) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiNone, false>), grid, dim3(256), 0, s, a, part, S);
-    else if (epi == kEpiBias) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBias, false>), grid, dim3(256), 0, s, a, part, S);
-    else hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBiasGelu, false>), grid, dim3(256), 0, s, a, part, S);
-  }
-  return hipGetLastError();
+  return launch_splitk_reduce(a, part, S, epi, out_bf16, s);
 }
 
 // ---- Small-M GEMM with K-contiguous weights, Wt [N, K] (the nn.Linear
@@ -904,6 +893,22 @@ ThinSplit thin_split_plan(int64_t M, int64_t N, int64_t K) {
   r.S = static_cast<int>((KT + ktc - 1) / ktc);
   r.ktc = static_cast<int>(ktc);
   return r;
+}
+
+hipError_t launch_splitk_reduce(const Bf16Args& a, const float* part, int S, int epi, int out_bf16,
+                                hipStream_t s) {
+  const int64_t quads = (static_cast<int64_t>(a.M) * a.N + 3) / 4;
+  const dim3 grid(static_cast<unsigned>((quads + 255) / 256));
+  if (out_bf16) {
+    if (epi == kEpiNone) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiNone, true>), grid, dim3(256), 0, s, a, part, S);
+    else if (epi == kEpiBias) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBias, true>), grid, dim3(256), 0, s, a, part, S);
+    else hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBiasGelu, true>), grid, dim3(256), 0, s, a, part, S);
+  } else {
+    if (epi == kEpiNone) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiNone, false>), grid, dim3(256), 0, s, a, part, S);
+    else if (epi == kEpiBias) hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBias, false>), grid, dim3(256), 0, s, a, part, S);
+    else hipLaunchKernelGGL((tgemm_splitk_reduce<kEpiBiasGelu, false>), grid, dim3(256), 0, s, a, part, S);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_bf16_thin_splitk(const Bf16Args& a, const ThinSplit& plan, float* part, int epi,

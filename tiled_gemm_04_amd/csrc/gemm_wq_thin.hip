@@ -173,10 +173,13 @@ __device__ __forceinline__ bf16x8 nibbles_to_bf16(uint32_t codes) {
 // Streams the workgroup's 512-column stripe of Q once and leaves the scaled
 // products in acc[mb][j] (16 x 16 blocks, transposed by the operand swap:
 // element e of lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the
-// wave's 64).  Ends with every load landed; the caller synchronises the
-// workgroup before reusing smem.
+// wave's 64).  Slices [tb, te) of K (te < 0: through the last) are summed;
+// a range starts and ends on a scale-group boundary (or at K), and its end
+// acts as K, so nothing past it is loaded.  Ends with no load still writing
+// LDS; the caller synchronises the workgroup before reusing smem.
 template <int BITS, int MB>
-__device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f32x4 (&acc)[MB][kFN]) {
+__device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f32x4 (&acc)[MB][kFN], int tb = 0,
+                                              int te = -1) {
   using Sh = WqShape<BITS>;
   constexpr int kBK = Sh::kBK;
   constexpr int kStage = Sh::kStage;
@@ -215,8 +218,11 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
   const int xc = BITS == 8 ? (lane & 3) ^ x_swz<BITS>(xr & 15) : (lane & 7) ^ x_swz<BITS>(xr & 15);
   const uint32_t x_off = static_cast<uint32_t>(xr * ldx2 + 16 * xc);
   const uint32_t x_dst = kWStage + (BITS == 8 ? (wave & 3) : wave) * 1024;
-  const int G = (p.K + kGroupK - 1) / kGroupK;
-  const int64_t q_rows = BITS == 8 ? p.K : p.K / 2;  // byte rows of Q
+  const int KT = (p.K + kBK - 1) / kBK;
+  if (te < 0) te = KT;
+  const int kend = p.K < te * kBK ? p.K : te * kBK;  // this range's end of K
+  const int G = (kend + kGroupK - 1) / kGroupK;       // groups up to it
+  const int64_t q_rows = BITS == 8 ? kend : kend / 2;  // byte rows of Q up to it
   auto issue_slice = [&](int t) {
     const uint32_t stage = smem_base + static_cast<uint32_t>((t % NS) * kStage);
     const int k0 = t * kBK;
@@ -224,8 +230,8 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     const i32x4 ww = make_window_words(p.Q + r0 * p.ldq + n0, (q_rows - r0 - 1) * p.ldq + (p.N - n0));
 #pragma unroll
     for (int i = 0; i < 2; ++i) buf_load16_lds(ww, stage + (4 * wave + 2 * i) * kWRow, w_off[i]);
-    const i32x4 wx = make_window_words(p.X + k0, (static_cast<int64_t>(p.M - 1) * p.ldx + (p.K - k0)) * 2);
-    buf_load16_lds(wx, stage + x_dst, x_off | (k0 + 8 * xc < p.K ? 0u : kOutOfRange));
+    const i32x4 wx = make_window_words(p.X + k0, (static_cast<int64_t>(p.M - 1) * p.ldx + (kend - k0)) * 2);
+    buf_load16_lds(wx, stage + x_dst, x_off | (k0 + 8 * xc < kend ? 0u : kOutOfRange));
     const int g = k0 / kGroupK;
     const i32x4 ws = make_window_words(p.S + static_cast<int64_t>(g) * p.N + n0,
                                        g < G ? static_cast<int64_t>(p.N - n0) * 4 : 0);
@@ -242,9 +248,9 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     for (int i = 0; i < 2; ++i)
       r.q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ww, w_off[i], 0, kCacheNT));
     const __amdgpu_buffer_rsrc_t wx =
-        wq_window(p.X + k0, (static_cast<int64_t>(p.M - 1) * p.ldx + (p.K - k0)) * 2);
+        wq_window(p.X + k0, (static_cast<int64_t>(p.M - 1) * p.ldx + (kend - k0)) * 2);
     r.x = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wx, x_off | (k0 + 8 * xc < p.K ? 0u : kOutOfRange), 0, 0));
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wx, x_off | (k0 + 8 * xc < kend ? 0u : kOutOfRange), 0, 0));
     const int g = k0 / kGroupK;
     const __amdgpu_buffer_rsrc_t ws = wq_window(p.S + static_cast<int64_t>(g) * p.N + n0,
                                                 g < G ? static_cast<int64_t>(p.N - n0) * 4 : 0);
@@ -283,16 +289,15 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
   // int4 operands carry 16 q.
   constexpr float kCodeScale = BITS == 8 ? 1.0f : 1.0f / 16.0f;
 
-  const int KT = (p.K + kBK - 1) / kBK;
-  if (KT > 0) {
+  if (te > tb) {
     f32x4 part[MB][kFN];  // sum over the current 128-row group of x * q
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < kFN; ++j) part[mb][j] = f32x4{};
     // One slice's operand reads, conversions and MFMAs, and the group fold
-    // when it ends a 128-row group.  A slice at or past KT (the partner of
-    // an odd last slice of a pair) reads zeros and adds nothing.
+    // when it ends a 128-row group or the range.  A slice at or past te (the
+    // partner of an odd last slice of a pair) reads zeros and adds nothing.
     auto process = [&](int t) {
       const uint8_t* base = smem + (t % NS) * kStage;
       constexpr int kSteps = kBK / 32;  // 16 x 16 x 32 MFMA steps per slice
@@ -319,7 +324,7 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
 #pragma unroll
           for (int j = 0; j < kFN; ++j)
             part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fx[u][mb], part[mb][j], 0, 0, 0);
-      if ((t % Sh::kSlicesPerGroup) == Sh::kSlicesPerGroup - 1 || t == KT - 1) {
+      if ((t % Sh::kSlicesPerGroup) == Sh::kSlicesPerGroup - 1 || t == te - 1) {
         // End of a scale group: acc += s * partial, per column.
 #pragma unroll
         for (int j = 0; j < kFN; ++j) {
@@ -348,24 +353,24 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
       };
       WqRegs r[R];
 #pragma unroll
-      for (int h = 0; h < R; ++h) load_regs(h, r[h]);
-      int t = 0;
-      for (; t + R <= KT; t += R) {
+      for (int h = 0; h < R; ++h) load_regs(tb + h, r[h]);
+      int t = tb;
+      for (; t + R <= te; t += R) {
 #pragma unroll
         for (int h = 0; h < R; ++h) step(t + h, r[h]);
       }
 #pragma unroll
       for (int h = 0; h < R - 1; ++h)
-        if (t + h < KT) step(t + h, r[h]);
+        if (t + h < te) step(t + h, r[h]);
     } else {
       // kPerBar slices per barrier; their loads go kAhead slices ahead,
       // into the stages the previous group of slices occupied.
       constexpr int kPerBar = Sh::kPerBar;
       constexpr int kAhead = NS - kPerBar;
-      for (int t = 0; t < kAhead; ++t) issue_slice(t);
+      for (int t = tb; t < tb + kAhead; ++t) issue_slice(t);
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
       lds_barrier();
-      for (int t = 0; t < KT; t += kPerBar) {
+      for (int t = tb; t < te; t += kPerBar) {
 #pragma unroll
         for (int h = 0; h < kPerBar; ++h) issue_slice(t + kAhead + h);
 #pragma unroll
@@ -439,6 +444,28 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_w4_thin(W8Args p) {
   f32x4 acc[MB][kFN];
   wq_accumulate<4, MB>(p, smem, acc);
   wq_store<MB, EPI, OUT_BF16>(p, acc);
+}
+
+// ---- Split-K for narrow weights.  With few 512-column stripes (a decode
+// FFN projection, N of a few thousand) each compute unit streams at a few
+// tens of GB/s and most units sit idle; the K range is then cut into
+// chunks of whole scale groups (grid z).  Workgroup (stripe, z) writes its
+// fp32 partial, already scaled group by group, to part[z][M][N]; the bf16
+// thin kernel's reduction adds the partials in order of z, then the bias
+// and the epilogue, and rounds once: deterministic, no atomics. ----
+template <int BITS, int MB>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_wq_thin_splitk(W8Args p, float* part, int ktc) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WqStages<BITS, MB>::kCount * WqShape<BITS>::kStage];
+  f32x4 acc[MB][kFN];
+  const int KT = (p.K + WqShape<BITS>::kBK - 1) / WqShape<BITS>::kBK;
+  const int tb = blockIdx.z * ktc;
+  const int te = tb + ktc < KT ? tb + ktc : KT;
+  wq_accumulate<BITS, MB>(p, smem, acc, tb, te);
+  W8Args pp = p;
+  pp.C = part + static_cast<int64_t>(blockIdx.z) * p.M * p.N;
+  pp.ldc = p.N;
+  pp.vec_c = (p.N % 4) == 0 ? 1 : 0;
+  wq_store<MB, kEpiNone, false>(pp, acc);
 }
 
 // ---- The low-precision LM head with bias and LogSoftmax (the GEMM
@@ -599,7 +626,65 @@ hipError_t launch_wq_thin_lsm(int bits, const W8Args& a, const LsmArgs& q, int o
   return launch_lsm_normalize(q, a.C, a.ldc, a.M, a.N, a.vec_c, out_bf16, s);
 }
 
+ThinSplit wq_split_plan(int64_t M, int64_t N, int64_t K) {
+  // Enough (stripe, chunk) workgroups to cover the compute units, chunks of
+  // whole 128-row groups, and partial traffic (2 S M N fp32 = 8 S M N bytes)
+  // at most half the int8 codes (K N bytes): S <= K / (16 M).  The plan does
+  // not depend on the code width, so int4 and int8 codes of equal values sum
+  // in the same order.
+  ThinSplit r{1, 0};
+  const int64_t stripes = (N + kBN - 1) / kBN;
+  const int64_t G = (K + kGroupK - 1) / kGroupK;
+  if (M < 1 || stripes > 128 || G < 2) return r;
+  const int cus = device_cus();
+  int64_t S = ((cus > 0 ? cus : 256) + stripes - 1) / stripes;
+  S = S < G ? S : G;
+  const int64_t cap = K / (16 * M);
+  S = S < cap ? S : cap;
+  if (S < 2) return r;
+  const int64_t gpc = (G + S - 1) / S;  // groups per chunk
+  r.S = static_cast<int>((G + gpc - 1) / gpc);
+  r.ktc = static_cast<int>(gpc);  // in groups; the launcher converts to slices
+  return r;
+}
+
+namespace {
+
+template <int BITS, int MB>
+hipError_t launch_splitk_bits_m(const W8Args& a, const ThinSplit& plan, float* part, hipStream_t s) {
+  const int ktc = plan.ktc * WqShape<BITS>::kSlicesPerGroup;
+  hipLaunchKernelGGL((tgemm_wq_thin_splitk<BITS, MB>), dim3((a.N + kBN - 1) / kBN, 1, plan.S), dim3(kThreads), 0,
+                     s, a, part, ktc);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_splitk_bits(const W8Args& a, const ThinSplit& plan, float* part, hipStream_t s) {
+  if (a.M <= 16) return launch_splitk_bits_m<BITS, 1>(a, plan, part, s);
+  if (a.M <= 32) return launch_splitk_bits_m<BITS, 2>(a, plan, part, s);
+  if (a.M <= 48) return launch_splitk_bits_m<BITS, 3>(a, plan, part, s);
+  return launch_splitk_bits_m<BITS, 4>(a, plan, part, s);
+}
+
+}  // namespace
+
 hipError_t launch_wq_thin(int bits, const W8Args& a, int epi, int out_bf16, hipStream_t s) {
+  const ThinSplit plan = wq_split_plan(a.M, a.N, a.K);
+  if (plan.S > 1) {
+    float* part = static_cast<float*>(device_scratch(static_cast<size_t>(plan.S) * a.M * a.N * sizeof(float), s));
+    if (part != nullptr) {
+      hipError_t e = bits == 8 ? launch_splitk_bits<8>(a, plan, part, s) : launch_splitk_bits<4>(a, plan, part, s);
+      if (e != hipSuccess) return e;
+      Bf16Args r{};
+      r.M = a.M;
+      r.N = a.N;
+      r.bias = a.bias;
+      r.C = a.C;
+      r.ldc = a.ldc;
+      r.vec_c = a.vec_c;
+      return launch_splitk_reduce(r, part, plan.S, epi, out_bf16, s);
+    }
+  }
   if (bits == 8) return dispatch_m<8>(a, epi, out_bf16, s);
   return dispatch_m<4>(a, epi, out_bf16, s);
 }

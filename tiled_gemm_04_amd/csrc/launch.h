@@ -116,6 +116,10 @@ ThinSplit thin_split_plan(int64_t M, int64_t N, int64_t K);
 // part: S * M * N fp32 of device scratch.
 hipError_t launch_bf16_thin_splitk(const Bf16Args& a, const ThinSplit& plan, float* part, int epilogue,
                                    int out_bf16, hipStream_t stream);
+// C = epilogue(sum over s < S of part[s] + bias), summed in order of s and
+// rounded once; reads a.M, a.N, a.bias, a.C, a.ldc and a.vec_c only.
+hipError_t launch_splitk_reduce(const Bf16Args& a, const float* part, int S, int epilogue, int out_bf16,
+                                hipStream_t stream);
 // Library-owned device scratch of at least `bytes` for work on `stream` of
 // the current device (one buffer per device and stream, grown on demand,
 // kept until the process ends); nullptr if it cannot be allocated.
@@ -153,6 +157,9 @@ hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
 // bits: 8 or 4 (the code width).
 hipError_t launch_wq_thin(int bits, const W8Args& a, int epilogue, int out_bf16, hipStream_t stream);
+// Split-K plan of the integer-weight kernel (chunks of whole 128-row scale
+// groups; the same for int8 and int4); S == 1: no split.
+ThinSplit wq_split_plan(int64_t M, int64_t N, int64_t K);
 bool wq_supported(int bits, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq);
 const char* wq_kernel_name(int bits, int M);
 // Thin-M GEMM + bias + row log-softmax, in two passes: the GEMM kernel
