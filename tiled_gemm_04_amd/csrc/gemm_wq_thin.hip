@@ -21,10 +21,11 @@
 //     512 contiguous bytes; the stripe is walked in slices of 32 byte rows
 //     (32 K rows of int8, 64 of int4), each with the matching 16-row blocks
 //     of X and the 512 scales of the slice's group, one load instruction
-//     per two byte rows.  int8 slices for up to 48 rows of X go through
-//     registers (four slices in flight per wave, codes with the
-//     non-temporal hint) into two LDS stages; int4 slices and int8 at 49-64
-//     rows go global -> LDS with direct buffer loads, six LDS stages deep;
+//     per two byte rows.  In the full-width kernels, int8 slices for up to
+//     48 rows of X and int4 slices for up to 32 go through registers (four
+//     slices in flight per wave, codes with the non-temporal hint) into two
+//     LDS stages; more rows and the split-K kernel go global -> LDS with
+//     direct buffer loads, six LDS stages deep;
 //   * eight waves (two per SIMD, so one wave's conversions overlap the
 //     other's MFMAs and loads) each own 64 columns over the whole of K.  A
 //     wave's MFMA operand for 16 columns comes from one ds_read_b64_tr_b8
@@ -75,14 +76,15 @@ struct WqShape {
   static_assert(kNS * kStage <= 160 * 1024, "LDS capacity");
 };
 
-// Load pipeline: int8 slices for up to 48 rows of X stream through
-// registers into two LDS stages.  int4 slices (twice the conversion work per
-// byte, two per barrier) and int8 at 49-64 rows (whose four register slices
-// would not fit beside the group partials and accumulators in a wave's 256
-// registers) go straight into LDS, kNS stages deep.
-template <int BITS, int MB>
+// Load pipeline: the full-width kernels stream int8 slices for up to 48 rows
+// of X and int4 slices for up to 32 through registers into two LDS stages.
+// More rows (whose four register slices would not fit beside the group
+// partials and accumulators in a wave's 256 registers) and the split-K
+// kernel (whose short chunks gain more from depth) load straight into LDS,
+// kNS stages deep.
+template <int BITS, int MB, bool SPLIT = false>
 struct WqStages {
-  static constexpr bool kRegisters = BITS == 8 && MB <= 3;
+  static constexpr bool kRegisters = !SPLIT && MB <= (BITS == 8 ? 3 : 2);
   static constexpr int kCount = kRegisters ? 2 : kNS;
 };
 
@@ -177,14 +179,14 @@ __device__ __forceinline__ bf16x8 nibbles_to_bf16(uint32_t codes) {
 // a range starts and ends on a scale-group boundary (or at K), and its end
 // acts as K, so nothing past it is loaded.  Ends with no load still writing
 // LDS; the caller synchronises the workgroup before reusing smem.
-template <int BITS, int MB>
+template <int BITS, int MB, bool SPLIT = false>
 __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f32x4 (&acc)[MB][kFN], int tb = 0,
                                               int te = -1) {
   using Sh = WqShape<BITS>;
   constexpr int kBK = Sh::kBK;
   constexpr int kStage = Sh::kStage;
   constexpr int kXStage = Sh::kXStage;
-  constexpr int NS = WqStages<BITS, MB>::kCount;
+  constexpr int NS = WqStages<BITS, MB, SPLIT>::kCount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -339,7 +341,7 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
         }
       }
     };
-    if constexpr (WqStages<BITS, MB>::kRegisters) {
+    if constexpr (WqStages<BITS, MB, SPLIT>::kRegisters) {
       // R slices in flight per wave in registers; slice t goes to LDS
       // stage t % 2, its registers are refilled with slice t + R, and after
       // the barrier (stage t complete in every wave, stage t - 1 no longer
@@ -455,12 +457,12 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_w4_thin(W8Args p) {
 // and the epilogue, and rounds once: deterministic, no atomics. ----
 template <int BITS, int MB>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_wq_thin_splitk(W8Args p, float* part, int ktc) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[WqStages<BITS, MB>::kCount * WqShape<BITS>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[WqStages<BITS, MB, true>::kCount * WqShape<BITS>::kStage];
   f32x4 acc[MB][kFN];
   const int KT = (p.K + WqShape<BITS>::kBK - 1) / WqShape<BITS>::kBK;
   const int tb = blockIdx.z * ktc;
   const int te = tb + ktc < KT ? tb + ktc : KT;
-  wq_accumulate<BITS, MB>(p, smem, acc, tb, te);
+  wq_accumulate<BITS, MB, true>(p, smem, acc, tb, te);
   W8Args pp = p;
   pp.C = part + static_cast<int64_t>(blockIdx.z) * p.M * p.N;
   pp.ldc = p.N;
