@@ -23,7 +23,8 @@
  * Memory.   All pointers are device pointers owned by the caller.  The
  *           library never allocates, frees or keeps them.  Two paths use
  *           library-owned device scratch instead (split-K of the small-M
- *           bf16 kernel; the split last round of gemm_fp8_blockscaled): one
+ *           bf16 kernel and of the integer-weight kernels for narrow
+ *           weights; the split last round of gemm_fp8_blockscaled): one
  *           buffer per device, stream and purpose, allocated on first use,
  *           grown on demand and kept until the process ends, so the first
  *           such call on a stream allocates (do not make it under graph
@@ -356,7 +357,12 @@ int64_t gemm_logsoftmax_workspace_size(int64_t M, int64_t N, int out_dtype);
  * Epilogue, output rounding and conventions as gemm_bf16.  Products X * Q
  * are exact and summed in fp32 per 128-row group, and each group's sum is
  * scaled by S in fp32 (no weight is rounded), so the result carries the
- * rounding of an fp32-accumulated GEMM.
+ * rounding of an fp32-accumulated GEMM.  A narrow weight (N <= 65536) is
+ * cut along K into chunks of whole 128-row groups when that fills more of
+ * the device; the chunks' fp32 partials go to library scratch (see Memory)
+ * and are summed in chunk order, then the bias and epilogue are applied and
+ * the result rounded once (deterministic; the summation order, so the last
+ * bits, differ from the unsplit call).
  * Supported: M <= 64, K % 8 == 0, N % 4 == 0, ldq % 4 == 0 (others return
  * TGEMM_ERR_UNSUPPORTED).  Returns TGEMM_OK, TGEMM_ERR_INVALID,
  * TGEMM_ERR_UNSUPPORTED or TGEMM_ERR_LAUNCH.
