@@ -126,6 +126,26 @@ def test_w4_matches_int8_kernel_bit_for_bit():
         assert torch.equal(c4.contiguous().view(torch.uint8), c8.view(torch.uint8))
 
 
+@pytest.mark.parametrize("M", [12, 40])
+def test_w4_matches_int8_full_width(M):
+    """The same codes on a weight wide enough not to be split (129 stripes
+    of 512 columns): int8 streams through registers up to 48 rows and int4
+    up to 32, so at M = 40 the int4 kernel's direct-to-LDS pipeline meets the
+    int8 kernel's register-staged one.  Bit-equal, and sampled columns
+    (incl. both edges) within the oracle's tolerance."""
+    dev = _dev()
+    N, K = 66048, 256
+    x, p, s, b = _inputs(M, N, K, 45 + M, dev, bias=True)
+    q8 = torch.from_numpy(og.unpack_int4(p.cpu().numpy())).to(dev)
+    cols = torch.cat([torch.arange(0, 256), torch.arange(N - 256, N),
+                      torch.randperm(N, generator=torch.Generator().manual_seed(M))[:512]]).to(dev)
+    c4 = _check(x, p, s, b, tg.EPI_BIAS, torch.bfloat16, "full width vs int8", cols=cols)
+    c8 = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    tg.gemm_bf16_w8(x, q8, s, b, c8, epilogue=tg.EPI_BIAS)
+    torch.cuda.synchronize()
+    assert torch.equal(c4.contiguous().view(torch.uint8), c8.view(torch.uint8))
+
+
 def test_w4_strided_and_unaligned():
     """X with row stride K + 3 starting one element into its buffer, packed
     Q with row stride N + 4 bytes starting 4 bytes in, C at an odd element
