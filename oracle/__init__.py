@@ -3,8 +3,9 @@
 Only the test suite, the package smoke check and the benchmark's CPU-baseline
 leg may import this package.  The GPU library never calls it and shares no
 code with it: every function here is written from the definitions on the
-source pages and from the number formats' own specifications, in float64,
-with numpy as the only dependency.
+source pages and from the number formats' own specifications, in float64.
+The contraction is the plain triple loop in C (contract.c, built with gcc by
+native.py); decoding, dequantisation, epilogue and log-softmax are numpy.
 
 Sources (cited by short name throughout):
   * "GEMM compute-cost page" -- kwkr.cn/news/191298, the article on why GEMM
@@ -18,8 +19,10 @@ Sources (cited by short name throughout):
 
 Modules:
   formats  -- bf16 and OCP e4m3fn decode / round-to-nearest-even encode.
-  gemm     -- the plain fp64 contraction, epilogue, FP8 dequantisation,
-              error metric and FLOP count.
+  gemm     -- the fp64 GEMM (decode, contraction, epilogue), FP8 / int8 /
+              int4 dequantisation, the log-softmax head and its error
+              bound, error metric and FLOP count.
+  native   -- builds and calls contract.c, the k-ascending triple loop.
   quant    -- per-group FP8 quantiser (amax / 448 scales).
 
 Parity status: every function is pinned by a CPU test against something other

@@ -5,8 +5,10 @@ What is computed (all in float64 on exactly decoded inputs):
 * Contraction.  ``y[i, j] = sum_k a[i, k] * b[k, j]`` for row-major
   ``a[M, K]`` and ``b[K, N]``: the naive triple loop that the DeepGEMM page
   (section 3.2, 朴素版的性能基线) keeps as the golden reference, with the
-  element ``A[m*K + k] * B[k*N + n]`` indexing of that section.  numpy's
-  float64 matmul serves as the summation step; its rounding error (about
+  element ``A[m*K + k] * B[k*N + n]`` indexing of that section.  The loop is
+  plain C in float64 (``contract.c``, called through ``native.py``): every
+  output element adds its K products one at a time, k ascending, each
+  product and each addition rounded once.  Its rounding error (at most about
   ``K * 2**-53`` relative to ``sum_k |a||b|``) is eight orders of magnitude
   below the tolerances it is used against.
 * Bias.  A linear layer is a GEMM followed by a bias add (GEMM compute-cost
@@ -36,11 +38,18 @@ What is computed (all in float64 on exactly decoded inputs):
   that follows it.  Per row: ``out[i, n] = y[i, n] - lse_i`` with
   ``y = x w + b`` and ``lse_i = m_i + log(sum_n exp(y[i, n] - m_i))``,
   ``m_i = max_n y[i, n]`` (the textbook log-sum-exp, shifted by the maximum
-  so no exponential overflows).  Error metric: a logit error ``d_n`` moves
-  ``lse`` by at most ``max_n |d_n|``, so an output's error is at most twice
-  the largest logit error of its row; with logit errors bounded by
-  ``tol * D`` (``D`` as below) and output rounding relative to the output,
-  the denominator is ``2 * max_n D[i, n] + |out[i, n]|``.
+  so no exponential overflows).  Error bound (the page gives none; this is
+  derived from the arithmetic): logits computed with fp32 accumulation
+  carry errors ``|e_n| <= tau * D[i, n]`` (``tau`` the fp32 GEMM tolerance,
+  ``D`` as below).  Since ``lse`` is a softmax-weighted mean of its
+  arguments to first order, it moves by at most ``max_n |e_n|``, so each
+  output moves by at most ``2 * tau * max_n D[i, n]`` (reached when the
+  dominant logit errs one way and another logit the other way).  The
+  normaliser itself is evaluated in fp32 (exponentials, their sum, the
+  logarithm), which adds ``tau * |lse_i|``.  Rounding the output to its
+  format adds half an ulp: at most ``2**-8 * |out|`` for bfloat16 (8
+  significant bits) and ``2**-23 * |out|`` for float32 (one ulp, covering
+  the final subtraction as well).  The bound is the sum of the three.
 * FLOP count.  A multiply-add counts as two operations, so an ``[M,K]x[K,N]``
   product costs ``2*M*N*K`` (GEMM compute-cost page, section 3.1); the bias is
   not counted.
@@ -54,6 +63,7 @@ import math
 
 import numpy as np
 
+from . import native
 from .formats import bf16_decode, e4m3_decode
 
 EPI_NONE = 0
@@ -85,12 +95,7 @@ def gemm_f64(a, b, bias=None, epilogue=EPI_NONE):
     if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"shape mismatch: a{a.shape} b{b.shape}")
     M, N = a.shape[0], b.shape[1]
-    if a.shape[1] == 0:
-        y = np.zeros((M, N))
-        d = np.zeros((M, N))
-    else:
-        y = a @ b
-        d = np.abs(a) @ np.abs(b)
+    y, d = native.contract(a, b)
     if epilogue in (EPI_BIAS, EPI_BIAS_GELU_TANH):
         if bias is None:
             raise ValueError("bias epilogue without bias")
@@ -186,40 +191,64 @@ def gemm_bf16_w4_bits(x_bits, packed, s, bias_bits=None, epilogue=EPI_NONE):
 
 def log_softmax_rows(y):
     """Row-wise log-softmax of float64 logits: y - (m + log sum exp(y - m))."""
+    out, _ = log_softmax_with_lse(y)
+    return out
+
+
+def log_softmax_with_lse(y):
+    """(y - lse, lse) per row, lse = m + log sum_n exp(y[:, n] - m), m = row max."""
     y = np.asarray(y, dtype=np.float64)
     m = np.max(y, axis=1, keepdims=True)
-    return y - (m + np.log(np.sum(np.exp(y - m), axis=1, keepdims=True)))
+    lse = m + np.log(np.sum(np.exp(y - m), axis=1, keepdims=True))
+    return y - lse, lse
+
+
+# Error bound of the log-softmax heads (module docstring): logit term
+# 2 * tau * max_n D, normaliser term tau * |lse|, output rounding r * |out|.
+LSM_TAU = 1e-5
+LSM_OUT_ROUNDING = {"bf16": 2.0 ** -8, "f32": 2.0 ** -23}
+
+
+def logsoftmax_bound(out, dmax, lse, out_format):
+    """Absolute error allowed on each log-softmax output.
+
+    out: float64 [M, N] reference outputs; dmax: [M, 1] the row maxima of
+    the logit denominators D; lse: [M, 1] the row normalisers; out_format
+    "bf16" or "f32".  Compare with ``compare(c, out, bound, 1.0)``.
+    """
+    r = LSM_OUT_ROUNDING[out_format]
+    return 2.0 * LSM_TAU * np.asarray(dmax) + LSM_TAU * np.abs(np.asarray(lse)) + r * np.abs(out)
+
+
+def _logsoftmax_reference(y, d):
+    out, lse = log_softmax_with_lse(y)
+    return out, np.max(d, axis=1, keepdims=True), lse
 
 
 def gemm_bf16_logsoftmax_bits(x_bits, w_bits, bias_bits=None):
-    """Oracle for the fused LM head: (out, denominators) with out the
-    row-wise log-softmax of ``x w + b`` and denominators
-    ``2 * max_n D[i, n] + |out[i, n]|``."""
+    """Oracle for the fused LM head: (out, dmax, lse) with out the row-wise
+    log-softmax of ``x w + b`` in float64, dmax the row maxima of the logit
+    denominators ``D = sum_k |x||w| + |b|`` and lse the row normalisers
+    (inputs of logsoftmax_bound)."""
     bias = None if bias_bits is None else bf16_decode(bias_bits)
     y, d = gemm_f64(bf16_decode(x_bits), bf16_decode(w_bits), bias, EPI_BIAS if bias is not None
                     else EPI_NONE)
-    out = log_softmax_rows(y)
-    return out, 2.0 * np.max(d, axis=1, keepdims=True) + np.abs(out)
-
-
-def _logsoftmax_with_denominators(y, d):
-    out = log_softmax_rows(y)
-    return out, 2.0 * np.max(d, axis=1, keepdims=True) + np.abs(out)
+    return _logsoftmax_reference(y, d)
 
 
 def gemm_bf16_w8_logsoftmax_bits(x_bits, q, s, bias_bits=None):
     """Oracle for the int8-weight LM head with bias and log-softmax (the GEMM
     compute-cost page, section 7.2, plans A and B together): the row-wise
-    log-softmax of ``x (q s) + b`` and the denominators of
+    log-softmax of ``x (q s) + b``, with dmax and lse as
     gemm_bf16_logsoftmax_bits."""
     y, d = gemm_bf16_w8_bits(x_bits, q, s, bias_bits, EPI_BIAS if bias_bits is not None else EPI_NONE)
-    return _logsoftmax_with_denominators(y, d)
+    return _logsoftmax_reference(y, d)
 
 
 def gemm_bf16_w4_logsoftmax_bits(x_bits, packed, s, bias_bits=None):
     """As gemm_bf16_w8_logsoftmax_bits for packed int4 codes."""
     y, d = gemm_bf16_w4_bits(x_bits, packed, s, bias_bits, EPI_BIAS if bias_bits is not None else EPI_NONE)
-    return _logsoftmax_with_denominators(y, d)
+    return _logsoftmax_reference(y, d)
 
 
 def gemm_fp8_blockscaled_bits(qa_bits, sa, qb_bits, sb):

@@ -8,8 +8,9 @@ pre-filled with a NaN canary and surrounded by guard rows / columns that must
 come back untouched.  The self-check list of the DeepGEMM page (section 4.4:
 small sizes element by element, non-aligned sizes such as 67 x 50, random
 and all-ones inputs) and its edge-tile advice (section 4.1) shape the cases.
-At the full workload sizes the oracle evaluates sampled rows (every M tile,
-both edges of each) or sampled columns for the thin-M shapes.
+At the full workload sizes the oracle evaluates sampled rows (both edges of
+every M tile and one random row of every 32-row block) or sampled columns for
+the thin-M shapes.
 """
 
 import numpy as np
@@ -263,10 +264,16 @@ def test_fp8_integer_codes_exact():
 
 # ------------------------------------------------------- full workloads ----
 
-def _tile_rows(M, tile=256, per_tile=3):
+def _tile_rows(M, tile=256, block=32, seed=93):
+    """Both edge rows of every output tile, plus one seeded random row in
+    every 32-row block (the row extent of one MFMA accumulator block), so
+    every block of every wave tile is sampled."""
+    rng = np.random.default_rng(seed)
     rows = set()
     for t0 in range(0, M, tile):
-        rows.update({t0, min(M - 1, t0 + tile - 1), min(M - 1, t0 + 37)})
+        rows.update({t0, min(M - 1, t0 + tile - 1)})
+    for b0 in range(0, M, block):
+        rows.add(int(rng.integers(b0, min(M, b0 + block))))
     return sorted(rows)
 
 

@@ -17,7 +17,7 @@ import torch
 import torch.nn.functional as F
 
 import workloads as wl
-from oracle import formats, gemm, quant
+from oracle import formats, gemm, native, quant
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
 
@@ -205,6 +205,63 @@ def test_rank_one_and_all_ones_closed_forms():
     ones_b = formats.bf16_encode_rne(np.ones((K, N), np.float32))
     y1, _ = gemm.gemm_bf16_bits(ones_a, ones_b)
     assert np.all(y1 == K)
+
+
+@pytest.mark.parametrize("K", [4096, 16384])
+def test_rank_one_and_all_ones_at_production_k(K):
+    """The FFN and LM-head depths (K = 4096, 16384): integer rank-1 operands
+    give C = K * u_i * v_j exactly and all-ones operands give C = K (every
+    partial sum is an integer below 2**53, so the plain loop is exact)."""
+    M, N = 3, 40
+    rng = np.random.default_rng(K)
+    u = rng.integers(-8, 9, M).astype(np.float32)
+    v = rng.integers(-8, 9, N).astype(np.float32)
+    a = formats.bf16_encode_rne(np.repeat(u[:, None], K, axis=1))
+    b = formats.bf16_encode_rne(np.repeat(v[None, :], K, axis=0))
+    y, d = gemm.gemm_bf16_bits(a, b)
+    assert np.array_equal(y, K * np.outer(u, v).astype(np.float64))
+    assert np.array_equal(d, K * np.abs(np.outer(u, v)).astype(np.float64))
+    ones_a = formats.bf16_encode_rne(np.ones((M, K), np.float32))
+    ones_b = formats.bf16_encode_rne(np.ones((K, N), np.float32))
+    y1, d1 = gemm.gemm_bf16_bits(ones_a, ones_b)
+    assert np.all(y1 == K) and np.all(d1 == K)
+
+
+def test_contraction_is_the_plain_loop_k_ascending_without_fma():
+    """The golden reference is the naive loop (DeepGEMM page, section 3.2):
+    each product rounded once, then added to the running sum, k ascending.
+    Two hand-worked cases separate it from other orders and from a fused
+    multiply-add:
+      * a = [1, 1, 1], b = [2**53, 1, -2**53]: k ascending gives
+        (2**53 + 1 -> 2**53, ties to even) - 2**53 = 0, while k descending
+        or an exact sum gives 1;
+      * a = [1, 1 + 2**-30], b = [-1, 1 + 2**-30]: the product
+        1 + 2**-29 + 2**-60 rounds to 1 + 2**-29 before the add, giving
+        2**-29; a fused multiply-add would keep the 2**-60."""
+    a = np.array([[1.0, 1.0, 1.0]])
+    b = np.array([[2.0 ** 53], [1.0], [-(2.0 ** 53)]])
+    y, d = gemm.gemm_f64(a, b)
+    assert y[0, 0] == 0.0 and d[0, 0] == 2.0 ** 54
+    y_rev, _ = gemm.gemm_f64(a[:, ::-1], b[::-1])
+    assert y_rev[0, 0] == 1.0
+    e = 1.0 + 2.0 ** -30
+    y2, _ = gemm.gemm_f64(np.array([[1.0, e]]), np.array([[-1.0], [e]]))
+    assert y2[0, 0] == 2.0 ** -29
+    assert float(Fraction(-1) + Fraction(e) * Fraction(e)) != 2.0 ** -29  # exact value differs
+
+
+def test_contraction_does_not_depend_on_the_thread_count():
+    rng = np.random.default_rng(8)
+    a = rng.standard_normal((37, 300))
+    b = rng.standard_normal((300, 51))
+    y1, d1 = native.contract(a, b, threads=1)
+    y7, d7 = native.contract(a, b, threads=7)
+    assert np.array_equal(y1, y7) and np.array_equal(d1, d7)
+    # strided views (every other row and column of a larger matrix)
+    big = rng.standard_normal((80, 700))
+    ys, ds = native.contract(big[::2, :300], b, threads=3)
+    yc, dc = native.contract(np.ascontiguousarray(big[::2, :300]), b, threads=3)
+    assert np.array_equal(ys, yc) and np.array_equal(ds, dc)
 
 
 def test_empty_k_gives_bias_only():
@@ -550,8 +607,9 @@ def test_log_softmax_uniform_logits_is_minus_log_n():
     rng = np.random.default_rng(51)
     x = formats.bf16_encode_rne(rng.standard_normal((3, 40)).astype(np.float32))
     w = formats.bf16_encode_rne(np.zeros((40, 1000), np.float32))
-    out, _ = gemm.gemm_bf16_logsoftmax_bits(x, w)
+    out, _, lse = gemm.gemm_bf16_logsoftmax_bits(x, w)
     assert np.allclose(out, -math.log(1000.0), rtol=0, atol=1e-15)
+    assert np.allclose(lse, math.log(1000.0), rtol=0, atol=1e-15)
 
 
 def test_log_softmax_two_columns_closed_form():
@@ -587,20 +645,24 @@ def test_logsoftmax_oracle_applies_bias_before_normalising():
     M, K, N = 4, 64, 96
     xb = formats.bf16_encode_rne(rng.standard_normal((M, K)).astype(np.float32))
     wb = formats.bf16_encode_rne((rng.standard_normal((K, N)) * 0.05).astype(np.float32))
-    out0, d0 = gemm.gemm_bf16_logsoftmax_bits(xb, wb)
+    out0, dmax0, lse0 = gemm.gemm_bf16_logsoftmax_bits(xb, wb)
     const = formats.bf16_encode_rne(np.full(N, 2.5, np.float32))
-    out1, _ = gemm.gemm_bf16_logsoftmax_bits(xb, wb, const)
+    out1, _, lse1 = gemm.gemm_bf16_logsoftmax_bits(xb, wb, const)
     assert np.allclose(out1, out0, rtol=0, atol=1e-12)
     one = np.zeros(N, np.float32)
     one[7] = 1.0
-    out2, _ = gemm.gemm_bf16_logsoftmax_bits(xb, wb, formats.bf16_encode_rne(one))
+    out2, _, _ = gemm.gemm_bf16_logsoftmax_bits(xb, wb, formats.bf16_encode_rne(one))
     y = formats.bf16_decode(xb) @ formats.bf16_decode(wb)
     y[:, 7] += 1.0
     ref = y - np.log(np.sum(np.exp(y), axis=1, keepdims=True))
     assert np.allclose(out2, ref, rtol=0, atol=1e-12)
-    # Denominators: twice the row's largest sum_k |x||w| plus |out|.
-    dk = np.abs(formats.bf16_decode(xb)) @ np.abs(formats.bf16_decode(wb))
-    assert np.allclose(d0, 2 * dk.max(axis=1, keepdims=True) + np.abs(out0), rtol=1e-15, atol=0)
+    # A constant bias of 2.5 moves every logit, so the normaliser, by 2.5.
+    assert np.allclose(lse1, lse0 + 2.5, rtol=0, atol=1e-12)
+    # The row maxima of the logit denominators sum_k |x||w|, by explicit loops.
+    xd, wd = formats.bf16_decode(xb), formats.bf16_decode(wb)
+    for i in range(M):
+        dk = [math.fsum(abs(float(xd[i, k]) * float(wd[k, n])) for k in range(K)) for n in range(N)]
+        assert abs(dmax0[i, 0] - max(dk)) <= 1e-13 * max(dk)
 
 
 # ------------------------------------------------------- K-contiguous weights ----
@@ -638,11 +700,11 @@ def test_w8_logsoftmax_equals_bf16_head_on_bf16_exact_weights():
     wb = formats.bf16_encode_rne(gemm.dequant_w8(q, s).astype(np.float32))
     bb = formats.bf16_encode_rne((0.3 * rng.standard_normal(N)).astype(np.float32))
     for bias in (None, bb):
-        o8, d8 = gemm.gemm_bf16_w8_logsoftmax_bits(xb, q, s, bias)
-        ob, db = gemm.gemm_bf16_logsoftmax_bits(xb, wb, bias)
-        assert np.array_equal(o8, ob) and np.array_equal(d8, db)
-        o4, d4 = gemm.gemm_bf16_w4_logsoftmax_bits(xb, quant.pack_int4(q), s, bias)
-        assert np.array_equal(o4, o8) and np.array_equal(d4, d8)
+        o8, d8, l8 = gemm.gemm_bf16_w8_logsoftmax_bits(xb, q, s, bias)
+        ob, db, lb = gemm.gemm_bf16_logsoftmax_bits(xb, wb, bias)
+        assert np.array_equal(o8, ob) and np.array_equal(d8, db) and np.array_equal(l8, lb)
+        o4, d4, l4 = gemm.gemm_bf16_w4_logsoftmax_bits(xb, quant.pack_int4(q), s, bias)
+        assert np.array_equal(o4, o8) and np.array_equal(d4, d8) and np.array_equal(l4, l8)
         assert np.allclose(np.exp(o8).sum(axis=1), 1.0, rtol=1e-12)
 
 
@@ -655,9 +717,89 @@ def test_w8_logsoftmax_brute_force_small():
     bias = formats.bf16_encode_rne(np.array([0.125, -1.0, 0.0], dtype=np.float32))
     x = formats.bf16_decode(xb)
     b = formats.bf16_decode(bias)
-    out, _ = gemm.gemm_bf16_w8_logsoftmax_bits(xb, q, s, bias)
+    out, _, _ = gemm.gemm_bf16_w8_logsoftmax_bits(xb, q, s, bias)
     for i in range(2):
         y = [sum(x[i, k] * q[k, n] * float(s[0, n]) for k in range(2)) + b[n] for n in range(3)]
         lse = math.log(sum(math.exp(v) for v in y))
         for n in range(3):
             assert abs(out[i, n] - (y[n] - lse)) <= 1e-14 * max(1.0, abs(y[n] - lse))
+
+
+# ------------------------------------------- log-softmax error bound ----
+
+def test_logsoftmax_logit_term_bounded_by_twice_the_largest_logit_error_and_tight():
+    """Perturbing every logit of a row by at most delta moves each output by
+    at most 2 * delta, and the factor 2 is reached: with one dominant logit
+    raised by delta (the normaliser follows it almost fully) and another
+    lowered by delta, that other output moves by 2 * delta (1 - p) with p the
+    dominant probability, here 1 - 1e-13."""
+    rng = np.random.default_rng(81)
+    delta = 1e-3
+    for _ in range(20):
+        y = rng.standard_normal((3, 500)) * 4.0
+        e = rng.uniform(-delta, delta, y.shape)
+        moved = np.abs(gemm.log_softmax_rows(y + e) - gemm.log_softmax_rows(y))
+        assert moved.max() <= 2 * delta * (1 + 1e-9)
+    y = np.zeros((1, 50))
+    y[0, 0] = 35.0  # p0 = 1 / (1 + 49 e^-35) ~ 1 - 3e-14
+    e = np.zeros_like(y)
+    e[0, 0], e[0, 1] = delta, -delta
+    moved = np.abs(gemm.log_softmax_rows(y + e) - gemm.log_softmax_rows(y))
+    assert abs(moved[0, 1] - 2 * delta) <= 1e-12
+    # One logit alone moved by delta moves the outputs by at most delta.
+    e1 = np.zeros_like(y)
+    e1[0, 7] = delta
+    assert np.abs(gemm.log_softmax_rows(y + e1) - gemm.log_softmax_rows(y)).max() <= delta * (1 + 1e-12)
+
+
+def test_logsoftmax_rounding_term_is_half_an_ulp_and_tight():
+    """Rounding to nearest moves a value by at most half an ulp: 2**-8 of
+    its magnitude for bfloat16 (8 significant bits), 2**-24 for float32 (the
+    bound uses 2**-23, one ulp); the bfloat16 ratio comes within 1 % of
+    2**-8 just below a power of two's first tie."""
+    rng = np.random.default_rng(82)
+    x = np.concatenate([rng.standard_normal(200000) * 10.0,
+                        1.0 + 2.0 ** -8 - rng.uniform(0, 2.0 ** -16, 1000)])
+    xb = formats.bf16_decode(formats.bf16_encode_rne(x.astype(np.float32)))
+    x32 = x.astype(np.float32).astype(np.float64)
+    rb = np.abs(xb - x32) / np.abs(x32)
+    assert rb.max() <= gemm.LSM_OUT_ROUNDING["bf16"] and rb.max() > 0.99 * 2.0 ** -8
+    r32 = np.abs(x32 - x) / np.abs(x)
+    assert r32.max() <= 2.0 ** -24 < gemm.LSM_OUT_ROUNDING["f32"]
+
+
+def _lm_head_case(M=4, K=4096, N=2048, seed=83):
+    """LM-head-like operands: x N(0,1), w N(0,0.02), bias N(0,0.02), bf16."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    w = (torch.randn(K, N, generator=g) * 0.02).to(torch.bfloat16)
+    b = (torch.randn(N, generator=g) * 0.02).to(torch.bfloat16)
+    return x, w, b
+
+
+def test_logsoftmax_bound_admits_fp32_arithmetic_and_rejects_planted_mistakes():
+    """At the LM head's depth (K = 4096, max D ~ 50) the bound is about
+    1.2e-3 nat for fp32 output and 2**-8 |out| more for bf16.  A plain fp32
+    implementation (fp32 GEMM, fp32 log-softmax) and its bf16 rounding pass;
+    a normaliser off by 0.01 nat (fp32) or 0.1 nat (bf16), a dropped bias, or
+    a normaliser that misses half of the exp-sum (ln 2) fail."""
+    x, w, b = _lm_head_case()
+    out, dmax, lse = gemm.gemm_bf16_logsoftmax_bits(wl.bits_u16(x), wl.bits_u16(w), wl.bits_u16(b))
+    assert 30.0 < float(dmax.min()) and float(dmax.max()) < 80.0
+    bf32 = gemm.logsoftmax_bound(out, dmax, lse, "f32")
+    bb16 = gemm.logsoftmax_bound(out, dmax, lse, "bf16")
+    assert float(bf32.max()) < 2e-3
+
+    def ok(c, bound):
+        return gemm.compare(c, out, bound, 1.0)["ok"]
+
+    logits32 = x.float() @ w.float() + b.float()
+    c32 = torch.log_softmax(logits32, dim=1).double().numpy()
+    assert ok(c32, bf32)
+    c16 = torch.log_softmax(logits32, dim=1).to(torch.bfloat16).double().numpy()
+    assert ok(c16, bb16)
+    assert not ok(out - 0.01, bf32)
+    assert not ok(out - 0.1, bb16)
+    no_bias = torch.log_softmax(x.double() @ w.double(), dim=1).numpy()
+    assert not ok(no_bias, bf32)
+    assert not ok(out + math.log(2.0), bf32) and not ok(out + math.log(2.0), bb16)
