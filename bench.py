@@ -11,22 +11,31 @@ compute-cost page, section 3.1; rates and utilisation are the "three numbers"
 of the DeepGEMM page, section 3.4).
 
 Also reported in the same line:
-  roofline      the dominant kernel's average launch time from HIP events on
-                the launch stream, as achieved TFLOP/s (or GB/s) against the
-                MI355X dense peak, plus HBM traffic from the committed
-                rocprofv3 counter summary when it matches the current source;
-  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded row sample
-                of the same workload (rank 0, one GPU only);
+  roofline      the dominant kernel's launch time from one pair of HIP events
+                per timed step on the launch stream (mean, median, min), as
+                achieved TFLOP/s (or GB/s, from the mean) against the MI355X
+                dense peak, plus HBM traffic from the committed rocprofv3
+                counter summary when it matches the current source;
+  clocks        shader and memory clocks read from the driver's sysfs before,
+                during (while the queued steps run) and after the timed region;
+  cpu_baseline  the fp64 CPU oracle (the plain triple loop in C) timed on this
+                host on a bounded row sample of the same workload, with its
+                thread count, the host's CPU count and model, and the oracle's
+                single-thread time on the 64^3 workload (rank 0, one GPU only);
   secondary     the other workloads (FFN pair, thin-M LM head at M = 1, 8,
-                32, 64, FP8 block-scaled and its ragged variant), each timed
-                the same way with its own roofline figure.
+                32, 64, FP8 block-scaled and its ragged variant, ...), each
+                timed the same way with its own roofline figure;
+  probes        reference rates of this machine (MFMA-only loops on random
+                register operands, a streaming read), informational only.
 """
 
 import argparse
+import glob
 import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -52,8 +61,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--secondary-steps", type=int, default=50)
-    ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the attainable-ceiling probes (MFMA loops, HBM stream read)")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the reference-rate probes (MFMA loops, HBM stream read)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (the reference kernel for "
                          "scaling HBM byte counters) and exit")
@@ -186,7 +195,7 @@ class Case:
             c = torch.empty(w.M, w.N, dtype=out, device=dev)
             self.launch = lambda: tg.gemm_bf16(a, b, bias, c, epilogue=w.epilogue)
             self.kernel = tg.gemm_bf16_kernel_name(w.M, w.N, w.K, w.epilogue,
-                                                   tg.OUT_F32 if w.out_f32 else tg.OUT_BF16)
+                                                   tg.OUT_F32 if w.out_f32 else tg.OUT_BF16)  # gemm_bf16: no workspace
             self.family = "thin" if "thin" in self.kernel else "tiled"
             out_bytes = 4 if w.out_f32 else 2
             self.bytes = 2 * (w.M * w.K + w.K * w.N) + out_bytes * w.M * w.N + (
@@ -251,7 +260,7 @@ class Case:
             fn = tg.gemm_bf16_w8_logsoftmax if bits == 8 else tg.gemm_bf16_w4_logsoftmax
             self.launch = lambda: fn(x, q, s, b, c, workspace=ws)
             self.bytes += 2 * N  # the bias
-            self.kernel = self.kernel.replace("_thin_", "_thin_lsm_")
+            self.kernel = f"tgemm_wq_thin_lsm<{bits}, {(M + 15) // 16}>+tgemm_lsm_normalize"
             self.family = "wq_lsm"
         else:
             fn = tg.gemm_bf16_w8 if bits == 8 else tg.gemm_bf16_w4
@@ -351,7 +360,7 @@ class Case:
         # X, W, bias and the log-probabilities, each once (the logits never
         # leave the chip).
         self.bytes = 2 * M * K + 2 * K * N + 2 * N + 2 * M * N
-        self.kernel = "tgemm_bf16_thin_lsm"
+        self.kernel = f"tgemm_bf16_thin_lsm<{(M + 15) // 16}>+tgemm_lsm_normalize"
         self.family = "lsm"
         self.bound, self.peak = "hbm", PEAK_HBM_GBS
         self.dtype = "bf16"
@@ -384,64 +393,151 @@ class Case:
         self.dtype = "bf16->fp8_e4m3"
         self.inputs_for_oracle = None
 
-    def time(self, steps, warmup):
-        """(ms per step from the bracketing synchronisations, mean kernel ms).
+    def time(self, steps, warmup, clocks=False):
+        """Timing of `steps` back-to-back calls after `warmup` untimed ones.
 
-        The kernel mean comes from one pair of HIP events on the launch
-        stream around the `steps` back-to-back launches (the timed region).
+        Returns a dict: ms_per_step from the wall clock between the two
+        synchronisations that bracket the timed region, and the per-call
+        kernel times from one pair of HIP events per call recorded on the
+        launch stream (torch's current stream, which the binding launches
+        on): mean, median, min.  With clocks, the driver's clock readings
+        before, during (right after the calls are queued, while they run)
+        and after the region.
         """
         import torch
 
         for _ in range(warmup):
             self.launch()
         torch.cuda.synchronize()
-        region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        clk = {"before": read_clocks()} if clocks else None
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        region[0].record()
-        for _ in range(steps):
+        for e0, e1 in ev:
+            e0.record()
             self.launch()
-        region[1].record()
+            e1.record()
+        if clocks:
+            clk["during"] = read_clocks()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        return (t1 - t0) * 1e3 / steps, region[0].elapsed_time(region[1]) / steps
+        if clocks:
+            clk["after"] = read_clocks()
+        per = [e0.elapsed_time(e1) for e0, e1 in ev]
+        return {"ms_per_step": (t1 - t0) * 1e3 / steps, "kernel_ms_mean": statistics.fmean(per),
+                "kernel_ms_median": statistics.median(per), "kernel_ms_min": min(per), "clocks": clk}
 
-    def roofline(self, kernel_ms):
-        if self.bound == "hbm":
-            achieved = self.bytes / (kernel_ms * 1e-3) / 1e9
-            unit = "GB/s"
-        else:
-            achieved = self.flops / (kernel_ms * 1e-3) / 1e12
-            unit = "TFLOP/s"
+    def roofline(self, t):
+        """Roofline entry from a time() result: achieved from the mean kernel time."""
+        def rate(ms):
+            if self.bound == "hbm":
+                return self.bytes / (ms * 1e-3) / 1e9
+            return self.flops / (ms * 1e-3) / 1e12
+
+        achieved = rate(t["kernel_ms_mean"])
         traffic = committed_traffic(self.name, self.family)
-        return {"bound": self.bound, "achieved": round(achieved, 2), "peak": self.peak, "unit": unit,
+        return {"bound": self.bound, "achieved": round(achieved, 2), "peak": self.peak,
+                "unit": "GB/s" if self.bound == "hbm" else "TFLOP/s",
                 "frac": round(achieved / self.peak, 4), "traffic": traffic,
-                "kernel": self.kernel, "kernel_ms_mean": round(kernel_ms, 5),
+                "kernel": self.kernel, "kernel_ms_mean": round(t["kernel_ms_mean"], 5),
+                "kernel_ms_median": round(t["kernel_ms_median"], 5),
+                "kernel_ms_min": round(t["kernel_ms_min"], 5),
+                "achieved_at_median": round(rate(t["kernel_ms_median"]), 2),
                 "algorithmic_bytes": self.bytes, "flop": self.flops}
 
 
-def cpu_baseline(case, budget_s=12.0):
+def read_clocks():
+    """Current shader and memory clocks (MHz) of the visible GPU from the
+    amdgpu driver's sysfs files (the level marked '*' in pp_dpm_sclk /
+    pp_dpm_mclk, and the hwmon sclk reading when present), or None.  With
+    several cards listed, the one whose PCI address matches torch's device 0
+    is used when torch reports it, else the first readable one."""
+    cards = sorted(glob.glob("/sys/class/drm/card[0-9]*/device"))
+    want = None
+    try:
+        import torch
+
+        props = torch.cuda.get_device_properties(0)
+        bus = getattr(props, "pci_bus_id", None)
+        dom = getattr(props, "pci_domain_id", 0) or 0
+        dev_ = getattr(props, "pci_device_id", None)
+        if bus is not None and dev_ is not None:
+            want = f"{dom:04x}:{bus:02x}:{dev_:02x}."
+    except Exception:  # clocks are informational
+        want = None
+    for card in cards:
+        real = os.path.realpath(card)
+        if want is not None and want not in real:
+            continue
+        out = {}
+        for key, fname in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+            try:
+                with open(os.path.join(card, fname)) as fh:
+                    for line in fh:
+                        if line.rstrip().endswith("*"):
+                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                            if m:
+                                out[key] = int(m.group(1))
+            except OSError:
+                pass
+        for f in glob.glob(os.path.join(card, "hwmon", "hwmon*", "freq1_input")):
+            try:
+                with open(f) as fh:
+                    out["sclk_hwmon_mhz"] = round(int(fh.read().strip()) / 1e6)
+            except (OSError, ValueError):
+                pass
+        if out:
+            out["card"] = os.path.basename(os.path.dirname(card))
+            return out
+    return None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(case, dev, budget_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the headline workload.
 
-    The sample is the whole GEMM when one oracle call fits the budget (then it
-    is repeated until about budget_s seconds have been spent), else the first
-    rows that fit.  Reported value: oracle FLOP/s in TFLOP/s.
+    The oracle decodes the bf16 inputs and runs the plain k-ascending triple
+    loop in C (oracle/contract.c) on its worker threads.  The sample is the
+    first rows of A that take about a quarter of budget_s (the whole GEMM if
+    it fits), repeated until about budget_s seconds have been spent.  Also
+    timed: one call on the 64 x 64 x 64 workload with one thread.  Reported
+    value: oracle FLOP/s in TFLOP/s.
     """
-    import threadpoolctl
-
     import workloads as wl
     from oracle import gemm as og
+    from oracle import native
+
+    threads = native.default_threads()
+    tiny = wl.WORKLOADS["tiny"]
+    ta, tb, _ = wl.bf16_inputs(tiny, device=dev)
+    ta_bits, tb_bits = wl.bits_u16(ta), wl.bits_u16(tb)
+    og.gemm_bf16_bits(ta_bits, tb_bits, threads=1)  # builds / loads the library
+    t0 = time.perf_counter()
+    reps_tiny = 20
+    for _ in range(reps_tiny):
+        og.gemm_bf16_bits(ta_bits, tb_bits, threads=1)
+    tiny_ms = (time.perf_counter() - t0) * 1e3 / reps_tiny
 
     a, b = case.inputs_for_oracle
     a_bits = wl.bits_u16(a)
     b_bits = wl.bits_u16(b)
-    rows = min(case.M, 64)
+    rows = min(case.M, 16)
     t0 = time.perf_counter()
     og.gemm_bf16_bits(a_bits[:rows], b_bits)
     probe = time.perf_counter() - t0
-    # cost ~ fixed (decode of B) + per row; grow the sample geometrically
     while rows < case.M and probe < budget_s / 4:
-        rows = min(case.M, rows * 4)
+        rows = min(case.M, rows * 2)
         t0 = time.perf_counter()
         og.gemm_bf16_bits(a_bits[:rows], b_bits)
         probe = time.perf_counter() - t0
@@ -450,20 +546,27 @@ def cpu_baseline(case, budget_s=12.0):
     for _ in range(reps):
         og.gemm_bf16_bits(a_bits[:rows], b_bits)
     dt = time.perf_counter() - t0
-    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
-                   if i.get("user_api") == "blas"), default=1)
     flops = 2 * rows * case.N * case.K * reps
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3),
+            "host_cpus": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": cpu_model(),
+            "single_thread_tiny_ms": round(tiny_ms, 3),
             "sample": f"{reps} x rows 0..{rows - 1} of the {case.M}x{case.N}x{case.K} {case.name} "
-                      f"GEMM (fp64 decode + contraction + |a||b| denominators)"}
+                      f"GEMM on {threads} threads (bf16 decode + plain fp64 k-ascending loop with "
+                      f"|a||b| denominators); single_thread_tiny_ms: the 64x64x64 workload on one "
+                      f"thread"}
 
 
-def measure_ceilings(dev):
-    """Attainable ceilings on this machine (informational): the library's MFMA-only
-    loops on random register operands and its streaming read of a 1 GiB buffer
-    (beyond the 256 MB last-level cache), each the best of three timed calls
-    after one warm-up, HIP events on the launch stream."""
+def measure_probes(dev):
+    """Reference rates of this machine (informational, not bounds): the library's
+    MFMA-only loops on random register operands and its streaming read of a
+    1 GiB buffer (beyond the 256 MB last-level cache), each the best of three
+    timed calls after one warm-up, HIP events on the launch stream.  A tuned
+    kernel can exceed them (the LM head reads faster than the stream probe)."""
     import torch
 
     import tiled_gemm_04_amd as tg
@@ -484,29 +587,19 @@ def measure_ceilings(dev):
     out = {}
     iters = 2000
     buf = torch.empty(tg.gemm_probe_out_elems(tg.PROBE_MFMA_BF16), dtype=torch.float32, device=dev)
-    for key, probe in (("mfma_bf16_tflops", tg.PROBE_MFMA_BF16), ("mfma_fp8_tflops", tg.PROBE_MFMA_FP8)):
+    for key, probe in (("mfma_bf16_loop_tflops", tg.PROBE_MFMA_BF16),
+                       ("mfma_fp8_loop_tflops", tg.PROBE_MFMA_FP8)):
         sec = best(lambda: tg.gemm_probe_mfma(probe, iters, buf))
         out[key] = round(tg.gemm_probe_mfma_flop(probe, iters) / sec / 1e12, 1)
     src = torch.ones(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
     xo = torch.empty(tg.gemm_probe_out_elems(tg.PROBE_STREAM_READ), dtype=torch.int32, device=dev)
     sec = best(lambda: tg.gemm_probe_stream_read(src, xo))
-    out["hbm_read_gbs"] = round((1 << 30) / sec / 1e9, 1)
-    out["note"] = ("measured on this box: MFMA-only loops on random register operands and a 1 GiB "
-                   "streaming read; frac_of_ceiling entries are achieved / these, informational")
+    out["stream_read_gbs"] = round((1 << 30) / sec / 1e9, 1)
+    out["note"] = ("reference rates on this box (MFMA-only loops on random register operands, a "
+                   "1 GiB streaming read), informational; not bounds")
     del buf, src, xo
     torch.cuda.empty_cache()
     return out
-
-
-def ceiling_frac(roof, ceilings, fp8):
-    """achieved / the measured ceiling of the kernel's bound (roof: a roofline
-    dict, or a secondary entry with tflops / gbs)."""
-    if not ceilings:
-        return None
-    hbm = roof["bound"] == "hbm"
-    c = ceilings["hbm_read_gbs"] if hbm else ceilings["mfma_fp8_tflops" if fp8 else "mfma_bf16_tflops"]
-    achieved = roof["achieved"] if "achieved" in roof else roof["gbs" if hbm else "tflops"]
-    return round(achieved / c, 4) if c > 0 else None
 
 
 def main():
@@ -527,7 +620,8 @@ def main():
         return
 
     head = Case(args.workload, dev)
-    ms_step, kern_ms = head.time(args.steps, args.warmup)
+    t = head.time(args.steps, args.warmup, clocks=True)
+    ms_step = t["ms_per_step"]
     value = head.flops / (ms_step * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -544,10 +638,10 @@ def main():
         "data": "synthetic (seeded, shapes and distributions of the source pages' workloads)",
         "config": {"workload": head.describe(), "M": head.M, "N": head.N, "K": head.K,
                    "kernel": head.kernel},
-        "roofline": head.roofline(kern_ms),
+        "roofline": head.roofline(t),
+        "clocks": t["clocks"],
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
     }
-    head_fp8 = head.family == "fp8"
     del head.launch
     torch.cuda.empty_cache()
 
@@ -562,31 +656,26 @@ def main():
             if name == args.workload:
                 continue
             c = Case(name, dev)
-            ms, km = c.time(args.secondary_steps, 5)
-            r = c.roofline(km)
-            sec[name] = {"ms_per_call": round(ms, 5), "kernel_ms_mean": r["kernel_ms_mean"],
-                         "tflops": round(c.flops / (km * 1e-3) / 1e12, 2),
-                         "gbs": round(c.bytes / (km * 1e-3) / 1e9, 1),
+            tc = c.time(args.secondary_steps, 5)
+            r = c.roofline(tc)
+            sec[name] = {"ms_per_call": round(tc["ms_per_step"], 5),
+                         "kernel_ms_mean": r["kernel_ms_mean"], "kernel_ms_median": r["kernel_ms_median"],
+                         "kernel_ms_min": r["kernel_ms_min"],
+                         "tflops": round(c.flops / (tc["kernel_ms_mean"] * 1e-3) / 1e12, 2),
+                         "gbs": round(c.bytes / (tc["kernel_ms_mean"] * 1e-3) / 1e9, 1),
                          "bound": r["bound"], "frac": r["frac"], "kernel": c.kernel,
                          "traffic": r["traffic"]}
-            sec[name]["_fp8"] = c.family == "fp8"
             del c
             torch.cuda.empty_cache()
         line["secondary"] = sec
 
     # The probes run last, so their heat and power draw do not colour the
     # measurements above.
-    ceilings = None if args.no_ceilings else measure_ceilings(dev)
-    if ceilings:
-        line["ceilings"] = ceilings
-        line["roofline"]["frac_of_ceiling"] = ceiling_frac(line["roofline"], ceilings, head_fp8)
-    for v in line.get("secondary", {}).values():
-        fp8 = v.pop("_fp8")
-        if ceilings:
-            v["frac_of_ceiling"] = ceiling_frac(v, ceilings, fp8)
+    if not args.no_probes:
+        line["probes"] = measure_probes(dev)
 
     if not args.no_cpu_baseline and head.inputs_for_oracle is not None:
-        line["cpu_baseline"] = cpu_baseline(head)
+        line["cpu_baseline"] = cpu_baseline(head, dev)
     print(json.dumps(line), flush=True)
 
 

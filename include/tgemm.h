@@ -21,17 +21,20 @@
  *           indexing of the DeepGEMM page, section 3.2).  The inner stride is
  *           always 1.
  * Memory.   All pointers are device pointers owned by the caller.  The
- *           library never allocates, frees or keeps them.  Two paths use
- *           library-owned device scratch instead (split-K of the small-M
- *           bf16 kernel and of the integer-weight kernels for narrow
- *           weights; the split last round of gemm_fp8_blockscaled): one
- *           buffer per device, stream and purpose, allocated on first use,
- *           grown on demand and kept until the process ends, so the first
- *           such call on a stream allocates (do not make it under graph
- *           capture).  The scratch table is guarded by a lock; calls from
- *           several host threads are safe, and calls on one stream
- *           serialise on it.  C must not overlap A, B, bias or the scale
- *           arrays (not checked).
+ *           library never allocates or frees device memory and keeps no
+ *           buffers between calls.  Paths that need scratch (the K splits
+ *           of the small-M bf16 kernel, of the integer-weight heads and of
+ *           the FP8 tile scheduler; the log-softmax heads' statistics) take
+ *           it from the caller as a `workspace` pointer and its size in
+ *           bytes, with a *_workspace_size query for the size a call needs.
+ *           A NULL workspace runs the unsplit kernels (the log-softmax heads
+ *           require one).  A non-NULL workspace must be 16-byte aligned and
+ *           at least the queried size, else TGEMM_ERR_INVALID.  Calls that
+ *           may run at the same time must not share a workspace.  C must
+ *           not overlap A, B, bias, the scale arrays or the workspace (not
+ *           checked).
+ * Threads.  The library holds no mutable state, so calls from several host
+ *           threads are independent (each with its own workspace).
  * Streams.  `stream` is a hipStream_t passed as void*; NULL is the default
  *           stream.  Calls only enqueue work on it and return; they never
  *           synchronise.  Results are visible to later work on that stream.
@@ -54,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TGEMM_ABI_VERSION 1
+#define TGEMM_ABI_VERSION 2
 
 typedef enum {
     TGEMM_OK = 0,
@@ -110,8 +113,9 @@ typedef enum {
  *
  * Pointers must be non-NULL when the matrix they point to is non-empty.
  * Any alignment is accepted; 16-byte aligned base pointers with strides that
- * are multiples of 8 elements take the vectorised load path.
- * Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
+ * are multiples of 8 elements take the vectorised load path.  No workspace
+ * is used (gemm_bf16_ex with a workspace may split small-M problems along
+ * K).  Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
  */
 int gemm_bf16(const void* A, const void* B, const void* bias, void* C,
               int64_t M, int64_t N, int64_t K,
@@ -173,14 +177,39 @@ int gemm_bf16_nt(const void* A, const void* Bt, const void* bias, void* C,
 const char* gemm_bf16_nt_kernel_name(int64_t M, int64_t N, int64_t K);
 
 /*
- * gemm_bf16_ex -- gemm_bf16 with an explicit kernel family (tgemm_algo_t).
- * TGEMM_ALGO_THIN with M > 64 returns TGEMM_ERR_UNSUPPORTED.  Used by tests
- * that cross-check the two kernel families and by the benchmark.
+ * gemm_bf16_ex -- gemm_bf16 with an explicit kernel family (tgemm_algo_t)
+ * and an optional workspace for the small-M K split.
+ *
+ * For M <= 64 (the thin kernel) and a weight with few 512-column stripes
+ * (N <= 65536) the thin kernel leaves most compute units idle; with a
+ * workspace it cuts K into chunks run by separate workgroups (the DeepGEMM
+ * page, section 2.1: a grid too small for the machine leaves units unused),
+ * writes each chunk's fp32 partial sums to the workspace, and a second
+ * kernel adds them in chunk order, applies bias and epilogue and rounds
+ * once (deterministic; only the fp32 summation order differs from the
+ * unsplit call).
+ *
+ *   algo             a tgemm_algo_t value
+ *   workspace        NULL (never split) or device memory of at least
+ *                    gemm_bf16_workspace_size(M, N, K, algo) bytes, 16-byte
+ *                    aligned, owned by the caller; contents on entry do not
+ *                    matter and are clobbered
+ *   workspace_bytes  its size
+ *
+ * TGEMM_ALGO_THIN with M > 64 returns TGEMM_ERR_UNSUPPORTED; a non-NULL
+ * workspace that is unaligned or short returns TGEMM_ERR_INVALID.  Other
+ * arguments and errors as gemm_bf16.
  */
 int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C,
                  int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc,
-                 int epilogue, int out_dtype, int algo, void* stream);
+                 int epilogue, int out_dtype, int algo,
+                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes gemm_bf16_ex needs to split this problem (a multiple of
+ * 256; 0 when it would not split); -1 for negative or oversized sizes or an
+ * unknown algo.  No GPU call. */
+int64_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int algo);
 
 /*
  * gemm_fp8_blockscaled -- C[i,j] = sum_g sA[i,g] * sB[g, j/128] *
@@ -199,43 +228,58 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C,
  *   C    bf16 [M, N], packed row-major
  *
  * Dequantised value = decode(code) * scale.  Scales must be finite; NaN
- * codes (0x7F, 0xFF) propagate to the outputs they touch.  Grids that would
- * keep few compute units busy are split along K (automatic plan of
- * gemm_fp8_blockscaled_ex; the split uses library scratch, see Memory).
- * Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
+ * codes (0x7F, 0xFF) propagate to the outputs they touch.  Every tile runs
+ * whole (gemm_fp8_blockscaled_ex with a workspace splits small grids along
+ * K).  Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
  */
 int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
                          void* C, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * gemm_fp8_blockscaled_ex -- gemm_fp8_blockscaled with the tile scheduler's
- * K split chosen by the caller (tests and tuning).
+ * K split, in a caller workspace.
  *
  * The direct kernel gives each 256 x 256 output tile to one workgroup, one
  * workgroup per compute unit at a time.  When the tiles would leave compute
  * units idle (the DeepGEMM page, section 2.1: a grid too small for the
  * machine leaves SMs unused), each tile of the last round is split along K
  * into P ranges of whole scale groups, run by P workgroups; their fp32
- * partial tiles go to library scratch and the workgroup that finishes last
+ * partial tiles go to the workspace and the workgroup that finishes last
  * adds them in range order and writes C.
  *
- *   split_parts  0: automatic (only when the tiles would keep at most a
- *                quarter of the compute units busy: P = compute units /
- *                tiles, at most 8, at least eight scale groups per range;
- *                measured on MI355X, a fuller grid runs faster unsplit);
- *                1: never split; 2 .. 8:
- *                split the last round's tiles into that many ranges (at
- *                most one per scale group), whatever the grid
+ *   split_parts      0: automatic (only when the tiles would keep at most a
+ *                    quarter of the compute units busy: P = compute units /
+ *                    tiles, at most 8, at least eight scale groups per range;
+ *                    measured on MI355X, a fuller grid runs faster unsplit);
+ *                    1: never split; 2 .. 8: split the last round's tiles
+ *                    into that many ranges (at most one per scale group),
+ *                    whatever the grid
+ *   workspace        NULL (never split) or device memory of at least
+ *                    gemm_fp8_workspace_size(M, N, K, split_parts) bytes,
+ *                    16-byte aligned, owned by the caller.  Layout: one
+ *                    32-bit arrival counter per split tile (the region
+ *                    rounded up to 256 bytes), then the fp32 partial tiles.
+ *                    The counters must be zero before the workspace is
+ *                    first used (allocate it zero-filled); every call
+ *                    returns them to zero when it completes, so a workspace
+ *                    kept for these calls needs no clearing between them.
+ *                    The partial tiles' contents on entry do not matter.
+ *   workspace_bytes  its size
  *
  * The result differs from the unsplit one only by fp32 summation order;
- * it does not depend on which workgroup finishes first.  If the scratch
- * cannot be allocated the call runs unsplit.  Operands the direct kernel
- * does not take run unsplit on the general kernel.  split_parts outside
- * 0 .. 8 returns TGEMM_ERR_INVALID; otherwise as gemm_fp8_blockscaled.
+ * it does not depend on which workgroup finishes first.  Operands the
+ * direct kernel does not take run unsplit on the general kernel.
+ * split_parts outside 0 .. 8, or a non-NULL workspace that is unaligned or
+ * short, returns TGEMM_ERR_INVALID; otherwise as gemm_fp8_blockscaled.
  */
 int gemm_fp8_blockscaled_ex(const void* A, const float* sA, const void* B, const float* sB,
                             void* C, int64_t M, int64_t N, int64_t K, int split_parts,
-                            void* stream);
+                            void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes gemm_fp8_blockscaled_ex needs on the current device (the
+ * plan depends on its compute-unit count): 0 when it would not split; -1
+ * for negative or oversized sizes or split_parts outside 0 .. 8. */
+int64_t gemm_fp8_workspace_size(int64_t M, int64_t N, int64_t K, int split_parts);
 
 /*
  * gemm_fp8_blockscaled_nt -- gemm_fp8_blockscaled with the weight stored
@@ -354,26 +398,40 @@ int64_t gemm_logsoftmax_workspace_size(int64_t M, int64_t N, int out_dtype);
  *   bias  bf16 [N] or NULL (required when epilogue != TGEMM_EPI_NONE)
  *   C     [M, N] bf16 or fp32 (out_dtype), row stride ldc >= N
  *
+ *   workspace        NULL (never split) or device memory of at least
+ *                    gemm_wq_workspace_size(M, N, K) bytes, 16-byte
+ *                    aligned, owned by the caller (contents irrelevant)
+ *   workspace_bytes  its size
+ *
  * Epilogue, output rounding and conventions as gemm_bf16.  Products X * Q
  * are exact and summed in fp32 per 128-row group, and each group's sum is
  * scaled by S in fp32 (no weight is rounded), so the result carries the
- * rounding of an fp32-accumulated GEMM.  A narrow weight (N <= 65536) is
- * cut along K into chunks of whole 128-row groups when that fills more of
- * the device; the chunks' fp32 partials go to library scratch (see Memory)
+ * rounding of an fp32-accumulated GEMM.  With a workspace, a narrow weight
+ * (N <= 65536) is cut along K into chunks of whole 128-row groups when that
+ * fills more of the device; the chunks' fp32 partials go to the workspace
  * and are summed in chunk order, then the bias and epilogue are applied and
  * the result rounded once (deterministic; the summation order, so the last
  * bits, differ from the unsplit call).
  * Supported: M <= 64, K % 8 == 0, N % 4 == 0, ldq % 4 == 0 (others return
- * TGEMM_ERR_UNSUPPORTED).  Returns TGEMM_OK, TGEMM_ERR_INVALID,
+ * TGEMM_ERR_UNSUPPORTED).  An unaligned or short non-NULL workspace returns
+ * TGEMM_ERR_INVALID.  Returns TGEMM_OK, TGEMM_ERR_INVALID,
  * TGEMM_ERR_UNSUPPORTED or TGEMM_ERR_LAUNCH.
  */
 int gemm_bf16_w8(const void* X, const void* Q, const float* S, const void* bias, void* C,
                  int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
-                 int epilogue, int out_dtype, void* stream);
+                 int epilogue, int out_dtype, void* workspace, int64_t workspace_bytes,
+                 void* stream);
 
-/* Name of the kernel gemm_bf16_w8 launches for packed operands of these
- * sizes, or NULL when they are unsupported or invalid.  No launch. */
-const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K);
+/* Workspace bytes gemm_bf16_w8 / gemm_bf16_w4 need to split this problem
+ * along K (a multiple of 256; 0 when they would not split) on the current
+ * device; -1 for negative or oversized sizes. */
+int64_t gemm_wq_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Name of the kernel (or kernel pair, "split+reduction") gemm_bf16_w8
+ * launches for packed operands of these sizes, with a sufficient workspace
+ * (with_workspace != 0) or without one; NULL when they are unsupported or
+ * invalid.  No launch. */
+const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K, int with_workspace);
 
 /*
  * gemm_bf16_w4 -- C[i,n] = epilogue( sum_k X[i,k] * (q[k,n] * S[k/128, n]) + bias[n] )
@@ -389,7 +447,7 @@ const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K);
  *         two's-complement code in [-8, 7]
  *   S     fp32 [ceil(K/128), N], packed row-major; row g scales K rows
  *         [128g, min(K, 128g+128)) (Q byte rows [64g, 64g+64))
- *   bias, C, epilogue, out_dtype, stream as gemm_bf16_w8
+ *   bias, C, epilogue, out_dtype, workspace, stream as gemm_bf16_w8
  *
  * Numerics as gemm_bf16_w8: products are exact and each 128-row group's
  * fp32 sum is scaled once.  Supported: M <= 64, K % 8 == 0, N % 4 == 0,
@@ -398,11 +456,11 @@ const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K);
  */
 int gemm_bf16_w4(const void* X, const void* Q, const float* S, const void* bias, void* C,
                  int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
-                 int epilogue, int out_dtype, void* stream);
+                 int epilogue, int out_dtype, void* workspace, int64_t workspace_bytes,
+                 void* stream);
 
-/* Name of the kernel gemm_bf16_w4 launches for packed operands of these
- * sizes, or NULL when they are unsupported or invalid.  No launch. */
-const char* gemm_w4_kernel_name(int64_t M, int64_t N, int64_t K);
+/* As gemm_w8_kernel_name for gemm_bf16_w4. */
+const char* gemm_w4_kernel_name(int64_t M, int64_t N, int64_t K, int with_workspace);
 
 /*
  * quantize_fp8_1x128 -- FP8 codes and scales for the A operand of
@@ -482,13 +540,15 @@ int gemm_bf16_quant_fp8(const void* A, const void* B, const void* bias, void* Q,
 int quantize_fp8_128x128(const void* W, void* Q, float* S, int64_t K, int64_t N, int64_t ldw,
                          void* stream);
 
-/* Name of the kernel configuration gemm_bf16_ex would launch for a problem
- * with 16-byte aligned operands (no launch, no validation of pointers;
- * operands that are not 16-byte aligned, or whose row strides are not
- * multiples of 8, run the register-staged kernel of the same tile shape).
- * Returns a static string, or NULL when the request is invalid. */
+/* Name of the kernel configuration (or kernel pair, "split+reduction")
+ * gemm_bf16_ex would launch for a problem with 16-byte aligned operands,
+ * given a sufficient workspace (with_workspace != 0) or none (as gemm_bf16
+ * always runs).  No launch, no validation of pointers; operands that are
+ * not 16-byte aligned, or whose row strides are not multiples of 8, run the
+ * register-staged kernel of the same tile shape.  Returns a static string,
+ * or NULL when the request is invalid. */
 const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue,
-                                  int out_dtype, int algo);
+                                  int out_dtype, int algo, int with_workspace);
 
 /* Name of the kernel configuration gemm_fp8_blockscaled launches for these
  * sizes (the direct-to-LDS kernel when K is a multiple of 16 and N >= 4, the

@@ -83,10 +83,11 @@ def gelu_tanh(y):
     return 0.5 * y * (1.0 + np.tanh(GELU_C * (y + GELU_A * y * y * y)))
 
 
-def gemm_f64(a, b, bias=None, epilogue=EPI_NONE):
+def gemm_f64(a, b, bias=None, epilogue=EPI_NONE, threads=None):
     """Reference result and tolerance denominators for ``epi(a @ b + bias)``.
 
-    a: float64 [M, K]; b: float64 [K, N]; bias: float64 [N] or None.
+    a: float64 [M, K]; b: float64 [K, N]; bias: float64 [N] or None;
+    threads: worker threads of the loop (None: native.default_threads()).
     Returns (y, D): y float64 [M, N] is the exact-input result (no output
     rounding); D float64 [M, N] is ``sum_k |a||b| (+ |bias|)``.
     """
@@ -95,7 +96,7 @@ def gemm_f64(a, b, bias=None, epilogue=EPI_NONE):
     if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"shape mismatch: a{a.shape} b{b.shape}")
     M, N = a.shape[0], b.shape[1]
-    y, d = native.contract(a, b)
+    y, d = native.contract(a, b, threads)
     if epilogue in (EPI_BIAS, EPI_BIAS_GELU_TANH):
         if bias is None:
             raise ValueError("bias epilogue without bias")
@@ -109,12 +110,12 @@ def gemm_f64(a, b, bias=None, epilogue=EPI_NONE):
     return y, d
 
 
-def gemm_bf16_bits(a_bits, b_bits, bias_bits=None, epilogue=EPI_NONE):
+def gemm_bf16_bits(a_bits, b_bits, bias_bits=None, epilogue=EPI_NONE, threads=None):
     """Oracle for the bf16 path on raw uint16 codes (row-major, any 2-D view)."""
     a = bf16_decode(a_bits)
     b = bf16_decode(b_bits)
     bias = None if bias_bits is None else bf16_decode(bias_bits)
-    return gemm_f64(a, b, bias, epilogue)
+    return gemm_f64(a, b, bias, epilogue, threads)
 
 
 def dequant_fp8_a(qa_bits, sa):

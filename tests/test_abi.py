@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_version_and_status_strings():
-    assert binding.gemm_abi_version() == 1
+    assert binding.gemm_abi_version() == 2
     assert binding.gemm_status_string(0) == "ok"
     assert "invalid" in binding.gemm_status_string(INV)
     assert binding.gemm_status_string(99) == "unknown status"
@@ -45,7 +45,7 @@ def _bf16(A=FAKE, B=FAKE, bias=FAKE, C=FAKE, M=64, N=64, K=64, lda=64, ldb=64, l
     L = binding.lib()
     if algo is None:
         return L.gemm_bf16(A, B, bias, C, M, N, K, lda, ldb, ldc, epi, out, NULL)
-    return L.gemm_bf16_ex(A, B, bias, C, M, N, K, lda, ldb, ldc, epi, out, algo, NULL)
+    return L.gemm_bf16_ex(A, B, bias, C, M, N, K, lda, ldb, ldc, epi, out, algo, NULL, 0, NULL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -80,7 +80,7 @@ def test_fp8_validation():
 
 def _w8(X=FAKE, Q=FAKE, S=FAKE, bias=FAKE, C=FAKE, M=8, N=64, K=64, ldx=64, ldq=64, ldc=64, epi=0,
         out=1, fn="gemm_bf16_w8"):
-    return getattr(binding.lib(), fn)(X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epi, out, NULL)
+    return getattr(binding.lib(), fn)(X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epi, out, NULL, 0, NULL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -97,6 +97,13 @@ def test_w8_validation(kw, status, fn):
 
 
 def test_w8_kernel_names():
+    # narrow weights: the split pair only when a workspace is given
+    assert binding.gemm_w8_kernel_name(8, 14336, 4096) == "tgemm_w8_thin_m16"
+    assert binding.gemm_w8_kernel_name(8, 14336, 4096, with_workspace=True) == \
+        "tgemm_w8_thin_splitk_m16+tgemm_splitk_reduce"
+    assert binding.gemm_w4_kernel_name(40, 4096, 4096, with_workspace=True) == \
+        "tgemm_w4_thin_splitk_m48+tgemm_splitk_reduce"
+    assert binding.gemm_w8_kernel_name(1, 128256, 4096, with_workspace=True) == "tgemm_w8_thin_m16"
     assert binding.gemm_w8_kernel_name(1, 128256, 4096) == "tgemm_w8_thin_m16"
     assert binding.gemm_w8_kernel_name(64, 128256, 4096) == "tgemm_w8_thin_m64"
     assert binding.gemm_w8_kernel_name(65, 128256, 4096) is None
@@ -129,6 +136,10 @@ def test_kernel_selection_table():
     assert name(2048, 4096, 16384) == "tgemm_bf16_tiled_256x128x64"
     assert name(64, 128256, 4096) == "tgemm_bf16_thin_m64"
     assert name(1, 128256, 4096) == "tgemm_bf16_thin_m16"
+    assert name(1, 128256, 4096, with_workspace=True) == "tgemm_bf16_thin_m16"
+    assert name(8, 4096, 4096) == "tgemm_bf16_thin_m16"
+    assert name(8, 4096, 4096, with_workspace=True) == "tgemm_bf16_thin_splitk_m16+tgemm_splitk_reduce"
+    assert name(64, 4096, 4096, with_workspace=True) == "tgemm_bf16_thin_splitk_m64+tgemm_splitk_reduce"
     assert name(64, 64, 64, algo=binding.ALGO_TILED).startswith("tgemm_bf16_tiled")
     assert name(65, 64, 64, algo=binding.ALGO_THIN) is None
     assert name(-1, 64, 64) is None
@@ -208,9 +219,38 @@ def test_strided_batched_validation():
 def test_fp8_ex_validation():
     L = binding.lib()
     for parts in (-1, 9):
-        assert L.gemm_fp8_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4, parts, NULL) == INV
-    assert L.gemm_fp8_blockscaled_ex(NULL, NULL, NULL, NULL, NULL, 0, 4, 4, 2, NULL) == OK
-    assert L.gemm_fp8_blockscaled_ex(FAKE, NULL, FAKE, FAKE, FAKE, 4, 4, 4, 2, NULL) == INV
+        assert L.gemm_fp8_blockscaled_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 4, parts, NULL, 0, NULL) == INV
+    assert L.gemm_fp8_blockscaled_ex(NULL, NULL, NULL, NULL, NULL, 0, 4, 4, 2, NULL, 0, NULL) == OK
+    assert L.gemm_fp8_blockscaled_ex(FAKE, NULL, FAKE, FAKE, FAKE, 4, 4, 4, 2, NULL, 0, NULL) == INV
+    assert L.gemm_fp8_workspace_size(-1, 4, 4, 0) == -1
+    assert L.gemm_fp8_workspace_size(4, 4, 4, 9) == -1
+    assert L.gemm_fp8_workspace_size(0, 4, 4, 0) == 0
+
+
+def test_workspace_sizes_and_validation():
+    """Size queries (host only) and the rejection of a short or unaligned
+    workspace before anything is enqueued."""
+    L = binding.lib()
+    # M = 8, N = K = 4096: 8 stripes; S = min(256/8, KT/4 = 32, K/(8M) = 64) = 32 chunks
+    assert L.gemm_bf16_workspace_size(8, 4096, 4096, 0) == 32 * 8 * 4096 * 4
+    assert L.gemm_bf16_workspace_size(8, 128256, 4096, 0) == 0      # 251 stripes: no split
+    assert L.gemm_bf16_workspace_size(65, 4096, 4096, 0) == 0       # tiled kernel
+    assert L.gemm_bf16_workspace_size(8, 4096, 4096, binding.ALGO_TILED) == 0
+    assert L.gemm_bf16_workspace_size(-1, 4096, 4096, 0) == -1
+    assert L.gemm_bf16_workspace_size(8, 4096, 4096, 9) == -1
+    assert L.gemm_wq_workspace_size(-1, 4, 4) == -1
+    assert L.gemm_wq_workspace_size(8, 128256, 4096) == 0
+    need = L.gemm_bf16_workspace_size(8, 4096, 4096, 0)
+
+    def call(ws, nbytes):
+        return L.gemm_bf16_ex(FAKE, FAKE, NULL, FAKE, 8, 4096, 4096, 4096, 4096, 4096, 0, 1, 0, ws, nbytes, NULL)
+
+    assert call(FAKE, need - 1) == INV
+    assert call(ctypes.c_void_p(0x1008), need) == INV     # not 16-byte aligned
+    wq = L.gemm_wq_workspace_size(8, 4096, 4096)
+    assert wq > 0 and wq % 256 == 0
+    assert L.gemm_bf16_w8(FAKE, FAKE, FAKE, NULL, FAKE, 8, 4096, 4096, 4096, 4096, 4096, 0, 1, FAKE, wq - 1,
+                          NULL) == INV
 
 
 def _tiles(M, N):

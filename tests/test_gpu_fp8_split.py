@@ -5,9 +5,9 @@ tiles runs as P workgroups over disjoint ranges of whole 128-wide scale
 groups; their fp32 partial tiles are added by the workgroup that finishes
 last (DeepGEMM page, section 2.1: small grids leave compute units idle).
 Every case is checked against the fp64 oracle at the FP8 tolerance; the
-split must not depend on arrival order (bit-identical repeats), must leave
-its counters at zero for the next call, and must not share scratch with the
-small-M bf16 split-K on the same stream.
+split must not depend on arrival order (bit-identical repeats) and must
+leave its counters (the head of the caller's workspace) at zero for the next
+call.
 """
 
 import pytest
@@ -29,11 +29,21 @@ def _dev():
     return torch.device("cuda")
 
 
-def _run(qa, sa, qb, sb, parts):
-    M, N = qa.shape[0], qb.shape[1]
+def _workspace(M, N, K, parts, dev):
+    """A zero-filled workspace for the split (None when the plan does not split)."""
+    need = tg.gemm_fp8_workspace_size(M, N, K, parts)
+    assert need >= 0 and need % 256 == 0
+    return torch.zeros(need, dtype=torch.uint8, device=dev) if need else None
+
+
+def _run(qa, sa, qb, sb, parts, ws="new"):
+    M, K = qa.shape
+    N = qb.shape[1]
+    if isinstance(ws, str):
+        ws = _workspace(M, N, K, parts, qa.device)
     buf = torch.full((M * N + 2,), CANARY_BF16, dtype=torch.int16, device=qa.device)
     c = buf[1:M * N + 1].view(torch.bfloat16).view(M, N)
-    tg.gemm_fp8_blockscaled_ex(qa, sa, qb, sb, c, split_parts=parts)
+    tg.gemm_fp8_blockscaled_ex(qa, sa, qb, sb, c, split_parts=parts, workspace=ws)
     torch.cuda.synchronize()
     assert int(buf[0]) == CANARY_BF16 and int(buf[M * N + 1]) == CANARY_BF16
     return c
@@ -76,29 +86,35 @@ def test_fp8_split_repeats_bit_identical():
     M, N, K = 600, 700, 2048
     print(f"[gpu] fp8 split repeats M={M} N={N} K={K}", flush=True)
     qa, sa, qb, sb = wl.fp8_inputs(wl.WORKLOADS["fp8"], device=dev, M=M, N=N, K=K)
-    first = _run(qa, sa, qb, sb, 8).clone()
+    ws = _workspace(M, N, K, 8, dev)
+    n_count = 256  # the counter region of 9 split tiles, rounded up to 256 bytes
+    first = _run(qa, sa, qb, sb, 8, ws).clone()
     _check(qa, sa, qb, sb, first)
     for _ in range(4):
-        again = _run(qa, sa, qb, sb, 8)
+        again = _run(qa, sa, qb, sb, 8, ws)
         assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+        assert int(ws[:n_count].count_nonzero()) == 0
 
 
-def test_fp8_split_shares_no_scratch_with_thin_splitk():
-    """The small-M bf16 split-K writes its partials to its own scratch; FP8
-    calls on the same stream before and after it stay correct."""
+def test_fp8_split_without_workspace_runs_unsplit():
+    """No workspace: every tile runs whole (within tolerance of the split
+    run); a short or unaligned workspace is rejected."""
     dev = _dev()
-    M, N, K = 513, 1000, 1024
-    print(f"[gpu] fp8 split + thin split-K M={M} N={N} K={K}", flush=True)
+    M, N, K = 600, 700, 2048
+    print(f"[gpu] fp8 split without workspace M={M} N={N} K={K}", flush=True)
     qa, sa, qb, sb = wl.fp8_inputs(wl.WORKLOADS["fp8"], device=dev, M=M, N=N, K=K)
-    c0 = _run(qa, sa, qb, sb, 4).clone()
-    x = wl.bf16((8, 4096), "normal", 1.0, 5, 1, dev)
-    w = wl.bf16((4096, 4096), "normal", 0.02, 5, 2, dev)
-    y = torch.empty(8, 4096, dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        tg.gemm_bf16(x, w, None, y)
-        c1 = _run(qa, sa, qb, sb, 4)
-        assert torch.equal(c0.view(torch.int16), c1.view(torch.int16))
+    c0 = _run(qa, sa, qb, sb, 4, None)
     _check(qa, sa, qb, sb, c0)
+    c1 = _run(qa, sa, qb, sb, 1, None)
+    assert torch.equal(c0.view(torch.int16), c1.view(torch.int16))
+    need = tg.gemm_fp8_workspace_size(M, N, K, 4)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(tg.TgemmError):
+        tg.gemm_fp8_blockscaled_ex(qa, sa, qb, sb, c, split_parts=4,
+                                   workspace=torch.zeros(need - 256, dtype=torch.uint8, device=dev))
+    big = torch.zeros(need + 16, dtype=torch.uint8, device=dev)
+    with pytest.raises(tg.TgemmError):
+        tg.gemm_fp8_blockscaled_ex(qa, sa, qb, sb, c, split_parts=4, workspace=big[4:need + 4])
 
 
 def test_fp8_full_size_split_against_unsplit():

@@ -55,12 +55,12 @@ def _inputs(M, N, K, seed, dev, bias=False):
     return x, p, s, b
 
 
-def _check(x, p, s, b, epi, out_dtype, label, cols=None):
+def _check(x, p, s, b, epi, out_dtype, label, cols=None, workspace=None):
     dev = x.device
     M, N = x.shape[0], p.shape[1]
     big, c = _guarded_out(M, N, out_dtype, dev)
     print(f"[gpu] w4 {label} M={M} N={N} K={x.shape[1]} epi={epi} out={out_dtype}", flush=True)
-    tg.gemm_bf16_w4(x, p, s, b, c, epilogue=epi)
+    tg.gemm_bf16_w4(x, p, s, b, c, epilogue=epi, workspace=workspace)
     torch.cuda.synchronize()
     assert _guards_intact(big, M, N)
     pc, sc = (p, s) if cols is None else (p[:, cols], s[:, cols])
@@ -87,11 +87,19 @@ def test_w4_shapes(shape):
 @pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
 def test_w4_split_k(shape, out):
     """Narrow weights (at most 128 stripes of 512 columns) are cut along K
-    into chunks of whole 128-row scale groups; the fp32 partials are summed
-    in chunk order with the bias and tanh-GeLU.  Checked against the oracle."""
+    into chunks of whole 128-row scale groups when a workspace is given; the
+    fp32 partials are summed in chunk order with the bias and tanh-GeLU.
+    Checked against the oracle with and without the workspace (unsplit)."""
     M, N, K = shape
-    x, q, s, b = _inputs(M, N, K, 4700 + M + K, _dev(), bias=True)
-    _check(x, q, s, b, tg.EPI_BIAS_GELU_TANH, out, "split-k")
+    dev = _dev()
+    x, q, s, b = _inputs(M, N, K, 4700 + M + K, dev, bias=True)
+    need = tg.gemm_wq_workspace_size(M, N, K)
+    assert need > 0 and need % 256 == 0
+    assert "splitk" in tg.gemm_w4_kernel_name(M, N, K, with_workspace=True)
+    assert "splitk" not in tg.gemm_w4_kernel_name(M, N, K)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    _check(x, q, s, b, tg.EPI_BIAS_GELU_TANH, out, "split-k", workspace=ws)
+    _check(x, q, s, b, tg.EPI_BIAS_GELU_TANH, out, "unsplit")
 
 
 @pytest.mark.parametrize("epi", [tg.EPI_NONE, tg.EPI_BIAS, tg.EPI_BIAS_GELU_TANH])
@@ -113,17 +121,22 @@ def test_w4_every_nibble_value_including_minus_eight():
 
 
 def test_w4_matches_int8_kernel_bit_for_bit():
-    """The same codes through gemm_bf16_w8 (as int8) give identical bits."""
+    """The same codes through gemm_bf16_w8 (as int8) give identical bits,
+    unsplit and split along K (the split plan does not depend on the code
+    width)."""
     dev = _dev()
     M, N, K = 12, 1024, 640
     x, p, s, b = _inputs(M, N, K, 44, dev, bias=True)
     q8 = torch.from_numpy(og.unpack_int4(p.cpu().numpy())).to(dev)
-    for out in (torch.float32, torch.bfloat16):
-        c4 = _check(x, p, s, b, tg.EPI_BIAS, out, "vs int8")
-        c8 = torch.empty(M, N, dtype=out, device=dev)
-        tg.gemm_bf16_w8(x, q8, s, b, c8, epilogue=tg.EPI_BIAS)
-        torch.cuda.synchronize()
-        assert torch.equal(c4.contiguous().view(torch.uint8), c8.view(torch.uint8))
+    need = tg.gemm_wq_workspace_size(M, N, K)
+    assert need > 0
+    for ws in (None, torch.empty(need, dtype=torch.uint8, device=dev)):
+        for out in (torch.float32, torch.bfloat16):
+            c4 = _check(x, p, s, b, tg.EPI_BIAS, out, "vs int8", workspace=ws)
+            c8 = torch.empty(M, N, dtype=out, device=dev)
+            tg.gemm_bf16_w8(x, q8, s, b, c8, epilogue=tg.EPI_BIAS, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(c4.contiguous().view(torch.uint8), c8.view(torch.uint8))
 
 
 @pytest.mark.parametrize("M", [12, 40])

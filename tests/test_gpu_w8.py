@@ -53,12 +53,12 @@ def _inputs(M, N, K, seed, dev, bias=False):
     return x, q, s, b
 
 
-def _check(x, q, s, b, epi, out_dtype, label, cols=None):
+def _check(x, q, s, b, epi, out_dtype, label, cols=None, workspace=None):
     dev = x.device
     M, N = x.shape[0], q.shape[1]
     big, c = _guarded_out(M, N, out_dtype, dev)
     print(f"[gpu] w8 {label} M={M} N={N} K={x.shape[1]} epi={epi} out={out_dtype}", flush=True)
-    tg.gemm_bf16_w8(x, q, s, b, c, epilogue=epi)
+    tg.gemm_bf16_w8(x, q, s, b, c, epilogue=epi, workspace=workspace)
     torch.cuda.synchronize()
     assert _guards_intact(big, M, N)
     qc, sc = (q, s) if cols is None else (q[:, cols], s[:, cols])
@@ -83,11 +83,19 @@ def test_w8_shapes(shape):
 @pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
 def test_w8_split_k(shape, out):
     """Narrow weights (at most 128 stripes of 512 columns) are cut along K
-    into chunks of whole 128-row scale groups; the fp32 partials are summed
-    in chunk order with the bias and tanh-GeLU.  Checked against the oracle."""
+    into chunks of whole 128-row scale groups when a workspace is given; the
+    fp32 partials are summed in chunk order with the bias and tanh-GeLU.
+    Checked against the oracle with and without the workspace (unsplit)."""
     M, N, K = shape
-    x, q, s, b = _inputs(M, N, K, 4700 + M + K, _dev(), bias=True)
-    _check(x, q, s, b, tg.EPI_BIAS_GELU_TANH, out, "split-k")
+    dev = _dev()
+    x, q, s, b = _inputs(M, N, K, 4700 + M + K, dev, bias=True)
+    need = tg.gemm_wq_workspace_size(M, N, K)
+    assert need > 0 and need % 256 == 0
+    assert "splitk" in tg.gemm_w8_kernel_name(M, N, K, with_workspace=True)
+    assert "splitk" not in tg.gemm_w8_kernel_name(M, N, K)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    _check(x, q, s, b, tg.EPI_BIAS_GELU_TANH, out, "split-k", workspace=ws)
+    _check(x, q, s, b, tg.EPI_BIAS_GELU_TANH, out, "unsplit")
 
 
 @pytest.mark.parametrize("epi", [tg.EPI_NONE, tg.EPI_BIAS, tg.EPI_BIAS_GELU_TANH])

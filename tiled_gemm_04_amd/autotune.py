@@ -61,14 +61,18 @@ def sweep(shapes=SHAPES, iters=10, seed=7):
         b = (torch.randn(K, N, generator=g, device=dev) * 0.02).to(torch.bfloat16)
         c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         flop = 2.0 * M * N * K
+        # The automatic choice with the workspace its split-K asks for (the
+        # candidates are timed as gemm_bf16 would run them, unsplit).
+        need = tg.gemm_bf16_workspace_size(M, N, K)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
         times = {}
         for name, algo in CANDIDATES:
             if algo == tg.ALGO_THIN and M > 64:
                 continue
             times[name] = time_call(lambda: tg.gemm_bf16_ex(a, b, None, c, algo=algo), iters)
-        t_auto = time_call(lambda: tg.gemm_bf16_ex(a, b, None, c, algo=tg.ALGO_AUTO), iters)
+        t_auto = time_call(lambda: tg.gemm_bf16_ex(a, b, None, c, algo=tg.ALGO_AUTO, workspace=ws), iters)
         best = min(times, key=times.get)
-        auto_kernel = tg.gemm_bf16_kernel_name(M, N, K)
+        auto_kernel = tg.gemm_bf16_kernel_name(M, N, K, with_workspace=ws is not None)
         rows.append({
             "M": M, "N": N, "K": K, "auto_kernel": auto_kernel, "auto_ms": round(t_auto, 5),
             "auto_tflops": round(flop / t_auto / 1e9, 1),
@@ -76,7 +80,7 @@ def sweep(shapes=SHAPES, iters=10, seed=7):
             "best": best, "best_ms": round(times[best], 5),
             "auto_vs_best": round(t_auto / times[best], 3),
         })
-        del a, b, c
+        del a, b, c, ws
         print(f"M={M:5d} N={N:6d} K={K:5d}  auto {auto_kernel:30s} {t_auto * 1e3:8.1f} us  "
               f"best {best:14s} {times[best] * 1e3:8.1f} us  ratio {t_auto / times[best]:.3f}", flush=True)
     return rows

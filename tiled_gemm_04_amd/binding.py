@@ -64,11 +64,17 @@ def lib():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.gemm_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
     L.gemm_bf16.restype = i32
-    L.gemm_bf16_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp]
+    L.gemm_bf16_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp, i64, vp]
     L.gemm_bf16_ex.restype = i32
+    L.gemm_bf16_workspace_size.argtypes = [i64, i64, i64, i32]
+    L.gemm_bf16_workspace_size.restype = i64
+    L.gemm_fp8_workspace_size.argtypes = [i64, i64, i64, i32]
+    L.gemm_fp8_workspace_size.restype = i64
+    L.gemm_wq_workspace_size.argtypes = [i64, i64, i64]
+    L.gemm_wq_workspace_size.restype = i64
     L.gemm_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.gemm_fp8_blockscaled.restype = i32
-    L.gemm_fp8_blockscaled_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    L.gemm_fp8_blockscaled_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp]
     L.gemm_fp8_blockscaled_ex.restype = i32
     L.gemm_fp8_split_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(i32),
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -88,9 +94,9 @@ def lib():
     L.gemm_fp8_blockscaled_nt.restype = i32
     L.gemm_bf16_quant_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
     L.gemm_bf16_quant_fp8.restype = i32
-    L.gemm_bf16_w8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.gemm_bf16_w8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp, i64, vp]
     L.gemm_bf16_w8.restype = i32
-    L.gemm_w8_kernel_name.argtypes = [i64, i64, i64]
+    L.gemm_w8_kernel_name.argtypes = [i64, i64, i64, i32]
     L.gemm_w8_kernel_name.restype = ctypes.c_char_p
     L.gemm_bf16_strided_batched.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                             i64, i32, i32, i32, vp]
@@ -103,15 +109,15 @@ def lib():
     L.gemm_bf16_logsoftmax.restype = i32
     L.gemm_logsoftmax_workspace_size.argtypes = [i64, i64, i32]
     L.gemm_logsoftmax_workspace_size.restype = i64
-    L.gemm_bf16_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp]
+    L.gemm_bf16_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, vp, i64, vp]
     L.gemm_bf16_w4.restype = i32
-    L.gemm_w4_kernel_name.argtypes = [i64, i64, i64]
+    L.gemm_w4_kernel_name.argtypes = [i64, i64, i64, i32]
     L.gemm_w4_kernel_name.restype = ctypes.c_char_p
     L.quantize_fp8_1x128.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     L.quantize_fp8_1x128.restype = i32
     L.quantize_fp8_128x128.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     L.quantize_fp8_128x128.restype = i32
-    L.gemm_bf16_kernel_name.argtypes = [i64, i64, i64, i32, i32, i32]
+    L.gemm_bf16_kernel_name.argtypes = [i64, i64, i64, i32, i32, i32, i32]
     L.gemm_bf16_kernel_name.restype = ctypes.c_char_p
     L.gemm_fp8_kernel_name.argtypes = [i64, i64, i64]
     L.gemm_fp8_kernel_name.restype = ctypes.c_char_p
@@ -154,12 +160,40 @@ def _check_cuda(*ts):
             raise ValueError("tensors must be on the GPU")
 
 
-def gemm_bf16_ex(A, B, bias, C, epilogue=EPI_NONE, algo=ALGO_AUTO, stream=None):
+def _workspace(ws):
+    """(pointer, bytes) of an optional workspace tensor (None: NULL, 0)."""
+    if ws is None:
+        return ctypes.c_void_p(0), 0
+    _check_cuda(ws)
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def gemm_bf16_workspace_size(M, N, K, algo=ALGO_AUTO):
+    """Bytes of workspace gemm_bf16_ex needs to split this problem (0: none)."""
+    return int(lib().gemm_bf16_workspace_size(M, N, K, int(algo)))
+
+
+def gemm_fp8_workspace_size(M, N, K, split_parts=0):
+    """Bytes of workspace gemm_fp8_blockscaled_ex needs on the current device
+    (0: it would not split).  Allocate it zero-filled (arrival counters)."""
+    return int(lib().gemm_fp8_workspace_size(M, N, K, int(split_parts)))
+
+
+def gemm_wq_workspace_size(M, N, K):
+    """Bytes of workspace gemm_bf16_w8 / gemm_bf16_w4 need to split (0: none)."""
+    return int(lib().gemm_wq_workspace_size(M, N, K))
+
+
+def gemm_bf16_ex(A, B, bias, C, epilogue=EPI_NONE, algo=ALGO_AUTO, workspace=None, stream=None):
     """C[M,N] = epilogue(A[M,K] @ B[K,N] + bias[N]) on the GPU (writes C in place).
 
     A, B: bfloat16, row-major (unit inner stride, any row stride).
     bias: bfloat16 [N] contiguous, or None for EPI_NONE.
     C: float32 or bfloat16 [M, N], row-major.
+    workspace: None (never split) or a device tensor of at least
+    gemm_bf16_workspace_size(M, N, K, algo) bytes for the small-M K split.
     """
     _check_cuda(A, B, bias, C)
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
@@ -176,32 +210,38 @@ def gemm_bf16_ex(A, B, bias, C, epilogue=EPI_NONE, algo=ALGO_AUTO, stream=None):
     K2, N = B.shape
     if K2 != K or tuple(C.shape) != (M, N) or (bias is not None and bias.numel() != N):
         raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    wp, wb = _workspace(workspace)
     st = lib().gemm_bf16_ex(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K,
                             _row_major(A, "A"), _row_major(B, "B"), _row_major(C, "C"),
-                            int(epilogue), out, int(algo), _stream_ptr(stream))
+                            int(epilogue), out, int(algo), wp, wb, _stream_ptr(stream))
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_bf16_ex")
     return C
 
 
 def gemm_bf16(A, B, bias, C, epilogue=EPI_NONE, stream=None):
-    """gemm_bf16 of the C ABI: the library picks the kernel family."""
-    return gemm_bf16_ex(A, B, bias, C, epilogue, ALGO_AUTO, stream)
+    """gemm_bf16 of the C ABI: the library picks the kernel family (no workspace)."""
+    _check_cuda(A, B, bias, C)
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("A and B must be bfloat16")
+    if C.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("C must be float32 or bfloat16")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N) or (bias is not None and bias.numel() != N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    out = OUT_F32 if C.dtype == torch.float32 else OUT_BF16
+    st = lib().gemm_bf16(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K,
+                         _row_major(A, "A"), _row_major(B, "B"), _row_major(C, "C"),
+                         int(epilogue), out, _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_bf16")
+    return C
 
 
-def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
-    """C[M,N] (bf16) = sum_g sA[:,g] sB[g,n/128] (A_g @ B_g) with e4m3fn A, B.
-
-    A: float8_e4m3fn [M, K] contiguous; sA: float32 [M, ceil(K/128)] contiguous;
-    B: float8_e4m3fn [K, N] contiguous; sB: float32 [ceil(K/128), ceil(N/128)];
-    C: bfloat16 [M, N] contiguous.
-    """
-    return gemm_fp8_blockscaled_ex(A, sA, B, sB, C, 0, stream)
-
-
-def gemm_fp8_blockscaled_ex(A, sA, B, sB, C, split_parts=0, stream=None):
-    """gemm_fp8_blockscaled_ex of the C ABI: split_parts 0 automatic, 1 never,
-    2..8 K ranges per tile of the last round."""
+def _fp8_operands(A, sA, B, sB, C):
     _check_cuda(A, sA, B, sB, C)
     if A.dtype != torch.float8_e4m3fn or B.dtype != torch.float8_e4m3fn:
         raise ValueError("A and B must be float8_e4m3fn")
@@ -215,8 +255,34 @@ def gemm_fp8_blockscaled_ex(A, sA, B, sB, C, split_parts=0, stream=None):
     G, H = (K + 127) // 128, (N + 127) // 128
     if K2 != K or tuple(C.shape) != (M, N) or tuple(sA.shape) != (M, G) or tuple(sB.shape) != (G, H):
         raise ValueError("shape mismatch")
+    return M, N, K
+
+
+def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
+    """C[M,N] (bf16) = sum_g sA[:,g] sB[g,n/128] (A_g @ B_g) with e4m3fn A, B.
+
+    A: float8_e4m3fn [M, K] contiguous; sA: float32 [M, ceil(K/128)] contiguous;
+    B: float8_e4m3fn [K, N] contiguous; sB: float32 [ceil(K/128), ceil(N/128)];
+    C: bfloat16 [M, N] contiguous.  Every tile runs whole.
+    """
+    M, N, K = _fp8_operands(A, sA, B, sB, C)
+    st = lib().gemm_fp8_blockscaled(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
+                                    _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_fp8_blockscaled")
+    return C
+
+
+def gemm_fp8_blockscaled_ex(A, sA, B, sB, C, split_parts=0, workspace=None, stream=None):
+    """gemm_fp8_blockscaled_ex of the C ABI: split_parts 0 automatic, 1 never,
+    2..8 K ranges per tile of the last round; workspace None (never split)
+    or a zero-initialised device tensor of at least
+    gemm_fp8_workspace_size(M, N, K, split_parts) bytes (its arrival counters
+    are left zero by every call, so it can be reused as is)."""
+    M, N, K = _fp8_operands(A, sA, B, sB, C)
+    wp, wb = _workspace(workspace)
     st = lib().gemm_fp8_blockscaled_ex(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
-                                       int(split_parts), _stream_ptr(stream))
+                                       int(split_parts), wp, wb, _stream_ptr(stream))
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_fp8_blockscaled_ex")
     return C
@@ -429,7 +495,7 @@ def gemm_bf16_logsoftmax(X, W, bias, C, workspace=None, stream=None):
     return C
 
 
-def _weight_only(name, bits, X, Q, S, bias, C, epilogue, stream):
+def _weight_only(name, bits, X, Q, S, bias, C, epilogue, workspace, stream):
     _check_cuda(X, Q, S, bias, C)
     qdt = torch.int8 if bits == 8 else torch.uint8
     if X.dtype != torch.bfloat16 or Q.dtype != qdt or S.dtype != torch.float32:
@@ -449,28 +515,31 @@ def _weight_only(name, bits, X, Q, S, bias, C, epilogue, stream):
     if not S.is_contiguous():
         raise ValueError("S must be contiguous")
     out = OUT_BF16 if C.dtype == torch.bfloat16 else OUT_F32
+    wp, wb = _workspace(workspace)
     st = getattr(lib(), name)(_ptr(X), _ptr(Q), _ptr(S), _ptr(bias), _ptr(C), M, N, K, ldx, ldq, ldc,
-                              int(epilogue), out, _stream_ptr(stream))
+                              int(epilogue), out, wp, wb, _stream_ptr(stream))
     if st != TGEMM_OK:
         raise TgemmError(st, name)
     return C
 
 
-def gemm_bf16_w8(X, Q, S, bias, C, epilogue=EPI_NONE, stream=None):
+def gemm_bf16_w8(X, Q, S, bias, C, epilogue=EPI_NONE, workspace=None, stream=None):
     """C[M,N] = epilogue(X[M,K] @ (Q[K,N] * S[k/128, N]) + bias[N]) on the GPU.
 
     X: bfloat16 [M, K] (unit inner stride); Q: int8 [K, N] (unit inner stride);
     S: float32 [ceil(K/128), N] contiguous; bias: bfloat16 [N] or None;
     C: bfloat16 or float32 [M, N] (unit inner stride), written in place.
+    workspace: None (never split) or a device tensor of at least
+    gemm_wq_workspace_size(M, N, K) bytes for the K split of narrow weights.
     """
-    return _weight_only("gemm_bf16_w8", 8, X, Q, S, bias, C, epilogue, stream)
+    return _weight_only("gemm_bf16_w8", 8, X, Q, S, bias, C, epilogue, workspace, stream)
 
 
-def gemm_bf16_w4(X, Q, S, bias, C, epilogue=EPI_NONE, stream=None):
+def gemm_bf16_w4(X, Q, S, bias, C, epilogue=EPI_NONE, workspace=None, stream=None):
     """gemm_bf16_w8 with int4 codes: Q is uint8 [K/2, N], byte (r, n) holding
     code (2r, n) in its low nibble and (2r+1, n) in its high nibble, each a
     4-bit two's-complement value."""
-    return _weight_only("gemm_bf16_w4", 4, X, Q, S, bias, C, epilogue, stream)
+    return _weight_only("gemm_bf16_w4", 4, X, Q, S, bias, C, epilogue, workspace, stream)
 
 
 def _weight_only_logsoftmax(name, bits, X, Q, S, bias, C, workspace, stream):
@@ -516,13 +585,13 @@ def gemm_bf16_w4_logsoftmax(X, Q, S, bias, C, workspace=None, stream=None):
     return _weight_only_logsoftmax("gemm_bf16_w4_logsoftmax", 4, X, Q, S, bias, C, workspace, stream)
 
 
-def gemm_w8_kernel_name(M, N, K):
-    r = lib().gemm_w8_kernel_name(M, N, K)
+def gemm_w8_kernel_name(M, N, K, with_workspace=False):
+    r = lib().gemm_w8_kernel_name(M, N, K, int(bool(with_workspace)))
     return None if r is None else r.decode()
 
 
-def gemm_w4_kernel_name(M, N, K):
-    r = lib().gemm_w4_kernel_name(M, N, K)
+def gemm_w4_kernel_name(M, N, K, with_workspace=False):
+    r = lib().gemm_w4_kernel_name(M, N, K, int(bool(with_workspace)))
     return None if r is None else r.decode()
 
 
@@ -564,8 +633,9 @@ def quantize_fp8_128x128(W, Q, S, stream=None):
     return _quantize("quantize_fp8_128x128", W, Q, S, True, stream)
 
 
-def gemm_bf16_kernel_name(M, N, K, epilogue=EPI_NONE, out_dtype=OUT_BF16, algo=ALGO_AUTO):
-    r = lib().gemm_bf16_kernel_name(M, N, K, epilogue, out_dtype, algo)
+def gemm_bf16_kernel_name(M, N, K, epilogue=EPI_NONE, out_dtype=OUT_BF16, algo=ALGO_AUTO,
+                          with_workspace=False):
+    r = lib().gemm_bf16_kernel_name(M, N, K, epilogue, out_dtype, algo, int(bool(with_workspace)))
     return None if r is None else r.decode()
 
 

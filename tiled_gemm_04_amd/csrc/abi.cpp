@@ -11,10 +11,6 @@
 #include "../../include/tgemm.h"
 #include "launch.h"
 
-#include <map>
-#include <tuple>
-#include <mutex>
-#include <utility>
 
 using tgemm::Bf16Args;
 using tgemm::Fp8Args;
@@ -100,17 +96,48 @@ bool use_thin(int64_t M, int algo) {
   return M <= kThinMaxM;
 }
 
-// Shared validation and launch of the two FP8 quantisers.
+// A workspace argument pair: NULL with any size means "none given"; a
+// non-NULL workspace must be 16-byte aligned and hold at least `need` bytes.
+bool workspace_ok(const void* ws, int64_t bytes, int64_t need) {
+  if (ws == nullptr) return true;
+  return aligned16(ws) && bytes >= need;
+}
+
+int64_t round256(int64_t bytes) { return (bytes + 255) / 256 * 256; }
+
+// Workspace bytes of the small-M bf16 split (0 when the plan does not split
+// or the call would not take the thin kernel).
+int64_t bf16_ws_bytes(int64_t M, int64_t N, int64_t K, int algo) {
+  if (M == 0 || N == 0 || !use_thin(M, algo)) return 0;
+  return round256(tgemm::thin_split_bytes(tgemm::thin_split_plan(M, N, K), M, N));
+}
+
+int64_t wq_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M == 0 || N == 0) return 0;
+  return round256(tgemm::thin_split_bytes(tgemm::wq_split_plan(M, N, K), M, N));
+}
+
+// FP8 split workspace: the per-tile counters first (4 bytes each, the
+// region rounded up to 256 bytes), then the fp32 partial tiles.
+int64_t fp8_counter_bytes(const tgemm::Fp8Split& plan) { return round256(int64_t{4} * plan.split_tiles); }
+
+int64_t fp8_ws_bytes(const tgemm::Fp8Split& plan) {
+  if (plan.parts <= 1) return 0;
+  return fp8_counter_bytes(plan) + static_cast<int64_t>(tgemm::fp8_split_part_bytes(plan));
+}
+
 // Weight-only integer GEMM (bits = 8 or 4): the argument rules of gemm_bf16
 // with Q in place of B (row stride in bytes; int4 rows hold two K rows each).
 int gemm_weight_only(int bits, const void* X, const void* Q, const float* S, const void* bias,
                      void* C, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
-                     int epilogue, int out_dtype, void* stream) {
+                     int epilogue, int out_dtype, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
   const int v = validate_bf16(X, Q, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype,
                               TGEMM_ALGO_AUTO);
   if (v != TGEMM_OK || M == 0 || N == 0) return v;
   if (K > 0 && S == nullptr) return TGEMM_ERR_INVALID;
   if (!tgemm::wq_supported(bits, M, N, K, ldx, ldq)) return TGEMM_ERR_UNSUPPORTED;
+  if (!workspace_ok(workspace, workspace_bytes, wq_ws_bytes(M, N, K))) return TGEMM_ERR_INVALID;
   tgemm::W8Args a;
   a.X = static_cast<const uint16_t*>(X);
   a.Q = static_cast<const uint8_t*>(Q);
@@ -126,7 +153,8 @@ int gemm_weight_only(int bits, const void* X, const void* Q, const float* S, con
   // A lane stores 4 consecutive outputs: 8 bytes of bf16 or 16 bytes of fp32.
   a.vec_c = ((out_dtype == TGEMM_OUT_BF16 ? aligned8(C) : aligned16(C)) && ldc % 4 == 0) ? 1 : 0;
   const hipError_t e = tgemm::launch_wq_thin(bits, a, epilogue, out_dtype == TGEMM_OUT_BF16 ? 1 : 0,
-                                             static_cast<hipStream_t>(stream));
+                                             static_cast<hipStream_t>(stream), static_cast<float*>(workspace),
+                                             workspace_bytes);
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
@@ -186,10 +214,11 @@ int gemm_wq_logsoftmax(int bits, const void* X, const void* Q, const float* S, c
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
-const char* weight_only_name(int bits, int64_t M, int64_t N, int64_t K) {
+const char* weight_only_name(int bits, int64_t M, int64_t N, int64_t K, int with_workspace) {
   if (M < 1 || N < 1 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return nullptr;
   if (!tgemm::wq_supported(bits, M, N, K, K, N)) return nullptr;
-  return tgemm::wq_kernel_name(bits, static_cast<int>(M));
+  const bool split = with_workspace != 0 && tgemm::wq_split_plan(M, N, K).S > 1;
+  return tgemm::wq_kernel_name(bits, static_cast<int>(M), split);
 }
 
 int quantize_fp8(const void* X, void* Q, float* S, int64_t rows, int64_t cols, int64_t ldx,
@@ -215,9 +244,11 @@ int quantize_fp8(const void* X, void* Q, float* S, int64_t rows, int64_t cols, i
 }
 
 // FP8 block-scaled GEMM with B given as [K, N] (bt false) or [N, K] (bt
-// true); the split plan and its scratch as gemm_fp8_blockscaled_ex documents.
+// true); the split plan and its workspace as gemm_fp8_blockscaled_ex
+// documents (no workspace: unsplit).
 int fp8_call(const void* A, const float* sA, const void* B, const float* sB, void* C, int64_t M,
-             int64_t N, int64_t K, int split_parts, bool bt, void* stream) {
+             int64_t N, int64_t K, int split_parts, bool bt, void* workspace, int64_t workspace_bytes,
+             void* stream) {
   if (split_parts < 0 || split_parts > tgemm::kFp8MaxParts) return TGEMM_ERR_INVALID;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return TGEMM_ERR_INVALID;
@@ -228,6 +259,10 @@ int fp8_call(const void* A, const float* sA, const void* B, const float* sB, voi
   if (!extent_ok(M, K, K) || !extent_ok(M, N, N)) return TGEMM_ERR_INVALID;
   if (bt ? !extent_ok(N, K, K) : !extent_ok(K, N, N)) return TGEMM_ERR_INVALID;
   if (bt && !tgemm::fp8_nt_ok(M, N, K)) return TGEMM_ERR_UNSUPPORTED;
+  const tgemm::Fp8Split plan =
+      workspace == nullptr ? tgemm::Fp8Split{0, 0, 1}
+                           : tgemm::fp8_split_plan(M, N, K, tgemm::device_cus(), split_parts);
+  if (!workspace_ok(workspace, workspace_bytes, fp8_ws_bytes(plan))) return TGEMM_ERR_INVALID;
 
   Fp8Args a;
   a.A = static_cast<const uint8_t*>(A);
@@ -245,16 +280,13 @@ int fp8_call(const void* A, const float* sA, const void* B, const float* sB, voi
   a.vec_c = (aligned16(C) && N % 8 == 0) ? 1 : 0;
   a.bt = bt ? 1 : 0;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  // Split the tiles along K when they leave most compute units idle (scratch
-  // for the partial tiles and their counters); without scratch the split is
-  // skipped.
-  const tgemm::Fp8Split plan = tgemm::fp8_split_plan(M, N, K, tgemm::device_cus(), split_parts);
+  // Split the tiles along K when they leave most compute units idle: the
+  // counters open the workspace, the partial tiles follow them.
   void* part = nullptr;
   uint32_t* count = nullptr;
-  if (plan.parts > 1 && plan.split_tiles <= tgemm::kFp8MaxSplitTiles) {
-    part = tgemm::device_scratch(tgemm::fp8_split_part_bytes(plan), s, tgemm::kScratchFp8Part);
-    count = static_cast<uint32_t*>(tgemm::device_scratch(
-        tgemm::kFp8MaxSplitTiles * sizeof(uint32_t), s, tgemm::kScratchFp8Count, true));
+  if (plan.parts > 1) {
+    count = static_cast<uint32_t*>(workspace);
+    part = static_cast<char*>(workspace) + fp8_counter_bytes(plan);
   }
   const hipError_t e = tgemm::launch_fp8_blockscaled(a, plan, part, count, s);
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
@@ -264,49 +296,10 @@ int fp8_call(const void* A, const float* sA, const void* B, const float* sB, voi
 
 namespace tgemm {
 
-void* device_scratch(size_t bytes, hipStream_t stream, int slot, bool zeroed) {
-  struct Buf {
-    void* ptr = nullptr;
-    size_t cap = 0;
-  };
-  static std::mutex mu;
-  static std::map<std::tuple<int, hipStream_t, int>, Buf> bufs;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  Buf& b = bufs[{dev, stream, slot}];
-  if (b.cap < bytes) {
-    // hipFree waits for the device, so no queued kernel still uses the old
-    // buffer.
-    if (b.ptr != nullptr && hipFree(b.ptr) != hipSuccess) return nullptr;
-    b.ptr = nullptr;
-    b.cap = 0;
-    const size_t want = bytes + bytes / 4;
-    if (hipMalloc(&b.ptr, want) != hipSuccess) {
-      b.ptr = nullptr;
-      return nullptr;
-    }
-    if (zeroed && hipMemsetAsync(b.ptr, 0, want, stream) != hipSuccess) {
-      (void)hipFree(b.ptr);
-      b.ptr = nullptr;
-      return nullptr;
-    }
-    b.cap = want;
-  }
-  return b.ptr;
-}
-
 int device_cus() {
-  static std::mutex mu;
-  static std::map<int, int> cus;
-  int dev = 0;
+  int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cus.find(dev);
-  if (it != cus.end()) return it->second;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-  cus[dev] = n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return n;
 }
 
@@ -316,10 +309,11 @@ extern "C" {
 
 int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
                  int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
-                 int algo, void* stream) {
+                 int algo, void* workspace, int64_t workspace_bytes, void* stream) {
   const int st = validate_bf16(A, B, bias, C, M, N, K, lda, ldb, ldc, epilogue, out_dtype, algo);
   if (st != TGEMM_OK) return st;
   if (M == 0 || N == 0) return TGEMM_OK;
+  if (!workspace_ok(workspace, workspace_bytes, bf16_ws_bytes(M, N, K, algo))) return TGEMM_ERR_INVALID;
 
   Bf16Args a;
   a.A = static_cast<const uint16_t*>(A);
@@ -341,11 +335,17 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (use_thin(M, algo)) {
-    e = tgemm::launch_bf16_thin(a, epilogue, out_bf16, s);
+    e = tgemm::launch_bf16_thin(a, epilogue, out_bf16, s, static_cast<float*>(workspace), workspace_bytes);
   } else {
     e = tgemm::launch_bf16_tiled(a, tiled_shape_for(M, N, algo), epilogue, out_bf16, s);
   }
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
+}
+
+int64_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int algo) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
+  if (algo < TGEMM_ALGO_AUTO || algo > TGEMM_ALGO_TILED_128x128) return -1;
+  return bf16_ws_bytes(M, N, K, algo);
 }
 
 int gemm_bf16_quant_fp8(const void* A, const void* B, const void* bias, void* Q, float* S,
@@ -500,7 +500,7 @@ int gemm_bf16(const void* A, const void* B, const void* bias, void* C, int64_t M
               int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
               void* stream) {
   return gemm_bf16_ex(A, B, bias, C, M, N, K, lda, ldb, ldc, epilogue, out_dtype,
-                      TGEMM_ALGO_AUTO, stream);
+                      TGEMM_ALGO_AUTO, nullptr, 0, stream);
 }
 
 int64_t gemm_logsoftmax_workspace_size(int64_t M, int64_t N, int out_dtype) {
@@ -556,34 +556,53 @@ int gemm_bf16_logsoftmax(const void* X, const void* W, const void* bias, void* C
 
 int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB, void* C,
                          int64_t M, int64_t N, int64_t K, void* stream) {
-  return gemm_fp8_blockscaled_ex(A, sA, B, sB, C, M, N, K, 0, stream);
+  return fp8_call(A, sA, B, sB, C, M, N, K, 0, false, nullptr, 0, stream);
 }
 
 int gemm_fp8_blockscaled_ex(const void* A, const float* sA, const void* B, const float* sB, void* C,
-                            int64_t M, int64_t N, int64_t K, int split_parts, void* stream) {
-  return fp8_call(A, sA, B, sB, C, M, N, K, split_parts, false, stream);
+                            int64_t M, int64_t N, int64_t K, int split_parts, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+  return fp8_call(A, sA, B, sB, C, M, N, K, split_parts, false, workspace, workspace_bytes, stream);
+}
+
+int64_t gemm_fp8_workspace_size(int64_t M, int64_t N, int64_t K, int split_parts) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
+  if (split_parts < 0 || split_parts > tgemm::kFp8MaxParts) return -1;
+  if (M == 0 || N == 0) return 0;
+  return fp8_ws_bytes(tgemm::fp8_split_plan(M, N, K, tgemm::device_cus(), split_parts));
 }
 
 int gemm_fp8_blockscaled_nt(const void* A, const float* sA, const void* Bt, const float* sB, void* C,
                             int64_t M, int64_t N, int64_t K, void* stream) {
-  return fp8_call(A, sA, Bt, sB, C, M, N, K, 0, true, stream);
+  return fp8_call(A, sA, Bt, sB, C, M, N, K, 0, true, nullptr, 0, stream);
 }
 
 int gemm_bf16_w8(const void* X, const void* Q, const float* S, const void* bias, void* C,
                  int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
-                 int epilogue, int out_dtype, void* stream) {
-  return gemm_weight_only(8, X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype, stream);
+                 int epilogue, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm_weight_only(8, X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype, workspace,
+                          workspace_bytes, stream);
 }
 
 int gemm_bf16_w4(const void* X, const void* Q, const float* S, const void* bias, void* C,
                  int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq, int64_t ldc,
-                 int epilogue, int out_dtype, void* stream) {
-  return gemm_weight_only(4, X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype, stream);
+                 int epilogue, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm_weight_only(4, X, Q, S, bias, C, M, N, K, ldx, ldq, ldc, epilogue, out_dtype, workspace,
+                          workspace_bytes, stream);
 }
 
-const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K) { return weight_only_name(8, M, N, K); }
+int64_t gemm_wq_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
+  return wq_ws_bytes(M, N, K);
+}
 
-const char* gemm_w4_kernel_name(int64_t M, int64_t N, int64_t K) { return weight_only_name(4, M, N, K); }
+const char* gemm_w8_kernel_name(int64_t M, int64_t N, int64_t K, int with_workspace) {
+  return weight_only_name(8, M, N, K, with_workspace);
+}
+
+const char* gemm_w4_kernel_name(int64_t M, int64_t N, int64_t K, int with_workspace) {
+  return weight_only_name(4, M, N, K, with_workspace);
+}
 
 int quantize_fp8_1x128(const void* X, void* Q, float* S, int64_t M, int64_t K, int64_t ldx,
                        void* stream) {
@@ -596,14 +615,17 @@ int quantize_fp8_128x128(const void* W, void* Q, float* S, int64_t K, int64_t N,
 }
 
 const char* gemm_bf16_kernel_name(int64_t M, int64_t N, int64_t K, int epilogue, int out_dtype,
-                                  int algo) {
+                                  int algo, int with_workspace) {
   // Pointers play no part in the choice; pass dummies so only sizes are checked.
   static const int kDummy = 0;
   const void* d = &kDummy;
   if (validate_bf16(d, d, d, d, M, N, K, K > 0 ? K : 1, N > 0 ? N : 1, N > 0 ? N : 1, epilogue,
                     out_dtype, algo) != TGEMM_OK)
     return nullptr;
-  if (use_thin(M, algo)) return tgemm::thin_kernel_name(static_cast<int>(M));
+  if (use_thin(M, algo))
+    return tgemm::thin_kernel_name(static_cast<int>(M),
+                                   with_workspace != 0 && tgemm::thin_split_plan(M, N, K).S > 1 && K % 8 == 0 &&
+                                       N % 8 == 0);
   return tgemm::tiled_shape_info(tiled_shape_for(M, N, algo)).name;
 }
 

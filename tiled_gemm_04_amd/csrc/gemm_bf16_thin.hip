@@ -931,26 +931,37 @@ hipError_t launch_bf16_thin_nt(const Bf16Args& a, int epi, int out_bf16, hipStre
   return dispatch_nt_epi<4>(a, epi, out_bf16, s);
 }
 
-const char* thin_kernel_name(int M) {
+const char* thin_kernel_name(int M, bool split) {
+  if (split) {
+    if (M <= 16) return "tgemm_bf16_thin_splitk_m16+tgemm_splitk_reduce";
+    if (M <= 32) return "tgemm_bf16_thin_splitk_m32+tgemm_splitk_reduce";
+    if (M <= 48) return "tgemm_bf16_thin_splitk_m48+tgemm_splitk_reduce";
+    return "tgemm_bf16_thin_splitk_m64+tgemm_splitk_reduce";
+  }
   if (M <= 16) return "tgemm_bf16_thin_m16";
   if (M <= 32) return "tgemm_bf16_thin_m32";
   if (M <= 48) return "tgemm_bf16_thin_m48";
   return "tgemm_bf16_thin_m64";
 }
 
-hipError_t launch_bf16_thin(const Bf16Args& a, int epi, int out_bf16, hipStream_t s) {
+bool thin_direct_ok(const Bf16Args& a) {
   // Direct loads need 16-byte aligned rows and per-lane offsets below 2^31
   // (a slice's 32 rows of W, 64 rows of X).
-  const bool direct = a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
-                      a.ldb * 2 * kBK < (int64_t{1} << 31) && a.lda * 2 * 64 < (int64_t{1} << 31);
-  if (!direct) return launch_bf16_thin_general(a, epi, out_bf16, s);
-  if (a.batch == 1) {
+  return a.vec_a && a.vec_b && a.K % 8 == 0 && a.N % 8 == 0 &&
+         a.ldb * 2 * kBK < (int64_t{1} << 31) && a.lda * 2 * 64 < (int64_t{1} << 31);
+}
+
+int64_t thin_split_bytes(const ThinSplit& plan, int64_t M, int64_t N) {
+  return plan.S > 1 ? static_cast<int64_t>(plan.S) * M * N * 4 : 0;
+}
+
+hipError_t launch_bf16_thin(const Bf16Args& a, int epi, int out_bf16, hipStream_t s, float* part,
+                            int64_t part_bytes) {
+  if (!thin_direct_ok(a)) return launch_bf16_thin_general(a, epi, out_bf16, s);
+  if (a.batch == 1 && part != nullptr) {
     const ThinSplit plan = thin_split_plan(a.M, a.N, a.K);
-    if (plan.S > 1) {
-      float* part = static_cast<float*>(
-          device_scratch(static_cast<size_t>(plan.S) * a.M * a.N * sizeof(float), s));
-      if (part != nullptr) return launch_bf16_thin_splitk(a, plan, part, epi, out_bf16, s);
-    }
+    if (plan.S > 1 && part_bytes >= thin_split_bytes(plan, a.M, a.N))
+      return launch_bf16_thin_splitk(a, plan, part, epi, out_bf16, s);
   }
   if (a.M <= 16) return dispatch_epi<1>(a, epi, out_bf16, s);
   if (a.M <= 32) return dispatch_epi<2>(a, epi, out_bf16, s);

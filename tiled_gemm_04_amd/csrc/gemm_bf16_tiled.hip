@@ -3,8 +3,10 @@
 // The method (DeepGEMM page, sections 2.1-2.3 and 3.3; tensor-core page,
 // "Chunking" and "Registers与Tensor Cores") maps onto CDNA4 as follows:
 //   * tiling -- each workgroup owns one BM x BN output tile and walks K in
-//     slices of BK; four waves split the tile 2 x 2, each owning a
-//     (BM/2) x (BN/2) block of 32 x 32 MFMA accumulators (AGPRs);
+//     slices of BK; the waves split the tile 2 (along M) x WN (along N), each
+//     owning a (BM/2) x (BN/WN) block of 32 x 32 MFMA accumulator blocks held
+//     in registers (256 x 256: eight waves, two per SIMD, 128 x 64 each;
+//     the smaller tiles: four waves, 2 x 2);
 //   * global -> LDS -- 16-byte buffer loads write straight into LDS (no
 //     register staging, no LDS store instructions).  Each wave instruction
 //     fills one contiguous KiB of LDS, lane l owning bytes 16l .. 16l+15, so
@@ -21,8 +23,8 @@
 //   * pipelining -- NS LDS stages: the loads of slice t+NS-1 are issued while
 //     slice t is multiplied, MFMA operands are double-buffered in registers,
 //     and every non-MFMA instruction is placed between MFMAs by a
-//     compile-time slot schedule, because with one wave per SIMD any burst of
-//     other instructions leaves the matrix unit idle;
+//     compile-time slot schedule, so that no burst of other instructions
+//     leaves the matrix unit idle;
 //   * epilogue -- bias, tanh-GeLU and output rounding applied to the fp32
 //     accumulators (GEMM compute-cost page, section 5.1), the tile routed
 //     through LDS so each lane stores 16 contiguous bytes; stores past M, N

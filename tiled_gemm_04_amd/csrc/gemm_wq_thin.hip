@@ -598,12 +598,17 @@ bool wq_supported(int bits, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_
          ldq * kRows < (int64_t{1} << 31) && ldx * 2 * 64 < (int64_t{1} << 31);
 }
 
-const char* wq_kernel_name(int bits, int M) {
+const char* wq_kernel_name(int bits, int M, bool split) {
   static const char* const kNames[2][4] = {
       {"tgemm_w8_thin_m16", "tgemm_w8_thin_m32", "tgemm_w8_thin_m48", "tgemm_w8_thin_m64"},
       {"tgemm_w4_thin_m16", "tgemm_w4_thin_m32", "tgemm_w4_thin_m48", "tgemm_w4_thin_m64"}};
+  static const char* const kSplit[2][4] = {
+      {"tgemm_w8_thin_splitk_m16+tgemm_splitk_reduce", "tgemm_w8_thin_splitk_m32+tgemm_splitk_reduce",
+       "tgemm_w8_thin_splitk_m48+tgemm_splitk_reduce", "tgemm_w8_thin_splitk_m64+tgemm_splitk_reduce"},
+      {"tgemm_w4_thin_splitk_m16+tgemm_splitk_reduce", "tgemm_w4_thin_splitk_m32+tgemm_splitk_reduce",
+       "tgemm_w4_thin_splitk_m48+tgemm_splitk_reduce", "tgemm_w4_thin_splitk_m64+tgemm_splitk_reduce"}};
   const int m = M <= 16 ? 0 : M <= 32 ? 1 : M <= 48 ? 2 : 3;
-  return kNames[bits == 8 ? 0 : 1][m];
+  return (split ? kSplit : kNames)[bits == 8 ? 0 : 1][m];
 }
 
 hipError_t launch_wq_thin_lsm(int bits, const W8Args& a, const LsmArgs& q, int out_bf16,
@@ -670,11 +675,11 @@ hipError_t launch_splitk_bits(const W8Args& a, const ThinSplit& plan, float* par
 
 }  // namespace
 
-hipError_t launch_wq_thin(int bits, const W8Args& a, int epi, int out_bf16, hipStream_t s) {
-  const ThinSplit plan = wq_split_plan(a.M, a.N, a.K);
-  if (plan.S > 1) {
-    float* part = static_cast<float*>(device_scratch(static_cast<size_t>(plan.S) * a.M * a.N * sizeof(float), s));
-    if (part != nullptr) {
+hipError_t launch_wq_thin(int bits, const W8Args& a, int epi, int out_bf16, hipStream_t s, float* part,
+                          int64_t part_bytes) {
+  if (part != nullptr) {
+    const ThinSplit plan = wq_split_plan(a.M, a.N, a.K);
+    if (plan.S > 1 && part_bytes >= thin_split_bytes(plan, a.M, a.N)) {
       hipError_t e = bits == 8 ? launch_splitk_bits<8>(a, plan, part, s) : launch_splitk_bits<4>(a, plan, part, s);
       if (e != hipSuccess) return e;
       Bf16Args r{};

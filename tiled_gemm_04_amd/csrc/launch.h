@@ -106,28 +106,28 @@ bool thin_nt_ok(const Bf16Args& a);
 // Register-staged kernel for operands the direct-to-LDS kernel cannot take.
 hipError_t launch_bf16_general(const Bf16Args& a, int shape, int epilogue, int out_bf16,
                                hipStream_t stream);
-hipError_t launch_bf16_thin(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream);
+// Small-M kernel.  part / part_bytes: caller workspace for the split-K
+// partials (nullptr: never split); the split runs when the plan asks for
+// one and part_bytes >= thin_split_bytes(plan, M, N).
+hipError_t launch_bf16_thin(const Bf16Args& a, int epilogue, int out_bf16, hipStream_t stream,
+                            float* part = nullptr, int64_t part_bytes = 0);
 // Split-K for the thin kernel: S chunks of ktc slices (S == 1: no split).
 struct ThinSplit {
   int S;
   int ktc;
 };
 ThinSplit thin_split_plan(int64_t M, int64_t N, int64_t K);
-// part: S * M * N fp32 of device scratch.
+// Bytes of fp32 partials a split plan writes: S * M * N * 4 (0 for S == 1).
+int64_t thin_split_bytes(const ThinSplit& plan, int64_t M, int64_t N);
+// The operands the direct-to-LDS thin kernel (and its split) takes.
+bool thin_direct_ok(const Bf16Args& a);
+// part: S * M * N fp32 of workspace.
 hipError_t launch_bf16_thin_splitk(const Bf16Args& a, const ThinSplit& plan, float* part, int epilogue,
                                    int out_bf16, hipStream_t stream);
 // C = epilogue(sum over s < S of part[s] + bias), summed in order of s and
 // rounded once; reads a.M, a.N, a.bias, a.C, a.ldc and a.vec_c only.
 hipError_t launch_splitk_reduce(const Bf16Args& a, const float* part, int S, int epilogue, int out_bf16,
                                 hipStream_t stream);
-// Library-owned device scratch of at least `bytes` for work on `stream` of
-// the current device (one buffer per device and stream, grown on demand,
-// kept until the process ends); nullptr if it cannot be allocated.
-// Separate buffers per purpose (slot); a `zeroed` buffer is cleared on the
-// stream whenever it is (re)allocated.
-enum ScratchSlot { kScratchThinSplit = 0, kScratchFp8Part = 1, kScratchFp8Count = 2 };
-void* device_scratch(size_t bytes, hipStream_t stream, int slot = kScratchThinSplit,
-                     bool zeroed = false);
 // Compute units of the current device (0 if unknown).
 int device_cus();
 // Register-transposing thin kernel for operands the direct-to-LDS one cannot take.
@@ -141,27 +141,30 @@ struct Fp8Split {
   int parts;
 };
 constexpr int kFp8MaxParts = 8;
-constexpr int kFp8MaxSplitTiles = 4096;  // counters held by the library scratch
+constexpr int kFp8MaxSplitTiles = 4096;
 // forced_parts: 0 automatic (split only a grid that keeps at most a quarter
 // of the compute units busy, at least eight scale groups per part); 1 never;
 // 2 .. kFp8MaxParts split the last round's tiles into that many parts (at
 // most one per scale group).
 Fp8Split fp8_split_plan(int64_t M, int64_t N, int64_t K, int cus, int forced_parts);
 size_t fp8_split_part_bytes(const Fp8Split& plan);
-// part: fp8_split_part_bytes(plan) of scratch; count: plan.split_tiles
+// part: fp8_split_part_bytes(plan) of workspace; count: plan.split_tiles
 // counters that are zero on entry (and again on exit).  Either NULL: no split.
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* part,
                                   uint32_t* count, hipStream_t stream);
 // Register-staged kernel for FP8 operands the direct-to-LDS kernel cannot take.
 hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
-// bits: 8 or 4 (the code width).
-hipError_t launch_wq_thin(int bits, const W8Args& a, int epilogue, int out_bf16, hipStream_t stream);
+// bits: 8 or 4 (the code width).  part / part_bytes: caller workspace for
+// the split-K partials (nullptr: never split), as launch_bf16_thin.
+hipError_t launch_wq_thin(int bits, const W8Args& a, int epilogue, int out_bf16, hipStream_t stream,
+                          float* part = nullptr, int64_t part_bytes = 0);
 // Split-K plan of the integer-weight kernel (chunks of whole 128-row scale
 // groups; the same for int8 and int4); S == 1: no split.
 ThinSplit wq_split_plan(int64_t M, int64_t N, int64_t K);
 bool wq_supported(int bits, int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldq);
-const char* wq_kernel_name(int bits, int M);
+// split: the name of the split-K pair (kernel + reduction).
+const char* wq_kernel_name(int bits, int M, bool split);
 // Thin-M GEMM + bias + row log-softmax, in two passes: the GEMM kernel
 // writes fp32 logits (row stride ldl) and per-stripe (max, sum exp) pairs
 // part [M, G] (G = lsm_workgroups(N)); the second kernel merges each row's
@@ -192,7 +195,7 @@ int64_t probe_stream_threads(int cus);
 hipError_t launch_probe_mfma(int kind, int cus, int iters, uint64_t seed, float* out, hipStream_t stream);
 hipError_t launch_probe_stream_read(const void* src, int64_t n16, int cus, uint32_t* out,
                                     hipStream_t stream);
-const char* thin_kernel_name(int M);
+const char* thin_kernel_name(int M, bool split);
 const char* fp8_kernel_name(int64_t M, int64_t N, int64_t K);
 bool fp8_direct_ok(int64_t M, int64_t N, int64_t K);
 // The direct kernel with B as [N, K]: K % 16 == 0 and offsets below 2^31.
