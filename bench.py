@@ -11,13 +11,15 @@ compute-cost page, section 3.1; rates and utilisation are the "three numbers"
 of the DeepGEMM page, section 3.4).
 
 Also reported in the same line:
-  roofline      the dominant kernel's launch time from one pair of HIP events
-                per timed step on the launch stream (mean, median, min), as
-                achieved TFLOP/s (or GB/s, from the mean) against the MI355X
-                dense peak, plus HBM traffic from the committed rocprofv3
-                counter summary when it matches the current source;
+  roofline      the dominant kernel's launch time from HIP events on the
+                launch stream (mean over the timed region; median and min from
+                a second pass with one event pair per call), as achieved
+                TFLOP/s (or GB/s, from the mean) against the MI355X dense
+                peak, plus HBM traffic from the committed rocprofv3 counter
+                summary when it matches the current source;
   clocks        shader and memory clocks read from the driver's sysfs before,
-                during (while the queued steps run) and after the timed region;
+                during (sampled by a thread while the steps run) and after the
+                timed region;
   cpu_baseline  the fp64 CPU oracle (the plain triple loop in C) timed on this
                 host on a bounded row sample of the same workload, with its
                 thread count, the host's CPU count and model, and the oracle's
@@ -396,37 +398,62 @@ class Case:
     def time(self, steps, warmup, clocks=False):
         """Timing of `steps` back-to-back calls after `warmup` untimed ones.
 
-        Returns a dict: ms_per_step from the wall clock between the two
-        synchronisations that bracket the timed region, and the per-call
-        kernel times from one pair of HIP events per call recorded on the
-        launch stream (torch's current stream, which the binding launches
-        on): mean, median, min.  With clocks, the driver's clock readings
-        before, during (right after the calls are queued, while they run)
-        and after the region.
+        The timed region (bracketed by two synchronisations) enqueues the
+        calls with one pair of HIP events around all of them on the launch
+        stream (torch's current stream, which the binding launches on):
+        ms_per_step is its wall-clock time per call, kernel_ms_mean the
+        events' time per call.  A second pass of `steps` calls, each between
+        its own pair of events, gives the per-call median and minimum (an
+        event pair per call adds queue gaps, so it is kept out of the timed
+        region).  With clocks, the driver's shader / memory clock is sampled
+        from sysfs by a thread before, during and after the timed region.
         """
+        import threading
+
         import torch
 
         for _ in range(warmup):
             self.launch()
         torch.cuda.synchronize()
+        region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                r = read_clocks()
+                if r:
+                    samples.append(r)
+                stop.wait(0.0005)
+
+        clk = {"before": read_clocks()} if clocks else None
+        poller = threading.Thread(target=poll, daemon=True) if clocks else None
+        torch.cuda.synchronize()
+        if poller:
+            poller.start()
+        t0 = time.perf_counter()
+        region[0].record()
+        for _ in range(steps):
+            self.launch()
+        region[1].record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if poller:
+            stop.set()
+            poller.join()
+            clk["after"] = read_clocks()
+            clk["during"] = summarize_clocks(samples)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
-        clk = {"before": read_clocks()} if clocks else None
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for e0, e1 in ev:
             e0.record()
             self.launch()
             e1.record()
-        if clocks:
-            clk["during"] = read_clocks()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        if clocks:
-            clk["after"] = read_clocks()
         per = [e0.elapsed_time(e1) for e0, e1 in ev]
-        return {"ms_per_step": (t1 - t0) * 1e3 / steps, "kernel_ms_mean": statistics.fmean(per),
-                "kernel_ms_median": statistics.median(per), "kernel_ms_min": min(per), "clocks": clk}
+        return {"ms_per_step": (t1 - t0) * 1e3 / steps,
+                "kernel_ms_mean": region[0].elapsed_time(region[1]) / steps,
+                "kernel_ms_median": statistics.median(per), "kernel_ms_min": min(per),
+                "kernel_ms_per_call_mean": statistics.fmean(per), "clocks": clk}
 
     def roofline(self, t):
         """Roofline entry from a time() result: achieved from the mean kernel time."""
@@ -443,6 +470,8 @@ class Case:
                 "kernel": self.kernel, "kernel_ms_mean": round(t["kernel_ms_mean"], 5),
                 "kernel_ms_median": round(t["kernel_ms_median"], 5),
                 "kernel_ms_min": round(t["kernel_ms_min"], 5),
+                "kernel_ms_timing": "mean: one HIP event pair around the timed region / steps; "
+                                    "median and min: a second pass with one event pair per call",
                 "achieved_at_median": round(rate(t["kernel_ms_median"]), 2),
                 "algorithmic_bytes": self.bytes, "flop": self.flops}
 
@@ -491,6 +520,16 @@ def read_clocks():
             out["card"] = os.path.basename(os.path.dirname(card))
             return out
     return None
+
+
+def summarize_clocks(samples):
+    """min / median / max of the sampled clocks and the sample count."""
+    out = {"samples": len(samples)}
+    for key in ("sclk_mhz", "mclk_mhz"):
+        vals = sorted(r[key] for r in samples if key in r)
+        if vals:
+            out[key] = {"min": vals[0], "median": vals[len(vals) // 2], "max": vals[-1]}
+    return out
 
 
 def cpu_model():
