@@ -63,7 +63,9 @@ typedef enum {
     TGEMM_OK = 0,
     TGEMM_ERR_INVALID = 1,      /* bad pointer, size, stride or enum value      */
     TGEMM_ERR_UNSUPPORTED = 2,  /* valid request the kernels do not support      */
-    TGEMM_ERR_LAUNCH = 3        /* the HIP runtime refused the kernel launch    */
+    TGEMM_ERR_LAUNCH = 3,       /* the HIP runtime refused the kernel launch    */
+    TGEMM_ERR_SCRATCH = 4       /* gemm_bf16_noalloc: the split needs more than
+                                   its fixed scratch (TGEMM_NOALLOC_SCRATCH_BYTES) */
 } tgemm_status_t;
 
 /* Epilogue applied to the fp32 accumulator before the single output rounding.
@@ -210,6 +212,32 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C,
  * 256; 0 when it would not split); -1 for negative or oversized sizes or an
  * unknown algo.  No GPU call. */
 int64_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int algo);
+
+/*
+ * gemm_bf16_noalloc -- gemm_bf16_ex with its small-M K split in a fixed
+ * device scratch array of the library instead of a caller workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments and results as gemm_bf16_ex with a sufficient workspace (the
+ * same kernels, split plan and bits).  The call allocates and frees
+ * nothing.  The scratch is TGEMM_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU,
+ * held by every GPU the library runs on until the process ends; its address
+ * on a device is looked up on the first call made with that device current.
+ * A problem whose split needs more (gemm_bf16_workspace_size above the
+ * limit) returns TGEMM_ERR_SCRATCH before anything is enqueued; problems
+ * that do not split use no scratch.  All calls on one GPU share that GPU's
+ * array and it keeps the last call's partials (no part of it needs to start
+ * at zero): calls that may overlap on one GPU (other streams, other host
+ * threads) race on it and must be serialised by the caller.  Returns
+ * TGEMM_OK, TGEMM_ERR_INVALID, TGEMM_ERR_UNSUPPORTED, TGEMM_ERR_SCRATCH or
+ * TGEMM_ERR_LAUNCH.
+ */
+#define TGEMM_NOALLOC_SCRATCH_BYTES (INT64_C(32) << 20)
+int gemm_bf16_noalloc(const void* A, const void* B, const void* bias, void* C,
+                      int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc,
+                      int epilogue, int out_dtype, int algo, void* stream);
 
 /*
  * gemm_fp8_blockscaled -- C[i,j] = sum_g sA[i,g] * sB[g, j/128] *

@@ -23,6 +23,8 @@ TGEMM_OK = 0
 TGEMM_ERR_INVALID = 1
 TGEMM_ERR_UNSUPPORTED = 2
 TGEMM_ERR_LAUNCH = 3
+TGEMM_ERR_SCRATCH = 4
+NOALLOC_SCRATCH_BYTES = 32 << 20  # TGEMM_NOALLOC_SCRATCH_BYTES
 
 EPI_NONE = 0
 EPI_BIAS = 1
@@ -66,6 +68,8 @@ def lib():
     L.gemm_bf16.restype = i32
     L.gemm_bf16_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp, i64, vp]
     L.gemm_bf16_ex.restype = i32
+    L.gemm_bf16_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp]
+    L.gemm_bf16_noalloc.restype = i32
     L.gemm_bf16_workspace_size.argtypes = [i64, i64, i64, i32]
     L.gemm_bf16_workspace_size.restype = i64
     L.gemm_fp8_workspace_size.argtypes = [i64, i64, i64, i32]
@@ -216,6 +220,31 @@ def gemm_bf16_ex(A, B, bias, C, epilogue=EPI_NONE, algo=ALGO_AUTO, workspace=Non
                             int(epilogue), out, int(algo), wp, wb, _stream_ptr(stream))
     if st != TGEMM_OK:
         raise TgemmError(st, "gemm_bf16_ex")
+    return C
+
+
+def gemm_bf16_noalloc(A, B, bias, C, epilogue=EPI_NONE, algo=ALGO_AUTO, stream=None):
+    """gemm_bf16_ex with the small-M K split in the library's fixed device
+    scratch (no workspace argument, nothing allocated); raises TgemmError
+    (status TGEMM_ERR_SCRATCH) when the split needs more than
+    NOALLOC_SCRATCH_BYTES.  Calls that overlap on one GPU share the scratch."""
+    _check_cuda(A, B, bias, C)
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("A and B must be bfloat16")
+    if C.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("C must be float32 or bfloat16")
+    if bias is not None and (bias.dtype != torch.bfloat16 or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous bfloat16 vector")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N) or (bias is not None and bias.numel() != N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    out = OUT_F32 if C.dtype == torch.float32 else OUT_BF16
+    st = lib().gemm_bf16_noalloc(_ptr(A), _ptr(B), _ptr(bias), _ptr(C), M, N, K,
+                                 _row_major(A, "A"), _row_major(B, "B"), _row_major(C, "C"),
+                                 int(epilogue), out, int(algo), _stream_ptr(stream))
+    if st != TGEMM_OK:
+        raise TgemmError(st, "gemm_bf16_noalloc")
     return C
 
 

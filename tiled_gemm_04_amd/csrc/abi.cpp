@@ -342,6 +342,20 @@ int gemm_bf16_ex(const void* A, const void* B, const void* bias, void* C, int64_
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 
+int gemm_bf16_noalloc(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N,
+                      int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int epilogue, int out_dtype,
+                      int algo, void* stream) {
+  static_assert(tgemm::kNoAllocScratchBytes == TGEMM_NOALLOC_SCRATCH_BYTES, "header and library agree");
+  const int st = validate_bf16(A, B, bias, C, M, N, K, lda, ldb, ldc, epilogue, out_dtype, algo);
+  if (st != TGEMM_OK) return st;
+  if (M == 0 || N == 0) return TGEMM_OK;
+  const int64_t need = bf16_ws_bytes(M, N, K, algo);
+  if (need > tgemm::kNoAllocScratchBytes) return TGEMM_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && tgemm::noalloc_scratch(&ws) != hipSuccess) return TGEMM_ERR_LAUNCH;
+  return gemm_bf16_ex(A, B, bias, C, M, N, K, lda, ldb, ldc, epilogue, out_dtype, algo, ws, need, stream);
+}
+
 int64_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K, int algo) {
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
   if (algo < TGEMM_ALGO_AUTO || algo > TGEMM_ALGO_TILED_128x128) return -1;
@@ -693,6 +707,8 @@ const char* gemm_status_string(int status) {
     case TGEMM_ERR_INVALID: return "invalid argument";
     case TGEMM_ERR_UNSUPPORTED: return "unsupported request";
     case TGEMM_ERR_LAUNCH: return "kernel launch failed";
+    case TGEMM_ERR_SCRATCH:
+      return "request needs more device scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

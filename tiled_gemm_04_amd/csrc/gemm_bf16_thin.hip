@@ -35,6 +35,16 @@
 #include "common.h"
 #include "launch.h"
 
+#include <mutex>
+
+// Device scratch of the allocation-free split entry point (gemm_bf16_noalloc):
+// the fp32 partials of the small-M K split, in a fixed array that every GPU
+// the library runs on holds for the life of the process.  Host code never
+// uses this name as an address (on the host it is only a stand-in for the
+// symbol): it takes each device's address of the array from
+// hipGetSymbolAddress (noalloc_scratch below) and passes that to the kernels.
+static __device__ __align__(256) float scratch[tgemm::kNoAllocScratchBytes / sizeof(float)];
+
 namespace tgemm {
 
 namespace {
@@ -942,6 +952,28 @@ const char* thin_kernel_name(int M, bool split) {
   if (M <= 32) return "tgemm_bf16_thin_m32";
   if (M <= 48) return "tgemm_bf16_thin_m48";
   return "tgemm_bf16_thin_m64";
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  // Once per device, with that device current (it is the caller's current
+  // device): the device address of this device's copy of the array.
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 bool thin_direct_ok(const Bf16Args& a) {

@@ -130,6 +130,10 @@ hipError_t launch_splitk_reduce(const Bf16Args& a, const float* part, int S, int
                                 hipStream_t stream);
 // Compute units of the current device (0 if unknown).
 int device_cus();
+// Size of the fixed device scratch of the allocation-free split entry point,
+// and its address on the current device (looked up once per device).
+constexpr int64_t kNoAllocScratchBytes = int64_t{32} << 20;
+hipError_t noalloc_scratch(void** ptr);
 // Register-transposing thin kernel for operands the direct-to-LDS one cannot take.
 hipError_t launch_bf16_thin_general(const Bf16Args& a, int epilogue, int out_bf16,
                                     hipStream_t stream);
