@@ -52,9 +52,14 @@ constexpr int kGroupM = 4;  // tile-rows per scheduling group
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-template <int BM_, int BN_, int BK_, int NS_, int SPREAD_ = 1, int WN_ = 2>
+template <int BM_, int BN_, int BK_, int NS_, int SPREAD_ = 1, int WN_ = 2, int MF_ = 32, int BAR_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_;
+  // MFMA shape: 32 (v_mfma_f32_32x32x16_bf16, two K sub-steps per 32-wide
+  // slice) or 16 (v_mfma_f32_16x16x32_bf16, one per 32-wide slice).
+  static constexpr int MF = MF_;
+  // 16 x 16 x 32 kernel: the slot before which each slice's barrier sits.
+  static constexpr int BAR = BAR_;
   // Waves: 2 along M times WN along N (WN = 4: two waves per SIMD).
   static constexpr int WN = WN_;
   static constexpr int WAVES = 2 * WN;
@@ -62,8 +67,8 @@ struct Cfg {
   // Loads of a slice are spread over the first KS*FM*FN/SPREAD MFMA slots.
   static constexpr int SPREAD = SPREAD_;
   static constexpr int WTM = BM / 2, WTN = BN / WN;  // wave tile
-  static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int KS = BK / 16;  // MFMA sub-steps per slice
+  static constexpr int FM = WTM / MF, FN = WTN / MF;
+  static constexpr int KS = BK / (MF == 32 ? 16 : 32);  // MFMA sub-steps per slice
   // A stage: BM rows of BK bf16 (A_CPR chunks of 16 bytes each).
   static constexpr int A_ROW = BK * 2;
   static constexpr int A_CPR = BK / 8;
@@ -82,7 +87,8 @@ struct Cfg {
   static constexpr int EPI_PITCH = WTN + 4;
   static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
   static_assert(BN >= 128, "the B-row swizzle needs at least 16 chunks per row");
-  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32 x 32 block");
+  static_assert(MF == 32 || MF == 16, "MFMA shape");
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold an MFMA block");
   static_assert(A_STAGE % (1024 * WAVES) == 0 && B_STAGE % (1024 * WAVES) == 0,
                 "stages must split into 1 KiB loads per wave");
   static_assert(NS >= 2, "at least two stages");
@@ -99,8 +105,53 @@ __device__ __forceinline__ int a_swz(int r) {
   return (r / (16 / C::A_CPR)) % C::A_CPR;
 }
 // XOR applied to the chunk index of B row k: the four K rows read together by
-// a transposed read land in four different 64-byte bank segments.
-__device__ __forceinline__ int b_swz(int k) { return 4 * (k & 3); }
+// a transposed read land in four different 64-byte bank segments.  With the
+// 16 x 16 x 32 MFMA the two 16-lane groups served together read K rows 8
+// apart at the same columns; bit 3 of the row moves them to the other half
+// of each 64-byte segment.
+template <class C>
+__device__ __forceinline__ int b_swz(int k) {
+  if constexpr (C::MF == 16) return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1));
+  else return 4 * (k & 3);
+}
+
+// Stores 8 consecutive outputs v of one row, columns gcol .. gcol+7 (those
+// below N), rounded to bf16 or as fp32: one 16-byte store (two for fp32)
+// when full_cols (aligned row, all 8 inside N), an unaligned one when the
+// row is not 16-byte aligned, element stores at the right edge.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_row8(const float (&v)[8], int row, int gcol, bool full_cols,
+                                           const Bf16Args& p) {
+  const int64_t off = static_cast<int64_t>(row) * p.ldc + gcol;
+  if constexpr (OUT_BF16) {
+    uint16_t* out = static_cast<uint16_t*>(p.C) + off;
+    if (full_cols) {
+      *reinterpret_cast<u32x4*>(out) =
+          u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    } else if (gcol + 8 <= p.N) {
+      // Row not 16-byte aligned: one unaligned 16-byte store.
+      *reinterpret_cast<u32x4_a2*>(out) = u32x4_a2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gcol + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
+    }
+  } else {
+    float* out = static_cast<float*>(p.C) + off;
+    if (full_cols) {
+      *reinterpret_cast<f32x4*>(out) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(out + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    } else if (gcol + 8 <= p.N) {
+      *reinterpret_cast<f32x4_a4*>(out) = f32x4_a4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4_a4*>(out + 4) = f32x4_a4{v[4], v[5], v[6], v[7]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gcol + e < p.N) out[e] = v[e];
+    }
+  }
+}
 
 // Epilogue of one wave: its FM x FN accumulator blocks (transposed 32 x 32
 // layout, see the kernels) go through a private LDS strip of 32 rows, one
@@ -148,39 +199,52 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], flo
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = apply_epilogue<EPI>(v[e], bias[e]);
       const int row = row0 + 32 * i + rr;
-      if (row < p.M) {
-        const int64_t off = static_cast<int64_t>(row) * p.ldc + gcol;
-        if constexpr (OUT_BF16) {
-          uint16_t* out = static_cast<uint16_t*>(p.C) + off;
-          if (full_cols) {
-            *reinterpret_cast<u32x4*>(out) =
-                u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                      pack_bf16x2(v[6], v[7])};
-          } else if (gcol + 8 <= p.N) {
-            // Row not 16-byte aligned: one unaligned 16-byte store.
-            *reinterpret_cast<u32x4_a2*>(out) =
-                u32x4_a2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                         pack_bf16x2(v[6], v[7])};
-          } else {
+      if (row < p.M) store_row8<OUT_BF16>(v, row, gcol, full_cols, p);
+    }
+  }
+}
+
+// Epilogue of one wave for the 16 x 16 accumulator layout (element e of
+// lane l of block (i, j) is row 16 i + l%16, column 16 j + 4 (l/16) + e):
+// each 16-row strip of the wave's tile goes through a private LDS strip so
+// that every lane stores 8 consecutive outputs; bias, tanh-GeLU and rounding
+// as store_wave_tile.
+template <int EPI, bool OUT_BF16, int FM, int FN>
+__device__ __forceinline__ void store_wave_tile16(const f32x4 (&acc)[FM][FN], float* strip, int lane,
+                                                  int row0, int col0, const Bf16Args& p) {
+  constexpr int WTN = 16 * FN;
+  constexpr int PITCH = WTN + 4;  // floats; 16 bytes of padding per row
+  constexpr int LANES_PER_ROW = WTN / 8;
+  constexpr int ROWS_PER_PASS = kWave / LANES_PER_ROW;
+  static_assert(16 % ROWS_PER_PASS == 0, "whole passes per strip");
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int erow = lane / LANES_PER_ROW;
+  const int ecol = 8 * (lane % LANES_PER_ROW);
+  const int gcol = col0 + ecol;
+  float bias[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (gcol + e < p.N) out[e] = f32_to_bf16_bits(v[e]);
-          }
-        } else {
-          float* out = static_cast<float*>(p.C) + off;
-          if (full_cols) {
-            *reinterpret_cast<f32x4*>(out) = f32x4{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<f32x4*>(out + 4) = f32x4{v[4], v[5], v[6], v[7]};
-          } else if (gcol + 8 <= p.N) {
-            *reinterpret_cast<f32x4_a4*>(out) = f32x4_a4{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<f32x4_a4*>(out + 4) = f32x4_a4{v[4], v[5], v[6], v[7]};
-          } else {
+  for (int e = 0; e < 8; ++e) {
+    bias[e] = 0.0f;
+    if constexpr (EPI != kEpiNone) {
+      if (gcol + e < p.N) bias[e] = bf16_bits_to_f32(p.bias[gcol + e]);
+    }
+  }
+  const bool full_cols = p.vec_c && gcol + 8 <= p.N;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (gcol + e < p.N) out[e] = v[e];
-          }
-        }
-      }
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) *reinterpret_cast<f32x4*>(strip + l16 * PITCH + 16 * j + 4 * lq) = acc[i][j];
+#pragma unroll
+    for (int pass = 0; pass < 16 / ROWS_PER_PASS; ++pass) {
+      const int rr = erow + ROWS_PER_PASS * pass;
+      const float* src = strip + rr * PITCH + ecol;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = apply_epilogue<EPI>(v[e], bias[e]);
+      const int row = row0 + 16 * i + rr;
+      if (row < p.M) store_row8<OUT_BF16>(v, row, gcol, full_cols, p);
     }
   }
 }
@@ -292,9 +356,97 @@ __device__ __forceinline__ void store_wave_tile_q8(const f32x16 (&acc)[FM][FN], 
   }
 }
 
+// Global -> LDS loads of one workgroup's A and B slices, shared by both MFMA
+// shapes.  A block i of a wave covers 16-byte slots S = 64*blk + lane; slot
+// S is chunk (S % A_CPR) ^ a_swz(row) of row S / A_CPR.  B likewise with
+// b_swz.  Every byte offset is carried in the per-lane offset so the buffer
+// range check sees all of it; OR-ing in kOutOfRange (offsets stay below
+// 2^31) turns a load into zeros.  The windows of the slice at column k0 are
+// A rows m0 .. M-1 from column k0 and B rows k0 .. K-1 from column n0 (BT:
+// B rows n0 .. N-1 from column k0), so bytes past M, N or K read as zeros;
+// the main loops step a pointer and a size by one slice per iteration
+// instead of recomputing them.
+template <class C, bool BT>
+struct TileLoader {
+  uint32_t a_goff[C::APW];
+  int a_kc[C::APW];
+  uint32_t b_goff[C::BPW];
+  int b_kc[C::BPW];  // BT: first K column of the chunk
+  const uint16_t* a_base0;
+  int64_t a_size0;
+  const uint16_t* b_base0;
+  int64_t b_size0;
+  int64_t b_step;  // elements per slice
+  int64_t ldb;
+  uint32_t smem_base;
+  int wave, K;
+
+  __device__ __forceinline__ TileLoader(const Bf16Args& p, int wave_, int lane, int m0, int n0,
+                                        uint32_t smem_base_)
+      : ldb(p.ldb), smem_base(smem_base_), wave(wave_), K(p.K) {
+    const int64_t lda2 = p.lda * 2, ldb2 = p.ldb * 2;
+#pragma unroll
+    for (int i = 0; i < C::APW; ++i) {
+      const int s = 64 * (wave * C::APW + i) + lane;
+      const int r = s / C::A_CPR;
+      const int c = (s % C::A_CPR) ^ a_swz<C>(r);
+      a_goff[i] = static_cast<uint32_t>(r * lda2 + 16 * c);
+      a_kc[i] = 8 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < C::BPW; ++i) {
+      const int s = 64 * (wave * C::BPW + i) + lane;
+      if constexpr (BT) {
+        const int n = s / C::A_CPR;
+        const int c = (s % C::A_CPR) ^ a_swz<C>(n);
+        b_goff[i] = static_cast<uint32_t>(n * ldb2 + 16 * c);
+        b_kc[i] = 8 * c;
+      } else {
+        const int k = s / C::B_CPR;
+        const int c = (s % C::B_CPR) ^ b_swz<C>(k);
+        b_goff[i] = static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange);
+        b_kc[i] = 0;
+      }
+    }
+    a_base0 = p.A + static_cast<int64_t>(m0) * p.lda;
+    a_size0 = (static_cast<int64_t>(p.M - m0 - 1) * p.lda + p.K) * 2;
+    b_base0 = BT ? p.B + static_cast<int64_t>(n0) * p.ldb : p.B + n0;
+    b_size0 = BT ? (static_cast<int64_t>(p.N - n0 - 1) * p.ldb + p.K) * 2
+                 : (static_cast<int64_t>(p.K - 1) * p.ldb + (p.N - n0)) * 2;
+    b_step = BT ? int64_t{C::BK} : static_cast<int64_t>(C::BK) * p.ldb;
+  }
+  __device__ __forceinline__ i32x4 window_a(int k0) const {
+    return make_window_words(a_base0 + k0, a_size0 - 2 * k0);
+  }
+  __device__ __forceinline__ i32x4 window_b(int k0) const {
+    const int64_t e = BT ? int64_t{k0} : static_cast<int64_t>(k0) * ldb;
+    return make_window_words(b_base0 + e, b_size0 - 2 * e);
+  }
+  __device__ __forceinline__ void issue_a(i32x4 w, int stage, int k0, int i) const {
+    const uint32_t off = a_goff[i] | (k0 + a_kc[i] < K ? 0u : kOutOfRange);
+    buf_load16_lds(w, smem_base + stage * C::STAGE + (wave * C::APW + i) * 1024, off);
+  }
+  __device__ __forceinline__ void issue_b(i32x4 w, int stage, int k0, int i) const {
+    const uint32_t off = BT ? (b_goff[i] | (k0 + b_kc[i] < K ? 0u : kOutOfRange)) : b_goff[i];
+    buf_load16_lds(w, smem_base + stage * C::STAGE + C::A_STAGE + (wave * C::BPW + i) * 1024, off);
+  }
+  // Slices 0 .. NS-2 into stages 0 .. NS-2 (past K the loads read zeros).
+  __device__ __forceinline__ void prologue() const {
+    static_for<C::NS - 1>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      const i32x4 wa = window_a(s * C::BK), wb = window_b(s * C::BK);
+#pragma unroll
+      for (int i = 0; i < C::APW; ++i) issue_a(wa, s, s * C::BK, i);
+#pragma unroll
+      for (int i = 0; i < C::BPW; ++i) issue_b(wb, s, s * C::BK, i);
+    });
+  }
+};
+
 template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
                                                                 int tiles_n) {
+  static_assert(C::MF == 32, "the 32 x 32 x 16 kernel");
   apply_batch(p, OUT_BF16 ? 2 : 4);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
@@ -317,65 +469,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
 
-  // ---- global -> LDS: per-lane offsets inside the slice windows ----
-  // A block i of this wave covers 16-byte slots S = 64*blk + lane; slot S is
-  // chunk (S % A_CPR) ^ a_swz(row) of row S / A_CPR.  B likewise with b_swz.
-  // Every byte offset is carried in the per-lane offset so the buffer range
-  // check sees all of it; OR-ing in kOutOfRange (offsets stay below 2^31)
-  // turns a load into zeros.
-  const int64_t lda2 = p.lda * 2, ldb2 = p.ldb * 2;
-  uint32_t a_goff[C::APW];
-  int a_kc[C::APW];
-#pragma unroll
-  for (int i = 0; i < C::APW; ++i) {
-    const int s = 64 * (wave * C::APW + i) + lane;
-    const int r = s / C::A_CPR;
-    const int c = (s % C::A_CPR) ^ a_swz<C>(r);
-    a_goff[i] = static_cast<uint32_t>(r * lda2 + 16 * c);
-    a_kc[i] = 8 * c;
-  }
-  uint32_t b_goff[C::BPW];
-  int b_kc[C::BPW];  // BT: first K column of the chunk
-#pragma unroll
-  for (int i = 0; i < C::BPW; ++i) {
-    const int s = 64 * (wave * C::BPW + i) + lane;
-    if constexpr (BT) {
-      const int n = s / C::A_CPR;
-      const int c = (s % C::A_CPR) ^ a_swz<C>(n);
-      b_goff[i] = static_cast<uint32_t>(n * ldb2 + 16 * c);
-      b_kc[i] = 8 * c;
-    } else {
-      const int k = s / C::B_CPR;
-      const int c = (s % C::B_CPR) ^ b_swz(k);
-      b_goff[i] = static_cast<uint32_t>(k * ldb2 + 16 * c) | (n0 + 8 * c < p.N ? 0u : kOutOfRange);
-      b_kc[i] = 0;
-    }
-  }
-  // Windows of the slice at column k0: A rows m0 .. M-1 from column k0, B
-  // rows k0 .. K-1 from column n0 (bytes past M or K read as zeros).  They
-  // move by one slice per iteration, so the loop steps a pointer and a size
-  // instead of recomputing them.
-  const uint16_t* const a_base0 = p.A + static_cast<int64_t>(m0) * p.lda;
-  const int64_t a_size0 = (static_cast<int64_t>(p.M - m0 - 1) * p.lda + p.K) * 2;
-  // BT: B rows n0 .. N-1 from column k0, stepping like A.
-  const uint16_t* const b_base0 = BT ? p.B + static_cast<int64_t>(n0) * p.ldb : p.B + n0;
-  const int64_t b_size0 = BT ? (static_cast<int64_t>(p.N - n0 - 1) * p.ldb + p.K) * 2
-                             : (static_cast<int64_t>(p.K - 1) * p.ldb + (p.N - n0)) * 2;
-  const int64_t b_step = BT ? int64_t{C::BK} : static_cast<int64_t>(C::BK) * p.ldb;  // elements per slice
-  auto window_a = [&](int k0) { return make_window_words(a_base0 + k0, a_size0 - 2 * k0); };
-  auto window_b = [&](int k0) {
-    const int64_t e = BT ? int64_t{k0} : static_cast<int64_t>(k0) * p.ldb;
-    return make_window_words(b_base0 + e, b_size0 - 2 * e);
-  };
+  // ---- global -> LDS ----
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
-  auto issue_a = [&](i32x4 w, int stage, int k0, int i) {
-    const uint32_t off = a_goff[i] | (k0 + a_kc[i] < p.K ? 0u : kOutOfRange);
-    buf_load16_lds(w, smem_base + stage * C::STAGE + (wave * C::APW + i) * 1024, off);
-  };
-  auto issue_b = [&](i32x4 w, int stage, int k0, int i) {
-    const uint32_t off = BT ? (b_goff[i] | (k0 + b_kc[i] < p.K ? 0u : kOutOfRange)) : b_goff[i];
-    buf_load16_lds(w, smem_base + stage * C::STAGE + C::A_STAGE + (wave * C::BPW + i) * 1024, off);
-  };
+  const TileLoader<C, BT> ld(p, wave, lane, m0, n0, smem_base);
 
   // ---- LDS -> registers ----
   const int lrow = lane & 31;
@@ -457,15 +553,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 
   const int KT = (p.K + C::BK - 1) / C::BK;
   if (KT > 0) {
-    // Slices 0 .. NS-2 into stages 0 .. NS-2 (past K the loads read zeros).
-    static_for<C::NS - 1>([&](auto sc) {
-      constexpr int s = decltype(sc)::value;
-      const i32x4 wa = window_a(s * C::BK), wb = window_b(s * C::BK);
-#pragma unroll
-      for (int i = 0; i < C::APW; ++i) issue_a(wa, s, s * C::BK, i);
-#pragma unroll
-      for (int i = 0; i < C::BPW; ++i) issue_b(wb, s, s * C::BK, i);
-    });
+    ld.prologue();
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * C::LPS) : "memory");
     lds_barrier();
 #pragma unroll
@@ -474,18 +562,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
     int cur = 0;
     int lst = C::NS - 1;  // stage receiving slice t+NS-1
     // Windows of slice t+NS-1, stepped once per iteration.
-    const uint16_t* a_ptr = a_base0 + (C::NS - 1) * C::BK;
-    int64_t a_left = a_size0 - 2 * (C::NS - 1) * C::BK;
-    const uint16_t* b_ptr = b_base0 + (C::NS - 1) * b_step;
-    int64_t b_left = b_size0 - 2 * (C::NS - 1) * b_step;
+    const uint16_t* a_ptr = ld.a_base0 + (C::NS - 1) * C::BK;
+    int64_t a_left = ld.a_size0 - 2 * (C::NS - 1) * C::BK;
+    const uint16_t* b_ptr = ld.b_base0 + (C::NS - 1) * ld.b_step;
+    int64_t b_left = ld.b_size0 - 2 * (C::NS - 1) * ld.b_step;
     for (int t = 0; t < KT; ++t) {
       const int nxt = cur + 1 == C::NS ? 0 : cur + 1;
       const int kl = (t + C::NS - 1) * C::BK;
       const i32x4 wa = make_window_words(a_ptr, a_left), wb = make_window_words(b_ptr, b_left);
       a_ptr += C::BK;
       a_left -= 2 * C::BK;
-      b_ptr += b_step;
-      b_left -= 2 * b_step;
+      b_ptr += ld.b_step;
+      b_left -= 2 * ld.b_step;
       static_for<kSlots>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         constexpr int u = s / kQ;
@@ -505,11 +593,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
         });
         static_for<C::APW>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (load_slot(i) == s) issue_a(wa, lst, kl, i);
+          if constexpr (load_slot(i) == s) ld.issue_a(wa, lst, kl, i);
         });
         static_for<C::BPW>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (load_slot(C::APW + i) == s) issue_b(wb, lst, kl, i);
+          if constexpr (load_slot(C::APW + i) == s) ld.issue_b(wb, lst, kl, i);
         });
       });
       TGEMM_SCHED_FENCE();
@@ -536,12 +624,192 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 }
 
 
+// The same GEMM with v_mfma_f32_16x16x32_bf16.  On random data the matrix
+// units deliver more FLOP per watt with this shape than with 32 x 32 x 16
+// (an MFMA-only loop on N(0,1)-like bf16 operands: 1.90 against 1.69
+// PFLOP/s on MI355X, whose bf16 GEMMs run power-bound), for the same LDS
+// traffic: a wave's operands per 32-wide slice are still its WTM rows of A
+// and WTN columns of B.  A slice is one MFMA step, so the schedule differs:
+//   * per slice, slot s runs the MFMA of block (s / FN, s % FN) (row-major);
+//   * the barrier sits before slot BAR and certifies that slice t+1 has
+//     landed; every operand read of slice t+1 comes after it;
+//   * an A operand is single-buffered: after the last MFMA of row block i
+//     (or right after the barrier, if that comes later) the next slice's row
+//     block i is read into the same registers;
+//   * B operands are double-buffered by slice parity (the loop is unrolled
+//     by two): the next slice's are read in the half slice after the barrier;
+//   * the loads of slice t+NS-1 are spread over the slots; they refill the
+//     stage of slice t-1, whose last reads came before the previous barrier.
+// Operand layouts (16 x 16 x 32): an A operand gives lane l row l%16 of its
+// block and K 8(l/16) .. +7 of the slice (one 16-byte read); a B operand
+// gives lane l column l%16 and the same K (two transposed reads: lane
+// 16g + 4e + q supplies K rows 8g + e and 8g + 4 + e, columns 4q .. 4q+3).
+// The operands are swapped as in the 32 x 32 kernel, so element e of lane l
+// of block (i, j) is row 16 i + l%16, column 16 j + 4 (l/16) + e.
+template <class C, bool BT, int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, int tiles_m,
+                                                                  int tiles_n) {
+  static_assert(C::MF == 16 && C::KS == 1, "one 16 x 16 x 32 step per slice");
+  static_assert(C::NS >= 3, "the slice after next is in flight at each barrier");
+  apply_batch(p, OUT_BF16 ? 2 : 4);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WN;
+  const int wn = wave % C::WN;
+
+  int tm, tn;
+  tile_coords(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, kGroupM, tm, tn);
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+
+  f32x4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{};
+
+  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
+  const TileLoader<C, BT> ld(p, wave, lane, m0, n0, smem_base);
+
+  // ---- LDS -> registers ----
+  const int l16 = lane & 15, lq = lane >> 4;
+  // A row block i: row wm*WTM + 16i + l16, chunk lq (the swizzle depends on
+  // l16 only: 16i and wm*WTM are multiples of 16).
+  const int a_rd = (wm * C::WTM + l16) * C::A_ROW;
+  const int a_ch = ((lq ^ a_swz<C>(l16)) * 16);
+  const int bg = lane >> 4, be = (lane >> 2) & 3, bq = lane & 3;
+  int b_rd[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    if constexpr (BT) {
+      b_rd[j] = C::A_STAGE + (wn * C::WTN + 16 * j + l16) * C::A_ROW + a_ch;
+    } else {
+      const int k = 8 * bg + be;
+      const int chunk = (2 * (wn * C::WTN / 16 + j) + (bq >> 1)) ^ b_swz<C>(k);
+      b_rd[j] = C::A_STAGE + k * C::B_ROW + chunk * 16 + 8 * (bq & 1);
+    }
+  }
+  bf16x8 fa[C::FM], fb[2][C::FN];
+  auto read_a = [&](int stage, int i) {
+    const uint8_t* base = smem + stage * C::STAGE + a_rd + 16 * i * C::A_ROW + a_ch;
+    fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base));
+  };
+  auto read_b = [&](int buf, int stage, int j) {
+    const uint8_t* q = smem + stage * C::STAGE + b_rd[j];
+    if constexpr (BT) {
+      fb[buf][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q));
+    } else {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, q));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(TGEMM_LDS(i16x4, q + 4 * C::B_ROW));
+      fb[buf][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  constexpr int kSlots = C::FM * C::FN;
+  constexpr int kBar = C::BAR;
+  static_assert(kSlots >= C::LPS && kBar + kSlots / 2 <= kSlots && kBar + C::FM <= kSlots, "slot schedule");
+  auto load_slot = [](int l) { return spread(l, C::LPS, 0, kSlots); };
+  auto b_slot = [](int j) { return spread(j, C::FN, kBar, kBar + kSlots / 2); };
+  auto a_slot = [](int i) { return i * C::FN + C::FN - 1 > kBar + i ? i * C::FN + C::FN - 1 : kBar + i; };
+  // Loads younger than slice t+1 when the barrier waits: the NS-3 slices
+  // issued in earlier iterations after it, plus this slice's loads issued
+  // before the barrier.
+  constexpr int kBefore = [] {
+    int n = 0;
+    for (int l = 0; l < C::LPS; ++l) n += (spread(l, C::LPS, 0, kSlots) < kBar) ? 1 : 0;
+    return n;
+  }();
+  constexpr int kAhead = (C::NS - 3) * C::LPS + kBefore;
+
+  const int KT = (p.K + C::BK - 1) / C::BK;
+  if (KT > 0) {
+    ld.prologue();
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NS - 2) * C::LPS) : "memory");
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) read_a(0, i);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) read_b(0, 0, j);
+
+    int cur = 0;
+    int lst = C::NS - 1;  // stage receiving slice t+NS-1
+    const uint16_t* a_ptr = ld.a_base0 + (C::NS - 1) * C::BK;
+    int64_t a_left = ld.a_size0 - 2 * (C::NS - 1) * C::BK;
+    const uint16_t* b_ptr = ld.b_base0 + (C::NS - 1) * ld.b_step;
+    int64_t b_left = ld.b_size0 - 2 * (C::NS - 1) * ld.b_step;
+
+    // One slice; P: the B operand buffer holding this slice's operands.
+    auto slice = [&](auto pc, int t) {
+      constexpr int P = decltype(pc)::value;
+      const int nxt = cur + 1 == C::NS ? 0 : cur + 1;
+      const int kl = (t + C::NS - 1) * C::BK;
+      const i32x4 wa = make_window_words(a_ptr, a_left), wb = make_window_words(b_ptr, b_left);
+      a_ptr += C::BK;
+      a_left -= 2 * C::BK;
+      b_ptr += ld.b_step;
+      b_left -= 2 * ld.b_step;
+      static_for<kSlots>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int i = s / C::FN, j = s % C::FN;
+        if constexpr (s == kBar) {
+          TGEMM_SCHED_FENCE();
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAhead) : "memory");
+          lds_barrier();
+        }
+        TGEMM_SCHED_FENCE();
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[P][j], fa[i], acc[i][j], 0, 0, 0);
+        TGEMM_SCHED_FENCE();
+        static_for<C::FM>([&](auto ic) {
+          constexpr int ii = decltype(ic)::value;
+          if constexpr (a_slot(ii) == s) read_a(nxt, ii);
+        });
+        static_for<C::FN>([&](auto jc) {
+          constexpr int jj = decltype(jc)::value;
+          if constexpr (b_slot(jj) == s) read_b(1 - P, nxt, jj);
+        });
+        static_for<C::APW>([&](auto ic) {
+          constexpr int l = decltype(ic)::value;
+          if constexpr (load_slot(l) == s) ld.issue_a(wa, lst, kl, l);
+        });
+        static_for<C::BPW>([&](auto ic) {
+          constexpr int l = decltype(ic)::value;
+          if constexpr (load_slot(C::APW + l) == s) ld.issue_b(wb, lst, kl, l);
+        });
+      });
+      TGEMM_SCHED_FENCE();
+      lst = cur;
+      cur = nxt;
+    };
+    int t = 0;
+    for (; t + 1 < KT; t += 2) {
+      slice(std::integral_constant<int, 0>{}, t);
+      slice(std::integral_constant<int, 1>{}, t + 1);
+    }
+    if (t < KT) slice(std::integral_constant<int, 0>{}, t);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
+  lds_barrier();  // every wave is done with the operand stages
+
+  static_assert(C::WAVES * 16 * (C::WTN + 4) * 4 <= C::LDS_BYTES, "epilogue strips fit in LDS");
+  store_wave_tile16<EPI, OUT_BF16, C::FM, C::FN>(acc, reinterpret_cast<float*>(smem) + wave * 16 * (C::WTN + 4),
+                                                 lane, m0 + wm * C::WTM, n0 + wn * C::WTN, p);
+}
+
 template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
 hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
   const int tiles_n = (a.N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16, QUANT>), dim3(tiles_m * tiles_n, a.batch),
-                     dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
+  if constexpr (C::MF == 16) {
+    static_assert(!QUANT, "the quantising epilogue runs on the 32 x 32 kernel");
+    hipLaunchKernelGGL((tgemm_bf16_tiled16<C, BT, EPI, OUT_BF16>), dim3(tiles_m * tiles_n, a.batch),
+                       dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
+  } else {
+    hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16, QUANT>), dim3(tiles_m * tiles_n, a.batch),
+                       dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
+  }
   return hipGetLastError();
 }
 
@@ -564,12 +832,18 @@ hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s)
   return launch_c<C, BT, kEpiBiasGelu, false>(a, s);
 }
 
-// Per tile shape (measured on MI355X): BK = 32 with four stages keeps three
-// slices of loads in flight; the 256 x 256 tile runs 8 waves (two per SIMD,
-// each 128 x 64 outputs), which hides one wave's LDS and memory waits behind
-// the other's MFMAs (about 10 % faster than 4 waves of 128 x 128).
-using Cfg256x256 = Cfg<256, 256, 32, 4, 1, 4>;
+// Per tile shape (measured on MI355X): BK = 32 keeps several slices of
+// loads in flight (five stages on 256 x 256, four on 128 x 128); the
+// 256 x 256 tile runs 8 waves (two per SIMD, each 128 x 64 outputs), which
+// hides one wave's LDS and memory waits behind the other's MFMAs, with the
+// 16 x 16 x 32 MFMA (2-3 % faster than 32 x 32 x 16 there, bit-identical
+// results; on the 256 x 128 tile it measured 10-50 % slower, so that tile
+// keeps 32 x 32 x 16 with 64-wide slices).
+using Cfg256x256 = Cfg<256, 256, 32, 5, 1, 4, 16, 16>;
 using Cfg256x128 = Cfg<256, 128, 64, 3>;
+// The quantising epilogue is written for the 32 x 32 accumulator layout.
+using Cfg256x256Q = Cfg<256, 256, 32, 4, 1, 4>;
+using Cfg256x128Q = Cfg<256, 128, 64, 3>;
 using Cfg128x128 = Cfg<128, 128, 64, 4>;
 
 }  // namespace
@@ -609,8 +883,8 @@ hipError_t launch_bf16_tiled(const Bf16Args& a, int shape, int epi, int out_bf16
 hipError_t launch_bf16_tiled_q8(const Bf16Args& a, int shape, int epi, hipStream_t s) {
   if (!bf16_direct_ok(a, shape) || a.batch != 1 || a.qscale == nullptr) return hipErrorInvalidValue;
   switch (shape) {
-    case kTile256x256: return dispatch_q8<Cfg256x256>(a, epi, s);
-    case kTile256x128: return dispatch_q8<Cfg256x128>(a, epi, s);
+    case kTile256x256: return dispatch_q8<Cfg256x256Q>(a, epi, s);
+    case kTile256x128: return dispatch_q8<Cfg256x128Q>(a, epi, s);
     default: return dispatch_q8<Cfg128x128>(a, epi, s);
   }
 }
