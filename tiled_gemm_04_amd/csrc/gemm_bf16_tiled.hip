@@ -88,6 +88,7 @@ struct Cfg {
   static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
   static_assert(BN >= 128, "the B-row swizzle needs at least 16 chunks per row");
   static_assert(MF == 32 || MF == 16, "MFMA shape");
+  static_assert(MF == 32 || BK == 32, "the 16 x 16 x 32 kernel takes 32-wide slices");
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold an MFMA block");
   static_assert(A_STAGE % (1024 * WAVES) == 0 && B_STAGE % (1024 * WAVES) == 0,
                 "stages must split into 1 KiB loads per wave");
@@ -96,23 +97,28 @@ struct Cfg {
   static_assert(WAVES * 32 * EPI_PITCH * 4 <= LDS_BYTES, "epilogue staging must fit in LDS");
 };
 
-// XOR applied to the 16-byte chunk index of A row r: consecutive rows that
-// share a 256-byte LDS bank row get different permutations, so 16 lanes
-// reading one chunk column of 16 consecutive rows touch 16 distinct bank
-// groups.
+// XOR applied to the 16-byte chunk index of A row r (and of B row n for a
+// K-contiguous B).  32 x 32 x 16 reads (lane 32h + r takes one chunk of row
+// r < 32): consecutive rows that share a 256-byte LDS bank row get
+// different permutations, so 16 lanes reading one chunk column of 16
+// consecutive rows touch 16 distinct bank groups.  16 x 16 x 32 reads with
+// 64-byte rows (lane 16q + r takes chunk q of row r < 16) were measured on
+// MI355X over every XOR that is linear in the bits of r: the pattern above
+// costs 2.15 ns per ds_read_b128 per compute unit, (r & 3) ^ 3 r[2] ^ 2 r[3]
+// 1.43 ns, the fastest measured.  Both depend on r mod 16 only, so row
+// blocks 16 apart share them.
 template <class C>
 __device__ __forceinline__ int a_swz(int r) {
-  return (r / (16 / C::A_CPR)) % C::A_CPR;
+  if constexpr (C::MF == 16 && C::A_CPR == 4) return (r & 3) ^ (3 * ((r >> 2) & 1)) ^ (2 * ((r >> 3) & 1));
+  else return (r / (16 / C::A_CPR)) % C::A_CPR;
 }
 // XOR applied to the chunk index of B row k: the four K rows read together by
-// a transposed read land in four different 64-byte bank segments.  With the
-// 16 x 16 x 32 MFMA the two 16-lane groups served together read K rows 8
-// apart at the same columns; bit 3 of the row moves them to the other half
-// of each 64-byte segment.
+// a transposed read land in four different 64-byte bank segments (measured
+// for the 16 x 16 x 32 reads too: other XORs of the row bits gave the same
+// 1.96-2.06 ns per ds_read_b64_tr_b16 per compute unit).
 template <class C>
 __device__ __forceinline__ int b_swz(int k) {
-  if constexpr (C::MF == 16) return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1));
-  else return 4 * (k & 3);
+  return 4 * (k & 3);
 }
 
 // Stores 8 consecutive outputs v of one row, columns gcol .. gcol+7 (those
