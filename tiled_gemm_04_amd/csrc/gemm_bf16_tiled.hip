@@ -112,13 +112,15 @@ __device__ __forceinline__ int a_swz(int r) {
   if constexpr (C::MF == 16 && C::A_CPR == 4) return (r & 3) ^ (3 * ((r >> 2) & 1)) ^ (2 * ((r >> 3) & 1));
   else return (r / (16 / C::A_CPR)) % C::A_CPR;
 }
-// XOR applied to the chunk index of B row k: the four K rows read together by
-// a transposed read land in four different 64-byte bank segments (measured
-// for the 16 x 16 x 32 reads too: other XORs of the row bits gave the same
-// 1.96-2.06 ns per ds_read_b64_tr_b16 per compute unit).
+// XOR applied to the chunk index of B row k.  The four K rows read together
+// by a transposed read land in four different 64-byte bank segments.  The
+// 16 x 16 x 32 kernel's reads also put rows k and k + 8 in one half-wave:
+// flipping chunk bit 1 with bit 3 of k moves those apart (SQ_LDS_BANK_CONFLICT
+// on the 4096^3 GEMM: 25 % of LDS-active cycles without it, 1.9 % with it).
 template <class C>
 __device__ __forceinline__ int b_swz(int k) {
-  return 4 * (k & 3);
+  if constexpr (C::MF == 16) return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1));
+  else return 4 * (k & 3);
 }
 
 // Stores 8 consecutive outputs v of one row, columns gcol .. gcol+7 (those
