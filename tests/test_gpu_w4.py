@@ -159,6 +159,21 @@ def test_w4_matches_int8_full_width(M):
     assert torch.equal(c4.contiguous().view(torch.uint8), c8.view(torch.uint8))
 
 
+def test_w4_stripe_beyond_2gib_rebuilds_windows_per_slice():
+    """Packed rows 32 MiB apart: a stripe of 128 byte rows (K = 256) spans
+    4.3 GB, past one buffer window, so the kernel builds a window per slice."""
+    dev = _dev()
+    M, N, K, ldq = 5, 600, 256, 1 << 25
+    assert (K // 2 - 1) * ldq >= 1 << 31
+    x, p0, s, b = _inputs(M, N, K, 35, dev, bias=True)
+    pbuf = torch.empty((K // 2) * ldq, dtype=torch.uint8, device=dev)
+    p = pbuf.view(K // 2, ldq)[:, :N]
+    p.copy_(p0)
+    _check(x, p, s, b, tg.EPI_BIAS, torch.float32, "rows 32 MiB apart")
+    del pbuf, p
+    torch.cuda.empty_cache()
+
+
 def test_w4_strided_and_unaligned():
     """X with row stride K + 3 starting one element into its buffer, packed
     Q with row stride N + 4 bytes starting 4 bytes in, C at an odd element

@@ -127,6 +127,22 @@ def test_w8_strided_and_unaligned():
     assert r["ok"], r
 
 
+def test_w8_stripe_beyond_2gib_rebuilds_windows_per_slice():
+    """A weight whose rows are 16 MiB apart: a stripe of 256 rows spans
+    4.3 GB, past what one buffer window can address, so the kernel builds a
+    window per slice instead of one for the whole stripe."""
+    dev = _dev()
+    M, N, K, ldq = 5, 600, 256, 1 << 24
+    assert (K - 1) * ldq >= 1 << 31
+    x, q0, s, b = _inputs(M, N, K, 34, dev, bias=True)
+    qbuf = torch.empty(K * ldq, dtype=torch.int8, device=dev)
+    q = qbuf.view(K, ldq)[:, :N]
+    q.copy_(q0)
+    _check(x, q, s, b, tg.EPI_BIAS, torch.float32, "rows 16 MiB apart")
+    del qbuf, q
+    torch.cuda.empty_cache()
+
+
 def test_w8_k_zero_is_epilogue_of_bias():
     dev = _dev()
     M, N = 3, 64
