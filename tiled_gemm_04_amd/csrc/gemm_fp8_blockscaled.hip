@@ -156,8 +156,10 @@ __device__ __forceinline__ void store_wave(const f32x4 (&acc)[FM][kFN], float* s
       if (row < p.M) {
         uint16_t* out = p.C + static_cast<int64_t>(row) * p.N + gcol;
         if (full_cols) {
-          *reinterpret_cast<u32x4*>(out) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                                                 pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+          // Written once, not read back: a non-temporal store.
+          __builtin_nontemporal_store(u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                            pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])},
+                                      reinterpret_cast<u32x4*>(out));
         } else if (gcol + 8 <= p.N) {
           // Row not 16-byte aligned (N % 8 != 0): one unaligned 16-byte store.
           *reinterpret_cast<u32x4_a2*>(out) = u32x4_a2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
