@@ -1,0 +1,106 @@
+"""The entry points inside a captured HIP graph (needs an MI355X).
+
+The library allocates nothing, issues no memset and never synchronises, so a
+sequence of its calls can be captured once and replayed.  The graph below
+holds the tiled bf16 GEMM with bias + tanh-GeLU, the small-M split-K with a
+caller workspace, the FP8 GEMM with its last round split in a workspace
+(whose arrival counters every call returns to zero) and the log-softmax LM
+head.  It is replayed four times with eager library calls and host
+synchronisations in between; every replay must reproduce the eager results
+bit for bit, which in turn are checked against the fp64 oracle.
+"""
+
+import pytest
+import torch
+
+import tiled_gemm_04_amd as tg
+import workloads as wl
+from oracle import gemm as og
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda")
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32).clone()
+
+
+def test_captured_sequence_replays_bit_for_bit():
+    dev = _dev()
+    print("[gpu] graph capture and replay", flush=True)
+    # tiled bf16 with bias + tanh-GeLU (several tiles, a ragged edge)
+    a1 = wl.bf16((600, 512), "normal", 1.0, 141, 1, dev)
+    b1 = wl.bf16((512, 700), "normal", 0.05, 141, 2, dev)
+    bias1 = wl.bf16((700,), "normal", 0.5, 141, 3, dev)
+    c1 = torch.empty(600, 700, dtype=torch.bfloat16, device=dev)
+    # small-M split-K in a caller workspace
+    a2 = wl.bf16((8, 4096), "normal", 1.0, 142, 1, dev)
+    b2 = wl.bf16((4096, 4096), "normal", 0.05, 142, 2, dev)
+    c2 = torch.empty(8, 4096, dtype=torch.float32, device=dev)
+    ws2 = torch.empty(tg.gemm_bf16_workspace_size(8, 4096, 4096), dtype=torch.uint8, device=dev)
+    assert ws2.numel() > 0
+    # FP8 with a split last round (counters at the head of the workspace)
+    qa, sa, qb, sb = wl.fp8_inputs(wl.WORKLOADS["fp8"], device=dev, M=600, N=700, K=2048)
+    c3 = torch.empty(600, 700, dtype=torch.bfloat16, device=dev)
+    ws3 = torch.zeros(tg.gemm_fp8_workspace_size(600, 700, 2048), dtype=torch.uint8, device=dev)
+    assert ws3.numel() > 0
+    # log-softmax LM head
+    x4 = wl.bf16((5, 1024), "normal", 1.0, 143, 1, dev)
+    w4 = wl.bf16((1024, 20000), "normal", 0.05, 143, 2, dev)
+    b4 = wl.bf16((20000,), "normal", 0.02, 143, 3, dev)
+    c4 = torch.empty(5, 20000, dtype=torch.float32, device=dev)
+    ws4 = torch.empty(tg.gemm_logsoftmax_workspace_size(5, 20000, tg.OUT_F32), dtype=torch.uint8, device=dev)
+
+    def calls():
+        tg.gemm_bf16(a1, b1, bias1, c1, epilogue=tg.EPI_BIAS_GELU_TANH)
+        tg.gemm_bf16_ex(a2, b2, None, c2, workspace=ws2)
+        tg.gemm_fp8_blockscaled_ex(qa, sa, qb, sb, c3, split_parts=0, workspace=ws3)
+        tg.gemm_bf16_logsoftmax(x4, w4, b4, c4, workspace=ws4)
+
+    outs = (c1, c2, c3, c4)
+    calls()
+    torch.cuda.synchronize()
+    eager = [_bits(c) for c in outs]
+
+    # The eager results against the oracle.
+    y, d = og.gemm_bf16_bits(wl.bits_u16(a1), wl.bits_u16(b1), wl.bits_u16(bias1), tg.EPI_BIAS_GELU_TANH)
+    assert og.compare(c1.float().cpu().double().numpy(), y, d, 8e-3)["ok"]
+    y, d = og.gemm_bf16_bits(wl.bits_u16(a2), wl.bits_u16(b2))
+    assert og.compare(c2.cpu().double().numpy(), y, d, 1e-5)["ok"]
+    y, d = og.gemm_fp8_blockscaled_bits(wl.bits_u8(qa), sa.cpu().numpy(), wl.bits_u8(qb), sb.cpu().numpy())
+    assert og.compare(c3.float().cpu().double().numpy(), y, d, 1.5e-2)["ok"]
+    out, dmax, lse = og.gemm_bf16_logsoftmax_bits(wl.bits_u16(x4), wl.bits_u16(w4), wl.bits_u16(b4))
+    assert og.compare(c4.cpu().double().numpy(), out, og.logsoftmax_bound(out, dmax, lse, "f32"), 1.0)["ok"]
+
+    # Capture (torch warms the stream up first; the library needs nothing).
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+
+    for replay in range(4):
+        for c in outs:
+            c.view(torch.uint8).fill_(0xFF)  # a fill kernel, outside the graph
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (c, ref) in enumerate(zip(outs, eager)):
+            assert torch.equal(_bits(c), ref), (replay, k)
+        # eager work between replays, on the same buffers
+        tg.gemm_bf16(a1, b1, None, c1)
+        tg.gemm_bf16_ex(a2, b2, None, c2, workspace=ws2)
+        torch.cuda.synchronize()
+    # the FP8 split left its counters at zero
+    cnt = ws3[: 4 * ((600 + 255) // 256) * ((700 + 255) // 256)].view(torch.int32)
+    assert int(cnt.abs().sum()) == 0
+    del graph
