@@ -367,6 +367,98 @@ __device__ __forceinline__ void store_wave_tile_q8(const f32x16 (&acc)[FM][FN], 
   }
 }
 
+// The quantising epilogue for the 16 x 16 accumulator layout (element e of
+// lane l of block (i, j) is row 16 i + l%16, column 16 j + 4 (l/16) + e):
+// the same two phases, each 16-row strip of the wave's tile going through
+// the wave's LDS strip as in store_wave_tile16.
+template <int EPI, int FM, int FN, int WN>
+__device__ __forceinline__ void store_wave_tile16_q8(const f32x4 (&acc)[FM][FN], float* strip,
+                                                     float* amax_tab, int lane, int wn, int trow0,
+                                                     int row0, int col0, const Bf16Args& p) {
+  constexpr int WTN = 16 * FN;
+  static_assert(WTN == 64, "a 128-column group must span a wave pair");
+  constexpr int PITCH = WTN + 4;
+  constexpr int LANES_PER_ROW = WTN / 8;
+  constexpr int ROWS_PER_PASS = kWave / LANES_PER_ROW;
+  constexpr int PASSES = 16 / ROWS_PER_PASS;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int erow = lane / LANES_PER_ROW;
+  const int ecol = 8 * (lane % LANES_PER_ROW);
+  const int gcol = col0 + ecol;
+  float bias[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bias[e] = 0.0f;
+    if constexpr (EPI != kEpiNone) {
+      if (gcol + e < p.N) bias[e] = bf16_bits_to_f32(p.bias[gcol + e]);
+    }
+  }
+  // Phase 1: rounded outputs (packed bf16 pairs) and per-row partial maxima.
+  u32x4 hv[FM][PASSES];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) *reinterpret_cast<f32x4*>(strip + l16 * PITCH + 16 * j + 4 * lq) = acc[i][j];
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int rr = erow + ROWS_PER_PASS * pass;
+      const float* src = strip + rr * PITCH + ecol;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = gcol + e < p.N ? apply_epilogue<EPI>(v[e], bias[e]) : 0.0f;
+      const u32x4 h = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                            pack_bf16x2(v[6], v[7])};
+      hv[i][pass] = h;
+      float m = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(h[d] << 16)));
+        m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(h[d] & 0xffff0000u)));
+      }
+#pragma unroll
+      for (int d = 1; d < LANES_PER_ROW; d <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, d, kWave));
+      if (lane % LANES_PER_ROW == 0) amax_tab[(trow0 + 16 * i + rr) * WN + wn] = m;
+    }
+  }
+  __syncthreads();
+  // Phase 2: the pair's maximum, scale, codes.
+  const int G = (p.N + 127) / 128;
+  uint8_t* const q = static_cast<uint8_t*>(p.C);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int rr = erow + ROWS_PER_PASS * pass;
+      const float* t = amax_tab + (trow0 + 16 * i + rr) * WN;
+      const float amax = __builtin_fmaxf(t[wn], t[wn ^ 1]);
+      const float scale = fp8q::group_scale(amax);
+      const u32x4 h = hv[i][pass];
+      float x[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        x[2 * d] = __uint_as_float(h[d] << 16);
+        x[2 * d + 1] = __uint_as_float(h[d] & 0xffff0000u);
+      }
+      const u32x2 codes = fp8q::codes8(x, scale);
+      const int row = row0 + 16 * i + rr;
+      if (row < p.M) {
+        uint8_t* out = q + static_cast<int64_t>(row) * p.ldc + gcol;
+        if (p.vec_c && gcol + 8 <= p.N) {
+          *reinterpret_cast<u32x2*>(out) = codes;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gcol + e < p.N) out[e] = static_cast<uint8_t>(codes[e / 4] >> (8 * (e % 4)));
+        }
+        if ((wn & 1) == 0 && ecol == 0 && col0 < p.N)
+          p.qscale[static_cast<int64_t>(row) * G + col0 / 128] = scale;
+      }
+    }
+  }
+}
+
 // Global -> LDS loads of one workgroup's A and B slices, shared by both MFMA
 // shapes.  A block i of a wave covers 16-byte slots S = 64*blk + lane; slot
 // S is chunk (S % A_CPR) ^ a_swz(row) of row S / A_CPR.  B likewise with
@@ -657,7 +749,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 // 16g + 4e + q supplies K rows 8g + e and 8g + 4 + e, columns 4q .. 4q+3).
 // The operands are swapped as in the 32 x 32 kernel, so element e of lane l
 // of block (i, j) is row 16 i + l%16, column 16 j + 4 (l/16) + e.
-template <class C, bool BT, int EPI, bool OUT_BF16>
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, int tiles_m,
                                                                   int tiles_n) {
   static_assert(C::MF == 16 && C::KS == 1, "one 16 x 16 x 32 step per slice");
@@ -805,8 +897,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, 
   lds_barrier();  // every wave is done with the operand stages
 
   static_assert(C::WAVES * 16 * (C::WTN + 4) * 4 <= C::LDS_BYTES, "epilogue strips fit in LDS");
-  store_wave_tile16<EPI, OUT_BF16, C::FM, C::FN>(acc, reinterpret_cast<float*>(smem) + wave * 16 * (C::WTN + 4),
-                                                 lane, m0 + wm * C::WTM, n0 + wn * C::WTN, p);
+  if constexpr (QUANT) {
+    static_assert((C::WAVES * 16 * (C::WTN + 4) + C::BM * C::WN) * 4 <= C::LDS_BYTES,
+                  "strips and the row-maximum table must fit in LDS");
+    store_wave_tile16_q8<EPI, C::FM, C::FN, C::WN>(
+        acc, reinterpret_cast<float*>(smem) + wave * 16 * (C::WTN + 4),
+        reinterpret_cast<float*>(smem) + C::WAVES * 16 * (C::WTN + 4), lane, wn, wm * C::WTM, m0 + wm * C::WTM,
+        n0 + wn * C::WTN, p);
+  } else {
+    store_wave_tile16<EPI, OUT_BF16, C::FM, C::FN>(acc, reinterpret_cast<float*>(smem) + wave * 16 * (C::WTN + 4),
+                                                   lane, m0 + wm * C::WTM, n0 + wn * C::WTN, p);
+  }
 }
 
 template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
@@ -814,8 +915,7 @@ hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
   const int tiles_n = (a.N + C::BN - 1) / C::BN;
   if constexpr (C::MF == 16) {
-    static_assert(!QUANT, "the quantising epilogue runs on the 32 x 32 kernel");
-    hipLaunchKernelGGL((tgemm_bf16_tiled16<C, BT, EPI, OUT_BF16>), dim3(tiles_m * tiles_n, a.batch),
+    hipLaunchKernelGGL((tgemm_bf16_tiled16<C, BT, EPI, OUT_BF16, QUANT>), dim3(tiles_m * tiles_n, a.batch),
                        dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   } else {
     hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16, QUANT>), dim3(tiles_m * tiles_n, a.batch),
@@ -852,8 +952,8 @@ hipError_t dispatch_epi(const Bf16Args& a, int epi, int out_bf16, hipStream_t s)
 // keeps 32 x 32 x 16 with 64-wide slices).
 using Cfg256x256 = Cfg<256, 256, 32, 5, 1, 4, 16, 16>;
 using Cfg256x128 = Cfg<256, 128, 64, 3>;
-// The quantising epilogue is written for the 32 x 32 accumulator layout.
-using Cfg256x256Q = Cfg<256, 256, 32, 4, 1, 4>;
+// The quantising epilogue on the 256 x 256 tile uses the same 16 x 16 kernel.
+using Cfg256x256Q = Cfg256x256;
 using Cfg256x128Q = Cfg<256, 128, 64, 3>;
 using Cfg128x128 = Cfg<128, 128, 64, 4>;
 
