@@ -4,9 +4,10 @@
 // "Chunking" and "Registers与Tensor Cores") maps onto CDNA4 as follows:
 //   * tiling -- each workgroup owns one BM x BN output tile and walks K in
 //     slices of BK; the waves split the tile 2 (along M) x WN (along N), each
-//     owning a (BM/2) x (BN/WN) block of 32 x 32 MFMA accumulator blocks held
-//     in registers (256 x 256: eight waves, two per SIMD, 128 x 64 each;
-//     the smaller tiles: four waves, 2 x 2);
+//     owning a (BM/2) x (BN/WN) block of MFMA accumulator blocks held in
+//     registers (256 x 256: eight waves, two per SIMD, 128 x 64 each, in
+//     16 x 16 blocks of v_mfma_f32_16x16x32_bf16; the smaller tiles: four
+//     waves, 2 x 2, in 32 x 32 blocks of v_mfma_f32_32x32x16_bf16);
 //   * global -> LDS -- 16-byte buffer loads write straight into LDS (no
 //     register staging, no LDS store instructions).  Each wave instruction
 //     fills one contiguous KiB of LDS, lane l owning bytes 16l .. 16l+15, so

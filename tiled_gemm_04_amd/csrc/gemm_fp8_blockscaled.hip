@@ -45,10 +45,10 @@
 // into P parts of whole scale groups, P = min(CUs / tiles, groups / 8, 8)
 // (DeepGEMM page, section 2.1: small grids leave compute units idle); a
 // caller may also force a split of the last round of a longer grid.  Every
-// part writes its fp32 partial tile to library scratch and bumps a per-tile
-// counter; the part that arrives last adds the partials in part order (the
-// same sum whatever the arrival order) and runs the epilogue.  No workgroup
-// ever waits for another.
+// part writes its fp32 partial tile to the caller's workspace and bumps a
+// per-tile counter there; the part that arrives last adds the partials in
+// part order (the same sum whatever the arrival order), resets the counter
+// and runs the epilogue.  No workgroup ever waits for another.
 //
 // Requirements (checked by the launcher, otherwise the general kernel runs):
 // K a multiple of 16 (whole 16-byte chunks of A along K) and per-lane byte
