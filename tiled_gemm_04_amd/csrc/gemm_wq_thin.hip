@@ -118,6 +118,26 @@ __device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, u
                : "memory", "m0");
 }
 
+// The 16- and 4-byte loads into LDS for a descriptor already made uniform
+// (uniform_words, once, before the slice loop), passed to the instruction
+// as scalar registers as it is.  A readfirstlane per load, as in the
+// helpers above, makes the compiler keep a loop-invariant descriptor in
+// vector registers and copy it back for every load (nine vector
+// instructions per slice here, about 3 % of the int8 head's time at 64
+// rows).
+__device__ __forceinline__ void buf_load16_lds_u(i32x4 window, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(window)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void buf_load4_lds_u(i32x4 window, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(window)
+               : "memory", "m0");
+}
+
 // int8 codes stream through registers (see wq_accumulate): one slice of
 // one wave in flight is its two 16-byte Q loads, its X load and its scale.
 constexpr int kRegSlices = 4;     // slices in flight per wave
@@ -241,9 +261,11 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
   // 5-8 % faster on the 4096 x 128256 heads).  Otherwise each slice builds
   // its own windows.
   const int64_t q_span = (q_rows - 1) * p.ldq + (p.N - n0);
-  const i32x4 wq_all = make_window_words(p.Q + n0, q_span);
-  const i32x4 wx_all = make_window_words(p.X, (static_cast<int64_t>(p.M - 1) * p.ldx + kend) * 2);
-  const i32x4 ws_all = make_window_words(p.S + n0, (static_cast<int64_t>(G - 1) * p.N + (p.N - n0)) * 4);
+  // Made uniform here, once: the loads below take them as scalar operands.
+  const i32x4 wq_all = uniform_words(make_window_words(p.Q + n0, q_span));
+  const i32x4 wx_all = uniform_words(make_window_words(p.X, (static_cast<int64_t>(p.M - 1) * p.ldx + kend) * 2));
+  const i32x4 ws_all =
+      uniform_words(make_window_words(p.S + n0, (static_cast<int64_t>(G - 1) * p.N + (p.N - n0)) * 4));
   const uint32_t q_step = static_cast<uint32_t>(kRows * p.ldq);  // Q bytes per slice
   const uint32_t s_step = static_cast<uint32_t>(p.N * 4);        // scale bytes per group
   const uint32_t s_lane = static_cast<uint32_t>((64 * wave + lane) * 4);
@@ -256,9 +278,9 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     if constexpr (WHOLE) {
       const uint32_t qo = static_cast<uint32_t>(t) * q_step;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) buf_load16_lds(wq_all, stage + (4 * wave + 2 * i) * kWRow, w_off[i] + qo);
-      buf_load16_lds(wx_all, stage + x_dst, (x_off + 2 * k0) | x_tail);
-      buf_load4_lds(ws_all, stage + kWStage + kXStage + 64 * wave * 4, s_lane + static_cast<uint32_t>(g) * s_step);
+      for (int i = 0; i < 2; ++i) buf_load16_lds_u(wq_all, stage + (4 * wave + 2 * i) * kWRow, w_off[i] + qo);
+      buf_load16_lds_u(wx_all, stage + x_dst, (x_off + 2 * k0) | x_tail);
+      buf_load4_lds_u(ws_all, stage + kWStage + kXStage + 64 * wave * 4, s_lane + static_cast<uint32_t>(g) * s_step);
     } else {
       const int64_t r0 = static_cast<int64_t>(t) * kRows;
       const i32x4 ww = make_window_words(p.Q + r0 * p.ldq + n0, (q_rows - r0 - 1) * p.ldq + (p.N - n0));
