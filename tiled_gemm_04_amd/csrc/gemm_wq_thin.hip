@@ -368,6 +368,13 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     // One slice's operand reads, conversions and MFMAs, and the group fold
     // when it ends a 128-row group or the range.  A slice at or past te (the
     // partner of an odd last slice of a pair) reads zeros and adds nothing.
+    // kZeroStart (int8 slices loaded straight into LDS): a group's first
+    // slice starts its MFMAs from a zero accumulator instead of the fold
+    // clearing the partial sums (one move per accumulator and group: 4-5 %
+    // of the int8 head's time at 64 rows).  The register-staged pipelines
+    // and int4 keep the clearing fold: there the second copy of the MFMA
+    // block costs registers (int4 split-K at 64 rows would spill).
+    constexpr bool kZeroStart = !WqStages<BITS, MB, SPLIT>::kRegisters && BITS == 8;
     auto process = [&](int t, int st) {
       const uint8_t* base = smem + st * kStage;
       constexpr int kSteps = kBK / 32;  // 16 x 16 x 32 MFMA steps per slice
@@ -393,13 +400,25 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
       // conversions, then one MFMA per few conversion instructions):
       // measured 2-5 % faster there; with three or four row blocks the
       // ordering alone did best.
+      auto mfmas = [&](auto zero_start) {
+        constexpr bool kZero = decltype(zero_start)::value;
 #pragma unroll
-      for (int j = 0; j < kFN; ++j)
+        for (int j = 0; j < kFN; ++j)
 #pragma unroll
-        for (int u = 0; u < kSteps; ++u)
+          for (int u = 0; u < kSteps; ++u)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fx[u][mb], part[mb][j], 0, 0, 0);
+            for (int mb = 0; mb < MB; ++mb)
+              part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fx[u][mb],
+                                                                    kZero && u == 0 ? f32x4{} : part[mb][j], 0, 0, 0);
+      };
+      if constexpr (kZeroStart) {
+        if (t % Sh::kSlicesPerGroup == 0 || t == tb)
+          mfmas(std::true_type{});
+        else
+          mfmas(std::false_type{});
+      } else {
+        mfmas(std::false_type{});
+      }
       if constexpr (MB == 2) {
         constexpr int kMfma = kSteps * MB * kFN;
         constexpr int kValuPerMfma = BITS == 8 ? 3 : 4;
@@ -411,7 +430,9 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
           __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU
         });
       }
-      if ((t % Sh::kSlicesPerGroup) == Sh::kSlicesPerGroup - 1 || t == te - 1) {
+      // (With kZeroStart the partial sums are not cleared, so a slice past
+      // te must not fold them again.)
+      if (((t % Sh::kSlicesPerGroup) == Sh::kSlicesPerGroup - 1 || t == te - 1) && (!kZeroStart || t < te)) {
         // End of a scale group: acc += s * partial, per column.
 #pragma unroll
         for (int j = 0; j < kFN; ++j) {
@@ -421,7 +442,7 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
           for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[mb][j][e] = __builtin_fmaf(part[mb][j][e], sc[e], acc[mb][j][e]);
-            part[mb][j] = f32x4{};
+            if constexpr (!kZeroStart) part[mb][j] = f32x4{};
           }
         }
       }
