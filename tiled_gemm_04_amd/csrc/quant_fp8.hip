@@ -55,9 +55,13 @@ __device__ __forceinline__ void load8(const uint16_t* row, int64_t c, int64_t nc
 }
 
 // Eight codes of one row starting at column c (columns >= ncols skipped).
+// The codes are written once and not read back by this kernel: whole 8-byte
+// stores carry the non-temporal hint (measured 4 % faster on the 1 x 128
+// quantiser and 12 % on the 128 x 128 one; the same hint on the loads made
+// both slower).
 __device__ __forceinline__ void store8(uint8_t* row, int64_t c, int64_t ncols, bool vec, u32x2 q) {
   if (vec && c + 8 <= ncols) {
-    *reinterpret_cast<u32x2*>(row + c) = q;
+    __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(row + c));
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
