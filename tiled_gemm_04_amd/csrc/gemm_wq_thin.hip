@@ -371,9 +371,10 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     // kZeroStart (int8 slices loaded straight into LDS): a group's first
     // slice starts its MFMAs from a zero accumulator instead of the fold
     // clearing the partial sums (one move per accumulator and group: 4-5 %
-    // of the int8 head's time at 64 rows).  The register-staged pipelines
-    // and int4 keep the clearing fold: there the second copy of the MFMA
-    // block costs registers (int4 split-K at 64 rows would spill).
+    // of the int8 head's time at 64 rows).  int4 and the register-staged
+    // pipelines keep the clearing fold: there the zero start measured
+    // slower (int4 3-5 %, also with the group's first slice known at
+    // compile time) or no faster.
     constexpr bool kZeroStart = !WqStages<BITS, MB, SPLIT>::kRegisters && BITS == 8;
     auto process = [&](int t, int st) {
       const uint8_t* base = smem + st * kStage;
