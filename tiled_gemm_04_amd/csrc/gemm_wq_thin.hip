@@ -32,9 +32,9 @@
 //     (lane i receives column i of 8 byte rows: the 8 K values one
 //     16 x 16 x 32 MFMA takes per lane for int8, those of two MFMAs for
 //     int4); every code becomes a bf16 exactly (a sign-extending byte to fp32
-//     conversion, then the upper half; int4 codes are first moved to the top
-//     nibble of their byte, which gives 16 q, and the 1/16 goes into the
-//     group scale);
+//     conversion, then the upper half; an int4 code goes through the 4-bit
+//     signed conversion, which gives q / 16, and the 16 goes into the group
+//     scale);
 //   * the MFMAs of a 128-row group accumulate sum_k x * q exactly as an fp32
 //     GEMM would; at the end of the group one FMA per accumulator folds it
 //     in with the column's scale, acc += s * partial -- the same grouped
@@ -174,18 +174,42 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(i32x2 codes) {
   return __builtin_bit_cast(bf16x8, u32x4{hi2(f[0], f[1]), hi2(f[2], f[3]), hi2(f[4], f[5]), hi2(f[6], f[7])});
 }
 
+// q / 16 for the 4-bit two's-complement code in bits 0-3 of byte E of v,
+// exactly: v_cvt_off_f32_i4 converts bits 0-3 of its operand that way, and
+// the SDWA byte select picks the byte in the same instruction (the compiler
+// would shift first; all 16 codes in all four bytes, low and shifted-down
+// high nibbles, checked on the GPU against q / 16).
+template <int E>
+__device__ __forceinline__ float nibble_q16(uint32_t v) {
+  float r;
+  if constexpr (E == 0)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(v));
+  if constexpr (E == 1)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
+  if constexpr (E == 2)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
+  if constexpr (E == 3)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
+  return r;
+}
+
 // Four bytes of int4 codes (byte e = K values 2e (low nibble), 2e + 1 (high
-// nibble)) as 8 bf16 holding 16 q, exactly: each nibble is moved to the top
-// of its byte, whose sign-extended value is then 16 times the code.
+// nibble)) as 8 bf16 holding q / 16, exactly: one conversion per code (the
+// high nibbles after one shift of the word), then the upper halves of two
+// fp32 words per permute -- 13 vector instructions per 8 codes (moving each
+// nibble to the top of its byte and converting the sign-extended byte, 16 q,
+// took 15; 2-4 % slower at M = 1 ... 32).
 __device__ __forceinline__ bf16x8 nibbles_to_bf16(uint32_t codes) {
-  const uint32_t lo = (codes << 4) & 0xf0f0f0f0u;
-  const uint32_t hi = codes & 0xf0f0f0f0u;
+  const uint32_t hi = codes >> 4;  // byte e's high nibble in its bits 0-3
   float f[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[2 * e] = static_cast<float>(static_cast<int8_t>(lo >> (8 * e)));
-    f[2 * e + 1] = static_cast<float>(static_cast<int8_t>(hi >> (8 * e)));
-  }
+  f[0] = nibble_q16<0>(codes);
+  f[1] = nibble_q16<0>(hi);
+  f[2] = nibble_q16<1>(codes);
+  f[3] = nibble_q16<1>(hi);
+  f[4] = nibble_q16<2>(codes);
+  f[5] = nibble_q16<2>(hi);
+  f[6] = nibble_q16<3>(codes);
+  f[7] = nibble_q16<3>(hi);
   auto hi2 = [](float a, float b) {
     return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
   };
@@ -356,8 +380,8 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
 #pragma unroll
   for (int u = 0; u < kBK / 32; ++u)
     x_rd[u] = kWStage + xrow * (kBK * 2) + (((4 * u + (lane >> 4)) ^ x_swz<BITS>(xrow)) * 16);
-  // int4 operands carry 16 q.
-  constexpr float kCodeScale = BITS == 8 ? 1.0f : 1.0f / 16.0f;
+  // int4 operands carry q / 16.
+  constexpr float kCodeScale = BITS == 8 ? 1.0f : 16.0f;
 
   if (te > tb) {
     f32x4 part[MB][kFN];  // sum over the current 128-row group of x * q
