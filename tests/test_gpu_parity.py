@@ -162,6 +162,34 @@ def test_strided_and_unaligned_operands():
     run_and_check_bf16(a2[:40], b2, None, tg.EPI_NONE, torch.bfloat16, tg.ALGO_THIN, label="unaligned thin")
 
 
+def test_tiled_weight_beyond_2gib_takes_slice_windows():
+    """A [K, N] weight whose rows are 4 MiB apart (row stride 2^21
+    elements): its K rows span 2.7 GB, more than one buffer window can
+    address, so the tiled kernels build a window per slice instead of one
+    over all of K.  Every tile shape (16 x 16 x 32 on 256 x 256, 32 x 32 x 16
+    on 256 x 128 and 128 x 128) matches the oracle and, bit for bit, the
+    same product with the weight packed (one window over all of K)."""
+    dev = _dev()
+    M, N, K, ldb = 300, 520, 640, 1 << 21
+    assert (K - 1) * ldb * 2 >= 1 << 31
+    a = _rand_bf16((M, K), 61, dev)
+    b0 = _rand_bf16((K, N), 62, dev, sigma=0.05)
+    bias = _rand_bf16((N,), 63, dev, sigma=0.5)
+    bbuf = torch.empty((K - 1) * ldb + N, dtype=torch.bfloat16, device=dev)
+    b = bbuf.as_strided((K, N), (ldb, 1))
+    b.copy_(b0)
+    for algo in (tg.ALGO_TILED_256x256, tg.ALGO_TILED_256x128, tg.ALGO_TILED_128x128):
+        run_and_check_bf16(a, b, bias, tg.EPI_BIAS_GELU_TANH, torch.bfloat16, algo, label=f"ldb=2^21 algo={algo}")
+        c_far = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        c_packed = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        tg.gemm_bf16_ex(a, b, bias, c_far, epilogue=tg.EPI_BIAS_GELU_TANH, algo=algo)
+        tg.gemm_bf16_ex(a, b0, bias, c_packed, epilogue=tg.EPI_BIAS_GELU_TANH, algo=algo)
+        torch.cuda.synchronize()
+        assert torch.equal(c_far.view(torch.int16), c_packed.view(torch.int16)), algo
+    del bbuf, b
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("algo", [tg.ALGO_TILED, tg.ALGO_THIN])
 def test_k_zero_is_bias_only(algo):
     dev = _dev()

@@ -221,6 +221,16 @@ __device__ __forceinline__ void buf_load16_lds(i32x4 window, uint32_t lds_base, 
                : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_words(window))
                : "memory", "m0");
 }
+// The same load for a descriptor already made uniform (uniform_words, once,
+// before a loop), passed to the instruction as scalar registers as it is.  A
+// readfirstlane per load makes the compiler keep a loop-invariant descriptor
+// in vector registers and copy it back for every load.
+__device__ __forceinline__ void buf_load16_lds_u(i32x4 window, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(window)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));

@@ -470,7 +470,11 @@ __device__ __forceinline__ void store_wave_tile16_q8(const f32x4 (&acc)[FM][FN],
 // B rows n0 .. N-1 from column k0), so bytes past M, N or K read as zeros;
 // the main loops step a pointer and a size by one slice per iteration
 // instead of recomputing them.
-template <class C, bool BT>
+// WHOLE (the launcher's choice when every offset of the call stays below
+// 2^31): one window per operand covers all of K, built and made uniform
+// once, and the slice's K offset rides in the per-lane offset.  Building two
+// windows per slice cost 4-7 % on the 4096^3 and FFN shapes.
+template <class C, bool BT, bool WHOLE>
 struct TileLoader {
   uint32_t a_goff[C::APW];
   int a_kc[C::APW];
@@ -518,21 +522,35 @@ struct TileLoader {
     b_size0 = BT ? (static_cast<int64_t>(p.N - n0 - 1) * p.ldb + p.K) * 2
                  : (static_cast<int64_t>(p.K - 1) * p.ldb + (p.N - n0)) * 2;
     b_step = BT ? int64_t{C::BK} : static_cast<int64_t>(C::BK) * p.ldb;
+    if constexpr (WHOLE) {
+      wa_all = uniform_words(make_window_words(a_base0, a_size0));
+      wb_all = uniform_words(make_window_words(b_base0, b_size0));
+    }
   }
+  i32x4 wa_all, wb_all;  // WHOLE: the operands' windows over all of K
   __device__ __forceinline__ i32x4 window_a(int k0) const {
-    return make_window_words(a_base0 + k0, a_size0 - 2 * k0);
+    if constexpr (WHOLE) return wa_all;
+    else return make_window_words(a_base0 + k0, a_size0 - 2 * k0);
   }
   __device__ __forceinline__ i32x4 window_b(int k0) const {
+    if constexpr (WHOLE) return wb_all;
     const int64_t e = BT ? int64_t{k0} : static_cast<int64_t>(k0) * ldb;
     return make_window_words(b_base0 + e, b_size0 - 2 * e);
   }
   __device__ __forceinline__ void issue_a(i32x4 w, int stage, int k0, int i) const {
-    const uint32_t off = a_goff[i] | (k0 + a_kc[i] < K ? 0u : kOutOfRange);
-    buf_load16_lds(w, smem_base + stage * C::STAGE + (wave * C::APW + i) * 1024, off);
+    const uint32_t lds = smem_base + stage * C::STAGE + (wave * C::APW + i) * 1024;
+    const uint32_t oor = k0 + a_kc[i] < K ? 0u : kOutOfRange;
+    if constexpr (WHOLE) buf_load16_lds_u(w, lds, (a_goff[i] + 2u * static_cast<uint32_t>(k0)) | oor);
+    else buf_load16_lds(w, lds, a_goff[i] | oor);
   }
   __device__ __forceinline__ void issue_b(i32x4 w, int stage, int k0, int i) const {
-    const uint32_t off = BT ? (b_goff[i] | (k0 + b_kc[i] < K ? 0u : kOutOfRange)) : b_goff[i];
-    buf_load16_lds(w, smem_base + stage * C::STAGE + C::A_STAGE + (wave * C::BPW + i) * 1024, off);
+    const uint32_t lds = smem_base + stage * C::STAGE + C::A_STAGE + (wave * C::BPW + i) * 1024;
+    const uint32_t oor = BT && k0 + b_kc[i] >= K ? kOutOfRange : 0u;
+    // [K, N]: a column past N keeps its out-of-range bit through the add
+    // (the sum stays below 2^32).
+    const uint32_t koff = 2u * static_cast<uint32_t>(k0) * (BT ? 1u : static_cast<uint32_t>(ldb));
+    if constexpr (WHOLE) buf_load16_lds_u(w, lds, (b_goff[i] + koff) | oor);
+    else buf_load16_lds(w, lds, b_goff[i] | oor);
   }
   // Slices 0 .. NS-2 into stages 0 .. NS-2 (past K the loads read zeros).
   __device__ __forceinline__ void prologue() const {
@@ -547,7 +565,7 @@ struct TileLoader {
   }
 };
 
-template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, bool WHOLE>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
                                                                 int tiles_n) {
   static_assert(C::MF == 32, "the 32 x 32 x 16 kernel");
@@ -575,7 +593,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 
   // ---- global -> LDS ----
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
-  const TileLoader<C, BT> ld(p, wave, lane, m0, n0, smem_base);
+  const TileLoader<C, BT, WHOLE> ld(p, wave, lane, m0, n0, smem_base);
 
   // ---- LDS -> registers ----
   const int lrow = lane & 31;
@@ -673,11 +691,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
     for (int t = 0; t < KT; ++t) {
       const int nxt = cur + 1 == C::NS ? 0 : cur + 1;
       const int kl = (t + C::NS - 1) * C::BK;
-      const i32x4 wa = make_window_words(a_ptr, a_left), wb = make_window_words(b_ptr, b_left);
-      a_ptr += C::BK;
-      a_left -= 2 * C::BK;
-      b_ptr += ld.b_step;
-      b_left -= 2 * ld.b_step;
+      i32x4 wa, wb;
+      if constexpr (WHOLE) {
+        wa = ld.wa_all;
+        wb = ld.wb_all;
+      } else {
+        wa = make_window_words(a_ptr, a_left);
+        wb = make_window_words(b_ptr, b_left);
+        a_ptr += C::BK;
+        a_left -= 2 * C::BK;
+        b_ptr += ld.b_step;
+        b_left -= 2 * ld.b_step;
+      }
       static_for<kSlots>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         constexpr int u = s / kQ;
@@ -750,7 +775,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 // 16g + 4e + q supplies K rows 8g + e and 8g + 4 + e, columns 4q .. 4q+3).
 // The operands are swapped as in the 32 x 32 kernel, so element e of lane l
 // of block (i, j) is row 16 i + l%16, column 16 j + 4 (l/16) + e.
-template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, bool WHOLE>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, int tiles_m,
                                                                   int tiles_n) {
   static_assert(C::MF == 16 && C::KS == 1, "one 16 x 16 x 32 step per slice");
@@ -776,7 +801,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, 
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{};
 
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
-  const TileLoader<C, BT> ld(p, wave, lane, m0, n0, smem_base);
+  const TileLoader<C, BT, WHOLE> ld(p, wave, lane, m0, n0, smem_base);
 
   // ---- LDS -> registers ----
   const int l16 = lane & 15, lq = lane >> 4;
@@ -850,11 +875,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, 
       constexpr int P = decltype(pc)::value;
       const int nxt = cur + 1 == C::NS ? 0 : cur + 1;
       const int kl = (t + C::NS - 1) * C::BK;
-      const i32x4 wa = make_window_words(a_ptr, a_left), wb = make_window_words(b_ptr, b_left);
-      a_ptr += C::BK;
-      a_left -= 2 * C::BK;
-      b_ptr += ld.b_step;
-      b_left -= 2 * ld.b_step;
+      i32x4 wa, wb;
+      if constexpr (WHOLE) {
+        wa = ld.wa_all;
+        wb = ld.wb_all;
+      } else {
+        wa = make_window_words(a_ptr, a_left);
+        wb = make_window_words(b_ptr, b_left);
+        a_ptr += C::BK;
+        a_left -= 2 * C::BK;
+        b_ptr += ld.b_step;
+        b_left -= 2 * ld.b_step;
+      }
       static_for<kSlots>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         constexpr int i = s / C::FN, j = s % C::FN;
@@ -911,18 +943,35 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, 
   }
 }
 
-template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
-hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
+// Whole-K windows fit when every per-lane offset of the call stays below
+// 2^31: a tile's rows of A plus K, and B's rows (all of K for [K, N], a
+// tile's for [N, K]), counting the slices the pipeline loads past K.
+template <class C, bool BT>
+bool whole_windows_ok(const Bf16Args& a) {
+  const int64_t kspan = int64_t{a.K} + int64_t{C::NS + 1} * C::BK;
+  const int64_t a_max = (int64_t{C::BM} * a.lda + kspan) * 2;
+  const int64_t b_max = BT ? (int64_t{C::BN} * a.ldb + kspan) * 2 : (kspan * a.ldb + C::BN) * 2;
+  return a_max < (int64_t{1} << 31) && b_max < (int64_t{1} << 31);
+}
+
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, bool WHOLE>
+hipError_t launch_cw(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
   const int tiles_n = (a.N + C::BN - 1) / C::BN;
   if constexpr (C::MF == 16) {
-    hipLaunchKernelGGL((tgemm_bf16_tiled16<C, BT, EPI, OUT_BF16, QUANT>), dim3(tiles_m * tiles_n, a.batch),
+    hipLaunchKernelGGL((tgemm_bf16_tiled16<C, BT, EPI, OUT_BF16, QUANT, WHOLE>), dim3(tiles_m * tiles_n, a.batch),
                        dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   } else {
-    hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16, QUANT>), dim3(tiles_m * tiles_n, a.batch),
+    hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16, QUANT, WHOLE>), dim3(tiles_m * tiles_n, a.batch),
                        dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   }
   return hipGetLastError();
+}
+
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
+hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
+  if (whole_windows_ok<C, BT>(a)) return launch_cw<C, BT, EPI, OUT_BF16, QUANT, true>(a, s);
+  return launch_cw<C, BT, EPI, OUT_BF16, QUANT, false>(a, s);
 }
 
 template <class C>

@@ -118,19 +118,11 @@ __device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, u
                : "memory", "m0");
 }
 
-// The 16- and 4-byte loads into LDS for a descriptor already made uniform
-// (uniform_words, once, before the slice loop), passed to the instruction
-// as scalar registers as it is.  A readfirstlane per load, as in the
-// helpers above, makes the compiler keep a loop-invariant descriptor in
-// vector registers and copy it back for every load (nine vector
-// instructions per slice here, about 3 % of the int8 head's time at 64
-// rows).
-__device__ __forceinline__ void buf_load16_lds_u(i32x4 window, uint32_t lds_base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(window)
-               : "memory", "m0");
-}
+// The 4-byte load for a descriptor already made uniform (as
+// buf_load16_lds_u): a readfirstlane per load made the compiler keep the
+// loop-invariant descriptors in vector registers and copy them back for
+// every load (nine vector instructions per slice here, about 3 % of the int8
+// head's time at 64 rows).
 __device__ __forceinline__ void buf_load4_lds_u(i32x4 window, uint32_t lds_base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
