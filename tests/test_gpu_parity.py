@@ -290,6 +290,35 @@ def test_fp8_integer_codes_exact():
     assert torch.equal(c.cpu().float(), exact.float().to(torch.bfloat16).float())
 
 
+def test_fp8_wide_weight_takes_slice_windows():
+    """A [K, N] FP8 weight of 1.9 GB (K = 2048, N = 917504): its per-lane
+    offsets over all of K pass 2^31, so the kernel builds windows per slice
+    instead of one over all of K.  The weight repeats one random 1024-column
+    block (and its scales) 896 times, so every 1024-column block of the
+    output must equal, bit for bit, the product with that one block -- which
+    takes the whole-K windows and is checked against the oracle."""
+    dev = _dev()
+    M, K, n_small, reps = 256, 2048, 1024, 896
+    N = n_small * reps
+    assert (K + 384) * N >= 1 << 31
+    qa, sa, qb, sb = wl.fp8_inputs(wl.WORKLOADS["fp8"], device=dev, M=M, N=n_small, K=K)
+    c_small = torch.empty(M, n_small, dtype=torch.bfloat16, device=dev)
+    tg.gemm_fp8_blockscaled(qa, sa, qb, sb, c_small)
+    torch.cuda.synchronize()
+    y, d = og.gemm_fp8_blockscaled_bits(wl.bits_u8(qa), sa.cpu().numpy(), wl.bits_u8(qb), sb.cpu().numpy())
+    assert og.compare(c_small.float().cpu().double().numpy(), y, d, TOL_FP8)["ok"]
+    qb_big = qb.view(torch.uint8).repeat(1, reps).view(torch.float8_e4m3fn)
+    sb_big = sb.repeat(1, reps).contiguous()
+    c_big = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    print(f"[gpu] fp8 wide weight M={M} N={N} K={K}", flush=True)
+    tg.gemm_fp8_blockscaled(qa, sa, qb_big, sb_big, c_big)
+    torch.cuda.synchronize()
+    blocks = c_big.view(torch.int16).view(M, reps, n_small)
+    assert bool((blocks == c_small.view(torch.int16).unsqueeze(1)).all())
+    del qb_big, c_big, blocks
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------- full workloads ----
 
 def _tile_rows(M, tile=256, block=32, seed=93):

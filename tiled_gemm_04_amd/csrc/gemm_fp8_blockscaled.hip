@@ -129,6 +129,13 @@ __device__ __forceinline__ void buf_load4_lds(i32x4 window, uint32_t lds_base, u
                : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_words(window))
                : "memory", "m0");
 }
+// The same for a descriptor already made uniform (as buf_load16_lds_u).
+__device__ __forceinline__ void buf_load4_lds_u(i32x4 window, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(window)
+               : "memory", "m0");
+}
 
 // Stores a wave's kFMxkFN blocks of 16 x 16 accumulators (rows row0 + 16 i
 // + l%16, columns col0 + 16 j + 4 (l/16) + e) as bf16, through a 16-row
@@ -225,8 +232,15 @@ struct SplitTail {
 // operands carry the same bytes as the [K, N] path's transposed reads.
 // KFULL: K is a multiple of 128, so every slice inside K is whole and the
 // loads need no per-lane column check (measured 1-2 % faster); slices past
-// K get an empty buffer window instead.
-template <bool BT, bool KFULL>
+// K read zeros through an out-of-range offset (A and a [N, K] B) or by
+// lying past the window ([K, N] B).
+// WHOLE (the launcher's choice when every offset of the call stays below
+// 2^31): one window per operand and one for the tile's A scales cover all of
+// K, built and made uniform once, and each slice's K offset rides in the
+// per-lane offset, instead of three windows built per slice (1 % on the
+// median, 3 % on the mean of the 4096 x 14336 x 4096 calls).  Otherwise the
+// windows of slice g start at its K offset and end past K.
+template <bool BT, bool KFULL, bool WHOLE>
 __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args p, int tiles_m,
                                                                      int tiles_n, SplitTail st) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
@@ -306,8 +320,16 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
                                        : static_cast<int64_t>(p.K - 1) * p.N + (p.N - n0));
   const int64_t wstep = a_like ? int64_t{kBK} : int64_t{kBK} * p.N;
   const uint32_t blk_stride = a_like ? 8u * p.K : 4u * p.N;  // bytes per block of rows
+  i32x4 w_all{}, sa_all{};
+  if constexpr (WHOLE) {
+    w_all = uniform_words(make_window_words(win0, wsize0));
+    sa_all = uniform_words(make_window_words(p.sA + static_cast<int64_t>(m0) * p.G,
+                                             static_cast<int64_t>(p.M - m0) * p.G * 4));
+  }
+  const uint32_t wstep32 = static_cast<uint32_t>(wstep);
   auto window = [&](int g) {
-    if constexpr (KFULL) return make_window_words(win0 + g * wstep, g < p.G ? wsize0 - g * wstep : 0);
+    if constexpr (WHOLE) return w_all;
+    else if constexpr (KFULL) return make_window_words(win0 + g * wstep, g < p.G ? wsize0 - g * wstep : 0);
     else return make_window_words(win0 + g * wstep, wsize0 - g * wstep);
   };
   // Waves 0-3 also fetch the scale column sA[m0 + 64*wave + lane, g].
@@ -325,13 +347,22 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   // zeros: their windows are empty past K) so the schedule needs no branch.
   auto issue = [&](i32x4 w, int g, int i) {
     uint32_t off = vo[i & 1] + off0 + static_cast<uint32_t>(i) * blk_stride;
+    if constexpr (WHOLE) off += static_cast<uint32_t>(g) * wstep32;  // keeps a column's out-of-range bit
     if constexpr (!KFULL) off |= g * kBK + kc[i & 1] < p.K ? 0u : kOutOfRange;
-    buf_load16_lds(w, dst0 + static_cast<uint32_t>((g & 1) * kStage + i * 1024), off);
+    else if (WHOLE && a_like) off |= g < p.G ? 0u : kOutOfRange;
+    const uint32_t lds = dst0 + static_cast<uint32_t>((g & 1) * kStage + i * 1024);
+    if constexpr (WHOLE) buf_load16_lds_u(w, lds, off);
+    else buf_load16_lds(w, lds, off);
   };
   auto issue_scales = [&](int g) {
     if (loads_a) {
-      const i32x4 w = make_window_words(p.sA + static_cast<int64_t>(m0) * p.G + g, g < p.G ? sa_size : 0);
-      buf_load4_lds(w, ssa_base + ((g & 1) * kBM + 64 * wave) * 4, sa_off);
+      const uint32_t lds = ssa_base + ((g & 1) * kBM + 64 * wave) * 4;
+      if constexpr (WHOLE) {
+        buf_load4_lds_u(sa_all, lds, (sa_off + 4u * static_cast<uint32_t>(g)) | (g < p.G ? 0u : kOutOfRange));
+      } else {
+        const i32x4 w = make_window_words(p.sA + static_cast<int64_t>(m0) * p.G + g, g < p.G ? sa_size : 0);
+        buf_load4_lds(w, lds, sa_off);
+      }
     }
   };
   // The tile holding column N-1 adds the products that the range check
@@ -603,6 +634,27 @@ size_t fp8_split_part_bytes(const Fp8Split& plan) {
   return static_cast<size_t>(plan.split_tiles) * plan.parts * kBM * kBN * sizeof(float);
 }
 
+// Whole-K windows fit when every per-lane offset stays below 2^31: a
+// tile's 256 rows of A (or of a [N, K] B) plus the slice offsets up to two
+// slices past K, or for a [K, N] B all of its rows up to three slices past
+// K.
+static bool fp8_whole_windows_ok(const Fp8Args& a) {
+  const int64_t lim = int64_t{1} << 31;
+  const int64_t rows = (int64_t{kBM} + 1) * a.K + 4 * kBK;  // A, and B given as [N, K]
+  if (rows >= lim) return false;
+  return a.bt || (static_cast<int64_t>(a.K) + 3 * kBK) * a.N + 4 * kBK < lim;
+}
+
+template <bool BT, bool KFULL>
+static hipError_t launch_fp8_w(const Fp8Args& a, bool whole, dim3 grid, int tiles_m, int tiles_n,
+                               const SplitTail& st, hipStream_t s) {
+  if (whole)
+    hipLaunchKernelGGL((tgemm_fp8_bs_256x256x128<BT, KFULL, true>), grid, dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
+  else
+    hipLaunchKernelGGL((tgemm_fp8_bs_256x256x128<BT, KFULL, false>), grid, dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* part, uint32_t* count,
                                   hipStream_t s) {
   if (a.bt && !fp8_nt_ok(a.M, a.N, a.K)) return hipErrorInvalidValue;
@@ -620,18 +672,13 @@ hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* 
   }
   const dim3 grid(st.whole + st.split_tiles * st.parts);
   const bool kfull = a.K % kBK == 0;
+  const bool whole = fp8_whole_windows_ok(a);
   if (a.bt) {
-    if (kfull)
-      hipLaunchKernelGGL((tgemm_fp8_bs_256x256x128<true, true>), grid, dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
-    else
-      hipLaunchKernelGGL((tgemm_fp8_bs_256x256x128<true, false>), grid, dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
-  } else {
-    if (kfull)
-      hipLaunchKernelGGL((tgemm_fp8_bs_256x256x128<false, true>), grid, dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
-    else
-      hipLaunchKernelGGL((tgemm_fp8_bs_256x256x128<false, false>), grid, dim3(kThreads), 0, s, a, tiles_m, tiles_n, st);
+    if (kfull) return launch_fp8_w<true, true>(a, whole, grid, tiles_m, tiles_n, st, s);
+    return launch_fp8_w<true, false>(a, whole, grid, tiles_m, tiles_n, st, s);
   }
-  return hipGetLastError();
+  if (kfull) return launch_fp8_w<false, true>(a, whole, grid, tiles_m, tiles_n, st, s);
+  return launch_fp8_w<false, false>(a, whole, grid, tiles_m, tiles_n, st, s);
 }
 
 }  // namespace tgemm
