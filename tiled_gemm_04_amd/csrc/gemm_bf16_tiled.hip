@@ -470,12 +470,20 @@ __device__ __forceinline__ void store_wave_tile16_q8(const f32x4 (&acc)[FM][FN],
 // B rows n0 .. N-1 from column k0), so bytes past M, N or K read as zeros;
 // the main loops step a pointer and a size by one slice per iteration
 // instead of recomputing them.
-// WHOLE (the launcher's choice when every offset of the call stays below
-// 2^31): one window per operand covers all of K, built and made uniform
-// once, and the slice's K offset rides in the per-lane offset.  Building two
-// windows per slice cost 4-7 % on the 4096^3 and FFN shapes.
-template <class C, bool BT, bool WHOLE>
+// WIN, the launcher's choice of windows:
+//   kWinSlice -- the windows of each slice, as above, with a per-lane check
+//                of the chunk's K columns;
+//   kWinWhole -- when every offset of the call stays below 2^31 and K is a
+//                multiple of BK: one window per operand covers all of K,
+//                built and made uniform once, and the slice's K offset rides
+//                in the per-lane offset (building two windows per slice cost
+//                4-7 % on the 4096^3 and FFN shapes); a slice lies wholly
+//                inside K or wholly past it, so the K check is one uniform
+//                compare instead of one per lane (2-3 % more).
+constexpr int kWinSlice = 0, kWinWhole = 1;
+template <class C, bool BT, int WIN>
 struct TileLoader {
+  static constexpr bool WHOLE = WIN == kWinWhole;
   uint32_t a_goff[C::APW];
   int a_kc[C::APW];
   uint32_t b_goff[C::BPW];
@@ -539,13 +547,13 @@ struct TileLoader {
   }
   __device__ __forceinline__ void issue_a(i32x4 w, int stage, int k0, int i) const {
     const uint32_t lds = smem_base + stage * C::STAGE + (wave * C::APW + i) * 1024;
-    const uint32_t oor = k0 + a_kc[i] < K ? 0u : kOutOfRange;
+    const uint32_t oor = (WHOLE ? k0 < K : k0 + a_kc[i] < K) ? 0u : kOutOfRange;
     if constexpr (WHOLE) buf_load16_lds_u(w, lds, (a_goff[i] + 2u * static_cast<uint32_t>(k0)) | oor);
     else buf_load16_lds(w, lds, a_goff[i] | oor);
   }
   __device__ __forceinline__ void issue_b(i32x4 w, int stage, int k0, int i) const {
     const uint32_t lds = smem_base + stage * C::STAGE + C::A_STAGE + (wave * C::BPW + i) * 1024;
-    const uint32_t oor = BT && k0 + b_kc[i] >= K ? kOutOfRange : 0u;
+    const uint32_t oor = BT && (WHOLE ? k0 >= K : k0 + b_kc[i] >= K) ? kOutOfRange : 0u;
     // [K, N]: a column past N keeps its out-of-range bit through the add
     // (the sum stays below 2^32).
     const uint32_t koff = 2u * static_cast<uint32_t>(k0) * (BT ? 1u : static_cast<uint32_t>(ldb));
@@ -565,7 +573,7 @@ struct TileLoader {
   }
 };
 
-template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, bool WHOLE>
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, int WIN>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, int tiles_m,
                                                                 int tiles_n) {
   static_assert(C::MF == 32, "the 32 x 32 x 16 kernel");
@@ -593,7 +601,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 
   // ---- global -> LDS ----
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
-  const TileLoader<C, BT, WHOLE> ld(p, wave, lane, m0, n0, smem_base);
+  const TileLoader<C, BT, WIN> ld(p, wave, lane, m0, n0, smem_base);
 
   // ---- LDS -> registers ----
   const int lrow = lane & 31;
@@ -692,7 +700,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
       const int nxt = cur + 1 == C::NS ? 0 : cur + 1;
       const int kl = (t + C::NS - 1) * C::BK;
       i32x4 wa, wb;
-      if constexpr (WHOLE) {
+      if constexpr (WIN == kWinWhole) {
         wa = ld.wa_all;
         wb = ld.wb_all;
       } else {
@@ -775,7 +783,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled(Bf16Args p, in
 // 16g + 4e + q supplies K rows 8g + e and 8g + 4 + e, columns 4q .. 4q+3).
 // The operands are swapped as in the 32 x 32 kernel, so element e of lane l
 // of block (i, j) is row 16 i + l%16, column 16 j + 4 (l/16) + e.
-template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, bool WHOLE>
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, int WIN>
 __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, int tiles_m,
                                                                   int tiles_n) {
   static_assert(C::MF == 16 && C::KS == 1, "one 16 x 16 x 32 step per slice");
@@ -801,7 +809,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, 
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{};
 
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(TGEMM_LDS(uint8_t, smem)));
-  const TileLoader<C, BT, WHOLE> ld(p, wave, lane, m0, n0, smem_base);
+  const TileLoader<C, BT, WIN> ld(p, wave, lane, m0, n0, smem_base);
 
   // ---- LDS -> registers ----
   const int l16 = lane & 15, lq = lane >> 4;
@@ -876,7 +884,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void tgemm_bf16_tiled16(Bf16Args p, 
       const int nxt = cur + 1 == C::NS ? 0 : cur + 1;
       const int kl = (t + C::NS - 1) * C::BK;
       i32x4 wa, wb;
-      if constexpr (WHOLE) {
+      if constexpr (WIN == kWinWhole) {
         wa = ld.wa_all;
         wb = ld.wb_all;
       } else {
@@ -954,15 +962,15 @@ bool whole_windows_ok(const Bf16Args& a) {
   return a_max < (int64_t{1} << 31) && b_max < (int64_t{1} << 31);
 }
 
-template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, bool WHOLE>
+template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT, int WIN>
 hipError_t launch_cw(const Bf16Args& a, hipStream_t s) {
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
   const int tiles_n = (a.N + C::BN - 1) / C::BN;
   if constexpr (C::MF == 16) {
-    hipLaunchKernelGGL((tgemm_bf16_tiled16<C, BT, EPI, OUT_BF16, QUANT, WHOLE>), dim3(tiles_m * tiles_n, a.batch),
+    hipLaunchKernelGGL((tgemm_bf16_tiled16<C, BT, EPI, OUT_BF16, QUANT, WIN>), dim3(tiles_m * tiles_n, a.batch),
                        dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   } else {
-    hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16, QUANT, WHOLE>), dim3(tiles_m * tiles_n, a.batch),
+    hipLaunchKernelGGL((tgemm_bf16_tiled<C, BT, EPI, OUT_BF16, QUANT, WIN>), dim3(tiles_m * tiles_n, a.batch),
                        dim3(C::THREADS), 0, s, a, tiles_m, tiles_n);
   }
   return hipGetLastError();
@@ -970,8 +978,8 @@ hipError_t launch_cw(const Bf16Args& a, hipStream_t s) {
 
 template <class C, bool BT, int EPI, bool OUT_BF16, bool QUANT = false>
 hipError_t launch_c(const Bf16Args& a, hipStream_t s) {
-  if (whole_windows_ok<C, BT>(a)) return launch_cw<C, BT, EPI, OUT_BF16, QUANT, true>(a, s);
-  return launch_cw<C, BT, EPI, OUT_BF16, QUANT, false>(a, s);
+  if (whole_windows_ok<C, BT>(a) && a.K % C::BK == 0) return launch_cw<C, BT, EPI, OUT_BF16, QUANT, kWinWhole>(a, s);
+  return launch_cw<C, BT, EPI, OUT_BF16, QUANT, kWinSlice>(a, s);
 }
 
 template <class C>
