@@ -26,7 +26,12 @@ Also reported in the same line:
                 single-thread time on the 64^3 workload (rank 0, one GPU only);
   secondary     the other workloads (FFN pair, thin-M LM head at M = 1, 8,
                 32, 64, FP8 block-scaled and its ragged variant, ...), each
-                timed the same way with its own roofline figure;
+                timed the same way with its own roofline figure, after at
+                least SECONDARY_WARM_MS of untimed back-to-back calls (the
+                first tens of milliseconds of calls after the idle gap in
+                which a workload's inputs are built run at lower clocks: on
+                MI355X the first 20 FP8 calls averaged 276 us, those after
+                the first hundred 224 us, on the same buffers);
   probes        reference rates of this machine (MFMA-only loops on random
                 register operands, a streaming read), informational only.
 """
@@ -50,6 +55,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "GEMM TFLOPS & % MFMA peak (bf16/fp8); HBM GB/s % peak on thin-M LM head"
 PROFILES = os.path.join(ROOT, "profiles")
+SECONDARY_WARM_MS = 50.0    # untimed back-to-back calls before a secondary's timing
 
 
 def parse():
@@ -395,8 +401,12 @@ class Case:
         self.dtype = "bf16->fp8_e4m3"
         self.inputs_for_oracle = None
 
-    def time(self, steps, warmup, clocks=False):
+    def time(self, steps, warmup, clocks=False, warm_ms=0.0):
         """Timing of `steps` back-to-back calls after `warmup` untimed ones.
+
+        warm_ms > 0: after those, untimed calls continue in batches of ten
+        until warm_ms of wall-clock time has passed, so that the timing
+        starts from the clocks of sustained load.
 
         The timed region (bracketed by two synchronisations) enqueues the
         calls with one pair of HIP events around all of them on the launch
@@ -415,6 +425,12 @@ class Case:
         for _ in range(warmup):
             self.launch()
         torch.cuda.synchronize()
+        if warm_ms > 0:
+            t_warm = time.perf_counter()
+            while (time.perf_counter() - t_warm) * 1e3 < warm_ms:
+                for _ in range(10):
+                    self.launch()
+                torch.cuda.synchronize()
         region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         samples, stop = [], threading.Event()
 
@@ -695,7 +711,7 @@ def main():
             if name == args.workload:
                 continue
             c = Case(name, dev)
-            tc = c.time(args.secondary_steps, 5)
+            tc = c.time(args.secondary_steps, 5, warm_ms=SECONDARY_WARM_MS)
             r = c.roofline(tc)
             sec[name] = {"ms_per_call": round(tc["ms_per_step"], 5),
                          "kernel_ms_mean": r["kernel_ms_mean"], "kernel_ms_median": r["kernel_ms_median"],
