@@ -256,9 +256,12 @@ int gemm_bf16_noalloc(const void* A, const void* B, const void* bias, void* C,
  *   C    bf16 [M, N], packed row-major
  *
  * Dequantised value = decode(code) * scale.  Scales must be finite; NaN
- * codes (0x7F, 0xFF) propagate to the outputs they touch.  Every tile runs
- * whole (gemm_fp8_blockscaled_ex with a workspace splits small grids along
- * K).  Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
+ * codes (0x7F, 0xFF) propagate to the outputs they touch.  Output tiles
+ * are 256 x 256; when the last round of tiles would occupy at most half of
+ * the compute units (one tile per unit), each of its tiles runs as two
+ * 128-row halves over all of K, which gives bit-identical results
+ * (gemm_fp8_blockscaled_ex with a workspace splits small grids along K
+ * instead).  Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
  */
 int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const float* sB,
                          void* C, int64_t M, int64_t N, int64_t K, void* stream);
@@ -278,10 +281,12 @@ int gemm_fp8_blockscaled(const void* A, const float* sA, const void* B, const fl
  *   split_parts      0: automatic (only when the tiles would keep at most a
  *                    quarter of the compute units busy: P = compute units /
  *                    tiles, at most 8, at least eight scale groups per range;
- *                    measured on MI355X, a fuller grid runs faster unsplit);
- *                    1: never split; 2 .. 8: split the last round's tiles
- *                    into that many ranges (at most one per scale group),
- *                    whatever the grid
+ *                    measured on MI355X, a fuller grid runs faster unsplit;
+ *                    otherwise the 128-row halves of gemm_fp8_blockscaled);
+ *                    1: never split, whole 256 x 256 tiles only (no halves
+ *                    either); 2 .. 8: split the last round's tiles into that
+ *                    many ranges (at most one per scale group), whatever the
+ *                    grid
  *   workspace        NULL (never split) or device memory of at least
  *                    gemm_fp8_workspace_size(M, N, K, split_parts) bytes,
  *                    16-byte aligned, owned by the caller.  Layout: one

@@ -292,7 +292,8 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
 
     A: float8_e4m3fn [M, K] contiguous; sA: float32 [M, ceil(K/128)] contiguous;
     B: float8_e4m3fn [K, N] contiguous; sB: float32 [ceil(K/128), ceil(N/128)];
-    C: bfloat16 [M, N] contiguous.  Every tile runs whole.
+    C: bfloat16 [M, N] contiguous.  A sparse last round of 256 x 256 tiles
+    runs as 128-row halves (bit-identical); never split along K.
     """
     M, N, K = _fp8_operands(A, sA, B, sB, C)
     st = lib().gemm_fp8_blockscaled(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
@@ -303,8 +304,9 @@ def gemm_fp8_blockscaled(A, sA, B, sB, C, stream=None):
 
 
 def gemm_fp8_blockscaled_ex(A, sA, B, sB, C, split_parts=0, workspace=None, stream=None):
-    """gemm_fp8_blockscaled_ex of the C ABI: split_parts 0 automatic, 1 never,
-    2..8 K ranges per tile of the last round; workspace None (never split)
+    """gemm_fp8_blockscaled_ex of the C ABI: split_parts 0 automatic, 1 never
+    (whole 256 x 256 tiles only), 2..8 K ranges per tile of the last round;
+    workspace None (never split along K)
     or a zero-initialised device tensor of at least
     gemm_fp8_workspace_size(M, N, K, split_parts) bytes (its arrival counters
     are left zero by every call, so it can be reused as is)."""

@@ -288,7 +288,8 @@ int fp8_call(const void* A, const float* sA, const void* B, const float* sB, voi
     count = static_cast<uint32_t*>(workspace);
     part = static_cast<char*>(workspace) + fp8_counter_bytes(plan);
   }
-  const hipError_t e = tgemm::launch_fp8_blockscaled(a, plan, part, count, s);
+  // Automatic mode also cuts a sparse last round of tiles into halves.
+  const hipError_t e = tgemm::launch_fp8_blockscaled(a, plan, part, count, split_parts == 0, s);
   return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_LAUNCH;
 }
 

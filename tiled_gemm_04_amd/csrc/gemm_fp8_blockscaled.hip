@@ -40,15 +40,19 @@
 //     loads of slice g+2 start right after that barrier (every wave is done
 //     with the stage) and finish early in slice g+1, one per slot.
 //
-// Tile scheduler: when the tiles would keep at most a quarter of the
-// compute units busy (one workgroup per unit), each tile is split along K
-// into P parts of whole scale groups, P = min(CUs / tiles, groups / 8, 8)
-// (DeepGEMM page, section 2.1: small grids leave compute units idle); a
-// caller may also force a split of the last round of a longer grid.  Every
-// part writes its fp32 partial tile to the caller's workspace and bumps a
-// per-tile counter there; the part that arrives last adds the partials in
-// part order (the same sum whatever the arrival order), resets the counter
-// and runs the epilogue.  No workgroup ever waits for another.
+// Tile scheduler (DeepGEMM page, section 2.1: a grid too small for the
+// machine leaves compute units idle).  Without a workspace, a last round of
+// tiles that would occupy at most half of the compute units (one workgroup
+// per unit) runs as two 128-row halves per tile, each over all of K: the
+// same MFMAs and folds per output element, so the result is bit-identical,
+// with twice as many units at work.  With a caller workspace, when the
+// tiles would keep at most a quarter of the units busy, each tile is split
+// along K instead into P parts of whole scale groups, P = min(CUs / tiles,
+// groups / 8, 8); a caller may also force a split of the last round of a
+// longer grid.  Every part writes its fp32 partial tile to the workspace
+// and bumps a per-tile counter there; the part that arrives last adds the
+// partials in part order (the same sum whatever the arrival order), resets
+// the counter and runs the epilogue.  No workgroup ever waits for another.
 //
 // Requirements (checked by the launcher, otherwise the general kernel runs):
 // K a multiple of 16 (whole 16-byte chunks of A along K) and per-lane byte
@@ -68,14 +72,10 @@ constexpr int kThreads = 512;
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 128;  // bytes of K per slice == one scale group
-constexpr int kWTM = 128;  // wave tile: 2 (M) x 4 (N) waves
-constexpr int kWTN = 64;
-constexpr int kFM = kWTM / 16;
+constexpr int kWTN = 64;   // wave tile columns: 2 (M) x 4 (N) waves
 constexpr int kFN = kWTN / 16;
-constexpr int kAStage = kBM * kBK;
 constexpr int kBStage = kBK * kBN;
-constexpr int kStage = kAStage + kBStage;
-constexpr int kBlocksPerWave = kStage / 1024 / 8;  // 1 KiB direct loads per wave and slice
+constexpr int kBBlocks = kBStage / 1024 / 4;  // 1 KiB direct B loads per B wave (4-7) and slice
 constexpr int kGroupM = 4;
 constexpr int kScaleOne = 127;  // E8M0 exponent of 1.0
 constexpr int kFmtE4M3 = 0;     // f8f6f4 operand format code for FP8 E4M3
@@ -84,13 +84,28 @@ constexpr int kEpiPitch = kWTN + 4;  // floats per row of the epilogue strip
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
 static_assert(128 % kWTN == 0, "a wave's columns must sit inside one 128-column scale block");
-static_assert(kAStage / 1024 == 4 * kBlocksPerWave, "waves 0-3 load A, waves 4-7 load B");
+constexpr int kEarly = 4;  // loads of slice g+2 issued after the barrier of slice g
 
-// Slot schedule of one slice (slot s runs MFMA (s / kFN, s % kFN)).
-constexpr int kSlots = kFM * kFN;
-constexpr int kBar = kSlots - kFN;  // barrier before the last row
-constexpr int kEarly = 4;           // loads of slice g+2 issued after the barrier of slice g
-static_assert(kBar + kEarly <= kSlots && kBlocksPerWave - kEarly <= kBar, "load slots");
+// Per tile height: a whole tile of kBM = 256 rows, or one of the two 128-row
+// halves a tail tile is cut into (see SplitTail).  The waves stay 2 (M) x 4
+// (N), each owning kWTM x 64 outputs; waves 0-3 load A (kABlocks blocks of
+// 1 KiB per slice), waves 4-7 load B (kBBlocks).  Slot schedule of one slice:
+// slot s runs MFMA (s / kFN, s % kFN).
+template <int BM>
+struct Fp8Shape {
+  static constexpr int kBM = BM;
+  static constexpr int kWTM = BM / 2;
+  static constexpr int kFM = kWTM / 16;
+  static constexpr int kAStage = BM * kBK;
+  static constexpr int kStage = kAStage + kBStage;
+  static constexpr int kABlocks = kAStage / 1024 / 4;
+  static constexpr int kSlots = kFM * kFN;
+  static constexpr int kBar = kSlots - kFN;  // barrier before the last row
+  static_assert(kBar + kEarly <= kSlots && kBBlocks - kEarly <= kBar && kABlocks >= kEarly &&
+                    kABlocks <= kBBlocks,
+                "load slots");
+};
+using Fp8Whole = Fp8Shape<kBM>;
 
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 #define TGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -216,15 +231,21 @@ __device__ __forceinline__ void add_tail_products(f32x4 (&acc)[FM][kFN], const F
 }
 
 // Work split of one launch: workgroups [0, whole) own whole tiles (logical
-// tiles 0 .. whole-1); the next split_tiles * parts workgroups own part q of
-// logical tile whole + t.  part: parts * split_tiles partial tiles of
-// kBM * kBN fp32; count: split_tiles counters, zero between calls.
+// tiles 0 .. whole-1).  Then either (halves > 0) the next 2 * halves
+// workgroups own the 128-row halves of logical tiles whole .. whole +
+// halves - 1 (two per tile, over all of K: the last round of tiles fills
+// twice as many compute units, and every output element sees the same MFMAs
+// and folds in the same order, so the result is bit-identical), or the next
+// split_tiles * parts workgroups own part q of logical tile whole + t.
+// part: parts * split_tiles partial tiles of kBM * kBN fp32; count:
+// split_tiles counters, zero between calls.
 struct SplitTail {
   int whole;
   int split_tiles;
   int parts;
   f32x4* part;
   uint32_t* count;
+  int halves;
 };
 
 // BT: B given as [N, K] (K-contiguous rows, the nn.Linear weight layout);
@@ -240,36 +261,27 @@ struct SplitTail {
 // per-lane offset, instead of three windows built per slice (1 % on the
 // median, 3 % on the mean of the 4096 x 14336 x 4096 calls).  Otherwise the
 // windows of slice g start at its K offset and end past K.
-template <bool BT, bool KFULL, bool WHOLE>
-__global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args p, int tiles_m,
-                                                                     int tiles_n, SplitTail st) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
-  __shared__ __attribute__((aligned(256))) float s_sa[2][kBM];
-  __shared__ int s_last;
-
+// One workgroup's share: the BM rows m0 .. of the 256 columns n0 .. (a
+// whole tile or a half, Fp8Shape), over scale groups [g0, g1) -- part kpart
+// of `parts` of logical tile `logical` when parts > 1.
+template <int BM, bool BT, bool KFULL, bool WHOLE>
+__device__ __forceinline__ void fp8_tile(const Fp8Args& p, const SplitTail& st, int logical, int kpart,
+                                         int parts, int m0, int n0, uint8_t* smem, float (*s_sa)[kBM],
+                                         int* s_last) {
+  using T = Fp8Shape<BM>;
+  constexpr int kFM = T::kFM;
+  constexpr int kWTM = T::kWTM;
+  constexpr int kAStage = T::kAStage;
+  constexpr int kStage = T::kStage;
+  constexpr int kSlots = T::kSlots;
+  constexpr int kBar = T::kBar;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2;
   const int wn = wave & 3;
-
-  // Tile and K range (whole scale groups [g0, g1)) of this workgroup.
-  int logical, kpart = 0;
-  const int bid = blockIdx.x;
-  if (bid < st.whole) {
-    logical = xcd_remap(bid, st.whole);
-  } else {
-    const int r = xcd_remap(bid - st.whole, st.split_tiles * st.parts);
-    logical = st.whole + r / st.parts;
-    kpart = r % st.parts;
-  }
-  const int parts = bid < st.whole ? 1 : st.parts;
   const int g0 = static_cast<int>(static_cast<int64_t>(p.G) * kpart / parts);
   const int g1 = static_cast<int>(static_cast<int64_t>(p.G) * (kpart + 1) / parts);
-  int tm, tn;
-  tile_coords(logical, tiles_m, tiles_n, kGroupM, tm, tn);
-  const int m0 = tm * kBM;
-  const int n0 = tn * kBN;
   const int hb = (n0 + wn * kWTN) / 128;  // this wave's B-scale column
 
   // acc[i][j]: 16 x 16 block, transposed by the operand swap: element e of
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   // (slot % chunks-per-row) ^ swizzle(row) of its row. ----
   const bool loads_a = wave < 4;
   const bool a_like = loads_a || BT;  // rows are K-contiguous, 8 per block
-  const int blk0 = (wave & 3) * kBlocksPerWave;
+  const int blk0 = (wave & 3) * (loads_a ? T::kABlocks : kBBlocks);
   // A block blk (rows 8 blk .. +7): slot 64 blk + lane is row 8 blk + lane/8,
   // physical chunk lane % 8, logical chunk (lane % 8) ^ a_swz(row), and
   // a_swz(row) = (lane/8) ^ (blk & 1) takes two forms by the parity of blk.
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     else if constexpr (KFULL) return make_window_words(win0 + g * wstep, g < p.G ? wsize0 - g * wstep : 0);
     else return make_window_words(win0 + g * wstep, wsize0 - g * wstep);
   };
-  // Waves 0-3 also fetch the scale column sA[m0 + 64*wave + lane, g].
+  // Waves 0 .. BM/64 - 1 also fetch the scale column sA[m0 + 64*wave + lane, g].
   const uint32_t sa_off = static_cast<uint32_t>((64 * (wave & 3) + lane) * p.G * 4);
   const int64_t sa_size = (static_cast<int64_t>(p.M - m0 - 1) * p.G + 1) * 4;
   // A loads past K read zeros: kc is the chunk's first column for A waves
@@ -355,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     else buf_load16_lds(w, lds, off);
   };
   auto issue_scales = [&](int g) {
-    if (loads_a) {
+    if (wave < BM / 64) {
       const uint32_t lds = ssa_base + ((g & 1) * kBM + 64 * wave) * 4;
       if constexpr (WHOLE) {
         buf_load4_lds_u(sa_all, lds, (sa_off + 4u * static_cast<uint32_t>(g)) | (g < p.G ? 0u : kOutOfRange));
@@ -448,7 +460,8 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
     {
       const i32x4 w = window(g0);
 #pragma unroll
-      for (int i = 0; i < kBlocksPerWave; ++i) issue(w, g0, i);
+      for (int i = 0; i < kBBlocks; ++i)
+        if (i < T::kABlocks || !loads_a) issue(w, g0, i);
       issue_scales(g0);
     }
     if (g1 - g0 > 1) {
@@ -510,8 +523,10 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
         }
         // Global -> LDS: blocks kEarly.. of slice g+1 in the first slots,
         // blocks 0 .. kEarly-1 of slice g+2 right after the barrier.
-        if constexpr (s < kBlocksPerWave - kEarly) issue(w1, g + 1, kEarly + s);
-        if constexpr (s == kBlocksPerWave - kEarly) issue_scales(g + 1);
+        if constexpr (s < kBBlocks - kEarly) {
+          if (kEarly + s < T::kABlocks || !loads_a) issue(w1, g + 1, kEarly + s);
+        }
+        if constexpr (s == kBBlocks - kEarly) issue_scales(g + 1);
         if constexpr (s >= kBar && s < kBar + kEarly) issue(w2, g + 2, s - kBar);
       });
       TGEMM_SCHED_FENCE();
@@ -526,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  if (parts > 1) {
+  if (BM == kBM && parts > 1) {
     // Publish this part's fp32 partial tile (lane-contiguous 16-byte
     // stores), then count the parts that are done; only the last one goes on.
     const int t = logical - st.whole;
@@ -548,10 +563,10 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
       const int last = done + 1 == static_cast<uint32_t>(parts);
       // The last part resets the counter for the next call.
       if (last) __hip_atomic_store(st.count + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
+      *s_last = last;
     }
     __syncthreads();  // thread 0's acquire (cache invalidation) precedes every wave's reads
-    if (!s_last) return;
+    if (!*s_last) return;
     // Sum in part order, ((P0 + P1) + P2) + ..., all read back from the
     // scratch (this part's own as well), so the bits do not depend on which
     // part came last.
@@ -578,6 +593,41 @@ __global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args 
   // ---- epilogue ----
   store_wave(acc, reinterpret_cast<float*>(smem) + wave * 16 * kEpiPitch, lane, m0 + wm * kWTM,
              n0 + wn * kWTN, p);
+}
+
+template <bool BT, bool KFULL, bool WHOLE>
+__global__ __launch_bounds__(kThreads, 1) void tgemm_fp8_bs_256x256x128(Fp8Args p, int tiles_m,
+                                                                     int tiles_n, SplitTail st) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Fp8Whole::kStage];
+  __shared__ __attribute__((aligned(256))) float s_sa[2][kBM];
+  __shared__ int s_last;
+
+  // Tile, tile half and K range of this workgroup (SplitTail).
+  const int bid = blockIdx.x;
+  int logical, kpart = 0, parts = 1, half = -1;
+  if (bid < st.whole) {
+    logical = xcd_remap(bid, st.whole);
+  } else if (st.halves > 0) {
+    const int r = xcd_remap(bid - st.whole, 2 * st.halves);
+    logical = st.whole + r / 2;
+    half = r & 1;
+  } else {
+    const int r = xcd_remap(bid - st.whole, st.split_tiles * st.parts);
+    logical = st.whole + r / st.parts;
+    kpart = r % st.parts;
+    parts = st.parts;
+  }
+  int tm, tn;
+  tile_coords(logical, tiles_m, tiles_n, kGroupM, tm, tn);
+  const int n0 = tn * kBN;
+  if (half < 0) {
+    fp8_tile<kBM, BT, KFULL, WHOLE>(p, st, logical, kpart, parts, tm * kBM, n0, smem, s_sa, &s_last);
+  } else {
+    // A tile row of at most 128 rows (the last, when M % 256 <= 128) has
+    // nothing in its second half: that workgroup ends at once.
+    const int m0 = tm * kBM + half * (kBM / 2);
+    if (m0 < p.M) fp8_tile<kBM / 2, BT, KFULL, WHOLE>(p, st, logical, 0, 1, m0, n0, smem, s_sa, &s_last);
+  }
 }
 
 
@@ -655,22 +705,35 @@ static hipError_t launch_fp8_w(const Fp8Args& a, bool whole, dim3 grid, int tile
   return hipGetLastError();
 }
 
+int fp8_tail_halves(int64_t tiles, int cus) {
+  if (cus <= 0 || tiles <= 0) return 0;
+  const int64_t left = tiles - (tiles - 1) / cus * cus;  // tiles of the last round
+  return 2 * left <= cus ? static_cast<int>(left) : 0;
+}
+
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* part, uint32_t* count,
-                                  hipStream_t s) {
+                                  bool halves, hipStream_t s) {
   if (a.bt && !fp8_nt_ok(a.M, a.N, a.K)) return hipErrorInvalidValue;
   if (!a.bt && !fp8_direct_ok(a.M, a.N, a.K)) return launch_fp8_general(a, s);
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.N + kBN - 1) / kBN;
-  SplitTail st{tiles_m * tiles_n, 0, 1, nullptr, nullptr};
-  if (plan.parts > 1 && part != nullptr && count != nullptr &&
-      plan.whole + plan.split_tiles == tiles_m * tiles_n) {
+  const int tiles = tiles_m * tiles_n;
+  SplitTail st{tiles, 0, 1, nullptr, nullptr, 0};
+  if (plan.parts > 1 && part != nullptr && count != nullptr && plan.whole + plan.split_tiles == tiles) {
     st.whole = plan.whole;
     st.split_tiles = plan.split_tiles;
     st.parts = plan.parts;
     st.part = static_cast<f32x4*>(part);
     st.count = count;
+  } else if (halves) {
+    // A last round of whole tiles that would leave at least half of the
+    // compute units idle runs as twice as many 128-row halves instead (the
+    // 4096 x 14336 grid's 3.5 rounds become 3 + one full round of halves:
+    // 4.6 % faster on MI355X; grids of 64 or 128 tiles 22-26 %).
+    st.halves = fp8_tail_halves(tiles, device_cus());
+    st.whole = tiles - st.halves;
   }
-  const dim3 grid(st.whole + st.split_tiles * st.parts);
+  const dim3 grid(st.whole + (st.halves > 0 ? 2 * st.halves : st.split_tiles * st.parts));
   const bool kfull = a.K % kBK == 0;
   const bool whole = fp8_whole_windows_ok(a);
   if (a.bt) {

@@ -154,8 +154,13 @@ Fp8Split fp8_split_plan(int64_t M, int64_t N, int64_t K, int cus, int forced_par
 size_t fp8_split_part_bytes(const Fp8Split& plan);
 // part: fp8_split_part_bytes(plan) of workspace; count: plan.split_tiles
 // counters that are zero on entry (and again on exit).  Either NULL: no split.
+// halves (without a split): the last round's tiles run as 128-row halves
+// when fp8_tail_halves says so (bit-identical results).
 hipError_t launch_fp8_blockscaled(const Fp8Args& a, const Fp8Split& plan, void* part,
-                                  uint32_t* count, hipStream_t stream);
+                                  uint32_t* count, bool halves, hipStream_t stream);
+// Tiles of the last round that run as two 128-row halves each: all of them
+// when they would occupy at most half of `cus` compute units, else none.
+int fp8_tail_halves(int64_t tiles, int cus);
 // Register-staged kernel for FP8 operands the direct-to-LDS kernel cannot take.
 hipError_t launch_fp8_general(const Fp8Args& a, hipStream_t stream);
 
