@@ -166,6 +166,16 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(i32x2 codes) {
   return __builtin_bit_cast(bf16x8, u32x4{hi2(f[0], f[1]), hi2(f[2], f[3]), hi2(f[4], f[5]), hi2(f[6], f[7])});
 }
 
+// Output word o (codes 2o, 2o+1 as two bf16) of codes_to_bf16: two
+// conversions and one permute.
+template <int O>
+__device__ __forceinline__ uint32_t codes_pair_bf16(i32x2 codes) {
+  const uint32_t w = static_cast<uint32_t>(codes[O >> 1]);
+  const float a = static_cast<float>(static_cast<int8_t>(w >> (8 * ((2 * O) & 3))));
+  const float b = static_cast<float>(static_cast<int8_t>(w >> (8 * ((2 * O + 1) & 3))));
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
 // q / 16 for the 4-bit two's-complement code in bits 0-3 of byte E of v,
 // exactly: v_cvt_off_f32_i4 converts bits 0-3 of its operand that way, and
 // the SDWA byte select picks the byte in the same instruction (the compiler
@@ -392,49 +402,88 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     // slower (int4 3-5 %, also with the group's first slice known at
     // compile time) or no faster.
     constexpr bool kZeroStart = !WqStages<BITS, MB, SPLIT>::kRegisters && BITS == 8;
-    auto process = [&](int t, int st) {
+    // pos: the slice's place in its group when known at compile time (the
+    // group-unrolled loop below), -1 when it follows from t.
+    auto process = [&](int t, int st, auto pos) {
+      constexpr int kPos = decltype(pos)::value;
       const uint8_t* base = smem + st * kStage;
       constexpr int kSteps = kBK / 32;  // 16 x 16 x 32 MFMA steps per slice
       bf16x8 fb[kSteps][kFN], fx[kSteps][MB];
+      if constexpr (BITS == 8 && MB >= 3 && kPos >= 0) {
+        // int8 with three or four row blocks, slices straight into LDS: the
+        // MFMAs and the conversions are interleaved by hand (fenced, one
+        // output word of the next column block after each MFMA), since the
+        // compiler otherwise converts all four blocks first and issues the
+        // sixteen MFMAs in one burst (5-6 % of the 64-row head's time).
+        i32x2 qc[kFN];
 #pragma unroll
-      for (int j = 0; j < kFN; ++j) {
-        const i32x2 q = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
-        if constexpr (BITS == 8) {
-          fb[0][j] = codes_to_bf16(q);
-        } else {
-          fb[0][j] = nibbles_to_bf16(static_cast<uint32_t>(q[0]));
-          fb[1][j] = nibbles_to_bf16(static_cast<uint32_t>(q[1]));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kSteps; ++u)
+        for (int j = 0; j < kFN; ++j) qc[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          fx[u][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[u] + mb * Sh::kXBlock));
-      // Column block by column block, so that the conversions of block j+1
-      // can run beside the MFMAs of block j.  With two row blocks the
-      // scheduler is also asked to interleave them (operand reads, block 0's
-      // conversions, then one MFMA per few conversion instructions):
-      // measured 2-5 % faster there; with three or four row blocks the
-      // ordering alone did best.
-      auto mfmas = [&](auto zero_start) {
-        constexpr bool kZero = decltype(zero_start)::value;
-#pragma unroll
-        for (int j = 0; j < kFN; ++j)
-#pragma unroll
-          for (int u = 0; u < kSteps; ++u)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fx[u][mb],
-                                                                    kZero && u == 0 ? f32x4{} : part[mb][j], 0, 0, 0);
-      };
-      if constexpr (kZeroStart) {
-        if (t % Sh::kSlicesPerGroup == 0 || t == tb)
-          mfmas(std::true_type{});
-        else
-          mfmas(std::false_type{});
+          fx[0][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[0] + mb * Sh::kXBlock));
+        u32x4 fw[kFN];
+        fw[0] = u32x4{codes_pair_bf16<0>(qc[0]), codes_pair_bf16<1>(qc[0]), codes_pair_bf16<2>(qc[0]),
+                      codes_pair_bf16<3>(qc[0])};
+        static_for<kFN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          static_for<MB>([&](auto mc) {
+            constexpr int mb = decltype(mc)::value;
+            TGEMM_SCHED_FENCE();
+            part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[j]), fx[0][mb],
+                                                                  kPos == 0 ? f32x4{} : part[mb][j], 0, 0, 0);
+            if constexpr (j + 1 < kFN) {
+              // Word o of block j+1 after MFMA min(o, MB-1) of block j.
+              static_for<4>([&](auto oc) {
+                constexpr int o = decltype(oc)::value;
+                if constexpr ((o < MB - 1 ? o : MB - 1) == mb) fw[j + 1][o] = codes_pair_bf16<o>(qc[j + 1]);
+              });
+            }
+          });
+        });
+        TGEMM_SCHED_FENCE();
       } else {
-        mfmas(std::false_type{});
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) {
+          const i32x2 q = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
+          if constexpr (BITS == 8) {
+            fb[0][j] = codes_to_bf16(q);
+          } else {
+            fb[0][j] = nibbles_to_bf16(static_cast<uint32_t>(q[0]));
+            fb[1][j] = nibbles_to_bf16(static_cast<uint32_t>(q[1]));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            fx[u][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[u] + mb * Sh::kXBlock));
+        // Column block by column block, so that the conversions of block j+1
+        // can run beside the MFMAs of block j.  With two row blocks the
+        // scheduler is also asked to interleave them (operand reads, block 0's
+        // conversions, then one MFMA per few conversion instructions):
+        // measured 2-5 % faster there; with three or four row blocks (int4,
+        // or int8 through registers) the ordering alone did best.
+        auto mfmas = [&](auto zero_start) {
+          constexpr bool kZero = decltype(zero_start)::value;
+#pragma unroll
+          for (int j = 0; j < kFN; ++j)
+#pragma unroll
+            for (int u = 0; u < kSteps; ++u)
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb)
+                part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fx[u][mb],
+                                                                      kZero && u == 0 ? f32x4{} : part[mb][j], 0, 0, 0);
+        };
+        if constexpr (kZeroStart && kPos >= 0) {
+          mfmas(std::integral_constant<bool, kPos == 0>{});
+        } else if constexpr (kZeroStart) {
+          if (t % Sh::kSlicesPerGroup == 0 || t == tb)
+            mfmas(std::true_type{});
+          else
+            mfmas(std::false_type{});
+        } else {
+          mfmas(std::false_type{});
+        }
       }
       if constexpr (MB == 2) {
         constexpr int kMfma = kSteps * MB * kFN;
@@ -449,7 +498,12 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
       }
       // (With kZeroStart the partial sums are not cleared, so a slice past
       // te must not fold them again.)
-      if (((t % Sh::kSlicesPerGroup) == Sh::kSlicesPerGroup - 1 || t == te - 1) && (!kZeroStart || t < te)) {
+      bool fold_now;
+      if constexpr (kPos >= 0)
+        fold_now = kPos == Sh::kSlicesPerGroup - 1 || t == te - 1;
+      else
+        fold_now = ((t % Sh::kSlicesPerGroup) == Sh::kSlicesPerGroup - 1 || t == te - 1) && (!kZeroStart || t < te);
+      if (fold_now) {
         // End of a scale group: acc += s * partial, per column.
 #pragma unroll
         for (int j = 0; j < kFN; ++j) {
@@ -474,7 +528,7 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
         store_regs(t, r);
         load_regs(t + R, r);
         lds_barrier();
-        process(t, t % NS);
+        process(t, t % NS, std::integral_constant<int, -1>{});
       };
       WqRegs r[R];
 #pragma unroll
@@ -498,19 +552,41 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
       lds_barrier();
       int si = kAhead, sp = 0;
-      for (int t = tb; t < te; t += kPerBar) {
-#pragma unroll
-        for (int h = 0; h < kPerBar; ++h) {
-          issue_slice(t + kAhead + h, si);
-          si = si + 1 == NS ? 0 : si + 1;
+      if constexpr (kZeroStart && kPerBar == 1) {
+        // One scale group per iteration (ranges start on a group boundary),
+        // so each slice's place in its group -- zero start, fold -- is known
+        // at compile time and its conversions and MFMAs form one block of
+        // straight-line code; only a partial last group checks te.
+        constexpr int kSpg = Sh::kSlicesPerGroup;
+        for (int t0 = tb; t0 < te; t0 += kSpg) {
+          static_for<kSpg>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            const int t = t0 + u;
+            if (u == 0 || t < te) {
+              issue_slice(t + kAhead, si);
+              si = si + 1 == NS ? 0 : si + 1;
+              process(t, sp, std::integral_constant<int, u>{});
+              sp = sp + 1 == NS ? 0 : sp + 1;
+              asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * kLoadsPerSlice) : "memory");
+              lds_barrier();  // the next slice landed everywhere; this one is no longer read
+            }
+          });
         }
+      } else {
+        for (int t = tb; t < te; t += kPerBar) {
 #pragma unroll
-        for (int h = 0; h < kPerBar; ++h) {
-          process(t + h, sp);
-          sp = sp + 1 == NS ? 0 : sp + 1;
+          for (int h = 0; h < kPerBar; ++h) {
+            issue_slice(t + kAhead + h, si);
+            si = si + 1 == NS ? 0 : si + 1;
+          }
+#pragma unroll
+          for (int h = 0; h < kPerBar; ++h) {
+            process(t + h, sp, std::integral_constant<int, -1>{});
+            sp = sp + 1 == NS ? 0 : sp + 1;
+          }
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
+          lds_barrier();  // the next slices landed everywhere; these are no longer read
         }
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - kPerBar) * kLoadsPerSlice) : "memory");
-        lds_barrier();  // the next slices landed everywhere; these are no longer read
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads past K still land in LDS
     }
