@@ -218,6 +218,16 @@ __device__ __forceinline__ bf16x8 nibbles_to_bf16(uint32_t codes) {
   return __builtin_bit_cast(bf16x8, u32x4{hi2(f[0], f[1]), hi2(f[2], f[3]), hi2(f[4], f[5]), hi2(f[6], f[7])});
 }
 
+// Words 2H and 2H+1 of nibbles_to_bf16(codes) (hi = codes >> 4): four
+// conversions and two permutes.
+template <int H>
+__device__ __forceinline__ u32x2 nibble_words(uint32_t codes, uint32_t hi) {
+  const float f0 = nibble_q16<2 * H>(codes), f1 = nibble_q16<2 * H>(hi);
+  const float f2 = nibble_q16<2 * H + 1>(codes), f3 = nibble_q16<2 * H + 1>(hi);
+  return u32x2{__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u),
+               __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u)};
+}
+
 // Streams the workgroup's 512-column stripe of Q once and leaves the scaled
 // products in acc[mb][j] (16 x 16 blocks, transposed by the operand swap:
 // element e of lane l is row 16*mb + l%16, column 16*j + 4*(l/16) + e of the
@@ -409,7 +419,49 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
       const uint8_t* base = smem + st * kStage;
       constexpr int kSteps = kBK / 32;  // 16 x 16 x 32 MFMA steps per slice
       bf16x8 fb[kSteps][kFN], fx[kSteps][MB];
-      if constexpr (BITS == 8 && MB >= 3 && kPos >= 0) {
+      if constexpr (BITS == 4) {
+        // int4: the two conversions of column block j+1 (four parts of two
+        // output words each) spread over the 2 MB MFMAs of block j, fenced
+        // so the compiler keeps them there (4-6 % at 1-32 rows, neutral at
+        // 64, bit-identical).
+        i32x2 qc[kFN];
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) qc[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            fx[u][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[u] + mb * Sh::kXBlock));
+        u32x4 fw[kFN][2];
+        uint32_t hic[kFN][2];
+        auto conv_part = [&](auto jc, auto pc) {  // part p of block j: step p/2, words 2(p%2), +1
+          constexpr int j = decltype(jc)::value, pp = decltype(pc)::value;
+          constexpr int u = pp / 2, h = pp % 2;
+          const uint32_t c = static_cast<uint32_t>(qc[j][u]);
+          if constexpr (h == 0) hic[j][u] = c >> 4;
+          const u32x2 w = nibble_words<h>(c, hic[j][u]);
+          fw[j][u][2 * h] = w[0];
+          fw[j][u][2 * h + 1] = w[1];
+        };
+        static_for<4>([&](auto pc) { conv_part(std::integral_constant<int, 0>{}, pc); });
+        static_for<kFN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          static_for<kSteps * MB>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int u = i / MB, mb = i % MB;
+            TGEMM_SCHED_FENCE();
+            part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[j][u]), fx[u][mb],
+                                                                  part[mb][j], 0, 0, 0);
+            if constexpr (j + 1 < kFN) {
+              static_for<4>([&](auto pc) {
+                constexpr int pp = decltype(pc)::value;
+                if constexpr (pp * kSteps * MB / 4 == i) conv_part(std::integral_constant<int, j + 1>{}, pc);
+              });
+            }
+          });
+        });
+        TGEMM_SCHED_FENCE();
+      } else if constexpr (BITS == 8 && MB >= 3 && kPos >= 0) {
         // int8 with three or four row blocks, slices straight into LDS: the
         // MFMAs and the conversions are interleaved by hand (fenced, one
         // output word of the next column block after each MFMA), since the
@@ -457,12 +509,12 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             fx[u][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[u] + mb * Sh::kXBlock));
-        // Column block by column block, so that the conversions of block j+1
-        // can run beside the MFMAs of block j.  With two row blocks the
-        // scheduler is also asked to interleave them (operand reads, block 0's
-        // conversions, then one MFMA per few conversion instructions):
-        // measured 2-5 % faster there; with three or four row blocks (int4,
-        // or int8 through registers) the ordering alone did best.
+        // int8 otherwise: column block by column block, so that the
+        // conversions of block j+1 can run beside the MFMAs of block j.  With
+        // two row blocks the scheduler is also asked to interleave them
+        // (operand reads, block 0's conversions, then one MFMA per few
+        // conversion instructions): measured 2-5 % faster there; with three
+        // row blocks through registers the ordering alone did best.
         auto mfmas = [&](auto zero_start) {
           constexpr bool kZero = decltype(zero_start)::value;
 #pragma unroll
@@ -485,10 +537,10 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
           mfmas(std::false_type{});
         }
       }
-      if constexpr (MB == 2) {
+      if constexpr (MB == 2 && BITS == 8) {
         constexpr int kMfma = kSteps * MB * kFN;
-        constexpr int kValuPerMfma = BITS == 8 ? 3 : 4;
-        constexpr int kFirstBlockValu = BITS == 8 ? 12 : 30;  // one block's conversions
+        constexpr int kValuPerMfma = 3;
+        constexpr int kFirstBlockValu = 12;  // one block's conversions
         __builtin_amdgcn_sched_group_barrier(0x100, kFN + kSteps * MB, 0);  // LDS reads
         __builtin_amdgcn_sched_group_barrier(0x002, kFirstBlockValu, 0);     // VALU
         static_for<kMfma>([&](auto) {
