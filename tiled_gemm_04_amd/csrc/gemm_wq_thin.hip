@@ -151,23 +151,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wq_window(const void* base, in
                                            static_cast<int>(kBufferFlags));
 }
 
-// Eight int8 codes (two dwords, K order) as 8 bf16, exactly.
-__device__ __forceinline__ bf16x8 codes_to_bf16(i32x2 codes) {
-  float f[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[e] = static_cast<float>(static_cast<int8_t>(static_cast<uint32_t>(codes[0]) >> (8 * e)));
-    f[4 + e] = static_cast<float>(static_cast<int8_t>(static_cast<uint32_t>(codes[1]) >> (8 * e)));
-  }
-  // Upper halves of two fp32 words into one (bytes 2, 3 of a then of b).
-  auto hi2 = [](float a, float b) {
-    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-  };
-  return __builtin_bit_cast(bf16x8, u32x4{hi2(f[0], f[1]), hi2(f[2], f[3]), hi2(f[4], f[5]), hi2(f[6], f[7])});
-}
-
-// Output word o (codes 2o, 2o+1 as two bf16) of codes_to_bf16: two
-// conversions and one permute.
+// Word o of eight int8 codes (two dwords, K order) as bf16, exactly: codes
+// 2o and 2o + 1, each through a sign-extending byte to fp32 conversion, then
+// the upper halves of the two fp32 words in one permute (1.5 vector
+// instructions per code).
 template <int O>
 __device__ __forceinline__ uint32_t codes_pair_bf16(i32x2 codes) {
   const uint32_t w = static_cast<uint32_t>(codes[O >> 1]);
@@ -196,30 +183,12 @@ __device__ __forceinline__ float nibble_q16(uint32_t v) {
 }
 
 // Four bytes of int4 codes (byte e = K values 2e (low nibble), 2e + 1 (high
-// nibble)) as 8 bf16 holding q / 16, exactly: one conversion per code (the
-// high nibbles after one shift of the word), then the upper halves of two
-// fp32 words per permute -- 13 vector instructions per 8 codes (moving each
-// nibble to the top of its byte and converting the sign-extended byte, 16 q,
-// took 15; 2-4 % slower at M = 1 ... 32).
-__device__ __forceinline__ bf16x8 nibbles_to_bf16(uint32_t codes) {
-  const uint32_t hi = codes >> 4;  // byte e's high nibble in its bits 0-3
-  float f[8];
-  f[0] = nibble_q16<0>(codes);
-  f[1] = nibble_q16<0>(hi);
-  f[2] = nibble_q16<1>(codes);
-  f[3] = nibble_q16<1>(hi);
-  f[4] = nibble_q16<2>(codes);
-  f[5] = nibble_q16<2>(hi);
-  f[6] = nibble_q16<3>(codes);
-  f[7] = nibble_q16<3>(hi);
-  auto hi2 = [](float a, float b) {
-    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-  };
-  return __builtin_bit_cast(bf16x8, u32x4{hi2(f[0], f[1]), hi2(f[2], f[3]), hi2(f[4], f[5]), hi2(f[6], f[7])});
-}
-
-// Words 2H and 2H+1 of nibbles_to_bf16(codes) (hi = codes >> 4): four
-// conversions and two permutes.
+// nibble)) are 8 bf16 holding q / 16, exactly: one conversion per code (the
+// high nibbles after one shift of the word, hi = codes >> 4), then the upper
+// halves of two fp32 words per permute -- 13 vector instructions per 8 codes
+// (moving each nibble to the top of its byte and converting the
+// sign-extended byte, 16 q, took 15; 2-4 % slower at M = 1 ... 32).  This
+// gives words 2H and 2H + 1 of the four.
 template <int H>
 __device__ __forceinline__ u32x2 nibble_words(uint32_t codes, uint32_t hi) {
   const float f0 = nibble_q16<2 * H>(codes), f1 = nibble_q16<2 * H>(hi);
@@ -416,140 +385,65 @@ __device__ __forceinline__ void wq_accumulate(const W8Args& p, uint8_t* smem, f3
     // group-unrolled loop below), -1 when it follows from t.
     auto process = [&](int t, int st, auto pos) {
       constexpr int kPos = decltype(pos)::value;
+      static_assert(!kZeroStart || kPos >= 0, "the zero start needs the slice's place in its group");
       const uint8_t* base = smem + st * kStage;
       constexpr int kSteps = kBK / 32;  // 16 x 16 x 32 MFMA steps per slice
-      bf16x8 fb[kSteps][kFN], fx[kSteps][MB];
-      if constexpr (BITS == 4) {
-        // int4: the two conversions of column block j+1 (four parts of two
-        // output words each) spread over the 2 MB MFMAs of block j, fenced
-        // so the compiler keeps them there (4-6 % at 1-32 rows, neutral at
-        // 64, bit-identical).
-        i32x2 qc[kFN];
+      // Operands: the codes of the wave's kFN column blocks (one transposed
+      // read each) and the X rows of every MFMA step.
+      i32x2 qc[kFN];
 #pragma unroll
-        for (int j = 0; j < kFN; ++j) qc[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
+      for (int j = 0; j < kFN; ++j) qc[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
+      bf16x8 fx[kSteps][MB];
 #pragma unroll
-        for (int u = 0; u < kSteps; ++u)
+      for (int u = 0; u < kSteps; ++u)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            fx[u][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[u] + mb * Sh::kXBlock));
-        u32x4 fw[kFN][2];
-        uint32_t hic[kFN][2];
-        auto conv_part = [&](auto jc, auto pc) {  // part p of block j: step p/2, words 2(p%2), +1
-          constexpr int j = decltype(jc)::value, pp = decltype(pc)::value;
-          constexpr int u = pp / 2, h = pp % 2;
+        for (int mb = 0; mb < MB; ++mb)
+          fx[u][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[u] + mb * Sh::kXBlock));
+      // Column block by column block; the conversions of block j+1 are
+      // placed by hand between the MFMAs of block j and fenced there.  Left
+      // to itself the compiler converted all blocks first and issued the
+      // MFMAs in one burst (with both waves of a SIMD in step after each
+      // barrier, one's conversions then rarely ran beside the other's
+      // MFMAs): int8 5-6 % at 64 rows and up to 4 % at 1-32, int4 4-6 % at
+      // 1-32 rows, bit-identical.  fw[j][u]: block j's bf16 operand of step u.
+      u32x4 fw[kFN][kSteps];
+      uint32_t hic[kFN][kSteps];
+      constexpr int kParts = 4;  // conversion parts per block
+      auto conv_part = [&](auto jc, auto pc) {
+        constexpr int j = decltype(jc)::value, pp = decltype(pc)::value;
+        if constexpr (BITS == 8) {
+          fw[j][0][pp] = codes_pair_bf16<pp>(qc[j]);  // word pp of the one step
+        } else {
+          constexpr int u = pp / 2, h = pp % 2;  // step u, words 2h and 2h+1
           const uint32_t c = static_cast<uint32_t>(qc[j][u]);
           if constexpr (h == 0) hic[j][u] = c >> 4;
           const u32x2 w = nibble_words<h>(c, hic[j][u]);
           fw[j][u][2 * h] = w[0];
           fw[j][u][2 * h + 1] = w[1];
-        };
-        static_for<4>([&](auto pc) { conv_part(std::integral_constant<int, 0>{}, pc); });
-        static_for<kFN>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          static_for<kSteps * MB>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            constexpr int u = i / MB, mb = i % MB;
-            TGEMM_SCHED_FENCE();
-            part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[j][u]), fx[u][mb],
-                                                                  part[mb][j], 0, 0, 0);
-            if constexpr (j + 1 < kFN) {
-              static_for<4>([&](auto pc) {
-                constexpr int pp = decltype(pc)::value;
-                if constexpr (pp * kSteps * MB / 4 == i) conv_part(std::integral_constant<int, j + 1>{}, pc);
-              });
-            }
-          });
-        });
-        TGEMM_SCHED_FENCE();
-      } else if constexpr (BITS == 8 && MB >= 3 && kPos >= 0) {
-        // int8 with three or four row blocks, slices straight into LDS: the
-        // MFMAs and the conversions are interleaved by hand (fenced, one
-        // output word of the next column block after each MFMA), since the
-        // compiler otherwise converts all four blocks first and issues the
-        // sixteen MFMAs in one burst (5-6 % of the 64-row head's time).
-        i32x2 qc[kFN];
-#pragma unroll
-        for (int j = 0; j < kFN; ++j) qc[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          fx[0][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[0] + mb * Sh::kXBlock));
-        u32x4 fw[kFN];
-        fw[0] = u32x4{codes_pair_bf16<0>(qc[0]), codes_pair_bf16<1>(qc[0]), codes_pair_bf16<2>(qc[0]),
-                      codes_pair_bf16<3>(qc[0])};
-        static_for<kFN>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          static_for<MB>([&](auto mc) {
-            constexpr int mb = decltype(mc)::value;
-            TGEMM_SCHED_FENCE();
-            part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[j]), fx[0][mb],
-                                                                  kPos == 0 ? f32x4{} : part[mb][j], 0, 0, 0);
-            if constexpr (j + 1 < kFN) {
-              // Word o of block j+1 after MFMA min(o, MB-1) of block j.
-              static_for<4>([&](auto oc) {
-                constexpr int o = decltype(oc)::value;
-                if constexpr ((o < MB - 1 ? o : MB - 1) == mb) fw[j + 1][o] = codes_pair_bf16<o>(qc[j + 1]);
-              });
-            }
-          });
-        });
-        TGEMM_SCHED_FENCE();
-      } else {
-#pragma unroll
-        for (int j = 0; j < kFN; ++j) {
-          const i32x2 q = __builtin_amdgcn_ds_read_tr8_b64_v2i32(TGEMM_LDS(i32x2, base + b_off[j]));
-          if constexpr (BITS == 8) {
-            fb[0][j] = codes_to_bf16(q);
-          } else {
-            fb[0][j] = nibbles_to_bf16(static_cast<uint32_t>(q[0]));
-            fb[1][j] = nibbles_to_bf16(static_cast<uint32_t>(q[1]));
+        }
+      };
+      static_for<kParts>([&](auto pc) { conv_part(std::integral_constant<int, 0>{}, pc); });
+      constexpr int kPerBlock = kSteps * MB;  // MFMAs per column block
+      static_for<kFN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        static_for<kPerBlock>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int u = i / MB, mb = i % MB;
+          TGEMM_SCHED_FENCE();
+          // kZeroStart: a group's first slice starts from zero.
+          part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, fw[j][u]), fx[u][mb],
+              (kZeroStart && kPos == 0 && u == 0) ? f32x4{} : part[mb][j], 0, 0, 0);
+          if constexpr (j + 1 < kFN) {
+            // Part pp of block j+1 after MFMA pp * kPerBlock / kParts of block j.
+            static_for<kParts>([&](auto pc) {
+              constexpr int pp = decltype(pc)::value;
+              if constexpr (pp * kPerBlock / kParts == i) conv_part(std::integral_constant<int, j + 1>{}, pc);
+            });
           }
-        }
-#pragma unroll
-        for (int u = 0; u < kSteps; ++u)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            fx[u][mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + x_rd[u] + mb * Sh::kXBlock));
-        // int8 otherwise: column block by column block, so that the
-        // conversions of block j+1 can run beside the MFMAs of block j.  With
-        // two row blocks the scheduler is also asked to interleave them
-        // (operand reads, block 0's conversions, then one MFMA per few
-        // conversion instructions): measured 2-5 % faster there; with three
-        // row blocks through registers the ordering alone did best.
-        auto mfmas = [&](auto zero_start) {
-          constexpr bool kZero = decltype(zero_start)::value;
-#pragma unroll
-          for (int j = 0; j < kFN; ++j)
-#pragma unroll
-            for (int u = 0; u < kSteps; ++u)
-#pragma unroll
-              for (int mb = 0; mb < MB; ++mb)
-                part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fx[u][mb],
-                                                                      kZero && u == 0 ? f32x4{} : part[mb][j], 0, 0, 0);
-        };
-        if constexpr (kZeroStart && kPos >= 0) {
-          mfmas(std::integral_constant<bool, kPos == 0>{});
-        } else if constexpr (kZeroStart) {
-          if (t % Sh::kSlicesPerGroup == 0 || t == tb)
-            mfmas(std::true_type{});
-          else
-            mfmas(std::false_type{});
-        } else {
-          mfmas(std::false_type{});
-        }
-      }
-      if constexpr (MB == 2 && BITS == 8) {
-        constexpr int kMfma = kSteps * MB * kFN;
-        constexpr int kValuPerMfma = 3;
-        constexpr int kFirstBlockValu = 12;  // one block's conversions
-        __builtin_amdgcn_sched_group_barrier(0x100, kFN + kSteps * MB, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, kFirstBlockValu, 0);     // VALU
-        static_for<kMfma>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU
         });
-      }
-      // (With kZeroStart the partial sums are not cleared, so a slice past
-      // te must not fold them again.)
+      });
+      TGEMM_SCHED_FENCE();
       bool fold_now;
       if constexpr (kPos >= 0)
         fold_now = kPos == Sh::kSlicesPerGroup - 1 || t == te - 1;
