@@ -26,15 +26,17 @@
 //     slices in flight per wave, codes with the non-temporal hint) into two
 //     LDS stages; more rows and the split-K kernel go global -> LDS with
 //     direct buffer loads, six LDS stages deep;
-//   * eight waves (two per SIMD, so one wave's conversions overlap the
-//     other's MFMAs and loads) each own 64 columns over the whole of K.  A
-//     wave's MFMA operand for 16 columns comes from one ds_read_b64_tr_b8
+//   * eight waves (two per SIMD) each own 64 columns over the whole of K.
+//     A wave's MFMA operand for 16 columns comes from one ds_read_b64_tr_b8
 //     (lane i receives column i of 8 byte rows: the 8 K values one
 //     16 x 16 x 32 MFMA takes per lane for int8, those of two MFMAs for
 //     int4); every code becomes a bf16 exactly (a sign-extending byte to fp32
 //     conversion, then the upper half; an int4 code goes through the 4-bit
 //     signed conversion, which gives q / 16, and the 16 goes into the group
-//     scale);
+//     scale).  The conversions of one 16-column block are placed by hand
+//     between the MFMAs of the previous one, so each wave keeps the matrix
+//     unit and the vector unit busy together (the two waves of a SIMD leave
+//     each slice's barrier in step, so they rarely cover each other);
 //   * the MFMAs of a 128-row group accumulate sum_k x * q exactly as an fp32
 //     GEMM would; at the end of the group one FMA per accumulator folds it
 //     in with the column's scale, acc += s * partial -- the same grouped
