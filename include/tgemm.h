@@ -117,7 +117,10 @@ typedef enum {
  * Any alignment is accepted; 16-byte aligned base pointers with strides that
  * are multiples of 8 elements take the vectorised load path.  No workspace
  * is used (gemm_bf16_ex with a workspace may split small-M problems along
- * K).  Returns TGEMM_OK, TGEMM_ERR_INVALID or TGEMM_ERR_LAUNCH.
+ * K).  Operands are used exactly as the bf16 values they hold, subnormals
+ * included (no flush to zero); a NaN in A[i, k] makes row i of C NaN, one in
+ * B[k, j] or bias[j] column j.  Returns TGEMM_OK, TGEMM_ERR_INVALID or
+ * TGEMM_ERR_LAUNCH.
  */
 int gemm_bf16(const void* A, const void* B, const void* bias, void* C,
               int64_t M, int64_t N, int64_t K,
