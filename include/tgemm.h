@@ -448,6 +448,9 @@ int64_t gemm_logsoftmax_workspace_size(int64_t M, int64_t N, int out_dtype);
  * and are summed in chunk order, then the bias and epilogue are applied and
  * the result rounded once (deterministic; the summation order, so the last
  * bits, differ from the unsplit call).
+ * X is used exactly as the bf16 values it holds, subnormals included (no
+ * flush to zero); a NaN in X[i, k] makes row i of C NaN, a NaN in S[g, n]
+ * or bias[n] column n.
  * Supported: M <= 64, K % 8 == 0, N % 4 == 0, ldq % 4 == 0 (others return
  * TGEMM_ERR_UNSUPPORTED).  An unaligned or short non-NULL workspace returns
  * TGEMM_ERR_INVALID.  Returns TGEMM_OK, TGEMM_ERR_INVALID,
