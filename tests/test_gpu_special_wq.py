@@ -8,8 +8,9 @@ and 64 rows (straight into LDS, int8 with the zero start of each group):
 * subnormal activations (exponent field 0) are used exactly: scaled by the
   weights they give normal fp32 outputs, equal to the oracle's at the fp32
   tolerance (a flush to zero would give zeros);
-* a NaN in X[i, k] makes row i of C NaN, a NaN scale S[g, j] column j;
-  everything else stays finite and matches the oracle.
+* a NaN in X[i, k] makes row i of C NaN, a NaN scale S[g, j] or bias
+  entry its column (through the bias + tanh-GeLU epilogue); everything
+  else stays finite and matches the oracle.
 """
 
 import numpy as np
@@ -35,16 +36,17 @@ def _weights(bits, K, N, seed, dev):
     return wl.w8_weights(K, N, seed, dev) if bits == 8 else wl.w4_weights(K, N, seed, dev)
 
 
-def _run(bits, x, q, s):
+def _run(bits, x, q, s, bias=None, epi=tg.EPI_NONE):
     c = torch.empty(x.shape[0], s.shape[1], dtype=torch.float32, device=x.device)
-    (tg.gemm_bf16_w8 if bits == 8 else tg.gemm_bf16_w4)(x, q, s, None, c)
+    (tg.gemm_bf16_w8 if bits == 8 else tg.gemm_bf16_w4)(x, q, s, bias, c, epilogue=epi)
     torch.cuda.synchronize()
     return c.cpu().double().numpy()
 
 
-def _oracle(bits, x, q, s):
+def _oracle(bits, x, q, s, bias=None, epi=tg.EPI_NONE):
     f = og.gemm_bf16_w8_bits if bits == 8 else og.gemm_bf16_w4_bits
-    return f(wl.bits_u16(x), q.cpu().numpy(), s.cpu().numpy())
+    bb = None if bias is None else wl.bits_u16(bias)
+    return f(wl.bits_u16(x), q.cpu().numpy(), s.cpu().numpy(), bb, epi)
 
 
 @pytest.mark.parametrize("bits", [8, 4])
@@ -73,16 +75,20 @@ def test_nan_reaches_its_row_and_column(bits, M):
     N, K = 1040, 512
     x = wl.bf16((M, K), "normal", 1.0, 23, 1, dev)
     q, s = _weights(bits, K, N, 24, dev)
-    i_nan, j_nan = M // 2, 517
+    bias = wl.bf16((N,), "normal", 0.5, 23, 2, dev)
+    i_nan, j_nan, j_bias = M // 2, 517, N - 3
     x[i_nan, 300] = float("nan")
     s[2, j_nan] = float("nan")
+    bias[j_bias] = float("nan")
+    epi = tg.EPI_BIAS_GELU_TANH
     print(f"[gpu] w{bits} NaN M={M} N={N} K={K}", flush=True)
-    got = _run(bits, x, q, s)
+    got = _run(bits, x, q, s, bias, epi)
     mask = np.zeros((M, N), dtype=bool)
     mask[i_nan, :] = True
     mask[:, j_nan] = True
+    mask[:, j_bias] = True
     assert np.isnan(got[mask]).all()
     assert np.isfinite(got[~mask]).all()
-    y, d = _oracle(bits, x, q, s)
+    y, d = _oracle(bits, x, q, s, bias, epi)
     r = og.compare(got[~mask], y[~mask], d[~mask], TOL_F32)
     assert r["ok"], r
