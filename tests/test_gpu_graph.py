@@ -6,8 +6,9 @@ holds the tiled bf16 GEMM with bias + tanh-GeLU, the small-M split-K with a
 caller workspace, the FP8 GEMM with its last round split in a workspace
 (whose arrival counters every call returns to zero), the log-softmax LM
 head, the int8 head split along K in a caller workspace (two launches), the
-FP8 GEMM with its last round as half tiles (no workspace) and the 1 x 128
-FP8 quantiser.  It is replayed four times with eager library calls and host
+FP8 GEMM with its last round as half tiles (no workspace), the 1 x 128
+FP8 quantiser and the allocation-free entry point (the same small-M split in
+the library's fixed scratch).  It is replayed four times with eager library calls and host
 synchronisations in between; every replay must reproduce the eager results
 bit for bit, which in turn are checked against the fp64 oracle.
 """
@@ -71,6 +72,8 @@ def test_captured_sequence_replays_bit_for_bit():
     x7 = wl.bf16((300, 1000), "normal", 1.0, 145, 1, dev)
     q7 = torch.empty(300, 1000, dtype=torch.uint8, device=dev)
     s7 = torch.empty(300, 8, dtype=torch.float32, device=dev)
+    # the allocation-free entry point on the small-M split's inputs
+    c8 = torch.empty(8, 4096, dtype=torch.float32, device=dev)
 
     def calls():
         tg.gemm_bf16(a1, b1, bias1, c1, epilogue=tg.EPI_BIAS_GELU_TANH)
@@ -80,8 +83,9 @@ def test_captured_sequence_replays_bit_for_bit():
         tg.gemm_bf16_w8(x5, q5, s5, None, c5, workspace=ws5)
         tg.gemm_fp8_blockscaled(qa6, sa6, qb6, sb6, c6)
         tg.quantize_fp8_1x128(x7, q7, s7)
+        tg.gemm_bf16_noalloc(a2, b2, None, c8)
 
-    outs = (c1, c2, c3, c4, c5, c6, q7, s7)
+    outs = (c1, c2, c3, c4, c5, c6, q7, s7, c8)
     calls()
     torch.cuda.synchronize()
     eager = [_bits(c) for c in outs]
@@ -99,6 +103,8 @@ def test_captured_sequence_replays_bit_for_bit():
     assert og.compare(c5.cpu().double().numpy(), y, d, 1e-5)["ok"]
     y, d = og.gemm_fp8_blockscaled_bits(wl.bits_u8(qa6), sa6.cpu().numpy(), wl.bits_u8(qb6), sb6.cpu().numpy())
     assert og.compare(c6.float().cpu().double().numpy(), y, d, 1.5e-2)["ok"]
+    y, d = og.gemm_bf16_bits(wl.bits_u16(a2), wl.bits_u16(b2))
+    assert og.compare(c8.cpu().double().numpy(), y, d, 1e-5)["ok"]
     rq, rs = oq.quantise_rows_1x128(x7.float().cpu().numpy())
     assert (q7.cpu().numpy() == rq).all() and (s7.cpu().numpy().view("u4") == rs.view("u4")).all()
 
